@@ -1,0 +1,104 @@
+"""Write the frozen codebook and rotation artifacts — oracle (test infrastructure only).
+
+Runs only the oracle's offline construction (FibQuant summary §2.2) and writes,
+for each (k, N) the workloads use, an ``.npz`` with the fp32 codewords
+(fp16-representable) plus the construction parameters, and the shared
+rotation Π (d = 64, seed 0; §1 / §2.1).  A MANIFEST.json records every file's
+sha256 so the tests can detect drift.  Lloyd uses multithreaded BLAS, so a
+rebuild on another machine may differ in the last bits; the committed files are
+the reference.
+
+Usage:  python -m oracle.build_codebooks [--only k,N] [--out DIR]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import time
+
+import numpy as np
+
+from .codebook import build_codebook
+from .rotation import shared_rotation
+
+D = 64
+# (k, N, seed, samples, max_iter) for the workloads' codebooks.
+SPECS = [
+    (2, 16, 201, None, 100),
+    (4, 256, 202, None, 100),
+    (8, 4096, 203, None, 60),
+    (64, 4096, 204, 64 * 4096, 30),
+]
+DEFAULT_OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "universal_vector_quantization_amd", "codebooks")
+
+
+def codebook_filename(k: int, N: int, d: int = D) -> str:
+    return f"fq_d{d}_k{k}_n{N}.npz"
+
+
+def sha256_file(path: str) -> str:
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def manifest_entry(path: str) -> dict:
+    """Manifest record of one artifact, read back from the file itself."""
+    z = np.load(path, allow_pickle=False)
+    e = {"sha256": sha256_file(path), "d": int(z["d"])}
+    if "codewords" in z.files:
+        k, N = int(z["k"]), int(z["N"])
+        e.update({"k": k, "N": N, "seed": int(z["seed"]), "samples": int(z["samples"]),
+                  "restarts": int(z["restarts"]), "valid_mse": float(z["valid_mse"]),
+                  "normalised_mse": float(z["valid_mse"]) / (k / int(z["d"])),
+                  "restart_valid_mse": [float(v) for v in z["restart_valid_mse"]],
+                  "iterations": int(len(z["history"]) - 1)})
+    else:
+        e["seed"] = int(z["seed"])
+    return e
+
+
+def write_manifest(out: str) -> None:
+    """(Re)write MANIFEST.json from every artifact present in ``out``."""
+    man = {}
+    for name in sorted(os.listdir(out)):
+        if name.endswith(".npz"):
+            man[name] = manifest_entry(os.path.join(out, name))
+    with open(os.path.join(out, "MANIFEST.json"), "w") as f:
+        json.dump(man, f, indent=1, sort_keys=True)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", default=None, help="k,N of one codebook to build")
+    ap.add_argument("--out", default=DEFAULT_OUT)
+    ap.add_argument("--no-rotation", action="store_true")
+    ap.add_argument("--manifest-only", action="store_true")
+    args = ap.parse_args()
+    os.makedirs(args.out, exist_ok=True)
+    if args.manifest_only:
+        write_manifest(args.out)
+        return
+    if not args.no_rotation:
+        path = os.path.join(args.out, "rotation_d64_seed0.npz")
+        np.savez(path, rotation=shared_rotation(D, 0), d=D, seed=0)
+    for k, N, seed, samples, max_iter in SPECS:
+        if args.only and args.only != f"{k},{N}":
+            continue
+        t0 = time.time()
+        cb = build_codebook(D, k, N, seed, restarts=3, samples=samples, max_iter=max_iter, rel_tol=1e-6)
+        path = os.path.join(args.out, codebook_filename(k, N))
+        np.savez(path, codewords=cb.codewords, d=D, k=k, N=N, seed=seed, law=cb.law, restarts=cb.restarts,
+                 samples=cb.samples, valid_mse=cb.valid_mse, restart_valid_mse=np.array(cb.restart_valid_mse),
+                 history=np.array(cb.history))
+        print(f"k={k} N={N}: valid MSE {cb.valid_mse:.6g} (normalised {cb.normalised_mse:.4f}), "
+              f"{len(cb.history) - 1} iterations, {time.time() - t0:.1f}s", flush=True)
+    write_manifest(args.out)
+
+
+if __name__ == "__main__":
+    main()
