@@ -1,0 +1,247 @@
+"""Benchmark of the FibQuant hot path on one MI355X.
+
+A step is one pass of the whole hot path over the GPT-2-small-shaped KV
+workload (294,912 fp16 vectors = 12 layers x 12 heads x 1024 tokens x {K, V},
+d = 64, codebook k = 4, N = 256, b = 2 bits per coordinate):
+
+    fq_encode   all 294,912 vectors -> fixed-address codes + fp16 norms
+    fq_decode   all codes -> fp16 reconstructions
+    fq_attn_decode  one decode query per (layer, head) over the encoded cache
+                (layers act as the batch, 12 query heads on 12 KV heads,
+                T = 1024) straight from the codes
+
+Inputs are resident in HBM before timing starts.  The metric is KV vectors per
+second through the step (fp16-equivalent GB/s = vectors/s x 128 B).  Per-kernel
+times come from HIP events on the stream the library launches on.  The
+decode-attention workload (B=16, 32 query heads on 4 KV heads, T=32768) is
+timed separately with the last-level cache flushed before every launch, and
+reported against the HBM roofline.  The CPU oracle is timed on a bounded sample
+(rank 0, one GPU only).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV vectors/sec encode+decode (GB/s fp16-equiv) and fused-attn GB/s; % roofline"
+HBM_PEAK_GBPS = 8000.0
+# Non-packed fp32 / fp64 FMA issue rate of the chip: 256 CUs x 64 lanes x 2 flop x 2.4 GHz.
+VALU_FMA_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+D = 64
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--attn-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-attn-workload", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "universal_vector_quantization_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(kernel)
+    if not rec or rec.get("source_sha") != source_sha(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s: float = 20.0):
+    """The oracle as it stands, on a bounded sample of the same step."""
+    import workloads
+    from oracle import attention as oatt
+    from oracle import codec as oc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    import universal_vector_quantization_amd as fq
+
+    cw, rot = fq.load_artifact(4, 256)
+    x = workloads.gpt2_small_kv()
+    n_s = 2048
+    t0 = time.perf_counter()
+    enc = oc.encode(x[:n_s], rot, cw, np.float16)
+    t_enc = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oc.round_output(oc.decode(enc.codes, enc.norms, rot, cw), np.float16)
+    t_dec = time.perf_counter() - t0
+    # attention: one (layer, head) query over its 1024 keys and 1024 values
+    T = workloads.GPT2_T
+    kx = x[:T]
+    vx = x[len(x) // 2: len(x) // 2 + T]
+    ke = oc.encode(kx, rot, cw, np.float16)
+    ve = oc.encode(vx, rot, cw, np.float16)
+    q = workloads.gpt2_small_queries()[:1, :1]
+    t0 = time.perf_counter()
+    oatt.attention(q, ke.codes.reshape(1, 1, T, 16), ke.norms.reshape(1, 1, T), ve.codes.reshape(1, 1, T, 16),
+                   ve.norms.reshape(1, 1, T), rot, cw, 0.125)
+    t_att = time.perf_counter() - t0
+    per_vec = t_enc / n_s + t_dec / n_s + t_att / (2 * T)
+    return {"value": 1.0 / per_vec, "unit": "vectors/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle encode+decode of the first {n_s} of the 294912 vectors plus attention of one "
+                      f"(layer, head) query over its {T} keys/values; per-vector times summed "
+                      f"(encode {t_enc:.2f}s, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+    import torch
+
+    import universal_vector_quantization_amd as fq
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- headline workload
+    w = workloads.WORKLOADS["gpt2s_kv"]
+    cb = fq.Codebook.from_artifact(w.k, w.N)
+    x_np = workloads.gpt2_small_kv(w.seed)
+    n = len(x_np)
+    x = torch.from_numpy(x_np).to(dev)
+    codes = torch.empty(cb.code_bytes(n), dtype=torch.uint8, device=dev)
+    norms = torch.empty(n, dtype=torch.float16, device=dev)
+    xr = torch.empty_like(x)
+    L, H, T = workloads.GPT2_L, workloads.GPT2_H, workloads.GPT2_T
+    q = torch.from_numpy(workloads.gpt2_small_queries()).to(dev)
+    half_bytes = cb.code_bytes(n // 2)
+    k_codes, v_codes = codes[:half_bytes], codes[half_bytes:]
+    k_norms, v_norms = norms[: n // 2], norms[n // 2:]
+    attn_out = torch.empty((L, H, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T), 16), dtype=torch.uint8, device=dev)
+
+    ev = {k: [] for k in ("enc", "dec", "att")}
+
+    def step(record: bool):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        fq.fq_encode(cb.handle, x, codes, norms, stream)
+        if record:
+            e[1].record(stream)
+        fq.fq_decode(cb.handle, codes, norms, xr, stream)
+        if record:
+            e[2].record(stream)
+        fq.fq_attn_decode(cb.handle, q, k_codes, k_norms, v_codes, v_norms, L, H, H, T, 0.125, attn_out, ws, stream)
+        if record:
+            e[3].record(stream)
+            ev["enc"].append((e[0], e[1]))
+            ev["dec"].append((e[1], e[2]))
+            ev["att"].append((e[2], e[3]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    ms_step = elapsed * 1e3 / args.steps
+    value = n * args.steps / elapsed
+
+    # dominant kernel roofline: the encoder's brute-force search (fp32 FMAs) and fp64 rotation
+    flops_per_vec = 2 * D * w.N + 2 * D * D
+    enc_s = ms["enc"] / 1e3
+    achieved = flops_per_vec * n / enc_s / 1e12
+    enc_bytes = n * (D * 2 + 2) + cb.code_bytes(n)
+    dec_bytes = enc_bytes
+    att_bytes = 2 * cb.code_bytes(n // 2) + 2 * (n // 2) * 2 + L * H * D * 2 + L * H * D * 4
+    traffic = measured_traffic("encode_valu_k4", "fq_encode.hip")
+    line = {
+        "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "gpt2s_kv", "vectors": n, "layout": "[2 KV][12 layers][12 heads][1024 tokens][64]",
+                   "input_dtype": "f16", "d": D, "k": w.k, "N": w.N, "bits_per_coordinate": np.log2(w.N) / w.k,
+                   "step": "fq_encode + fq_decode + fq_attn_decode(B=12 layers, Hq=Hkv=12, T=1024)"},
+        "fp16_equiv_GBps": value * D * 2 / 1e9,
+        "breakdown_us": {"encode": ms["enc"] * 1e3, "decode": ms["dec"] * 1e3, "attention": ms["att"] * 1e3},
+        "breakdown_GBps": {"encode": enc_bytes / (ms["enc"] / 1e3) / 1e9,
+                           "decode": dec_bytes / (ms["dec"] / 1e3) / 1e9,
+                           "attention": att_bytes / (ms["att"] / 1e3) / 1e9},
+        "roofline": {"kernel": "encode_valu<k=4> (fq_encode)", "bound": "alu", "achieved": achieved,
+                     "peak": VALU_FMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / VALU_FMA_PEAK_TFLOPS,
+                     "traffic": traffic,
+                     "work": f"{flops_per_vec} flop/vector (2dN search multiply-adds + 2d^2 rotation) x {n}"},
+    }
+
+    # ---------------------------------------------------------------- decode-attention workload
+    if not args.no_attn_workload:
+        B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+        qa_np, kv_np = workloads.attention_inputs()
+        kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
+        na = B * Hkv * Ta
+        ac = torch.empty(2 * cb.code_bytes(na), dtype=torch.uint8, device=dev)
+        an = torch.empty(2 * na, dtype=torch.float16, device=dev)
+        fq.fq_encode(cb.handle, kv, ac, an, stream)
+        del kv
+        qa = torch.from_numpy(qa_np).to(dev)
+        ao = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        aws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, Ta), dtype=torch.uint8, device=dev)
+        kcs, vcs = ac[: cb.code_bytes(na)], ac[cb.code_bytes(na):]
+        kns, vns = an[:na], an[na:]
+        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        times = []
+        for it in range(args.attn_iters + 3):
+            flush.fill_(it & 0xff)  # evict L2 and the 256 MB last-level cache
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fq.fq_attn_decode(cb.handle, qa, kcs, kns, vcs, vns, B, Hq, Hkv, Ta, 0.125, ao, aws, stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if it >= 3:
+                times.append(e0.elapsed_time(e1))
+        t_att = float(np.median(times)) / 1e3
+        abytes = 2 * cb.code_bytes(na) + 2 * na * 2 + B * Hq * D * 2 + B * Hq * D * 4
+        line["attn_b16_t32k"] = {
+            "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms, cache flushed per launch",
+            "us_per_step": t_att * 1e6, "hbm_bytes": abytes, "GBps": abytes / t_att / 1e9,
+            "fp16_equiv_GBps": 2 * na * D * 2 / t_att / 1e9,
+            "roofline": {"bound": "hbm", "achieved": abytes / t_att / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": abytes / t_att / 1e9 / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("attn_split_k4", "fq_attn.hip")},
+        }
+        del flush
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    cb.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,136 @@
+/*
+ * fq.h — C ABI of the FibQuant KV-cache codec for AMD MI355X (gfx950).
+ *
+ * Method: "FibQuant: universal vector quantisation for random-access KV-cache
+ * compression", technical summary on gist.science (paper 2605.11478, Korean and
+ * Dutch pages with the same section numbers).
+ *
+ *   encode (§2.3): store the norm nu = ||x||_2, rotate the unit vector Pi x / nu
+ *                  with one shared Haar rotation, split it into d/k blocks of k
+ *                  consecutive coordinates and store, for every block, the index
+ *                  of its nearest codeword in one shared codebook of N words.
+ *   decode (§2.3): gather the codewords, concatenate the blocks, apply the
+ *                  inverse rotation and scale by the norm.
+ *   rate   (§2.3, §3.3): b = log2(N)/k bits per coordinate.
+ *   store  (§1):   fixed-rate codes at fixed addresses, so every vector decodes
+ *                  alone by address arithmetic.
+ *   attention (§5): the fixed addresses let decompression be fused into
+ *                  attention: q.k_j = nu_j (Pi q).c_j straight from the codes.
+ *
+ * Conventions shared by every call
+ *   - d = 64.  k divides d (1, 2, 4, 8, 16, 32 or 64).  N is a power of two,
+ *     2 <= N <= 65536.  Every codeword coordinate must be exactly representable
+ *     as an fp16 normal number or zero (the offline construction rounds to that
+ *     grid), so matrix units can use the codewords exactly.
+ *   - Rotation: row-major d x d fp32 matrix Pi with y = Pi x.
+ *   - Code store: B = (d/k) * log2(N) bits per vector; vector i starts at bit
+ *     i*B, its block j at bit i*B + j*log2(N); bits are LSB-first inside
+ *     little-endian bytes; the store holds ceil(n*B/8) bytes and pad bits are 0.
+ *   - Nearest codeword: the minimum of sum_i (y_i - c_i)^2 with y the exactly
+ *     rotated unit vector; among exactly equal distances the lowest index.  The
+ *     device search runs in fp32 and certifies every result against a rigorous
+ *     fp32 error bound; blocks it cannot certify are searched again in fp64.
+ *   - Norms: nu is accumulated in fp64 and stored round-to-nearest-even in the
+ *     norm dtype directly from fp64 (fp16 overflow stores +inf).  nu = 0 gives
+ *     the all-smallest-norm codes and decodes to exactly 0.
+ *   - Memory: every bulk pointer is caller-owned device memory on the device
+ *     that was current at fq_codebook_load, 16-byte aligned.  Inputs are only
+ *     read, outputs only written.  Nothing here allocates except
+ *     fq_codebook_load.
+ *   - Asynchrony: fq_encode, fq_decode and fq_attn_decode only enqueue work on
+ *     `stream` (a hipStream_t; NULL is the default stream) and return; they
+ *     never synchronise and never read results back.
+ *   - Errors: arguments are checked on the host before any launch and return
+ *     FQ_ERR_ARG / FQ_ERR_UNSUPPORTED / FQ_ERR_WORKSPACE with nothing enqueued;
+ *     a failed launch returns FQ_ERR_HIP.  No call aborts or throws.  n = 0 (or
+ *     T = 0 keys) is a no-op that returns FQ_OK.  NaN or Inf inputs give
+ *     unspecified codes.
+ */
+#ifndef FQ_H
+#define FQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct fq_codebook fq_codebook; /* opaque; immutable after load */
+
+typedef enum fq_status {
+  FQ_OK = 0,
+  FQ_ERR_ARG = 1,         /* null pointer, bad size, misaligned pointer, wrong device, bad codebook values */
+  FQ_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  FQ_ERR_WORKSPACE = 3,   /* attention workspace missing or too small */
+  FQ_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} fq_status;
+
+typedef enum fq_dtype { FQ_F32 = 0, FQ_F16 = 1 } fq_dtype;
+
+/* Load a codebook and the shared rotation (FibQuant summary §2.1 shared
+ * rotation, §2.2 shared offline codebook) onto the current HIP device.
+ *   codewords: host fp32 [N][k], fp16-representable values (see above).
+ *   rotation:  host fp32 [d][d] row-major, y = Pi x.
+ *   out:       receives the handle; free it with fq_codebook_free.
+ * Synchronous.  Allocates under 2 MiB of device memory that the handle owns.
+ * Returns FQ_ERR_ARG for bad sizes or values, FQ_ERR_UNSUPPORTED for d != 64,
+ * FQ_ERR_HIP if an allocation or copy fails (nothing is leaked). */
+fq_status fq_codebook_load(int d, int k, int N, const float* codewords, const float* rotation,
+                           fq_codebook** out);
+
+/* Release a handle from fq_codebook_load (NULL is ignored).  The caller must
+ * make sure no enqueued work still uses it. */
+void fq_codebook_free(fq_codebook* cb);
+
+/* Bytes of the fixed-address code store for n vectors: ceil(n * B / 8)
+ * (FibQuant summary §1, §2.3).  Returns -1 for a NULL handle or n < 0. */
+int64_t fq_code_bytes(const fq_codebook* cb, int64_t n);
+
+/* Encode n vectors (FibQuant summary §2.3 encoder).
+ *   x:      device [n][d] in x_dtype (FQ_F32 or FQ_F16), row-major.
+ *   codes:  device, fq_code_bytes(cb, n) bytes, written completely (pad bits 0).
+ *   norms:  device [n] in norm_dtype.
+ * Codes equal the exact nearest codeword (lowest index on exact ties) for
+ * every block; see the conventions above for how that is guaranteed. */
+fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
+                    void* norms, fq_dtype norm_dtype, void* stream);
+
+/* Decode n vectors (FibQuant summary §2.3 decoder): x_out = nu * Pi^T concat(c).
+ *   codes:  device, fq_code_bytes(cb, n) bytes.  norms: device [n] in norm_dtype.
+ *   x_out:  device [n][d] in out_dtype, each value rounded once (RNE) from an
+ *           fp32 accumulation. */
+fq_status fq_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
+                    int64_t n, void* x_out, fq_dtype out_dtype, void* stream);
+
+/* Workspace bytes fq_attn_decode needs for these sizes (0 when T = 0;
+ * 0 as well for a NULL handle or invalid sizes). */
+size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
+
+/* Decode-step attention over a compressed cache (FibQuant summary §5: fixed
+ * addresses allow decompression fused into attention).  For every batch b and
+ * query head h, with KV head g = h / (Hq/Hkv):
+ *     out[b][h] = sum_j softmax_j(scale * q[b][h] . k_j) v_j
+ * where k_j, v_j are the decoded keys / values of (b, g), computed straight
+ * from the codes as nu_j Pi^T c_j without materialising them.
+ *   q:        device fp16 [B][Hq][d].
+ *   k_codes, v_codes: device code stores of B*Hkv*T vectors in [B][Hkv][T] order
+ *             (exactly what fq_encode writes for a [B][Hkv][T][d] tensor).
+ *   k_norms, v_norms: device fp16 [B][Hkv][T].
+ *   out:      device fp32 [B][Hq][d].
+ *   workspace: device, at least fq_attn_workspace_bytes(...) bytes.
+ * Hq must be a multiple of Hkv with Hq/Hkv <= 16, and the codebook must fit
+ * N*k <= 32768 (its fp16 copy lives in LDS); otherwise FQ_ERR_UNSUPPORTED.
+ * There is no mask: the single query attends to all T keys. */
+fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                         const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,
+                         float scale, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* fq_status_string(fq_status st);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQ_H */

@@ -1,0 +1,42 @@
+// Device helpers used by several kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fq {
+
+// Round a double to the nearest fp16 value, ties to even, in one step (no
+// detour through fp32, whose double rounding can differ).  Returns the fp16
+// bit pattern; |v| >= 65520 gives +-inf, NaN gives a quiet NaN.
+__device__ inline uint16_t f64_to_f16_bits(double v) {
+  uint64_t u = __double_as_longlong(v);
+  uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  double a = fabs(v);
+  if (!(a == a)) return (uint16_t)(sign | 0x7e00u);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
+  if (a < 6.103515625e-05) {  // below 2^-14: subnormal grid, spacing 2^-24
+    double r = rint(a * 16777216.0);  // exact scaling; rint rounds half to even
+    return (uint16_t)(sign | (uint16_t)r);  // r == 1024 is the smallest normal
+  }
+  int e = (int)((u >> 52) & 0x7ff) - 1023;       // a is a normal double here
+  double q = ldexp(a, 10 - e);                    // in [1024, 2048), exact
+  double r = rint(q);
+  if (r >= 2048.0) { r = 1024.0; e += 1; }
+  if (e > 15) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+// Read one `bits`-wide code (bits <= 16) that starts at bit `bitoff` of an
+// LSB-first little-endian bitstream.  Touches only the bytes the code spans.
+__device__ inline uint32_t load_code(const uint8_t* __restrict__ p, int64_t bitoff, int bits) {
+  int64_t byte = bitoff >> 3;
+  int sh = (int)(bitoff & 7);
+  uint32_t v = p[byte];
+  int need = sh + bits;
+  if (need > 8) v |= (uint32_t)p[byte + 1] << 8;
+  if (need > 16) v |= (uint32_t)p[byte + 2] << 16;
+  return (v >> sh) & ((1u << bits) - 1u);
+}
+
+}  // namespace fq

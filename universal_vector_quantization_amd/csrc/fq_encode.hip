@@ -1,0 +1,271 @@
+// FibQuant encoder (FibQuant summary §2.3): norm, rotation, d/k blocks of k
+// consecutive coordinates, nearest codeword per block, fixed-address packing
+// (§1).  One lane owns one vector.
+//
+// Precision plan (the codes must be the exact nearest codewords):
+//   * nu and y = Pi x / nu are computed in fp64 (products of fp32 Pi entries and
+//     fp16/fp32 inputs are exact in fp64), then y is rounded to fp32.
+//   * Search: score_n = ||c_n||^2 - 2 y_b . c_n with an fp32 FMA chain; each lane
+//     keeps the best and second-best score and the best index per block.
+//   * Certificate: every fp32 score is within E_b of the exact score, with
+//       E_b = 1.01 (k+2) 2^-24 (max||c||^2 + 2 ||y_b|| max||c||)
+//     (k FMA roundings, the rounding of ||c||^2 and of y, first order).  If
+//     second - best > 2 E_b the fp32 winner is the exact unique minimiser.
+//   * Otherwise the block is searched again in fp64 with the direct distance
+//     sum_t (y_t - c_t)^2, lowest index on exact ties.
+#include "fq_device.h"
+#include "fq_internal.h"
+
+namespace fq {
+namespace {
+
+constexpr int D = kD;
+constexpr int WG = 256;
+
+template <bool F16>
+__device__ inline void load_row(const void* __restrict__ xv, int64_t i, float (&xf)[D]) {
+  if constexpr (F16) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const _Float16*>(xv) + i * D);
+#pragma unroll
+    for (int q = 0; q < D / 8; q++) {
+      uint4 w = p[q];
+      uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int h = 0; h < 4; h++) {
+        xf[8 * q + 2 * h] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[h] & 0xffffu));
+        xf[8 * q + 2 * h + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[h] >> 16));
+      }
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(xv) + i * D);
+#pragma unroll
+    for (int q = 0; q < D / 4; q++) {
+      float4 w = p[q];
+      xf[4 * q] = w.x;
+      xf[4 * q + 1] = w.y;
+      xf[4 * q + 2] = w.z;
+      xf[4 * q + 3] = w.w;
+    }
+  }
+}
+
+template <int K, bool XF16, bool NF16>
+__global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, int64_t n,
+                                                  const float* __restrict__ cw, const float* __restrict__ cn2,
+                                                  const double* __restrict__ pi64t, int N, int bits, float cmax,
+                                                  float c2max, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+  constexpr int NB = D / K;
+  constexpr int PK_WORDS = 2 * NB * 16;  // 64 lanes * B bits / 32, for bits <= 16
+  __shared__ uint32_t pk[WG / 64][PK_WORDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+  const bool valid = i < n;
+  const int B = NB * bits;
+
+  // ---- norm and fp64 rotation
+  float xf[D];
+  if (valid) {
+    load_row<XF16>(xv, i, xf);
+  } else {
+#pragma unroll
+    for (int j = 0; j < D; j++) xf[j] = 0.f;
+  }
+  double nu2 = 0.0;
+#pragma unroll
+  for (int j = 0; j < D; j++) nu2 = fma((double)xf[j], (double)xf[j], nu2);
+  const double nu = sqrt(nu2);
+  const double inv = nu > 0.0 ? 1.0 / nu : 0.0;
+
+  float m2y[D];  // -2 y in fp32 (exact doubling of the rounded y)
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    double acc[D / 2];
+#pragma unroll
+    for (int r = 0; r < D / 2; r++) acc[r] = 0.0;
+#pragma unroll
+    for (int j = 0; j < D; j++) {
+      const double xj = (double)xf[j];
+#pragma unroll
+      for (int r = 0; r < D / 2; r++) acc[r] = fma(pi64t[j * D + p * (D / 2) + r], xj, acc[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < D / 2; r++) m2y[p * (D / 2) + r] = -2.0f * (float)(acc[r] * inv);
+  }
+
+  // ---- fp32 search with best / second-best per block
+  float m1[NB], m2[NB];
+  int ix[NB];
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    m1[b] = __builtin_huge_valf();
+    m2[b] = __builtin_huge_valf();
+    ix[b] = 0;
+  }
+  for (int nn = 0; nn < N; nn++) {
+    float c[K];
+#pragma unroll
+    for (int t = 0; t < K; t++) c[t] = cw[nn * K + t];
+    const float cn = cn2[nn];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      float s = cn;
+#pragma unroll
+      for (int t = 0; t < K; t++) s = fmaf(m2y[b * K + t], c[t], s);
+      m2[b] = __builtin_amdgcn_fmed3f(m1[b], m2[b], s);
+      const bool lt = s < m1[b];
+      ix[b] = lt ? nn : ix[b];
+      m1[b] = lt ? s : m1[b];
+    }
+  }
+
+  // ---- certificate: blocks whose fp32 winner is not provably exact
+  const double u = 5.9604644775390625e-08;  // 2^-24
+  uint64_t unsure = 0;
+#pragma unroll
+  for (int b = 0; b < NB; b++) {
+    float yn2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < K; t++) yn2 = fmaf(m2y[b * K + t], m2y[b * K + t], yn2);
+    const double yn = 0.5 * sqrt((double)yn2) * 1.01;  // ||y_b||, rounded up
+    const double E = 1.01 * (K + 2) * u * ((double)c2max + 2.0 * yn * (double)cmax);
+    if (!(((double)m2[b] - (double)m1[b]) > 2.0 * E)) unsure |= 1ull << b;
+  }
+  if (!valid) unsure = 0;
+
+  // ---- norm store (fp64 -> storage dtype, one rounding)
+  if (valid) {
+    if constexpr (NF16)
+      reinterpret_cast<uint16_t*>(norms)[i] = f64_to_f16_bits(nu);
+    else
+      reinterpret_cast<float*>(norms)[i] = (float)nu;
+  }
+
+  // ---- pack this wave's 64 records (64*B bits, dword aligned) through LDS
+  for (int w = lane; w < 2 * B; w += 64) pk[wave][w] = 0u;
+  __syncthreads();
+  const uint32_t cmask = (1u << bits) - 1u;
+  if (valid) {
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      const uint32_t code = (uint32_t)ix[b];
+      const int bo = lane * B + b * bits;
+      const int sh = bo & 31;
+      atomicOr(&pk[wave][bo >> 5], code << sh);
+      if (sh + bits > 32) atomicOr(&pk[wave][(bo >> 5) + 1], code >> (32 - sh));
+    }
+  }
+
+  // ---- fp64 direct-distance search of the uncertified blocks; patch their bits
+  if (unsure) {
+    float xr[D];
+    load_row<XF16>(xv, i, xr);
+    while (unsure) {
+      const int b = __builtin_ctzll(unsure);
+      unsure &= unsure - 1;
+      double yb[K];
+#pragma unroll
+      for (int t = 0; t < K; t++) {
+        double a = 0.0;
+#pragma unroll
+        for (int j = 0; j < D; j++) a = fma(pi64t[j * D + b * K + t], (double)xr[j], a);
+        yb[t] = a * inv;
+      }
+      double best = __builtin_huge_val();
+      uint32_t bi = 0;
+      for (int nn = 0; nn < N; nn++) {
+        double dd = 0.0;
+#pragma unroll
+        for (int t = 0; t < K; t++) {
+          const double df = yb[t] - (double)cw[nn * K + t];
+          dd = fma(df, df, dd);
+        }
+        if (dd < best) {
+          best = dd;
+          bi = (uint32_t)nn;
+        }
+      }
+      const int bo = lane * B + b * bits;
+      const int sh = bo & 31;
+      atomicAnd(&pk[wave][bo >> 5], ~(cmask << sh));
+      atomicOr(&pk[wave][bo >> 5], bi << sh);
+      if (sh + bits > 32) {
+        atomicAnd(&pk[wave][(bo >> 5) + 1], ~(cmask >> (32 - sh)));
+        atomicOr(&pk[wave][(bo >> 5) + 1], bi >> (32 - sh));
+      }
+    }
+  }
+  __syncthreads();
+  const int64_t v0 = i - lane;
+  if (v0 < n) {
+    const int64_t nv = (n - v0) < 64 ? (n - v0) : 64;
+    const int64_t nbytes = (nv * B + 7) / 8;
+    uint8_t* dst = codes + (v0 / 64) * (int64_t)(8 * B);
+    const int nfull = (int)(nbytes / 4);
+    for (int w = lane; w < nfull; w += 64) reinterpret_cast<uint32_t*>(dst)[w] = pk[wave][w];
+    const int rem = (int)(nbytes - 4 * (int64_t)nfull);
+    if (lane < rem) dst[4 * nfull + lane] = (uint8_t)((pk[wave][nfull] >> (8 * lane)) & 0xffu);
+  }
+}
+
+}  // namespace
+
+// Launcher for one block size; each K is instantiated in its own translation
+// unit (compiled with -DFQ_ONLY_K=K) so the build can run in parallel.
+template <int K>
+hipError_t launch_encode_k(const fq_codebook* cb, const void* x, fq_dtype xd, int64_t n, uint8_t* codes,
+                           void* norms, fq_dtype nd, hipStream_t s) {
+  const dim3 grid((unsigned)((n + WG - 1) / WG)), block(WG);
+  const bool xf16 = xd == FQ_F16, nf16 = nd == FQ_F16;
+#define FQ_ENC(XF, NF)                                                                                          \
+  hipLaunchKernelGGL((encode_valu<K, XF, NF>), grid, block, 0, s, x, n, cb->cw, cb->cn2, cb->pi64t, cb->N,     \
+                     cb->bits, cb->cmax, cb->c2max, codes, norms)
+  if (xf16 && nf16)
+    FQ_ENC(true, true);
+  else if (xf16)
+    FQ_ENC(true, false);
+  else if (nf16)
+    FQ_ENC(false, true);
+  else
+    FQ_ENC(false, false);
+#undef FQ_ENC
+  return hipGetLastError();
+}
+
+#ifdef FQ_ONLY_K
+template hipError_t launch_encode_k<FQ_ONLY_K>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*, void*,
+                                               fq_dtype, hipStream_t);
+#else
+extern template hipError_t launch_encode_k<1>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<2>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<4>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<8>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<16>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<32>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+extern template hipError_t launch_encode_k<64>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
+                                                 void*, fq_dtype, hipStream_t);
+
+hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
+                         void* norms, fq_dtype norm_dtype, hipStream_t s) {
+  switch (cb->k) {
+    case 1: return launch_encode_k<1>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 2: return launch_encode_k<2>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 4: return launch_encode_k<4>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 8: return launch_encode_k<8>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 16: return launch_encode_k<16>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 32: return launch_encode_k<32>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 64: return launch_encode_k<64>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+#endif
+
+}  // namespace fq
