@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--attn-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-workload", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -124,6 +126,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale factor between counter readings and bytes moved.
+        nbytes = 256 * 1024 * 1024
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
+        return
 
     # ---------------------------------------------------------------- headline workload
     w = workloads.WORKLOADS["gpt2s_kv"]
