@@ -197,3 +197,69 @@ def test_decode_of_oracle_encode_roundtrip(dev):
     xs = x.astype(np.float64)
     nmse = np.sum((got.astype(np.float64) - xs) ** 2) / np.sum(xs ** 2)
     assert 0.05 < nmse < 0.15
+
+
+# ------------------------------------------------------------------ the generic one-lane-per-vector encoder
+@pytest.mark.parametrize("k,N,n", [(4, 256, 3000 + 7), (8, 4096, 1500 + 3)])
+def test_encode_valu_kernel_parity(dev, k, N, n):
+    # k = 4 and 8 normally run on the matrix-core encoder; FQ_ENCODE_KERNEL=valu at
+    # load time selects the generic kernel, which must meet the same bar.
+    import os
+
+    cw, rot = artifact_or_skip(k, N)
+    os.environ["FQ_ENCODE_KERNEL"] = "valu"
+    try:
+        cbv = fq.Codebook(cw, rot)
+    finally:
+        del os.environ["FQ_ENCODE_KERNEL"]
+    x = workloads.tinyllama_kv()[:n] if k == 8 else workloads.gpt2_small_kv()[7000:7000 + n]
+    gc, gn = gpu_encode(cbv, x, dev, np.float16)
+    check_encode(x, rot, cw, gc, gn, np.float16, k, N)
+    cbv.close()
+
+
+def test_encode_kernels_agree_on_full_gpt2s(dev):
+    # Both encoders on the whole 294,912-vector workload: identical stores except
+    # where the oracle calls the block a near-tie.
+    import os
+
+    cb, cw, rot = codebook(4, 256)
+    os.environ["FQ_ENCODE_KERNEL"] = "valu"
+    try:
+        cbv = fq.Codebook(cw, rot)
+    finally:
+        del os.environ["FQ_ENCODE_KERNEL"]
+    x = workloads.gpt2_small_kv()
+    a = gpu_encode(cb, x, dev, np.float16)
+    b = gpu_encode(cbv, x, dev, np.float16)
+    assert np.array_equal(a[1].view(np.uint16), b[1].view(np.uint16))
+    diff = np.flatnonzero(a[0] != b[0])  # k=4, N=256: one byte per block
+    print(f"[kernels agree] {len(diff)} of {len(a[0])} blocks differ", flush=True)
+    if len(diff):
+        vec, blk = diff // 16, diff % 16
+        uv, inv = np.unique(vec, return_inverse=True)
+        enc = oc.encode(x[uv], rot, cw, np.float16)
+        assert enc.near_tie[inv, blk].all(), "the two encoders differ outside oracle near-ties"
+    cbv.close()
+
+
+@pytest.mark.parametrize("k,N,n", [(4, 256, 2000 + 5), (64, 4096, 1000 + 1), (2, 16, 777)])
+def test_decode_valu_kernel_parity(dev, k, N, n):
+    # FQ_DECODE_KERNEL=valu at load time selects the one-lane-per-vector decoder.
+    import os
+
+    cw, rot = artifact_or_skip(k, N)
+    os.environ["FQ_DECODE_KERNEL"] = "valu"
+    try:
+        cbv = fq.Codebook(cw, rot)
+    finally:
+        del os.environ["FQ_DECODE_KERNEL"]
+    B = (D // k) * oc.code_bits(N)
+    store = workloads.random_code_store((n * B + 7) // 8, 90 + k)
+    if (n * B) % 8:
+        store[-1] &= (1 << ((n * B) % 8)) - 1
+    norms = workloads.random_norms(n, 91 + k, np.float16)
+    got = gpu_decode(cbv, store, norms, dev, np.float16)
+    ref = oc.decode(oc.unpack_codes(store, n, D // k, oc.code_bits(N)), norms, rot, cw)
+    assert max_rel_rows(got, ref) <= TOL
+    cbv.close()

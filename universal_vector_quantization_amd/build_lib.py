@@ -23,7 +23,7 @@ OUT = os.path.join(PKG, "libfq.so")
 BUILD = os.path.join(ROOT, "_build")
 KS = (1, 2, 4, 8, 16, 32, 64)
 PER_K = ("fq_encode", "fq_decode", "fq_attn")
-SINGLE = ("fq_api",)
+SINGLE = ("fq_api", "fq_encode_mfma", "fq_decode_mfma")
 ARCH = os.environ.get("FQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          # no packed-fp32 instruction forms in any kernel

@@ -1,6 +1,7 @@
 // Host side of the C ABI in include/fq.h: argument checks (before any HIP call
 // where possible), codebook upload, and dispatch to the kernel launchers.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <new>
@@ -47,7 +48,93 @@ void release(fq_codebook* cb) {
   (void)hipFree(cb->cn2);
   (void)hipFree(cb->pi64t);
   (void)hipFree(cb->pi32);
+  (void)hipFree(cb->amfma);
+  (void)hipFree(cb->cinit);
+  (void)hipFree(cb->cn2s);
+  (void)hipFree(cb->pi64m);
+  (void)hipFree(cb->pi64);
+  (void)hipFree(cb->dec_a);
   delete cb;
+}
+
+template <class T>
+fq_status upload(T** dst, const T* src, size_t count) {
+  if (hipMalloc(dst, count * sizeof(T)) != hipSuccess) return FQ_ERR_HIP;
+  return hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice) == hipSuccess ? FQ_OK : FQ_ERR_HIP;
+}
+
+// Operand layouts of the matrix-core encoder, built once per codebook.
+fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const float* rotation, const float* cn2) {
+  const int d = cb->d, k = cb->k, N = cb->N;
+  // Pi in fp64, row-major and as the A operand of mfma_f64_16x16x4 (lane l: row l%16, k l/16).
+  double* pr = new (std::nothrow) double[(size_t)d * d];
+  double* pm = new (std::nothrow) double[(size_t)d * d];
+  if (!pr || !pm) {
+    delete[] pr;
+    delete[] pm;
+    return FQ_ERR_HIP;
+  }
+  for (int i = 0; i < d * d; i++) pr[i] = (double)rotation[i];
+  for (int r = 0; r < 4; r++)
+    for (int s = 0; s < 16; s++)
+      for (int l = 0; l < 64; l++) pm[(r * 16 + s) * 64 + l] = pr[(16 * r + (l % 16)) * d + 4 * s + l / 16];
+  fq_status st = upload(&cb->pi64, pr, (size_t)d * d);
+  if (st == FQ_OK) st = upload(&cb->pi64m, pm, (size_t)d * d);
+  // Decoder operand: A[o][i] = Pi[i][o] split into fp16 hi + lo; lane l of tile (r, s)
+  // holds row o = 32 r + l % 32 and k = 8 (l / 32) + j, i.e. input dim 16 s + 8 (l / 32) + j.
+  _Float16* da = new (std::nothrow) _Float16[2 * 4 * 2 * 64 * 8];
+  if (!da) st = FQ_ERR_HIP;
+  if (st == FQ_OK) {
+    for (int r = 0; r < 2; r++)
+      for (int s = 0; s < 4; s++)
+        for (int l = 0; l < 64; l++)
+          for (int j = 0; j < 8; j++) {
+            const int o = 32 * r + (l % 32), i = 16 * s + 8 * (l / 32) + j;
+            const float v = rotation[i * d + o];
+            const _Float16 hi = (_Float16)v;
+            const _Float16 lo = (_Float16)(v - (float)hi);
+            da[(((r * 4 + s) * 2 + 0) * 64 + l) * 8 + j] = hi;
+            da[(((r * 4 + s) * 2 + 1) * 64 + l) * 8 + j] = lo;
+          }
+    st = upload(&cb->dec_a, da, (size_t)2 * 4 * 2 * 64 * 8);
+  }
+  delete[] da;
+  delete[] pr;
+  delete[] pm;
+  if (st != FQ_OK || !((k == 4 || k == 8) && N % 32 == 0)) return st;
+
+  const int NT = N / 32;
+  _Float16* am = new (std::nothrow) _Float16[(size_t)NT * 64 * 8]();
+  float* ci = new (std::nothrow) float[(size_t)NT * 2 * 16];
+  float* cs = new (std::nothrow) float[N];
+  if (!am || !ci || !cs) {
+    delete[] am;
+    delete[] ci;
+    delete[] cs;
+    return FQ_ERR_HIP;
+  }
+  for (int n = 0; n < N; n++) cs[n] = 256.0f * cn2[n];  // exact power-of-two scaling
+  for (int t = 0; t < NT; t++) {
+    for (int l = 0; l < 64; l++) {
+      const int row = 32 * t + (l % 32), h = l / 32;
+      _Float16* a = am + ((size_t)t * 64 + l) * 8;
+      for (int j = 0; j < 8; j++) {
+        float v = 0.0f;
+        if (k == 8) v = codewords[(size_t)row * 8 + j];                 // k = 0..7 and 8..15: c
+        else if (h == 0) v = codewords[(size_t)row * 4 + (j & 3)];      // k = 0..3, 4..7: c, c; 8..15: 0
+        a[j] = (_Float16)v;
+      }
+    }
+    for (int h = 0; h < 2; h++)
+      for (int e = 0; e < 16; e++) ci[((size_t)t * 2 + h) * 16 + e] = cs[32 * t + (e / 4) * 8 + 4 * h + (e % 4)];
+  }
+  st = upload(&cb->amfma, am, (size_t)NT * 64 * 8);
+  if (st == FQ_OK) st = upload(&cb->cinit, ci, (size_t)NT * 2 * 16);
+  if (st == FQ_OK) st = upload(&cb->cn2s, cs, (size_t)N);
+  delete[] am;
+  delete[] ci;
+  delete[] cs;
+  return st;
 }
 
 }  // namespace
@@ -85,6 +172,12 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   cb->bits = log2i(N);
   cb->nblk = d / k;
   cb->B = cb->nblk * cb->bits;
+  {
+    const char* ek = getenv("FQ_ENCODE_KERNEL");
+    cb->force_valu = ek && strcmp(ek, "valu") == 0;
+    const char* dk = getenv("FQ_DECODE_KERNEL");
+    cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
+  }
   if (hipGetDevice(&cb->device) != hipSuccess) {
     delete cb;
     return FQ_ERR_HIP;
@@ -131,6 +224,7 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
        hipMemcpy(cb->pi64t, hpi64t, (size_t)d * d * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
        hipMemcpy(cb->pi32, rotation, (size_t)d * d * sizeof(float), hipMemcpyHostToDevice) != hipSuccess))
     st = FQ_ERR_HIP;
+  if (st == FQ_OK) st = upload_mfma_operands(cb, codewords, rotation, hcn2);
   delete[] h16;
   delete[] hcn2;
   delete[] hpi64t;

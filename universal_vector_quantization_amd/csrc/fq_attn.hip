@@ -245,26 +245,265 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
 }
 
 // Log-sum-exp merge of the chunk partials and the single inverse rotation.
+// Lane c < nchunks reads chunk c's statistics; the max and the weighted sum are
+// wave reductions; every lane then sums its own dim over the chunks.
 __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws, const float* __restrict__ pi32,
                                                    int nchunks, float* __restrict__ out) {
   __shared__ float ot[D];
+  __shared__ float wsh[256];
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
   const float* rec = ws + bh * nchunks * REC;
   float M = -__builtin_huge_valf();
-  for (int c = 0; c < nchunks; c++) M = fmaxf(M, rec[c * REC]);
-  float Ls = 0.f, A = 0.f;
+  for (int c = lane; c < nchunks; c += 64) M = fmaxf(M, rec[c * REC]);
+#pragma unroll
+  for (int s2 = 32; s2 >= 1; s2 >>= 1) M = fmaxf(M, __shfl_xor(M, s2));
+  float Ls = 0.f;
+  for (int c = lane; c < nchunks; c += 64) {
+    const float wgt = exp2f(rec[c * REC] - M);
+    if (c < 256) wsh[c] = wgt;
+    Ls += rec[c * REC + 1] * wgt;
+  }
+#pragma unroll
+  for (int s2 = 32; s2 >= 1; s2 >>= 1) Ls += __shfl_xor(Ls, s2);
+  __syncthreads();
+  float A = 0.f;
   for (int c = 0; c < nchunks; c++) {
-    const float w = exp2f(rec[c * REC] - M);
-    Ls += rec[c * REC + 1] * w;
-    A += rec[c * REC + 2 + lane] * w;
+    const float wgt = c < 256 ? wsh[c] : exp2f(rec[c * REC] - M);
+    A = fmaf(rec[c * REC + 2 + lane], wgt, A);
   }
   ot[lane] = A / Ls;
   __syncthreads();
   float o = 0.f;
-#pragma unroll
+#pragma unroll 8
   for (int j = 0; j < D; j++) o = fmaf(pi32[j * D + lane], ot[j], o);
   out[bh * D + lane] = o;
+}
+
+// ---------------------------------------------------------------------------
+// Fast path for k = 4 with 8-bit codes (N <= 256), the attention workload's
+// codebook.  Differences from attn_split:
+//   * MFMA k-slot (lane group q, element j) of k-step s carries dimension
+//     16q + 8s + j, i.e. blocks 4q + 2s and 4q + 2s + 1, so a lane's four codes
+//     for one token are one aligned dword of the token's 16-byte code record and
+//     one load instruction reads 16 consecutive records (256 B, coalesced).
+//   * The value transpose selects, for k-step s and half hh, the dims
+//     32hh + 16(r/8) + 8s + r%8 (r = 0..15); the accumulator rows follow that
+//     order and are put back in place when the partial record is written.
+//   * The next tile's codes and norms are loaded before the current tile is
+//     processed; the rotated queries come precomputed from attn_prep.
+__device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, uint32_t c1) {
+  const half4 a = *reinterpret_cast<const half4*>(cbL + c0 * 4);
+  const half4 b = *reinterpret_cast<const half4*>(cbL + c1 * 4);
+  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+__device__ inline float h16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float h16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+__global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
+    const float* __restrict__ qrot, const uint32_t* __restrict__ kc, const _Float16* __restrict__ kn,
+    const uint32_t* __restrict__ vc, const _Float16* __restrict__ vn, const _Float16* __restrict__ cw16, int N,
+    int Hq, int Hkv, int64_t T, int64_t Tc, int nchunks, float* __restrict__ ws) {
+  __shared__ __align__(16) _Float16 cbL[256 * 4];
+  __shared__ float sm[AW * GMAX], sl[AW * GMAX];
+  __shared__ float so[AW * GMAX * D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  for (int w = tid; w < N * 4 * 2 / 16; w += AW * 64)
+    reinterpret_cast<uint4*>(cbL)[w] = reinterpret_cast<const uint4*>(cw16)[w];
+  const int col = lane & 15, grp = lane >> 4;
+  // Q^T operands (hi / lo) for k-steps 0 and 1: head = col, dims 16 grp + 8 s + j
+  half8 qhi[2], qlo[2], isel[2];
+  {
+    const float* qr = qrot + ((int64_t)b * Hq + (int64_t)g * G + (col < G ? col : 0)) * D;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float v = col < G ? qr[16 * grp + 8 * s2 + j] : 0.f;
+        const _Float16 hv = (_Float16)v;
+        qhi[s2][j] = hv;
+        qlo[s2][j] = (_Float16)(v - (float)hv);
+        isel[s2][j] = (_Float16)((grp == 2 * s2 + col / 8 && j == col % 8) ? 1.0f : 0.0f);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t c0 = (int64_t)chunk * Tc;
+  const int64_t c1 = (c0 + Tc) < T ? (c0 + Tc) : T;
+  const int64_t base = ((int64_t)b * Hkv + g) * T;
+  const bool nal = (T & 3) == 0;  // 4 consecutive norms are one aligned 8-byte load
+  const float NEG = -__builtin_huge_valf();
+  float m = NEG, l = 0.f;
+  f32x4 o[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // tile data of this lane: code dwords of token rows t0 + 16a + col, norms of
+  // tokens t0 + 16a + 4grp + i
+  uint32_t kd[2], vd[2];
+  float kv[2][4], vv[2][4];
+  auto load_tile = [&](int64_t t0) {
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+      const int64_t tr = t0 + 16 * a + col;
+      kd[a] = tr < c1 ? kc[(base + tr) * 4 + grp] : 0u;
+      vd[a] = tr < c1 ? vc[(base + tr) * 4 + grp] : 0u;
+      const int64_t tk = t0 + 16 * a + 4 * grp;
+      if (nal && tk + 3 < c1) {
+        const uint2 kw = *reinterpret_cast<const uint2*>(kn + base + tk);
+        const uint2 vw = *reinterpret_cast<const uint2*>(vn + base + tk);
+        kv[a][0] = h16lo(kw.x);
+        kv[a][1] = h16hi(kw.x);
+        kv[a][2] = h16lo(kw.y);
+        kv[a][3] = h16hi(kw.y);
+        vv[a][0] = h16lo(vw.x);
+        vv[a][1] = h16hi(vw.x);
+        vv[a][2] = h16lo(vw.y);
+        vv[a][3] = h16hi(vw.y);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          kv[a][i] = tk + i < c1 ? (float)kn[base + tk + i] : 0.f;
+          vv[a][i] = tk + i < c1 ? (float)vn[base + tk + i] : 0.f;
+        }
+      }
+    }
+  };
+
+  int64_t t0 = c0 + (int64_t)wave * TILE;
+  if (t0 < c1) load_tile(t0);
+  for (; t0 < c1; t0 += AW * TILE) {
+    const uint32_t kd0 = kd[0], kd1 = kd[1], vd0 = vd[0], vd1 = vd[1];
+    float kvc[2][4], vvc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        kvc[a][i] = kv[a][i];
+        vvc[a][i] = vv[a][i];
+      }
+    if (t0 + AW * TILE < c1) load_tile(t0 + AW * TILE);
+
+    float L[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+      const uint32_t d = a ? kd1 : kd0;
+      const half8 k0 = gather2(cbL, d & 0xffu, (d >> 8) & 0xffu);
+      const half8 k1 = gather2(cbL, (d >> 16) & 0xffu, d >> 24);
+      f32x4 S = {0.f, 0.f, 0.f, 0.f};
+      S = mfma16(k0, qhi[0], S);
+      S = mfma16(k0, qlo[0], S);
+      S = mfma16(k1, qhi[1], S);
+      S = mfma16(k1, qlo[1], S);
+#pragma unroll
+      for (int i = 0; i < 4; i++) L[a][i] = (t0 + 16 * a + 4 * grp + i) < c1 ? S[i] * kvc[a][i] : NEG;
+    }
+    float mx = NEG;
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, L[a][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);  // finite: the tile holds at least one token
+    const float alpha = exp2f(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; c++) o[c] *= alpha;
+    half8 phi, plo;
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float p = exp2f(L[a][i] - mn);
+        l += p;
+        const float pv = p * vvc[a][i];
+        const _Float16 hv = (_Float16)pv;
+        phi[4 * a + i] = hv;
+        plo[4 * a + i] = (_Float16)(pv - (float)hv);
+      }
+    }
+    half8 av[4];
+#pragma unroll
+    for (int a = 0; a < 2; a++) {
+      const uint32_t d = a ? vd1 : vd0;
+      const half8 v0 = gather2(cbL, d & 0xffu, (d >> 8) & 0xffu);
+      const half8 v1 = gather2(cbL, (d >> 16) & 0xffu, d >> 24);
+#pragma unroll
+      for (int c = 0; c < 4; c++) {  // value tile c = (k-step c >> 1, half c & 1)
+        const f32x4 X = mfma16((c >> 1) ? v1 : v0, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      o[c] = mfma16(av[c], phi, o[c]);
+      o[c] = mfma16(av[c], plo, o[c]);
+    }
+    m = mn;
+  }
+
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (grp == 0) {
+    sm[wave * GMAX + col] = m;
+    sl[wave * GMAX + col] = l;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int s2 = c >> 1, hh = c & 1;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = 4 * grp + i;
+      so[(wave * GMAX + col) * D + 32 * hh + 16 * (r >> 3) + 8 * s2 + (r & 7)] = o[c][i];
+    }
+  }
+  __syncthreads();
+  {
+    const int h = tid >> 4, d0 = (tid & 15) * 4;
+    if (h < G) {
+      float M = NEG;
+#pragma unroll
+      for (int w = 0; w < AW; w++) M = fmaxf(M, sm[w * GMAX + h]);
+      float wt[AW], Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < AW; w++) {
+        wt[w] = exp2f(sm[w * GMAX + h] - M);
+        Ls += sl[w * GMAX + h] * wt[w];
+      }
+      float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nchunks + chunk) * REC;
+      if (d0 == 0) {
+        rec[0] = M;
+        rec[1] = Ls;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float A = 0.f;
+#pragma unroll
+        for (int w = 0; w < AW; w++) A += so[(w * GMAX + h) * D + d0 + e] * wt[w];
+        rec[2 + d0 + e] = A;
+      }
+    }
+  }
+}
+
+// Rotated, scaled queries for the fast path: qrot = (scale log2 e) Pi q, fp32.
+__global__ __launch_bounds__(64) void attn_prep(const _Float16* __restrict__ q, const float* __restrict__ pi32,
+                                                float qscale, float* __restrict__ qrot) {
+  __shared__ float qs[D];
+  const int64_t bh = blockIdx.x;
+  const int i = threadIdx.x;
+  qs[i] = (float)q[bh * D + i];
+  __syncthreads();
+  float a = 0.f;
+#pragma unroll 8
+  for (int j = 0; j < D; j++) a = fmaf(pi32[i * D + j], qs[j], a);
+  qrot[bh * D + i] = a * qscale;
 }
 
 size_t attn_smem_bytes(int N, int K) {
@@ -288,7 +527,8 @@ AttnPlan attn_plan(int B, int Hkv, int64_t T) {
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int nchunks) {
-  return (size_t)B * (size_t)Hq * (size_t)nchunks * REC * sizeof(float);
+  // chunk partial records, then the rotated queries of the fast path
+  return (size_t)B * (size_t)Hq * ((size_t)nchunks * REC + D) * sizeof(float);
 }
 #endif
 
@@ -330,6 +570,19 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* kn = reinterpret_cast<const _Float16*>(k_norms);
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
+  if (cb->k == 4 && cb->bits == 8) {
+    float* qrot = ws + (size_t)B * Hq * plan.nchunks * REC;
+    hipLaunchKernelGGL(attn_prep, dim3((unsigned)(B * Hq)), dim3(64), 0, s, qh, cb->pi32, qscale, qrot);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_split_k4b8, grid, dim3(AW * 64), 0, s, qrot,
+                       reinterpret_cast<const uint32_t*>(k_codes), kn, reinterpret_cast<const uint32_t*>(v_codes),
+                       vn, cb->cw16, cb->N, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);
+    return hipGetLastError();
+  }
 #define FQ_ATT(KK)                                                                                                \
   e = launch_attn_split_k<KK>(grid, sh, s, qh, k_codes, kn, v_codes, vn, cb, Hq, Hkv, T, plan.chunk_tokens,       \
                               plan.nchunks, qscale, ws)

@@ -20,14 +20,31 @@ struct fq_codebook {
   float* pi32;      // [d][d] Pi row-major, fp32
   float cmax;       // max_n ||c_n||, rounded up
   float c2max;      // max_n ||c_n||^2, rounded up
+  // Operands of the matrix-core encoder (k = 4 or 8, N a multiple of 32; else null):
+  _Float16* amfma;  // [N/32][64 lanes][8]: codeword tile t as the A operand of
+                    // mfma_f32_32x32x16_f16 (row = codeword, k = [c | c] for the
+                    // hi / lo parts of the scaled query; zeros where unused)
+  float* cinit;     // [N/32][2][16]: 256 ||c||^2 of the 16 rows a lane half holds
+  float* cn2s;      // [N] 256 ||c_n||^2 (fp32)
+  double* pi64m;    // [4 row tiles][16 k steps][64 lanes]: Pi as the A operand of mfma_f64_16x16x4
+  double* pi64;     // [d][d] Pi row-major, fp64
+  _Float16* dec_a;  // [2 row tiles][4 k steps][hi, lo][64 lanes][8]: Pi^T as the A operand of
+                    // mfma_f32_32x32x16_f16 for the decoder (row = output dim, k = input dim)
+  bool force_valu;  // FQ_ENCODE_KERNEL=valu at load time: always use the one-lane-per-vector encoder
+  bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
 };
 
 namespace fq {
 
 constexpr int kD = 64;
 
+// Matrix-core encoder; returns hipErrorNotSupported when the codebook shape is not covered.
+hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
+                              void* norms, fq_dtype norm_dtype, hipStream_t s);
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, hipStream_t s);
+hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
+                              int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                          int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
 
