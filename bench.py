@@ -36,8 +36,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KV vectors/sec encode+decode (GB/s fp16-equiv) and fused-attn GB/s; % roofline"
 HBM_PEAK_GBPS = 8000.0
-# Non-packed fp32 / fp64 FMA issue rate of the chip: 256 CUs x 64 lanes x 2 flop x 2.4 GHz.
-VALU_FMA_PEAK_TFLOPS = 256 * 64 * 2 * 2.4e9 / 1e12
+# VALU lane-op rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s.  A
+# three-input minimum resolves two comparisons per lane-op, so the search's
+# compare work peaks at 78.6 T comparisons/s (the same figure as non-packed FMAs).
+VALU_LANE_OPS = 256 * 64 * 2.4e9
+CMP_PEAK_T = 2 * VALU_LANE_OPS / 1e12
 D = 64
 
 
@@ -49,6 +52,7 @@ def parse():
     ap.add_argument("--attn-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-workload", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -110,6 +114,51 @@ def cpu_baseline(budget_s: float = 20.0):
             "sample": f"oracle encode+decode of the first {n_s} of the 294912 vectors plus attention of one "
                       f"(layer, head) query over its {T} keys/values; per-vector times summed "
                       f"(encode {t_enc:.2f}s, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
+
+
+def workload_timings(fq, workloads, dev, stream, reps: int = 5):
+    """Encode and decode time of every codec workload at full size (event-timed,
+    median of ``reps`` launches; inputs resident, no cache flush)."""
+    import torch
+
+    out = {}
+    gens = {"iid4096": lambda: workloads.iid_gaussian(4096, 101), "gpt2s_kv": workloads.gpt2_small_kv,
+            "tinyllama_kv": workloads.tinyllama_kv, "fullvec_kv": workloads.fullvec_kv}
+    for name, gen in gens.items():
+        w = workloads.WORKLOADS[name]
+        try:
+            cb = fq.Codebook.from_artifact(w.k, w.N)
+        except FileNotFoundError:
+            out[name] = {"skipped": "codebook artifact missing"}
+            continue
+        x = torch.from_numpy(gen()).to(dev)
+        n = x.shape[0]
+        codes = torch.empty(cb.code_bytes(n), dtype=torch.uint8, device=dev)
+        norms = torch.empty(n, dtype=torch.float16 if w.norm_dtype == "f16" else torch.float32, device=dev)
+        xr = torch.empty_like(x)
+        te, td = [], []
+        for r in range(reps + 1):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            fq.fq_encode(cb.handle, x, codes, norms, stream)
+            e[1].record(stream)
+            fq.fq_decode(cb.handle, codes, norms, xr, stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            if r:
+                te.append(e[0].elapsed_time(e[1]))
+                td.append(e[1].elapsed_time(e[2]))
+        t_e, t_d = float(np.median(te)) / 1e3, float(np.median(td)) / 1e3
+        vb = x.element_size() * D + norms.element_size() + cb.code_bytes(n) / n
+        out[name] = {"n": n, "k": w.k, "N": w.N, "encode_us": t_e * 1e6, "decode_us": t_d * 1e6,
+                     "encode_vec_per_s": n / t_e, "decode_vec_per_s": n / t_d,
+                     "encode_GBps": n * vb / t_e / 1e9, "decode_GBps": n * vb / t_d / 1e9,
+                     "decode_hbm_frac": n * vb / t_d / 1e9 / HBM_PEAK_GBPS,
+                     "encode_cmp_frac": (D // w.k) * w.N * n / t_e / 1e12 / CMP_PEAK_T}
+        cb.close()
+        del x, codes, norms, xr
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -187,14 +236,15 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     value = n * args.steps / elapsed
 
-    # dominant kernel roofline: the encoder's brute-force search (fp32 FMAs) and fp64 rotation
-    flops_per_vec = 2 * D * w.N + 2 * D * D
+    # dominant kernel roofline: the encoder's nearest-codeword search; every
+    # candidate score needs at least one comparison (two per three-input min)
+    cmp_per_vec = (D // w.k) * w.N
     enc_s = ms["enc"] / 1e3
-    achieved = flops_per_vec * n / enc_s / 1e12
+    achieved = cmp_per_vec * n / enc_s / 1e12
     enc_bytes = n * (D * 2 + 2) + cb.code_bytes(n)
     dec_bytes = enc_bytes
     att_bytes = 2 * cb.code_bytes(n // 2) + 2 * (n // 2) * 2 + L * H * D * 2 + L * H * D * 4
-    traffic = measured_traffic("encode_valu_k4", "fq_encode.hip")
+    traffic = measured_traffic("encode_mfma_k4", "fq_encode_mfma.hip")
     line = {
         "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -207,10 +257,11 @@ def main():
         "breakdown_GBps": {"encode": enc_bytes / (ms["enc"] / 1e3) / 1e9,
                            "decode": dec_bytes / (ms["dec"] / 1e3) / 1e9,
                            "attention": att_bytes / (ms["att"] / 1e3) / 1e9},
-        "roofline": {"kernel": "encode_valu<k=4> (fq_encode)", "bound": "alu", "achieved": achieved,
-                     "peak": VALU_FMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / VALU_FMA_PEAK_TFLOPS,
+        "roofline": {"kernel": "encode_mfma<k=4> (fq_encode)", "bound": "alu", "achieved": achieved,
+                     "peak": CMP_PEAK_T, "unit": "TFLOP/s", "frac": achieved / CMP_PEAK_T,
                      "traffic": traffic,
-                     "work": f"{flops_per_vec} flop/vector (2dN search multiply-adds + 2d^2 rotation) x {n}"},
+                     "work": f"{cmp_per_vec} candidate-score comparisons per vector ((d/k) N) x {n} vectors; "
+                             f"peak = 2 comparisons per VALU lane-op (three-input min) x 39.3 T lane-ops/s"},
     }
 
     # ---------------------------------------------------------------- decode-attention workload
@@ -251,6 +302,8 @@ def main():
         }
         del flush
 
+    if not args.no_workloads:
+        line["workloads"] = workload_timings(fq, workloads, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     cb.close()

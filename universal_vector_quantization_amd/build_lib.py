@@ -23,6 +23,10 @@ OUT = os.path.join(PKG, "libfq.so")
 BUILD = os.path.join(ROOT, "_build")
 KS = (1, 2, 4, 8, 16, 32, 64)
 PER_K = ("fq_encode", "fq_decode", "fq_attn")
+# Kernel translation units: no NaN semantics (inputs are finite by contract) so
+# min / max need no canonicalisation, and matrix-core results stay in VGPRs.
+KERNEL_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+NO_KERNEL_FLAGS = ("fq_api",)
 SINGLE = ("fq_api", "fq_encode_mfma", "fq_decode_mfma")
 ARCH = os.environ.get("FQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
@@ -39,7 +43,8 @@ def _hipcc() -> str:
 
 def _compile(job):
     src, obj, defs = job
-    cmd = [_hipcc(), *FLAGS, *defs, "-c", src, "-o", obj]
+    extra = [] if os.path.basename(src)[:-4] in NO_KERNEL_FLAGS else KERNEL_FLAGS
+    cmd = [_hipcc(), *FLAGS, *extra, *defs, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "not a recognized feature" not in l)
     if r.returncode != 0:

@@ -291,7 +291,9 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
 //     32hh + 16(r/8) + 8s + r%8 (r = 0..15); the accumulator rows follow that
 //     order and are put back in place when the partial record is written.
 //   * The next tile's codes and norms are loaded before the current tile is
-//     processed; the rotated queries come precomputed from attn_prep.
+//     processed; token offsets are 32-bit within one (batch, KV head) slab;
+//     only the last tile of a chunk carries masks; the rotated queries come
+//     precomputed from attn_prep.
 __device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, uint32_t c1) {
   const half4 a = *reinterpret_cast<const half4*>(cbL + c0 * 4);
   const half4 b = *reinterpret_cast<const half4*>(cbL + c1 * 4);
@@ -301,20 +303,144 @@ __device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, u
 __device__ inline float h16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ inline float h16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
+struct TileData {
+  uint32_t kd[2], vd[2];   // code dwords of tokens t0 + 16a + col (lane group grp)
+  float kv[2][4], vv[2][4];  // norms of tokens t0 + 16a + 4grp + i
+};
+
+struct AttnState {
+  float m, l;
+  f32x4 o[4];
+};
+
+template <bool MASK>
+__device__ inline void process_tile(AttnState& st, const TileData& d, const _Float16* __restrict__ cbL,
+                                    const half8 (&qhi)[2], const half8 (&qlo)[2], const half8 (&isel)[2], int t0,
+                                    int tend, int grp) {
+  const float NEG = -__builtin_huge_valf();
+  float L[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; a++) {
+    const uint32_t w = d.kd[a];
+    const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
+    const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    S = mfma16(k0, qhi[0], S);
+    S = mfma16(k0, qlo[0], S);
+    S = mfma16(k1, qhi[1], S);
+    S = mfma16(k1, qlo[1], S);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      L[a][i] = S[i] * d.kv[a][i];
+      if constexpr (MASK) L[a][i] = (t0 + 16 * a + 4 * grp + i) < tend ? L[a][i] : NEG;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
+                   fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mn = fmaxf(st.m, mx);  // finite: the tile holds at least one token
+  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+  st.l *= alpha;
+#pragma unroll
+  for (int c = 0; c < 4; c++) st.o[c] *= alpha;
+  half8 phi, plo;
+#pragma unroll
+  for (int a = 0; a < 2; a++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float p = __builtin_amdgcn_exp2f(L[a][i] - mn);
+      st.l += p;
+      const float pv = p * d.vv[a][i];
+      const _Float16 hv = (_Float16)pv;
+      phi[4 * a + i] = hv;
+      plo[4 * a + i] = (_Float16)(pv - (float)hv);
+    }
+  }
+  half8 av[4];
+#pragma unroll
+  for (int a = 0; a < 2; a++) {
+    const uint32_t w = d.vd[a];
+    const half8 v0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
+    const half8 v1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {  // value tile c = (k-step c >> 1, half c & 1)
+      const f32x4 X = mfma16((c >> 1) ? v1 : v0, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    st.o[c] = mfma16(av[c], phi, st.o[c]);
+    st.o[c] = mfma16(av[c], plo, st.o[c]);
+  }
+  st.m = mn;
+}
+
+// Chunk-resident variant: the workgroup first copies its whole chunk (codes and
+// norms of up to FCHUNK tokens, ~34 KB) into LDS with every load in flight at
+// once, then the waves run the tile loop from LDS.  With several workgroups
+// per CU one loads while another computes.
+constexpr int FCHUNK = 512;
+
+template <bool NAL>
 __global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
     const float* __restrict__ qrot, const uint32_t* __restrict__ kc, const _Float16* __restrict__ kn,
     const uint32_t* __restrict__ vc, const _Float16* __restrict__ vn, const _Float16* __restrict__ cw16, int N,
-    int Hq, int Hkv, int64_t T, int64_t Tc, int nchunks, float* __restrict__ ws) {
+    int Hq, int Hkv, int64_t T, int nchunks, float* __restrict__ ws) {
+  __shared__ __align__(16) uint32_t kcL[FCHUNK * 4];
+  __shared__ __align__(16) uint32_t vcL[FCHUNK * 4];
+  __shared__ __align__(16) _Float16 knL[FCHUNK];
+  __shared__ __align__(16) _Float16 vnL[FCHUNK];
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ float sm[AW * GMAX], sl[AW * GMAX];
   __shared__ float so[AW * GMAX * D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  for (int w = tid; w < N * 4 * 2 / 16; w += AW * 64)
-    reinterpret_cast<uint4*>(cbL)[w] = reinterpret_cast<const uint4*>(cw16)[w];
+  const int64_t base = ((int64_t)b * Hkv + g) * T + (int64_t)chunk * FCHUNK;
+  const int rem = (int)(T - (int64_t)chunk * FCHUNK);
+  const int nt = rem < FCHUNK ? rem : FCHUNK;
+
+  // ---- bulk copy: codes (16 B per token), norms, codebook
+  {
+    const uint4* ks = reinterpret_cast<const uint4*>(kc) + base;
+    const uint4* vs = reinterpret_cast<const uint4*>(vc) + base;
+    uint4 kr[FCHUNK / (AW * 64)], vr[FCHUNK / (AW * 64)];
+#pragma unroll
+    for (int i = 0; i < FCHUNK / (AW * 64); i++) {
+      const int t = tid + i * AW * 64;
+      kr[i] = t < nt ? ks[t] : make_uint4(0u, 0u, 0u, 0u);
+      vr[i] = t < nt ? vs[t] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint4 nr = make_uint4(0u, 0u, 0u, 0u);
+    const int q = tid & 63;  // 64 threads x 8 norms per array
+    const _Float16* nsrc = (tid < 64 ? kn : vn) + base;
+    if (tid < 128) {
+      if (NAL && 8 * q + 7 < nt) {
+        nr = reinterpret_cast<const uint4*>(nsrc)[q];
+      } else {
+        uint16_t hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++)
+          hv[j] = 8 * q + j < nt ? __builtin_bit_cast(uint16_t, nsrc[8 * q + j]) : (uint16_t)0;
+        nr = make_uint4(hv[0] | (uint32_t)hv[1] << 16, hv[2] | (uint32_t)hv[3] << 16, hv[4] | (uint32_t)hv[5] << 16,
+                        hv[6] | (uint32_t)hv[7] << 16);
+      }
+    }
+    for (int w = tid; w < N * 4 * 2 / 16; w += AW * 64)
+      reinterpret_cast<uint4*>(cbL)[w] = reinterpret_cast<const uint4*>(cw16)[w];
+#pragma unroll
+    for (int i = 0; i < FCHUNK / (AW * 64); i++) {
+      const int t = tid + i * AW * 64;
+      reinterpret_cast<uint4*>(kcL)[t] = kr[i];
+      reinterpret_cast<uint4*>(vcL)[t] = vr[i];
+    }
+    if (tid < 128) reinterpret_cast<uint4*>(tid < 64 ? knL : vnL)[q] = nr;
+  }
+
   const int col = lane & 15, grp = lane >> 4;
-  // Q^T operands (hi / lo) for k-steps 0 and 1: head = col, dims 16 grp + 8 s + j
   half8 qhi[2], qlo[2], isel[2];
   {
     const float* qr = qrot + ((int64_t)b * Hq + (int64_t)g * G + (col < G ? col : 0)) * D;
@@ -332,126 +458,40 @@ __global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
   }
   __syncthreads();
 
-  const int64_t c0 = (int64_t)chunk * Tc;
-  const int64_t c1 = (c0 + Tc) < T ? (c0 + Tc) : T;
-  const int64_t base = ((int64_t)b * Hkv + g) * T;
-  const bool nal = (T & 3) == 0;  // 4 consecutive norms are one aligned 8-byte load
-  const float NEG = -__builtin_huge_valf();
-  float m = NEG, l = 0.f;
-  f32x4 o[4];
+  AttnState st;
+  st.m = -__builtin_huge_valf();
+  st.l = 0.f;
 #pragma unroll
-  for (int c = 0; c < 4; c++) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // tile data of this lane: code dwords of token rows t0 + 16a + col, norms of
-  // tokens t0 + 16a + 4grp + i
-  uint32_t kd[2], vd[2];
-  float kv[2][4], vv[2][4];
-  auto load_tile = [&](int64_t t0) {
+  for (int c = 0; c < 4; c++) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int t0 = wave * TILE;
+  TileData d;
+  for (; t0 < nt; t0 += AW * TILE) {
 #pragma unroll
     for (int a = 0; a < 2; a++) {
-      const int64_t tr = t0 + 16 * a + col;
-      kd[a] = tr < c1 ? kc[(base + tr) * 4 + grp] : 0u;
-      vd[a] = tr < c1 ? vc[(base + tr) * 4 + grp] : 0u;
-      const int64_t tk = t0 + 16 * a + 4 * grp;
-      if (nal && tk + 3 < c1) {
-        const uint2 kw = *reinterpret_cast<const uint2*>(kn + base + tk);
-        const uint2 vw = *reinterpret_cast<const uint2*>(vn + base + tk);
-        kv[a][0] = h16lo(kw.x);
-        kv[a][1] = h16hi(kw.x);
-        kv[a][2] = h16lo(kw.y);
-        kv[a][3] = h16hi(kw.y);
-        vv[a][0] = h16lo(vw.x);
-        vv[a][1] = h16hi(vw.x);
-        vv[a][2] = h16lo(vw.y);
-        vv[a][3] = h16hi(vw.y);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          kv[a][i] = tk + i < c1 ? (float)kn[base + tk + i] : 0.f;
-          vv[a][i] = tk + i < c1 ? (float)vn[base + tk + i] : 0.f;
-        }
-      }
+      d.kd[a] = kcL[(t0 + 16 * a + col) * 4 + grp];
+      d.vd[a] = vcL[(t0 + 16 * a + col) * 4 + grp];
+      const uint2 kw = *reinterpret_cast<const uint2*>(knL + t0 + 16 * a + 4 * grp);
+      const uint2 vw = *reinterpret_cast<const uint2*>(vnL + t0 + 16 * a + 4 * grp);
+      d.kv[a][0] = h16lo(kw.x);
+      d.kv[a][1] = h16hi(kw.x);
+      d.kv[a][2] = h16lo(kw.y);
+      d.kv[a][3] = h16hi(kw.y);
+      d.vv[a][0] = h16lo(vw.x);
+      d.vv[a][1] = h16hi(vw.x);
+      d.vv[a][2] = h16lo(vw.y);
+      d.vv[a][3] = h16hi(vw.y);
     }
-  };
-
-  int64_t t0 = c0 + (int64_t)wave * TILE;
-  if (t0 < c1) load_tile(t0);
-  for (; t0 < c1; t0 += AW * TILE) {
-    const uint32_t kd0 = kd[0], kd1 = kd[1], vd0 = vd[0], vd1 = vd[1];
-    float kvc[2][4], vvc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        kvc[a][i] = kv[a][i];
-        vvc[a][i] = vv[a][i];
-      }
-    if (t0 + AW * TILE < c1) load_tile(t0 + AW * TILE);
-
-    float L[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; a++) {
-      const uint32_t d = a ? kd1 : kd0;
-      const half8 k0 = gather2(cbL, d & 0xffu, (d >> 8) & 0xffu);
-      const half8 k1 = gather2(cbL, (d >> 16) & 0xffu, d >> 24);
-      f32x4 S = {0.f, 0.f, 0.f, 0.f};
-      S = mfma16(k0, qhi[0], S);
-      S = mfma16(k0, qlo[0], S);
-      S = mfma16(k1, qhi[1], S);
-      S = mfma16(k1, qlo[1], S);
-#pragma unroll
-      for (int i = 0; i < 4; i++) L[a][i] = (t0 + 16 * a + 4 * grp + i) < c1 ? S[i] * kvc[a][i] : NEG;
-    }
-    float mx = NEG;
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) mx = fmaxf(mx, L[a][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);  // finite: the tile holds at least one token
-    const float alpha = exp2f(m - mn);
-    l *= alpha;
-#pragma unroll
-    for (int c = 0; c < 4; c++) o[c] *= alpha;
-    half8 phi, plo;
-#pragma unroll
-    for (int a = 0; a < 2; a++) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = exp2f(L[a][i] - mn);
-        l += p;
-        const float pv = p * vvc[a][i];
-        const _Float16 hv = (_Float16)pv;
-        phi[4 * a + i] = hv;
-        plo[4 * a + i] = (_Float16)(pv - (float)hv);
-      }
-    }
-    half8 av[4];
-#pragma unroll
-    for (int a = 0; a < 2; a++) {
-      const uint32_t d = a ? vd1 : vd0;
-      const half8 v0 = gather2(cbL, d & 0xffu, (d >> 8) & 0xffu);
-      const half8 v1 = gather2(cbL, (d >> 16) & 0xffu, d >> 24);
-#pragma unroll
-      for (int c = 0; c < 4; c++) {  // value tile c = (k-step c >> 1, half c & 1)
-        const f32x4 X = mfma16((c >> 1) ? v1 : v0, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-        for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      o[c] = mfma16(av[c], phi, o[c]);
-      o[c] = mfma16(av[c], plo, o[c]);
-    }
-    m = mn;
+    if (t0 + TILE <= nt)
+      process_tile<false>(st, d, cbL, qhi, qlo, isel, t0, nt, grp);
+    else
+      process_tile<true>(st, d, cbL, qhi, qlo, isel, t0, nt, grp);
   }
 
+  float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (grp == 0) {
-    sm[wave * GMAX + col] = m;
+    sm[wave * GMAX + col] = st.m;
     sl[wave * GMAX + col] = l;
   }
 #pragma unroll
@@ -460,11 +500,12 @@ __global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int r = 4 * grp + i;
-      so[(wave * GMAX + col) * D + 32 * hh + 16 * (r >> 3) + 8 * s2 + (r & 7)] = o[c][i];
+      so[(wave * GMAX + col) * D + 32 * hh + 16 * (r >> 3) + 8 * s2 + (r & 7)] = st.o[c][i];
     }
   }
   __syncthreads();
   {
+    const float NEG = -__builtin_huge_valf();
     const int h = tid >> 4, d0 = (tid & 15) * 4;
     if (h < G) {
       float M = NEG;
@@ -473,7 +514,7 @@ __global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
       float wt[AW], Ls = 0.f;
 #pragma unroll
       for (int w = 0; w < AW; w++) {
-        wt[w] = exp2f(sm[w * GMAX + h] - M);
+        wt[w] = sm[w * GMAX + h] == NEG ? 0.f : __builtin_amdgcn_exp2f(sm[w * GMAX + h] - M);
         Ls += sl[w * GMAX + h] * wt[w];
       }
       float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nchunks + chunk) * REC;
@@ -513,7 +554,11 @@ size_t attn_smem_bytes(int N, int K) {
 }  // namespace
 
 #ifndef FQ_ONLY_K
-AttnPlan attn_plan(int B, int Hkv, int64_t T) {
+// k = 4 with 8-bit codes runs the chunk-resident kernel.
+bool attn_fast_path(const fq_codebook* cb, int64_t T) { return cb->k == 4 && cb->bits == 8 && T < ((int64_t)1 << 40); }
+
+AttnPlan attn_plan(const fq_codebook* cb, int B, int Hkv, int64_t T) {
+  if (attn_fast_path(cb, T)) return AttnPlan{(int)((T + FCHUNK - 1) / FCHUNK), (int64_t)FCHUNK};
   const int64_t per = (int64_t)AW * TILE;
   const int64_t groups = (int64_t)B * Hkv;
   const int64_t want = (2048 + groups - 1) / groups;
@@ -561,7 +606,7 @@ extern FQ_ATT_DECL(64);
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
                        float* out, void* workspace, hipStream_t s) {
-  const AttnPlan plan = attn_plan(B, Hkv, T);
+  const AttnPlan plan = attn_plan(cb, B, Hkv, T);
   const float qscale = scale * 1.4426950408889634f;  // log2(e)
   const dim3 grid((unsigned)plan.nchunks, (unsigned)Hkv, (unsigned)B);
   const size_t sh = attn_smem_bytes(cb->N, cb->k);
@@ -570,14 +615,21 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* kn = reinterpret_cast<const _Float16*>(k_norms);
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
-  if (cb->k == 4 && cb->bits == 8) {
+  if (attn_fast_path(cb, T)) {
     float* qrot = ws + (size_t)B * Hq * plan.nchunks * REC;
     hipLaunchKernelGGL(attn_prep, dim3((unsigned)(B * Hq)), dim3(64), 0, s, qh, cb->pi32, qscale, qrot);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_split_k4b8, grid, dim3(AW * 64), 0, s, qrot,
-                       reinterpret_cast<const uint32_t*>(k_codes), kn, reinterpret_cast<const uint32_t*>(v_codes),
-                       vn, cb->cw16, cb->N, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
+    const bool nal = (T % 8) == 0;  // 8 consecutive norms of a chunk are one aligned 16-byte load
+#define FQ_FAST(NA)                                                                                           \
+  hipLaunchKernelGGL(attn_split_k4b8<NA>, grid, dim3(AW * 64), 0, s, qrot,                                    \
+                     reinterpret_cast<const uint32_t*>(k_codes), kn, reinterpret_cast<const uint32_t*>(v_codes), \
+                     vn, cb->cw16, cb->N, Hq, Hkv, T, plan.nchunks, ws)
+    if (nal)
+      FQ_FAST(true);
+    else
+      FQ_FAST(false);
+#undef FQ_FAST
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);

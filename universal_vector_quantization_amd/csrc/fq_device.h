@@ -12,8 +12,8 @@ namespace fq {
 __device__ inline uint16_t f64_to_f16_bits(double v) {
   uint64_t u = __double_as_longlong(v);
   uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  if ((u & 0x7fffffffffffffffull) > 0x7ff0000000000000ull) return (uint16_t)(sign | 0x7e00u);  // NaN (bit test)
   double a = fabs(v);
-  if (!(a == a)) return (uint16_t)(sign | 0x7e00u);
   if (a >= 65520.0) return (uint16_t)(sign | 0x7c00u);
   if (a < 6.103515625e-05) {  // below 2^-14: subnormal grid, spacing 2^-24
     double r = rint(a * 16777216.0);  // exact scaling; rint rounds half to even

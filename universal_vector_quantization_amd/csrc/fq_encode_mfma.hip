@@ -43,13 +43,12 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Minimum of 16 values as a chain of 7 three-input minima and one two-input minimum.
 __device__ inline float min16(const f32x16& v) {
-  float a = fminf(fminf(v[0], v[1]), v[2]);
-  float b = fminf(fminf(v[3], v[4]), v[5]);
-  float c = fminf(fminf(v[6], v[7]), v[8]);
-  float d = fminf(fminf(v[9], v[10]), v[11]);
-  float e = fminf(fminf(v[12], v[13]), v[14]);
-  return fminf(fminf(fminf(a, b), fminf(c, d)), fminf(e, v[15]));
+  float m = fminf(fminf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fminf(fminf(m, v[i]), v[i + 1]);
+  return fminf(m, v[15]);
 }
 
 __device__ inline double shfl_xor_f64(double v, int m) {
@@ -71,7 +70,12 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
   constexpr int VG = 256 / NB;     // vectors per group
   constexpr int NSUB = VG / 16;    // 16-vector rotation sub-groups
   constexpr int XB = XF16 ? 2 : 4; // input bytes per coordinate
-  __shared__ float ytile[WAVES][VG * D];  // the x tile first, then y (fp32)
+  // Row strides are padded so that the 16 rows a rotation sub-group touches in
+  // one instruction fall into different LDS banks.
+  constexpr int YS = D + 4;             // y rows: fp32, 272 B
+  constexpr int XS = XF16 ? D + 8 : D + 4;  // x rows: 144 B (fp16) or 272 B (fp32)
+  __shared__ __align__(16) float ytile[WAVES][VG * YS];
+  __shared__ __align__(16) char xtile[WAVES][VG * XS * XB];
   __shared__ double sinv[WAVES][VG];
   __shared__ uint32_t spk[WAVES][8 * 16];  // 256 codes x bits <= 4096 bits
   constexpr int CBL = K == 4 ? 1024 : 1;   // k = 4 keeps the codebook (N <= 1024) in LDS
@@ -90,9 +94,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
   const int NT = N / 32;
   const int B = NB * bits;
   float* yt = ytile[w];
-  // fp16 x sits in the upper half of the tile so that writing y of one 16-vector
-  // sub-group never overwrites x of a later one (fp32 x and y of a vector share bytes).
-  char* xs = reinterpret_cast<char*>(yt) + (XF16 ? VG * D * 2 : 0);
+  char* xs = xtile[w];
   const double u = 5.9604644775390625e-08;
 
   for (int64_t g = (int64_t)blockIdx.x * WAVES + w; g < ngroups; g += (int64_t)gridDim.x * WAVES) {
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
         const int o = lane * LB + q * 16;
         uint4 val = make_uint4(0u, 0u, 0u, 0u);
         if (o < nv * D * XB) val = *reinterpret_cast<const uint4*>(xg + o);
-        *reinterpret_cast<uint4*>(xs + o) = val;
+        *reinterpret_cast<uint4*>(xs + (o / (D * XB)) * (XS * XB) + o % (D * XB)) = val;
         const uint32_t wv[4] = {val.x, val.y, val.z, val.w};
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -155,19 +157,18 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
         const int co = 4 * ks + (lane >> 4);
         double xb;
         if constexpr (XF16)
-          xb = (double)reinterpret_cast<const _Float16*>(xs)[vec * D + co];
+          xb = (double)reinterpret_cast<const _Float16*>(xs)[vec * XS + co];
         else
-          xb = (double)reinterpret_cast<const float*>(xs)[vec * D + co];
+          xb = (double)reinterpret_cast<const float*>(xs)[vec * XS + co];
 #pragma unroll
         for (int r = 0; r < 4; r++)
           acc[r] = __builtin_amdgcn_mfma_f64_16x16x4f64(pi64m[(r * 16 + ks) * 64 + lane], xb, acc[r], 0, 0, 0);
       }
-      wave_lds_sync();  // this sub-group's x reads are done before its y is written
       const double inv = sinv[w][vec];
 #pragma unroll
       for (int r = 0; r < 4; r++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) yt[vec * D + 16 * r + (lane >> 4) + 4 * e] = (float)(acc[r][e] * inv);
+        for (int e = 0; e < 4; e++) yt[vec * YS + 16 * r + (lane >> 4) + 4 * e] = (float)(acc[r][e] * inv);
     }
     wave_lds_sync();
 
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
 #pragma unroll
     for (int tb = 0; tb < 8; tb++) {
       const int gb = 32 * tb + c;
-      const float* yp = yt + gb * K;  // block gb of the group = coordinates [K gb, K gb + K)
+      const float* yp = yt + (gb / NB) * YS + (gb % NB) * K;  // block gb of the group
       half8 b = {};
       if constexpr (K == 4) {
         if (h == 0) {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
 #pragma unroll
     for (int tb = 0; tb < 8; tb++) {
       const int gb = 32 * tb + c;
-      const float* yp = yt + gb * K;
+      const float* yp = yt + (gb / NB) * YS + (gb % NB) * K;
       float my[K];
       float yn2 = 0.f;
 #pragma unroll
