@@ -218,6 +218,71 @@ def test_encode_valu_kernel_parity(dev, k, N, n):
     cbv.close()
 
 
+@pytest.mark.parametrize("k,N,n", [(4, 256, 3000 + 7), (8, 4096, 1500 + 3)])
+def test_encode_mfma64_kernel_parity(dev, k, N, n):
+    # fp16 input normally runs on the fp16-split-rotation encoder; FQ_ENCODE_KERNEL=mfma64
+    # selects the fp64-rotation matrix-core encoder (the fp32-input path) for it too.
+    import os
+
+    cw, rot = artifact_or_skip(k, N)
+    os.environ["FQ_ENCODE_KERNEL"] = "mfma64"
+    try:
+        cbm = fq.Codebook(cw, rot)
+    finally:
+        del os.environ["FQ_ENCODE_KERNEL"]
+    x = workloads.tinyllama_kv()[:n] if k == 8 else workloads.gpt2_small_kv()[9000:9000 + n]
+    gc, gn = gpu_encode(cbm, x, dev, np.float16)
+    check_encode(x, rot, cw, gc, gn, np.float16, k, N)
+    cbm.close()
+
+
+def _synthetic_codebook(k, N, seed):
+    # fp16-exact, normal-or-zero codewords of the scale of a unit vector's k-block
+    rng = np.random.default_rng(seed)
+    c = (rng.standard_normal((N, k)) * np.sqrt(1.0 / D) * 1.2).astype(np.float16).astype(np.float32)
+    c[np.abs(c) < 2.0 ** -14] = 0.0
+    assert len(np.unique(c, axis=0)) == N
+    return c
+
+
+@pytest.mark.parametrize("k,N", [(4, 32), (4, 64), (4, 2048), (8, 32), (8, 512)])
+def test_encode_synthetic_codebooks(dev, k, N):
+    # Codebook sizes from one tile of 32 codewords to 64 tiles, on the fp16-input
+    # matrix-core encoder (and fp32 input on the fp64-rotation one).
+    cw = _synthetic_codebook(k, N, 300 + N + k)
+    _, rot = artifact_or_skip(4, 256)
+    cb = fq.Codebook(cw, rot)
+    x = workloads.gpt2_small_kv()[12000:12000 + 700 + 9]
+    for dt in (np.float16, np.float32):
+        xs = x.astype(dt)
+        print(f"[synthetic codebook] k={k} N={N} x={np.dtype(dt).name}", flush=True)
+        gc, gn = gpu_encode(cb, xs, dev, np.float16)
+        check_encode(xs, rot, cw, gc, gn, np.float16, k, N)
+    cb.close()
+
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_encode_exact_ties_take_lowest_index(dev, k):
+    # Codewords 3 and 5 are negatives of each other and the two shortest, so a zero
+    # vector is at exactly the same distance from both: no certificate can separate
+    # them and the fp64 re-search must return the lower index, 3.
+    N = 64
+    cw = _synthetic_codebook(k, N, 900 + k)
+    cw[3] = cw[3] * np.float32(2.0 ** -6)
+    cw[5] = -cw[3]
+    cw[np.abs(cw) < 2.0 ** -14] = 0.0
+    assert np.abs(cw[3]).max() > 0
+    _, rot = artifact_or_skip(4, 256)
+    cb = fq.Codebook(cw, rot)
+    x = workloads.gpt2_small_kv()[:300].copy()
+    x[::7] = 0  # zero vectors interleaved with ordinary ones
+    gc, gn = gpu_encode(cb, x, dev, np.float16)
+    check_encode(x, rot, cw, gc, gn, np.float16, k, N)
+    g = oc.unpack_codes(gc, len(x), D // k, oc.code_bits(N))
+    assert (g[::7] == 3).all()
+    cb.close()
+
+
 def test_encode_kernels_agree_on_full_gpt2s(dev):
     # Both encoders on the whole 294,912-vector workload: identical stores except
     # where the oracle calls the block a near-tie.

@@ -54,6 +54,10 @@ void release(fq_codebook* cb) {
   (void)hipFree(cb->pi64m);
   (void)hipFree(cb->pi64);
   (void)hipFree(cb->dec_a);
+  (void)hipFree(cb->rot16);
+  (void)hipFree(cb->crec);
+  (void)hipFree(cb->rot32);
+  (void)hipFree(cb->frec);
   delete cb;
 }
 
@@ -64,6 +68,52 @@ fq_status upload(T** dst, const T* src, size_t count) {
 }
 
 // Operand layouts of the matrix-core encoder, built once per codebook.
+// Operands of the k = d = 64 encoder: the rotation as 32 x 32 x 16 A operands (three
+// fp16 parts of 1024 Pi, rows permuted so that a lane ends up with 32 consecutive
+// coordinates) and the codeword tiles in their LDS layout.
+fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const float* rotation) {
+  const int d = cb->d, N = cb->N;
+  const int tiles = N / 32, chunks = (tiles + 7) / 8;
+  const size_t rec_bytes = (size_t)chunks * 8 * 32 * 144;
+  _Float16* rt = new (std::nothrow) _Float16[2 * 4 * 3 * 64 * 8];
+  uint8_t* rc = new (std::nothrow) uint8_t[rec_bytes]();
+  if (!rt || !rc) {
+    delete[] rt;
+    delete[] rc;
+    return FQ_ERR_HIP;
+  }
+  for (int r = 0; r < 2; r++)
+    for (int s = 0; s < 4; s++)
+      for (int l = 0; l < 64; l++)
+        for (int j = 0; j < 8; j++) {
+          const int rho = l % 32, a = rho / 8, hh = (rho / 4) % 2, b = rho % 4;
+          const int coord = 32 * hh + 16 * r + 4 * a + b, in = 16 * s + 8 * (l / 32) + j;
+          const double P = 1024.0 * (double)rotation[coord * d + in];
+          const _Float16 hi = (_Float16)P;
+          const _Float16 mid = (_Float16)(P - (double)hi);
+          const _Float16 lo = (_Float16)(P - (double)hi - (double)mid);
+          const _Float16 parts[3] = {hi, mid, lo};
+          for (int p = 0; p < 3; p++) rt[((((r * 4 + s) * 3 + p) * 64) + l) * 8 + j] = parts[p];
+        }
+  for (int n = 0; n < N; n++) {
+    uint8_t* row = rc + (size_t)n * 144;
+    double c2 = 0.0;
+    for (int t = 0; t < d; t++) {
+      const double v = (double)codewords[(size_t)n * d + t];
+      const _Float16 hv = (_Float16)v;  // exact: codewords are fp16 values
+      memcpy(row + 2 * t, &hv, 2);
+      c2 += v * v;
+    }
+    const float s2 = (float)(256.0 * c2);
+    memcpy(rc + (size_t)(n & ~3) * 144 + 128 + 4 * (n & 3), &s2, 4);
+  }
+  fq_status st = upload(&cb->rot32, rt, (size_t)2 * 4 * 3 * 64 * 8);
+  if (st == FQ_OK) st = upload(&cb->frec, rc, rec_bytes);
+  delete[] rt;
+  delete[] rc;
+  return st;
+}
+
 fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const float* rotation, const float* cn2) {
   const int d = cb->d, k = cb->k, N = cb->N;
   // Pi in fp64, row-major and as the A operand of mfma_f64_16x16x4 (lane l: row l%16, k l/16).
@@ -101,6 +151,7 @@ fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const fl
   delete[] da;
   delete[] pr;
   delete[] pm;
+  if (st == FQ_OK && k == 64 && N % 32 == 0) st = upload_full_operands(cb, codewords, rotation);
   if (st != FQ_OK || !((k == 4 || k == 8) && N % 32 == 0)) return st;
 
   const int NT = N / 32;
@@ -134,6 +185,47 @@ fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const fl
   delete[] am;
   delete[] ci;
   delete[] cs;
+  if (st != FQ_OK) return st;
+
+  // fp16-input encoder.  Rotation: P = 1024 Pi (exact), hi = fp16(P), mid = fp16(P - hi),
+  // lo = fp16(P - hi - mid); the differences are exact in fp64.
+  _Float16* rt = new (std::nothrow) _Float16[2 * 4 * 3 * 64 * 8];
+  _Float16* rc = new (std::nothrow) _Float16[(size_t)N * 8]();
+  if (!rt || !rc) {
+    delete[] rt;
+    delete[] rc;
+    return FQ_ERR_HIP;
+  }
+  for (int s = 0; s < 2; s++)
+    for (int r = 0; r < 4; r++)
+      for (int l = 0; l < 64; l++)
+        for (int j = 0; j < 8; j++) {
+          const int rho = l % 16, coord = 16 * (rho / 4) + 4 * r + rho % 4, in = 32 * s + 8 * (l / 16) + j;
+          const double P = 1024.0 * (double)rotation[coord * d + in];
+          const _Float16 hi = (_Float16)P;
+          const _Float16 mid = (_Float16)(P - (double)hi);
+          const _Float16 lo = (_Float16)(P - (double)hi - (double)mid);
+          const _Float16 parts[3] = {hi, mid, lo};
+          for (int p = 0; p < 3; p++) rt[((((s * 4 + r) * 3 + p) * 64) + l) * 8 + j] = parts[p];
+        }
+  for (int n = 0; n < N; n++) {
+    double c2 = 0.0;
+    for (int t = 0; t < k; t++) {
+      const double v = (double)codewords[(size_t)n * k + t];
+      rc[(size_t)n * 8 + t] = (_Float16)v;  // exact: codewords are fp16 values
+      c2 += v * v;
+    }
+    if (k == 4) {  // 256 ||c||^2 as fp16 hi + lo (22 bits)
+      const double s2 = 256.0 * c2;
+      const _Float16 hi = (_Float16)s2;
+      rc[(size_t)n * 8 + 4] = hi;
+      rc[(size_t)n * 8 + 5] = (_Float16)(s2 - (double)hi);
+    }
+  }
+  st = upload(&cb->rot16, rt, (size_t)2 * 4 * 3 * 64 * 8);
+  if (st == FQ_OK) st = upload(&cb->crec, rc, (size_t)N * 8);
+  delete[] rt;
+  delete[] rc;
   return st;
 }
 
@@ -175,13 +267,17 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   {
     const char* ek = getenv("FQ_ENCODE_KERNEL");
     cb->force_valu = ek && strcmp(ek, "valu") == 0;
+    cb->force_mfma64 = ek && strcmp(ek, "mfma64") == 0;
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
   }
-  if (hipGetDevice(&cb->device) != hipSuccess) {
+  int lds_max = 0;
+  if (hipGetDevice(&cb->device) != hipSuccess ||
+      hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, cb->device) != hipSuccess) {
     delete cb;
     return FQ_ERR_HIP;
   }
+  cb->max_lds = (size_t)lds_max;
 
   // Host staging: fp16 copy (padded to 16 bytes), ||c||^2, bounds, rotations.
   const size_t cw16_bytes = ((nk * 2 + 15) / 16) * 16;
@@ -208,6 +304,15 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   }
   cb->c2max = nextafterf((float)c2max, INFINITY);
   cb->cmax = nextafterf((float)sqrt(c2max), INFINITY);
+  {
+    // Score error bound of the fp16-input matrix-core encoder (derivation at the kernel);
+    // 1.02 covers the 1.01 slack of the bound and its fp32 evaluation in the kernel.
+    const double u = 0x1p-24, sk = sqrt((double)k), cm = cb->cmax, c2 = cb->c2max;
+    const double rel = 1.02 * (2 * k + 7) * u * 512.0 * cm;
+    const double abs_ = 1.02 * ((2 * k + 7) * u * 256.0 * c2 + 35840.0 * sk * cm * u + 0x1p-25 * (1.0 + sk * cm));
+    cb->h16_erel = nextafterf((float)rel, INFINITY);
+    cb->h16_eabs = nextafterf((float)abs_, INFINITY);
+  }
   for (int i = 0; i < d; i++)
     for (int j = 0; j < d; j++) hpi64t[j * d + i] = (double)rotation[i * d + j];
 

@@ -254,7 +254,14 @@ extern template hipError_t launch_encode_k<64>(const fq_codebook*, const void*, 
 
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, hipStream_t s) {
-  if (!cb->force_valu && cb->amfma) return launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+  if (!cb->force_valu && !cb->force_mfma64 && x_dtype == FQ_F16 && encode_h16_supported(cb))
+    return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, s);
+  if (!cb->force_valu && x_dtype == FQ_F16 && encode_full_supported(cb))
+    return launch_encode_full(cb, x, n, codes, norms, norm_dtype, s);
+  if (!cb->force_valu && cb->amfma) {
+    const hipError_t e = launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    if (e != hipErrorNotSupported) return e;
+  }
   switch (cb->k) {
     case 1: return launch_encode_k<1>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
     case 2: return launch_encode_k<2>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);

@@ -1,0 +1,348 @@
+// Matrix-core FibQuant encoder for k = d = 64 (the whole rotated unit vector is
+// one block; FibQuant summary §2.3 with d/k = 1, nearest codeword among N),
+// fp16 input.  The search is a dense contraction: scores 256 (||c||^2 - 2 y.c)
+// for every (codeword, vector) pair, reduced by a minimum over codewords.
+//
+// A wave owns 32 vectors (one column tile).  The workgroup streams the codebook
+// through LDS in chunks of 8 tiles of 32 codewords (double buffered, loaded
+// straight from global memory into LDS), so every codeword read from L2 serves
+// all 16 waves.
+//
+//  1. Rotation on the fp16 matrix core (mfma_f32_32x32x16_f16): 1024 Pi split
+//     into fp16 hi + mid + lo, x is fp16, products exact, hi and mid / lo
+//     products summed in fp32 separately.  The rows of Pi are permuted so that
+//     lane l holds coordinates 32 (l / 32) .. + 31 of vector l % 32.
+//  2. -512 y is split into fp16 hi + lo; lanes exchange halves so that lane c
+//     holds hi of all 64 coordinates of vector c and lane c + 32 the lo parts:
+//     the B operands of 8 K-steps (coordinates 8 s .. 8 s + 7).
+//  3. Per codeword tile: 8 chained matrix ops starting from 256 ||c||^2; the
+//     lane keeps the minimum of its 16 rows, the second-best tile minimum, and
+//     the 16 scores of its best tile (copied when a tile improves the minimum).
+//  4. The best row of the best tile, merged over the two lanes of the column,
+//     is certified with the same error bound as the k = 4 / 8 encoder:
+//     E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y|) + 35840 sqrt(k) cmax u
+//               + 2^-25 (1 + sqrt(k) cmax)); |y| <= 1 here.
+//  5. Uncertified vectors are searched again by the whole wave in fp64 with the
+//     direct distance (lowest index on exact ties).
+#include "fq_device.h"
+#include "fq_internal.h"
+
+namespace fq {
+namespace {
+
+constexpr int D = kD;
+constexpr int WAVES = 16;
+constexpr int CT = 8;                          // codeword tiles per LDS chunk
+constexpr int ROWB = 144;                      // bytes per codeword row: 64 fp16 + 16 (256 ||c||^2 of 4 rows)
+constexpr int TILEB = 32 * ROWB;               // 4608
+constexpr int CHUNKB = CT * TILEB;             // 36864
+constexpr int SCR_DW = 2 * 64 * 2 + 16;        // per wave: x and y (fp64) of a re-searched vector + codes
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline float min16(const f32x16& v) {
+  float m = fminf(fminf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fminf(fminf(m, v[i]), v[i + 1]);
+  return fminf(m, v[15]);
+}
+
+__device__ inline double shfl_xor_f64(double v, int m) {
+  const int2 w = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __shfl_xor(w.x, m);
+  r.y = __shfl_xor(w.y, m);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline uint32_t pack_h2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Copy chunk `ch` of the tile records into LDS buffer `dst`: each wave moves
+// 1 KiB pieces (lane i: bytes 16 i .. 16 i + 15 of the piece) straight to LDS.
+__device__ inline void load_chunk(const uint8_t* __restrict__ rec, int ch, int nchunk_bytes, char* dst, int w,
+                                  int lane) {
+  const uint8_t* src = rec + (size_t)ch * CHUNKB;
+  for (int p = w; p * 1024 < nchunk_bytes; p += WAVES)
+    __builtin_amdgcn_global_load_lds(src + p * 1024 + lane * 16, (lds_void*)(dst + p * 1024), 16, 0, 0);
+}
+
+constexpr size_t full_lds_bytes() { return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4; }
+
+template <bool NF16>
+__global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
+    const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rotA,
+    const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64, int N, int bits,
+    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+  extern __shared__ uint4 smem[];
+  char* buf0 = reinterpret_cast<char*>(smem);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5;
+  uint32_t* scr = reinterpret_cast<uint32_t*>(buf0 + 2 * CHUNKB) + w * SCR_DW;
+  double* xs = reinterpret_cast<double*>(scr);  // 64 fp64
+  double* ys = xs + 64;                          // 64 fp64
+  uint32_t* spk = scr + 256;                     // 16 words: 32 codes x <= 16 bits
+  const int NT = N / 32;
+  const int nch = (NT + CT - 1) / CT;
+
+  for (int64_t base = (int64_t)blockIdx.x * WAVES; base < ngroups; base += (int64_t)gridDim.x * WAVES) {
+    const int64_t g = base + w;
+    const int64_t v0 = g * 32;
+    const int nv = g < ngroups ? (int)((n - v0) < 32 ? (n - v0) : 32) : 0;
+    const bool valid = c < nv;
+
+    // first chunk on its way while the rotation runs
+    load_chunk(rec, 0, (NT < CT ? NT : CT) * TILEB, buf0, w, lane);
+
+    // ---- 1. x, nu, rotation.  Lane l: vector l % 32, inputs 16 s + 8 h .. + 7.
+    uint4 xin[4];
+#pragma unroll
+    for (int s = 0; s < 4; s++) xin[s] = make_uint4(0u, 0u, 0u, 0u);
+    if (valid) {
+      const uint4* xp = reinterpret_cast<const uint4*>(x + (v0 + c) * D);
+#pragma unroll
+      for (int s = 0; s < 4; s++) xin[s] = xp[2 * s + h];
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const uint32_t wv[4] = {xin[s].x, xin[s].y, xin[s].z, xin[s].w};
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const double a = (double)h_lo(wv[t]), b = (double)h_hi(wv[t]);
+        sq = fma(a, a, sq);
+        sq = fma(b, b, sq);
+      }
+    }
+    sq += shfl_xor_f64(sq, 32);
+    const double nu = sqrt(sq);
+    if (h == 0 && valid) {
+      if constexpr (NF16)
+        reinterpret_cast<uint16_t*>(norms)[v0 + c] = f64_to_f16_bits(nu);
+      else
+        reinterpret_cast<float*>(norms)[v0 + c] = (float)nu;
+    }
+    const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
+
+    // An offset the compiler cannot see through: keeps the 24 operand loads inside
+    // the loop instead of hoisted into (spilled) registers.
+    int rot_off = 0;
+    __asm__ volatile("" : "+s"(rot_off));
+    uint32_t hi[16], lo[16];  // coordinates 32 h + 16 r + e as packed fp16 pairs
+#pragma unroll
+    for (int r = 0; r < 2; r++) {
+      f32x16 ah, am;
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        ah[e] = 0.f;
+        am[e] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const half8 xv = __builtin_bit_cast(half8, xin[s]);
+        const uint4* op = rotA + rot_off + ((r * 4 + s) * 3) * 64 + lane;
+        ah = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, op[0]), xv, ah, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, op[64]), xv, am, 0, 0, 0);
+        am = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, op[128]), xv, am, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float va = -512.0f * ((ah[e] + am[e]) * inv);
+        const float vb = -512.0f * ((ah[e + 1] + am[e + 1]) * inv);
+        const float ha = (float)(_Float16)va, hb = (float)(_Float16)vb;
+        hi[8 * r + e / 2] = pack_h2(ha, hb);
+        lo[8 * r + e / 2] = pack_h2(va - ha, vb - hb);
+      }
+    }
+    // ---- 2. B operands: lane c gets hi of coordinates 32 .. 63 from lane c + 32,
+    //         lane c + 32 gets lo of 0 .. 31 from lane c.
+    uint32_t bq[8][4];
+#pragma unroll
+    for (int d = 0; d < 16; d++) {
+      const uint32_t recv = (uint32_t)__shfl_xor((int)(h == 0 ? lo[d] : hi[d]), 32);
+      // coordinates 0..31 are dwords 0..15 of lane c's packs, 32..63 those of lane c + 32
+      bq[d / 4][d % 4] = h == 0 ? hi[d] : recv;
+      bq[4 + d / 4][d % 4] = h == 0 ? recv : lo[d];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+      for (int d = 0; d < 4; d++) __asm__ volatile("" : "+v"(bq[s][d]));
+
+    // ---- 3. stream the codebook
+    float m1 = __builtin_huge_valf(), m2 = __builtin_huge_valf();
+    int tid = 0;
+    f32x16 bestD;
+#pragma unroll
+    for (int e = 0; e < 16; e++) bestD[e] = __builtin_huge_valf();
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces of chunk 0 are in LDS
+    __syncthreads();
+    for (int ch = 0; ch < nch; ch++) {
+      char* cur = buf0 + (ch & 1) * CHUNKB;
+      if (ch + 1 < nch) {
+        const int nt = (NT - (ch + 1) * CT) < CT ? (NT - (ch + 1) * CT) : CT;
+        load_chunk(rec, ch + 1, nt * TILEB, buf0 + ((ch + 1) & 1) * CHUNKB, w, lane);
+      }
+      const int nt = (NT - ch * CT) < CT ? (NT - ch * CT) : CT;
+      for (int tt = 0; tt < nt; tt++) {
+        const char* tile = cur + tt * TILEB;
+        f32x16 acc;
+#pragma unroll
+        for (int a = 0; a < 4; a++) {
+          const float4 cv = *reinterpret_cast<const float4*>(tile + (8 * a + 4 * h) * ROWB + 128);
+          acc[4 * a] = cv.x;
+          acc[4 * a + 1] = cv.y;
+          acc[4 * a + 2] = cv.z;
+          acc[4 * a + 3] = cv.w;
+        }
+        const char* arow = tile + c * ROWB;
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const half8 A = *reinterpret_cast<const half8*>(arow + 16 * s);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[s]), acc, 0, 0, 0);
+        }
+        const float tm = min16(acc);
+        const bool better = tm < m1;
+        m2 = __builtin_amdgcn_fmed3f(m1, m2, tm);
+        tid = better ? ch * CT + tt : tid;
+        m1 = fminf(m1, tm);
+#pragma unroll
+        for (int e = 0; e < 16; e++) bestD[e] = better ? acc[e] : bestD[e];
+      }
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+      __syncthreads();
+    }
+
+    // ---- 4. best row of the best tile, merge, certificate
+    float r1 = __builtin_huge_valf(), r2 = __builtin_huge_valf();
+    int ri = 0;
+#pragma unroll
+    for (int e = 0; e < 16; e++) {
+      const float v = bestD[e];
+      r2 = __builtin_amdgcn_fmed3f(r1, r2, v);
+      ri = v < r1 ? e : ri;  // first (lowest row) minimum: rows grow with e
+      r1 = fminf(r1, v);
+    }
+    ri = 32 * tid + (ri >> 2) * 8 + 4 * h + (ri & 3);
+    const float o1 = __shfl_xor(r1, 32), o2 = __shfl_xor(r2, 32), om = __shfl_xor(m2, 32);
+    const int oi = __shfl_xor(ri, 32);
+    const bool other = (o1 < r1) || (o1 == r1 && oi < ri);
+    const float best = other ? o1 : r1;
+    const float second = fminf(fminf(fmaxf(r1, o1), fminf(r2, o2)), fminf(m2, om));
+    const uint32_t code = (uint32_t)(other ? oi : ri);
+    const bool sure = (second - best) > 2.0f * (e_abs + e_rel * 1.01f);
+
+    const int words = bits;  // 32 codes x bits
+    for (int i = lane; i < words; i += 64) spk[i] = 0u;
+    wave_lds_sync();
+    if (h == 0 && valid && sure) {
+      const int bo = c * bits, sh = bo & 31;
+      atomicOr(&spk[bo >> 5], code << sh);
+      if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], code >> (32 - sh));
+    }
+    // ---- 5. fp64 re-search of the uncertified vectors, one at a time
+    uint64_t todo = __ballot(h == 0 && valid && !sure);
+    while (todo) {
+      const int cc = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const double xj = (double)x[(v0 + cc) * D + lane];
+      xs[lane] = xj;
+      double s2 = xj * xj;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) s2 += shfl_xor_f64(s2, m);
+      const double nuf = sqrt(s2);
+      const double iv = nuf > 0.0 ? 1.0 / nuf : 0.0;
+      wave_lds_sync();
+      double yt = 0.0;  // coordinate `lane` of y
+      for (int j = 0; j < D; j++) yt = fma(pi64[lane * D + j], xs[j], yt);
+      ys[lane] = yt * iv;
+      wave_lds_sync();
+      double bd = __builtin_huge_val();
+      int bn = 0x7fffffff;
+      for (int nn = lane; nn < N; nn += 64) {
+        const float* cp = cw + (size_t)nn * D;
+        double dd = 0.0;
+        for (int t = 0; t < D; t++) {
+          const double df = ys[t] - (double)cp[t];
+          dd = fma(df, df, dd);
+        }
+        if (dd < bd) {
+          bd = dd;
+          bn = nn;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const double od = shfl_xor_f64(bd, m);
+        const int on = __shfl_xor(bn, m);
+        if (od < bd || (od == bd && on < bn)) {
+          bd = od;
+          bn = on;
+        }
+      }
+      if (lane == 0) {
+        const uint32_t cv = (uint32_t)bn;
+        const int bo = cc * bits, sh = bo & 31;
+        atomicOr(&spk[bo >> 5], cv << sh);
+        if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
+      }
+      wave_lds_sync();
+    }
+    wave_lds_sync();
+    if (nv > 0) {
+      const int nbytes = (nv * bits + 7) / 8;
+      uint8_t* dst = codes + g * (int64_t)(4 * bits);  // group g starts at bit g * 32 * bits
+      const int nfull = nbytes / 4;
+      for (int i = lane; i < nfull; i += 64) reinterpret_cast<uint32_t*>(dst)[i] = spk[i];
+      const int rem = nbytes - 4 * nfull;
+      if (lane < rem) dst[4 * nfull + lane] = (uint8_t)((spk[nfull] >> (8 * lane)) & 0xffu);
+    }
+    wave_lds_sync();
+  }
+}
+
+template <bool NF16>
+hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
+  const size_t lds = full_lds_bytes();
+  int per_cu = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_full<NF16>, WAVES * 64, lds);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cb->device);
+  if (e != hipSuccess) return e;
+  const int64_t ngroups = (n + 31) / 32;
+  int64_t wgs = (ngroups + WAVES - 1) / WAVES;
+  const int64_t resident = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
+  if (wgs > resident) wgs = resident;
+  hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
+                     reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),
+                     reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
+                     cb->h16_erel, codes, norms);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool encode_full_supported(const fq_codebook* cb) {
+  return cb->k == D && cb->rot32 && cb->frec && cb->N % 32 == 0 && cb->N >= 32 && cb->bits <= 16 &&
+         full_lds_bytes() <= cb->max_lds;
+}
+
+hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                              fq_dtype norm_dtype, hipStream_t s) {
+  if (!encode_full_supported(cb)) return hipErrorNotSupported;
+  return norm_dtype == FQ_F16 ? launch_full<true>(cb, x, n, codes, norms, s)
+                              : launch_full<false>(cb, x, n, codes, norms, s);
+}
+
+}  // namespace fq

@@ -1,0 +1,474 @@
+// Matrix-core FibQuant encoder for fp16 input and block sizes k = 4 and 8
+// (FibQuant summary §2.3: norm, Haar rotation of the unit vector, d/k blocks of
+// k consecutive coordinates, nearest codeword; §1: fixed-address codes).
+//
+// A wave owns a "group" of 256 blocks (16 vectors for k = 4, 32 for k = 8) at a
+// time; the workgroup keeps the codebook and the rotation operands in LDS.
+//
+//  1. Each lane loads 16 of the 64 inputs of one vector straight into the
+//     B operand of mfma_f32_16x16x32_f16 (lane l: vector l % 16, inputs
+//     32 s + 8 (l / 16) .. + 7); nu is summed in fp64 from those registers.
+//  2. Rotation on the fp16 matrix core: 1024 Pi is split exactly enough into
+//     fp16 hi + mid + lo (33 bits), x is fp16, so every product is exact; the
+//     hi products and the mid / lo products are accumulated in fp32 separately.
+//     The rows of Pi are permuted so that lane l ends up holding coordinates
+//     16 (l / 16) .. + 15 of its vector: 4 whole blocks (k = 4) or 2 (k = 8).
+//  3. Scores 256 (||c||^2 - 2 y.c) for 32 codewords x 32 blocks per
+//     mfma_f32_32x32x16_f16: A = codeword record (fp16-exact), B = -512 y split
+//     into fp16 hi (lanes 0-31) + lo (lanes 32-63).  For k = 4 the record also
+//     carries 256 ||c||^2 as fp16 hi + lo in K slots the block does not use (B
+//     holds 1 there), so the accumulator starts at 0; for k = 8 it starts at
+//     256 ||c||^2 read from LDS.  A lane keeps the minimum of its 16 rows
+//     (v_min3 chains), the best and second-best such minimum and the best
+//     tile; the next tile's matrix op is issued before this one is reduced.
+//  4. Recovery: the lane recomputes its best tile's 16 scores in fp32 FMAs,
+//     the two lanes of a column merge.
+//  5. Certificate: every computed score is within
+//        E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 35840 sqrt(k) cmax u
+//                  + 2^-25 (1 + sqrt(k) cmax)),   u = 2^-24,
+//     of the exact scaled score: (2k+3) roundings of the matrix / FMA sums, the
+//     fp16 lo parts of -512 y and of 256 ||c||^2 (2^-22 relative, 2^-25 absolute
+//     when subnormal), and the rotation: each coordinate of y is within 70 u of
+//     Pi x / nu (64 + 2 roundings of the hi sum over |Pi_t| |x| <= nu, the add,
+//     1 / nu and the product; the mid / lo sums are 2^-11 smaller), which moves
+//     a score by at most 512 |c| sqrt(k) 70 u.  The host folds E into
+//     e_abs + e_rel |y_b| (with 1.02 for the fp32 evaluation here).  If
+//     second - best > 2E the winner is the exact unique minimiser.
+//  6. Uncertified blocks are listed in LDS and searched again, one at a time by
+//     the whole wave, in fp64 with the direct distance sum_t (y_t - c_t)^2
+//     (lowest index on exact ties).
+//  7. Codes are assembled in LDS and written as whole dwords.
+#include "fq_device.h"
+#include "fq_internal.h"
+
+namespace fq {
+namespace {
+
+constexpr int D = kD;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int K>
+struct Shape;
+template <>
+struct Shape<4> {
+  static constexpr int WAVES = 8;  // 2 workgroups of 8 waves per CU
+  static constexpr int NSUB = 1;   // 16-vector rotation sub-groups per group
+};
+template <>
+struct Shape<8> {
+  static constexpr int WAVES = 16;  // the 4096-word codebook fills most of the LDS
+  static constexpr int NSUB = 2;
+};
+
+constexpr int ROT_OPS = 2 * 4 * 3 * 64;  // [k step][row tile][piece][lane] half8 operands
+constexpr int SPK_WORDS = 128;           // 256 codes x 16 bits
+constexpr int WAVE_WORDS = SPK_WORDS + 128;  // + 256 uint16 entries of uncertified blocks
+
+__device__ inline float min16(const f32x16& v) {
+  float m = fminf(fminf(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int i = 3; i < 15; i += 2) m = fminf(fminf(m, v[i]), v[i + 1]);
+  return fminf(m, v[15]);
+}
+
+__device__ inline double shfl_xor_f64(double v, int m) {
+  const int2 w = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __shfl_xor(w.x, m);
+  r.y = __shfl_xor(w.y, m);
+  return __builtin_bit_cast(double, r);
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ inline uint32_t pack_h2(float a, float b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// Bytes of dynamic LDS the kernel needs: rotation operands, codeword records,
+// 256 ||c||^2 (k = 8), and per wave the code-packing words and the list of
+// uncertified blocks.
+// Record n sits at slot n + n / 32 and 256 ||c_n||^2 at n + 4 (n / 32): without the
+// padding every tile maps to the same LDS banks, and the recovery's per-lane reads
+// (each lane in its own best tile) would all collide.
+__host__ __device__ constexpr size_t h16_lds_bytes(int K, int N, int waves) {
+  return (size_t)ROT_OPS * 16 + (size_t)(N + N / 32) * 16 + (K == 8 ? (size_t)(N + N / 8) * 4 : 0) +
+         (size_t)waves * WAVE_WORDS * 4;
+}
+__device__ inline int rslot(int n) { return n + (n >> 5); }
+__device__ inline int cslot(int n) { return n + 4 * (n >> 5); }
+
+template <int K, bool NF16>
+__global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
+    const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
+    const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
+    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+  constexpr int WAVES = Shape<K>::WAVES;
+  constexpr int NSUB = Shape<K>::NSUB;
+  constexpr int VG = 16 * NSUB;    // vectors per group
+  constexpr int DW = K / 2;        // dwords of fp16 hi (or lo) per block
+  constexpr int SLOTS = 4 / NSUB;  // block slots a lane fills per sub-group
+  extern __shared__ uint4 smem[];
+  uint4* rotL = smem;
+  uint4* recL = smem + ROT_OPS;
+  float* c2L = reinterpret_cast<float*>(recL + N + N / 32);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + (K == 8 ? N + N / 8 : 0)) + w * WAVE_WORDS;
+  uint16_t* todoL = reinterpret_cast<uint16_t*>(spk + SPK_WORDS);
+  for (int i = threadIdx.x; i < ROT_OPS; i += WAVES * 64) rotL[i] = rot16[i];
+  for (int i = threadIdx.x; i < N; i += WAVES * 64) {
+    recL[rslot(i)] = crec[i];
+    if constexpr (K == 8) c2L[cslot(i)] = cn2s[i];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 31, h = lane >> 5, q = lane >> 4, vl = lane & 15;
+  const int NT = N / 32;
+  const _Float16* cbh = reinterpret_cast<const _Float16*>(recL);  // record n: halfs 8 rslot(n) .. + 7
+
+  for (int64_t g = (int64_t)blockIdx.x * WAVES + w; g < ngroups; g += (int64_t)gridDim.x * WAVES) {
+    const int64_t v0 = g * VG;
+    const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
+
+    // ---- 1-3 per 16-vector sub-group: x, nu, rotation, B operands
+    // bq[2 sigma + hp]: B operand of the tile whose column c is block slot sigma of lane c + 32 hp.
+    uint32_t bq[8][4];
+#pragma unroll
+    for (int sg = 0; sg < NSUB; sg++) {
+      const int vec = 16 * sg + vl;
+      uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
+      if (vec < nv) {
+        const uint4* xp = reinterpret_cast<const uint4*>(x + (v0 + vec) * D);
+        xa = xp[q];
+        xb = xp[4 + q];
+      }
+      double s = 0.0;
+      {
+        const uint32_t wv[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+        for (int t = 0; t < 8; t++) {
+          const double a = (double)h_lo(wv[t]), b = (double)h_hi(wv[t]);
+          s = fma(a, a, s);
+          s = fma(b, b, s);
+        }
+      }
+      s += shfl_xor_f64(s, 16);
+      s += shfl_xor_f64(s, 32);
+      const double nu = sqrt(s);
+      if (q == 0 && vec < nv) {
+        if constexpr (NF16)
+          reinterpret_cast<uint16_t*>(norms)[v0 + vec] = f64_to_f16_bits(nu);
+        else
+          reinterpret_cast<float*>(norms)[v0 + vec] = (float)nu;
+      }
+      const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
+
+      f32x4 ah[4], am[4];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        ah[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        am[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        const half8 xv = __builtin_bit_cast(half8, ks ? xb : xa);
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const uint4* op = rotL + ((ks * 4 + r) * 3) * 64 + lane;
+          ah[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[0]), xv, ah[r], 0, 0, 0);
+          am[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[64]), xv, am[r], 0, 0, 0);
+          am[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[128]), xv, am[r], 0, 0, 0);
+        }
+      }
+      // v = -512 y for coordinates 16 q + 4 r + i; hi / lo fp16 parts packed two per dword.
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float va = -512.0f * ((ah[r][i] + am[r][i]) * inv);
+          const float vb = -512.0f * ((ah[r][i + 1] + am[r][i + 1]) * inv);
+          const float ha = (float)(_Float16)va, hb = (float)(_Float16)vb;
+          hi[2 * r + i / 2] = pack_h2(ha, hb);
+          lo[2 * r + i / 2] = pack_h2(va - ha, vb - hb);
+        }
+      // Block slots of this sub-group: k = 4: slot r = coordinates 16 q + 4 r ..;
+      // k = 8: slot 2 sg + s = coordinates 16 q + 8 s ...
+#pragma unroll
+      for (int sl = 0; sl < SLOTS; sl++) {
+        const int sigma = sg * SLOTS + sl;
+        uint32_t recv[DW];
+#pragma unroll
+        for (int d = 0; d < DW; d++) {
+          const uint32_t send = h == 0 ? lo[sl * DW + d] : hi[sl * DW + d];
+          recv[d] = (uint32_t)__shfl_xor((int)send, 32);
+        }
+#pragma unroll
+        for (int d = 0; d < DW; d++) {
+          bq[2 * sigma][d] = h == 0 ? hi[sl * DW + d] : recv[d];
+          bq[2 * sigma + 1][d] = h == 0 ? recv[d] : lo[sl * DW + d];
+        }
+        if constexpr (K == 4) {
+          bq[2 * sigma][2] = bq[2 * sigma + 1][2] = h == 0 ? 0x3c003c00u : 0u;  // 1.0, 1.0 against 256 ||c||^2
+          bq[2 * sigma][3] = bq[2 * sigma + 1][3] = 0u;
+        }
+      }
+    }
+
+    // The operands are opaque from here on: otherwise the compiler folds the
+    // recovery's selects through the ones above and keeps hi / lo alive as well.
+#pragma unroll
+    for (int tb = 0; tb < 8; tb++)
+#pragma unroll
+      for (int d = 0; d < 4; d++) __asm__ volatile("" : "+v"(bq[tb][d]));
+
+    // ---- 3b. matrix-core search with per-lane tile minima
+    float m1[8], m2[8];
+    int tid[8];
+#pragma unroll
+    for (int tb = 0; tb < 8; tb++) {
+      m1[tb] = __builtin_huge_valf();
+      m2[tb] = __builtin_huge_valf();
+      tid[tb] = 0;
+    }
+    half8 A = __builtin_bit_cast(half8, recL[c]);
+    for (int t = 0; t < NT; t++) {
+      const half8 An = __builtin_bit_cast(half8, recL[(t + 1 < NT ? 33 * (t + 1) : 0) + c]);
+      f32x16 C;
+      if constexpr (K == 8) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float4 cv = *reinterpret_cast<const float4*>(c2L + 36 * t + 8 * j + 4 * h);
+          C[4 * j] = cv.x;
+          C[4 * j + 1] = cv.y;
+          C[4 * j + 2] = cv.z;
+          C[4 * j + 3] = cv.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; e++) C[e] = 0.f;
+      }
+      f32x16 Dc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[0]), C, 0, 0, 0);
+#pragma unroll
+      for (int tb = 0; tb < 8; tb++) {
+        f32x16 Dn;
+        if (tb < 7) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[tb + 1]), C, 0, 0, 0);
+        const float tm = min16(Dc);
+        m2[tb] = __builtin_amdgcn_fmed3f(m1[tb], m2[tb], tm);
+        tid[tb] = tm < m1[tb] ? t : tid[tb];
+        m1[tb] = fminf(m1[tb], tm);
+        if (tb < 7) Dc = Dn;
+      }
+      A = An;
+    }
+
+    // ---- 4-5. recovery and certificate; uncertified blocks go to a list
+    uint32_t code[8];  // code | block index << 16, or ~0 when there is nothing to pack from this lane
+    int ntodo = 0;
+#pragma unroll
+    for (int tb = 0; tb < 8; tb++) {
+      const int sigma = tb >> 1, hp = tb & 1;
+      // hi and lo of this column's block: one half is ours, the partner lane holds the other
+      float vp[K];
+      {
+        uint32_t X[DW];
+#pragma unroll
+        for (int d = 0; d < DW; d++) X[d] = (uint32_t)__shfl_xor((int)bq[tb][d], 32);
+#pragma unroll
+        for (int d = 0; d < DW; d++) {
+          const uint32_t hw = h == 0 ? bq[tb][d] : X[d];
+          const uint32_t lw = h == 0 ? X[d] : bq[tb][d];
+          vp[2 * d] = h_lo(hw) + h_lo(lw);  // exact: the value the matrix core multiplied
+          vp[2 * d + 1] = h_hi(hw) + h_hi(lw);
+        }
+      }
+      float vn2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < K; i++) vn2 = fmaf(vp[i], vp[i], vn2);
+      const int t0 = tid[tb];
+      float r1 = __builtin_huge_valf(), r2 = __builtin_huge_valf();
+      int ri = 0;
+#pragma unroll
+      for (int qq = 0; qq < 4; qq++) {
+        const int n0 = 32 * t0 + 8 * qq + 4 * h;  // rows n0 .. n0 + 3 of this lane
+        float4 c2v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (K == 8) c2v = *reinterpret_cast<const float4*>(c2L + cslot(n0));
+        const float c2a[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const uint4 rw = recL[rslot(n0 + e)];
+          const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
+          float sc;
+          if constexpr (K == 4)
+            sc = h_lo(ww[2]) + h_hi(ww[2]);  // 256 ||c||^2 as stored (hi + lo, exact)
+          else
+            sc = c2a[e];
+#pragma unroll
+          for (int i = 0; i < K; i += 2) {
+            sc = fmaf(h_lo(ww[i / 2]), vp[i], sc);
+            sc = fmaf(h_hi(ww[i / 2]), vp[i + 1], sc);
+          }
+          r2 = __builtin_amdgcn_fmed3f(r1, r2, sc);
+          ri = sc < r1 ? (n0 + e) : ri;
+          r1 = fminf(r1, sc);
+        }
+      }
+      const float o1 = __shfl_xor(r1, 32), o2 = __shfl_xor(r2, 32), om = __shfl_xor(m2[tb], 32);
+      const int oi = __shfl_xor(ri, 32);
+      const bool other = (o1 < r1) || (o1 == r1 && oi < ri);
+      const float best = other ? o1 : r1;
+      const float second = fminf(fminf(fmaxf(r1, o1), fminf(r2, o2)), fminf(m2[tb], om));
+      // block of this column: slot sigma of lane o = c + 32 hp
+      const int o = c + 32 * hp;
+      const int vec = K == 4 ? (o & 15) : 16 * (sigma >> 1) + (o & 15);
+      const int bi = K == 4 ? 4 * (o >> 4) + sigma : 2 * (o >> 4) + (sigma & 1);
+      const float yn = __builtin_sqrtf(vn2) * (1.01f / 512.0f);
+      const bool sure = (second - best) > 2.0f * (e_abs + e_rel * yn);
+      const bool mine = h == 0 && vec < nv;
+      code[tb] = (mine && sure) ? ((uint32_t)(other ? oi : ri) | ((uint32_t)(vec * (D / K) + bi) << 16)) : ~0u;
+      const uint64_t um = __ballot(mine && !sure);
+      if (um) {
+        if (mine && !sure) {
+          const int pos = ntodo + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
+          todoL[pos] = (uint16_t)((tb << 8) | c);
+        }
+        ntodo += __builtin_popcountll(um);
+      }
+    }
+
+    // ---- 6-7. pack the certified codes, search the listed blocks again in fp64, store
+    const int words = 8 * bits;
+    for (int i = lane; i < words; i += 64) spk[i] = 0u;
+    wave_lds_sync();
+#pragma unroll
+    for (int tb = 0; tb < 8; tb++) {
+      if (code[tb] != ~0u) {
+        const uint32_t cv = code[tb] & 0xffffu;
+        const int bo = (int)(code[tb] >> 16) * bits, sh = bo & 31;
+        atomicOr(&spk[bo >> 5], cv << sh);
+        if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
+      }
+    }
+    for (int it = 0; it < ntodo; it++) {
+      const int ent = __builtin_amdgcn_readfirstlane((int)todoL[it]);
+      const int tb = ent >> 8, cc = ent & 255;
+      const int sigma = tb >> 1, hp = tb & 1;
+      const int oc = cc + 32 * hp;
+      const int fvec = K == 4 ? (oc & 15) : 16 * (sigma >> 1) + (oc & 15);
+      const int fbi = K == 4 ? 4 * (oc >> 4) + sigma : 2 * (oc >> 4) + (sigma & 1);
+      // exact y_b: every lane contributes coordinate j = lane of x
+      const double xj = (double)x[(v0 + fvec) * D + lane];
+      double s2 = xj * xj;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) s2 += shfl_xor_f64(s2, m);
+      const double nuf = sqrt(s2);
+      const double inv = nuf > 0.0 ? 1.0 / nuf : 0.0;
+      double yb[K];
+#pragma unroll
+      for (int i = 0; i < K; i++) {
+        double p = pi64[(fbi * K + i) * D + lane] * xj;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) p += shfl_xor_f64(p, m);
+        yb[i] = p * inv;
+      }
+      double bd = __builtin_huge_val();
+      int bn = 0x7fffffff;
+      for (int nn = lane; nn < N; nn += 64) {
+        double dd = 0.0;
+#pragma unroll
+        for (int i = 0; i < K; i++) {
+          const double df = yb[i] - (double)cbh[8 * rslot(nn) + i];
+          dd = fma(df, df, dd);
+        }
+        if (dd < bd) {
+          bd = dd;
+          bn = nn;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const double od = shfl_xor_f64(bd, m);
+        const int on = __shfl_xor(bn, m);
+        if (od < bd || (od == bd && on < bn)) {
+          bd = od;
+          bn = on;
+        }
+      }
+      if (lane == 0) {
+        const uint32_t cv = (uint32_t)bn;
+        const int bo = (fvec * (D / K) + fbi) * bits, sh = bo & 31;
+        atomicOr(&spk[bo >> 5], cv << sh);
+        if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
+      }
+    }
+    wave_lds_sync();
+    {
+      const int64_t nbytes = ((int64_t)nv * (D / K) * bits + 7) / 8;
+      uint8_t* dst = codes + g * (int64_t)(32 * bits);  // group g starts at bit g * 256 * bits
+      const int nfull = (int)(nbytes / 4);
+      for (int i = lane; i < nfull; i += 64) reinterpret_cast<uint32_t*>(dst)[i] = spk[i];
+      const int rem = (int)(nbytes - 4 * (int64_t)nfull);
+      if (lane < rem) dst[4 * nfull + lane] = (uint8_t)((spk[nfull] >> (8 * lane)) & 0xffu);
+    }
+    wave_lds_sync();
+  }
+}
+
+// Workgroups that stay resident at once (persistent grid size), per instantiation.
+template <int K, bool NF16>
+hipError_t resident_wgs(const fq_codebook* cb, size_t lds, int64_t* out) {
+  int per_cu = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_h16<K, NF16>, Shape<K>::WAVES * 64, lds);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cb->device);
+  if (e != hipSuccess) return e;
+  *out = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
+  return hipSuccess;
+}
+
+template <int K, bool NF16>
+hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
+  constexpr int WAVES = Shape<K>::WAVES;
+  constexpr int VG = 16 * Shape<K>::NSUB;
+  const size_t lds = h16_lds_bytes(K, cb->N, WAVES);
+  int64_t resident = 0;
+  const hipError_t e = resident_wgs<K, NF16>(cb, lds, &resident);
+  if (e != hipSuccess) return e;
+  const int64_t ngroups = (n + VG - 1) / VG;
+  int64_t wgs = (ngroups + WAVES - 1) / WAVES;
+  if (wgs > resident) wgs = resident;
+  hipLaunchKernelGGL((encode_h16<K, NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
+                     reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot16),
+                     reinterpret_cast<const uint4*>(cb->crec), cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
+                     cb->h16_erel, codes, norms);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool encode_h16_supported(const fq_codebook* cb) {
+  if (!cb->rot16 || !cb->crec || cb->N % 32 != 0 || cb->N < 32) return false;
+  if (!((cb->k == 4 && cb->N <= 2048) || (cb->k == 8 && cb->N <= 4096))) return false;
+  const int waves = cb->k == 4 ? Shape<4>::WAVES : Shape<8>::WAVES;
+  return h16_lds_bytes(cb->k, cb->N, waves) <= cb->max_lds;
+}
+
+hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                             fq_dtype norm_dtype, hipStream_t s) {
+  if (!encode_h16_supported(cb)) return hipErrorNotSupported;
+  const bool nf = norm_dtype == FQ_F16;
+  if (cb->k == 4) return nf ? launch_h16<4, true>(cb, x, n, codes, norms, s) : launch_h16<4, false>(cb, x, n, codes, norms, s);
+  return nf ? launch_h16<8, true>(cb, x, n, codes, norms, s) : launch_h16<8, false>(cb, x, n, codes, norms, s);
+}
+
+}  // namespace fq

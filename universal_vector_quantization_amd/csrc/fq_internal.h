@@ -30,7 +30,20 @@ struct fq_codebook {
   double* pi64;     // [d][d] Pi row-major, fp64
   _Float16* dec_a;  // [2 row tiles][4 k steps][hi, lo][64 lanes][8]: Pi^T as the A operand of
                     // mfma_f32_32x32x16_f16 for the decoder (row = output dim, k = input dim)
+  // Operands of the fp16-input matrix-core encoder (k = 4 or 8, N a multiple of 32; else null):
+  _Float16* rot16;  // [2 k steps][4 row tiles][hi, mid, lo][64 lanes][8]: 1024 Pi split into three
+                    // fp16 parts, as the A operand of mfma_f32_16x16x32_f16; row rho of tile r is
+                    // coordinate 16 (rho / 4) + 4 r + rho % 4, k is input 32 s + 8 (lane / 16) + j
+  _Float16* crec;   // [N][8]: codeword records, k = 4: c0..c3, hi, lo of 256 ||c||^2, 0, 0; k = 8: c0..c7
+  // Operands of the k = d = 64 matrix-core encoder (N a multiple of 32; else null):
+  _Float16* rot32;  // [2 row tiles][4 k steps][hi, mid, lo][64 lanes][8]: 1024 Pi as the A operand of
+                    // mfma_f32_32x32x16_f16; row 8 a + 4 hh + b of tile r is coordinate 32 hh + 16 r + 4 a + b
+  uint8_t* frec;    // [N / 32 tiles][32 rows][144 bytes], zero-padded to whole chunks of 8 tiles:
+                    // 64 fp16 coordinates, then (rows 4 m only) 256 ||c||^2 of rows 4 m .. 4 m + 3 (fp32)
+  float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
+  size_t max_lds;   // bytes of LDS one workgroup may use on the device
   bool force_valu;  // FQ_ENCODE_KERNEL=valu at load time: always use the one-lane-per-vector encoder
+  bool force_mfma64;  // FQ_ENCODE_KERNEL=mfma64: the fp64-rotation matrix-core encoder for every input dtype
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
 };
 
@@ -41,6 +54,14 @@ constexpr int kD = 64;
 // Matrix-core encoder; returns hipErrorNotSupported when the codebook shape is not covered.
 hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                               void* norms, fq_dtype norm_dtype, hipStream_t s);
+// Matrix-core encoder for fp16 input (fp16-split rotation); see encode_h16_supported.
+bool encode_h16_supported(const fq_codebook* cb);
+hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                             fq_dtype norm_dtype, hipStream_t s);
+// Matrix-core encoder for k = d = 64 and fp16 input; see encode_full_supported.
+bool encode_full_supported(const fq_codebook* cb);
+hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                              fq_dtype norm_dtype, hipStream_t s);
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, hipStream_t s);
 hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
