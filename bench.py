@@ -244,7 +244,7 @@ def main():
     enc_bytes = n * (D * 2 + 2) + cb.code_bytes(n)
     dec_bytes = enc_bytes
     att_bytes = 2 * cb.code_bytes(n // 2) + 2 * (n // 2) * 2 + L * H * D * 2 + L * H * D * 4
-    traffic = measured_traffic("encode_mfma_k4", "fq_encode_mfma.hip")
+    traffic = measured_traffic("encode_h16_k4", "fq_encode_h16.hip")
     line = {
         "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -257,11 +257,14 @@ def main():
         "breakdown_GBps": {"encode": enc_bytes / (ms["enc"] / 1e3) / 1e9,
                            "decode": dec_bytes / (ms["dec"] / 1e3) / 1e9,
                            "attention": att_bytes / (ms["att"] / 1e3) / 1e9},
-        "roofline": {"kernel": "encode_mfma<k=4> (fq_encode)", "bound": "alu", "achieved": achieved,
+        "roofline": {"kernel": "encode_h16<k=4> (fq_encode, fp16 input)", "bound": "alu", "achieved": achieved,
                      "peak": CMP_PEAK_T, "unit": "TFLOP/s", "frac": achieved / CMP_PEAK_T,
                      "traffic": traffic,
                      "work": f"{cmp_per_vec} candidate-score comparisons per vector ((d/k) N) x {n} vectors; "
-                             f"peak = 2 comparisons per VALU lane-op (three-input min) x 39.3 T lane-ops/s"},
+                             f"peak = 2 comparisons per VALU lane-op (three-input min) x 39.3 T lane-ops/s",
+                     # the same time against the VALU-search model (k/2 + 1 lane-ops per score: packed
+                     # FMAs plus a select), for comparison with designs that score on the VALU
+                     "frac_vs_valu_search_model": cmp_per_vec * (w.k / 2 + 1) * n / VALU_LANE_OPS / enc_s},
     }
 
     # ---------------------------------------------------------------- decode-attention workload
@@ -296,9 +299,10 @@ def main():
             "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms, cache flushed per launch",
             "us_per_step": t_att * 1e6, "hbm_bytes": abytes, "GBps": abytes / t_att / 1e9,
             "fp16_equiv_GBps": 2 * na * D * 2 / t_att / 1e9,
-            "roofline": {"bound": "hbm", "achieved": abytes / t_att / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "roofline": {"kernel": "attn_k4b8 (+ attn_combine: the events bracket the whole fq_attn_decode call)",
+                         "bound": "hbm", "achieved": abytes / t_att / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": abytes / t_att / 1e9 / HBM_PEAK_GBPS,
-                         "traffic": measured_traffic("attn_split_k4", "fq_attn.hip")},
+                         "traffic": measured_traffic("attn_k4b8", "fq_attn.hip")},
         }
         del flush
 

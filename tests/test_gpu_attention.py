@@ -102,6 +102,25 @@ def test_attention_full_size_sampled_heads(dev, cb4):
         assert max_rel_rows(got[b:b + 1, g * G:(g + 1) * G], ref) <= TOL
 
 
+def test_attention_multi_chunk_workgroups(dev, cb4):
+    # B=16, Hkv=4, T=16392: each workgroup of the fast path owns two 512-token
+    # chunks and the last chunk holds 8 tokens (three of its four waves see none);
+    # sampled (batch, KV head) groups checked against the oracle.
+    cb, cw, rot = cb4
+    B, Hq, Hkv, T = 16, 32, 4, 16392
+    kc, kn, vc, vn = _random_cache(B, Hkv, T, 5151)
+    q = np.random.default_rng(12).standard_normal((B, Hq, D)).astype(np.float16)
+    print("[attention multi-chunk] B=16 Hq=32 Hkv=4 T=16392", flush=True)
+    got = _gpu_attn(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, T)
+    G = Hq // Hkv
+    for b, g in [(0, 0), (9, 2), (15, 3)]:
+        idx = np.arange(T) + (b * Hkv + g) * T
+        ref = oatt.attention(q[b:b + 1, g * G:(g + 1) * G], unpack_sampled(kc, idx, 16, 8).reshape(1, 1, T, 16),
+                             kn[idx].reshape(1, 1, T), unpack_sampled(vc, idx, 16, 8).reshape(1, 1, T, 16),
+                             vn[idx].reshape(1, 1, T), rot, cw, 0.125)
+        assert max_rel_rows(got[b:b + 1, g * G:(g + 1) * G], ref) <= TOL
+
+
 def test_attention_on_oracle_encoded_cache(dev, cb4):
     # Keys and values are real encodes (by the oracle) of the attention workload's
     # first (batch, KV head) slab, truncated to 4096 tokens.

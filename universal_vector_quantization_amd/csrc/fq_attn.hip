@@ -281,270 +281,302 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
 }
 
 // ---------------------------------------------------------------------------
-// Fast path for k = 4 with 8-bit codes (N <= 256), the attention workload's
-// codebook.  Differences from attn_split:
-//   * MFMA k-slot (lane group q, element j) of k-step s carries dimension
-//     16q + 8s + j, i.e. blocks 4q + 2s and 4q + 2s + 1, so a lane's four codes
-//     for one token are one aligned dword of the token's 16-byte code record and
-//     one load instruction reads 16 consecutive records (256 B, coalesced).
-//   * The value transpose selects, for k-step s and half hh, the dims
-//     32hh + 16(r/8) + 8s + r%8 (r = 0..15); the accumulator rows follow that
-//     order and are put back in place when the partial record is written.
-//   * The next tile's codes and norms are loaded before the current tile is
-//     processed; token offsets are 32-bit within one (batch, KV head) slab;
-//     only the last tile of a chunk carries masks; the rotated queries come
-//     precomputed from attn_prep.
+// Fast path: k = 4 with 8-bit codes (N = 256), up to 8 query heads per KV head,
+// T a multiple of 8 (the attention workload's shape).  Differences from
+// attn_split:
+//   * Query hi and lo parts sit in different MFMA columns (heads in 0..7, their
+//     lo parts in 8..15), so QK takes 4 matrix ops per 32 tokens; one DPP add
+//     (lane col + lane col ^ 8) recombines them.
+//   * PV puts P' hi in rows 0..7 and lo in rows 8..15 (summed once at the end)
+//     and reads the value operand transposed straight from the LDS codebook
+//     with ds_read_tr16_b64: lane 4a + b of a 16-lane group receives element b
+//     of the 8-byte rows addressed by lanes a, a+4, a+8, a+12, so lanes
+//     address (token a', block) rows and receive 4 tokens of one dimension.
+//     The K order inside a 32-token tile is permuted (k = 8 grp + 4 a + i is
+//     token 16 a + 4 grp + i) so P' comes straight from the QK registers.
+//   * A wave computes all scores of its 128 tokens of a chunk first, so the
+//     running max and the rescaling happen once per chunk, not per tile.
+//   * A workgroup is persistent over `cpw` consecutive chunks of one (batch,
+//     KV head) slab and double-buffers them in LDS with direct global-to-LDS
+//     loads; it writes one partial record per query head.
+constexpr int FC = 512;  // tokens per chunk
+constexpr int GF = 8;    // query heads per KV head on the fast path
+constexpr int CB_KC = 0, CB_VC = FC * 16, CB_KN = 2 * FC * 16, CB_VN = 2 * FC * 16 + FC * 2;
+constexpr int CB_BYTES = 2 * FC * 16 + 4 * FC;  // 18432
+
+typedef short short4_ __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_ lds_s4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 __device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, uint32_t c1) {
   const half4 a = *reinterpret_cast<const half4*>(cbL + c0 * 4);
   const half4 b = *reinterpret_cast<const half4*>(cbL + c1 * 4);
   return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-__device__ inline float h16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
-__device__ inline float h16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+__device__ inline _Float16 hlo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ inline _Float16 hhi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-struct TileData {
-  uint32_t kd[2], vd[2];   // code dwords of tokens t0 + 16a + col (lane group grp)
-  float kv[2][4], vv[2][4];  // norms of tokens t0 + 16a + 4grp + i
-};
-
-struct AttnState {
-  float m, l;
-  f32x4 o[4];
-};
-
-template <bool MASK>
-__device__ inline void process_tile(AttnState& st, const TileData& d, const _Float16* __restrict__ cbL,
-                                    const half8 (&qhi)[2], const half8 (&qlo)[2], const half8 (&isel)[2], int t0,
-                                    int tend, int grp) {
-  const float NEG = -__builtin_huge_valf();
-  float L[2][4];
-#pragma unroll
-  for (int a = 0; a < 2; a++) {
-    const uint32_t w = d.kd[a];
-    const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
-    const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    S = mfma16(k0, qhi[0], S);
-    S = mfma16(k0, qlo[0], S);
-    S = mfma16(k1, qhi[1], S);
-    S = mfma16(k1, qlo[1], S);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      L[a][i] = S[i] * d.kv[a][i];
-      if constexpr (MASK) L[a][i] = (t0 + 16 * a + 4 * grp + i) < tend ? L[a][i] : NEG;
-    }
-  }
-  float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
-                   fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mn = fmaxf(st.m, mx);  // finite: the tile holds at least one token
-  const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
-  st.l *= alpha;
-#pragma unroll
-  for (int c = 0; c < 4; c++) st.o[c] *= alpha;
-  half8 phi, plo;
-#pragma unroll
-  for (int a = 0; a < 2; a++) {
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float p = __builtin_amdgcn_exp2f(L[a][i] - mn);
-      st.l += p;
-      const float pv = p * d.vv[a][i];
-      const _Float16 hv = (_Float16)pv;
-      phi[4 * a + i] = hv;
-      plo[4 * a + i] = (_Float16)(pv - (float)hv);
-    }
-  }
-  half8 av[4];
-#pragma unroll
-  for (int a = 0; a < 2; a++) {
-    const uint32_t w = d.vd[a];
-    const half8 v0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
-    const half8 v1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
-#pragma unroll
-    for (int c = 0; c < 4; c++) {  // value tile c = (k-step c >> 1, half c & 1)
-      const f32x4 X = mfma16((c >> 1) ? v1 : v0, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    st.o[c] = mfma16(av[c], phi, st.o[c]);
-    st.o[c] = mfma16(av[c], plo, st.o[c]);
-  }
-  st.m = mn;
+// value of lane (l ^ 8) within its 16-lane row
+__device__ inline float swap8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, true));
 }
 
-// Chunk-resident variant: the workgroup first copies its whole chunk (codes and
-// norms of up to FCHUNK tokens, ~34 KB) into LDS with every load in flight at
-// once, then the waves run the tile loop from LDS.  With several workgroups
-// per CU one loads while another computes.
-constexpr int FCHUNK = 512;
-
-template <bool NAL>
-__global__ __launch_bounds__(AW * 64) void attn_split_k4b8(
-    const float* __restrict__ qrot, const uint32_t* __restrict__ kc, const _Float16* __restrict__ kn,
-    const uint32_t* __restrict__ vc, const _Float16* __restrict__ vn, const _Float16* __restrict__ cw16, int N,
-    int Hq, int Hkv, int64_t T, int nchunks, float* __restrict__ ws) {
-  __shared__ __align__(16) uint32_t kcL[FCHUNK * 4];
-  __shared__ __align__(16) uint32_t vcL[FCHUNK * 4];
-  __shared__ __align__(16) _Float16 knL[FCHUNK];
-  __shared__ __align__(16) _Float16 vnL[FCHUNK];
-  __shared__ __align__(16) _Float16 cbL[256 * 4];
-  __shared__ float sm[AW * GMAX], sl[AW * GMAX];
-  __shared__ float so[AW * GMAX * D];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
-  const int64_t base = ((int64_t)b * Hkv + g) * T + (int64_t)chunk * FCHUNK;
-  const int rem = (int)(T - (int64_t)chunk * FCHUNK);
-  const int nt = rem < FCHUNK ? rem : FCHUNK;
-
-  // ---- bulk copy: codes (16 B per token), norms, codebook
-  {
-    const uint4* ks = reinterpret_cast<const uint4*>(kc) + base;
-    const uint4* vs = reinterpret_cast<const uint4*>(vc) + base;
-    uint4 kr[FCHUNK / (AW * 64)], vr[FCHUNK / (AW * 64)];
-#pragma unroll
-    for (int i = 0; i < FCHUNK / (AW * 64); i++) {
-      const int t = tid + i * AW * 64;
-      kr[i] = t < nt ? ks[t] : make_uint4(0u, 0u, 0u, 0u);
-      vr[i] = t < nt ? vs[t] : make_uint4(0u, 0u, 0u, 0u);
+// Codes and norms of chunk `c` of the slab into LDS buffer `dst`: 18 pieces of
+// 1 KiB (8 of K codes, 8 of V codes, K norms, V norms); lane i of a piece
+// moves bytes 16 i .. 16 i + 15, and only bytes of tokens below `nt` are read.
+__device__ inline void attn_chunk_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                       const _Float16* __restrict__ kn, const _Float16* __restrict__ vn,
+                                       int64_t tok0, int nt, char* dst, int w, int lane) {
+  for (int p = w; p < 18; p += AW) {
+    const uint8_t* src;
+    int first;  // first token of the lane's 16 bytes
+    if (p < 16) {
+      const int t = 64 * (p & 7) + lane;
+      src = ((p < 8) ? kc : vc) + (tok0 + t) * 16;
+      first = t;
+    } else {
+      src = reinterpret_cast<const uint8_t*>(((p == 16) ? kn : vn) + tok0 + 8 * lane);
+      first = 8 * lane;  // T % 8 == 0, so the 8 norms are all valid or all past the end
     }
-    uint4 nr = make_uint4(0u, 0u, 0u, 0u);
-    const int q = tid & 63;  // 64 threads x 8 norms per array
-    const _Float16* nsrc = (tid < 64 ? kn : vn) + base;
-    if (tid < 128) {
-      if (NAL && 8 * q + 7 < nt) {
-        nr = reinterpret_cast<const uint4*>(nsrc)[q];
-      } else {
-        uint16_t hv[8];
+    if (first < nt) __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + p * 1024), 16, 0, 0);
+  }
+}
+
+// One wave's 128 tokens [tw, tw + 128) of the chunk in LDS `cur`, as two halves
+// of 64 tokens: scores first, then one max / rescale, then the exponentials and
+// PV.  MASK: tokens at or past `nt` are excluded.
+template <bool MASK>
+__device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float16* __restrict__ cbL,
+                                      const half8 (&qb)[2], int tw, int nt, int col, int grp, bool hi_col,
+                                      float& m_run, float& l_run, f32x4 (&O)[4]) {
+  const float NEG = -__builtin_huge_valf();
+#pragma unroll 1
+  for (int hf = 0; hf < 2; hf++) {
+    // ---- scores: L[u][a][i] is token tw + 64 hf + 32 u + 16 a + 4 grp + i
+    float L[2][2][4];
 #pragma unroll
-        for (int j = 0; j < 8; j++)
-          hv[j] = 8 * q + j < nt ? __builtin_bit_cast(uint16_t, nsrc[8 * q + j]) : (uint16_t)0;
-        nr = make_uint4(hv[0] | (uint32_t)hv[1] << 16, hv[2] | (uint32_t)hv[3] << 16, hv[4] | (uint32_t)hv[5] << 16,
-                        hv[6] | (uint32_t)hv[7] << 16);
+    for (int u = 0; u < 2; u++) {
+      const int tb = tw + 64 * hf + 32 * u;
+#pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const uint32_t* rec = reinterpret_cast<const uint32_t*>(cur + CB_KC + (tb + 16 * a + col) * 16);
+        const uint32_t w0 = rec[grp >> 1], w1 = rec[2 + (grp >> 1)];
+        const int sh = (grp & 1) * 16;
+        const half8 k0 = gather2(cbL, __builtin_amdgcn_ubfe(w0, sh, 8), __builtin_amdgcn_ubfe(w0, sh + 8, 8));
+        const half8 k1 = gather2(cbL, __builtin_amdgcn_ubfe(w1, sh, 8), __builtin_amdgcn_ubfe(w1, sh + 8, 8));
+        f32x4 S = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        S = mfma16(k1, qb[1], S);
+        const uint2 nw = *reinterpret_cast<const uint2*>(cur + CB_KN + 2 * (tb + 16 * a + 4 * grp));
+        const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float st = S[i] + swap8(S[i]);
+          L[u][a][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
+          if constexpr (MASK) L[u][a][i] = (tb + 16 * a + 4 * grp + i) < nt ? L[u][a][i] : NEG;
+        }
       }
     }
-    for (int w = tid; w < N * 4 * 2 / 16; w += AW * 64)
-      reinterpret_cast<uint4*>(cbL)[w] = reinterpret_cast<const uint4*>(cw16)[w];
+    // ---- max per head over these 64 tokens and rescaling of the running state
+    float mx = NEG;
 #pragma unroll
-    for (int i = 0; i < FCHUNK / (AW * 64); i++) {
-      const int t = tid + i * AW * 64;
-      reinterpret_cast<uint4*>(kcL)[t] = kr[i];
-      reinterpret_cast<uint4*>(vcL)[t] = vr[i];
-    }
-    if (tid < 128) reinterpret_cast<uint4*>(tid < 64 ? knL : vnL)[q] = nr;
-  }
-
-  const int col = lane & 15, grp = lane >> 4;
-  half8 qhi[2], qlo[2], isel[2];
-  {
-    const float* qr = qrot + ((int64_t)b * Hq + (int64_t)g * G + (col < G ? col : 0)) * D;
+    for (int u = 0; u < 2; u++)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float v = col < G ? qr[16 * grp + 8 * s2 + j] : 0.f;
-        const _Float16 hv = (_Float16)v;
-        qhi[s2][j] = hv;
-        qlo[s2][j] = (_Float16)(v - (float)hv);
-        isel[s2][j] = (_Float16)((grp == 2 * s2 + col / 8 && j == col % 8) ? 1.0f : 0.0f);
-      }
-    }
-  }
-  __syncthreads();
-
-  AttnState st;
-  st.m = -__builtin_huge_valf();
-  st.l = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; c++) st.o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int t0 = wave * TILE;
-  TileData d;
-  for (; t0 < nt; t0 += AW * TILE) {
-#pragma unroll
-    for (int a = 0; a < 2; a++) {
-      d.kd[a] = kcL[(t0 + 16 * a + col) * 4 + grp];
-      d.vd[a] = vcL[(t0 + 16 * a + col) * 4 + grp];
-      const uint2 kw = *reinterpret_cast<const uint2*>(knL + t0 + 16 * a + 4 * grp);
-      const uint2 vw = *reinterpret_cast<const uint2*>(vnL + t0 + 16 * a + 4 * grp);
-      d.kv[a][0] = h16lo(kw.x);
-      d.kv[a][1] = h16hi(kw.x);
-      d.kv[a][2] = h16lo(kw.y);
-      d.kv[a][3] = h16hi(kw.y);
-      d.vv[a][0] = h16lo(vw.x);
-      d.vv[a][1] = h16hi(vw.x);
-      d.vv[a][2] = h16lo(vw.y);
-      d.vv[a][3] = h16hi(vw.y);
-    }
-    if (t0 + TILE <= nt)
-      process_tile<false>(st, d, cbL, qhi, qlo, isel, t0, nt, grp);
-    else
-      process_tile<true>(st, d, cbL, qhi, qlo, isel, t0, nt, grp);
-  }
-
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (grp == 0) {
-    sm[wave * GMAX + col] = st.m;
-    sl[wave * GMAX + col] = l;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const int s2 = c >> 1, hh = c & 1;
+      for (int a = 0; a < 2; a++)
+        mx = fmaxf(fmaxf(mx, fmaxf(L[u][a][0], L[u][a][1])), fmaxf(L[u][a][2], L[u][a][3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (MASK && mx == NEG) continue;  // no tokens of the wave here (uniform)
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
+    l_run *= alpha;
+    // accumulator rows 4 grp + i belong to head 4 (grp & 1) + i
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const int r = 4 * grp + i;
-      so[(wave * GMAX + col) * D + 32 * hh + 16 * (r >> 3) + 8 * s2 + (r & 7)] = st.o[c][i];
+      const float ai = __shfl(alpha, 4 * (grp & 1) + i);
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) O[dt][i] *= ai;
     }
+    m_run = m_new;
+
+    // ---- P' = p nu_v (hi in rows 0..7, lo in rows 8..15) and PV
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int tb = tw + 64 * hf + 32 * u;
+      uint32_t Pw[4];  // P' as 4 packed fp16 pairs: element 4 a + i
+#pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const uint2 nw = *reinterpret_cast<const uint2*>(cur + CB_VN + 2 * (tb + 16 * a + 4 * grp));
+        const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float p = __builtin_amdgcn_exp2f(L[u][a][i] - m_new);  // 0 for masked tokens
+          l_run += p;
+          pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
+          if constexpr (MASK) pv[i] = (tb + 16 * a + 4 * grp + i) < nt ? pv[i] : 0.f;
+        }
+        // hi rounds toward zero (any rounding works: lo takes the exact remainder)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[i], pv[i + 1]));
+          const float ra = __builtin_fmaf((float)hlo(hw), -1.0f, pv[i]);
+          const float rb = __builtin_fmaf((float)hhi(hw), -1.0f, pv[i + 1]);
+          const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+          Pw[2 * a + i / 2] = hi_col ? hw : lw;
+        }
+      }
+      const half8 P = __builtin_bit_cast(half8, uint4{Pw[0], Pw[1], Pw[2], Pw[3]});
+      // value operands: this lane addresses token tb + 16 a + 4 grp + col / 4, block 4 dt + col % 4
+      short4_ vt[2][4];
+#pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const uint4 rw = *reinterpret_cast<const uint4*>(cur + CB_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16);
+        const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int sh = 8 * (col & 3);
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++)
+          vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + __builtin_amdgcn_ubfe(ww[dt], sh, 8) * 4));
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        const short4_ v0 = vt[0][dt], v1 = vt[1][dt];
+        const half8 V = __builtin_bit_cast(half8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        O[dt] = mfma16(P, V, O[dt]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q, const float* __restrict__ pi32,
+                                                        float qscale, const uint8_t* __restrict__ kc,
+                                                     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
+                                                     const _Float16* __restrict__ vn,
+                                                     const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
+                                                     int nchunks, int cpw, int nrec, float* __restrict__ ws) {
+  __shared__ __align__(16) char bufs[2 * CB_BYTES];
+  __shared__ __align__(16) _Float16 cbL[256 * 4];
+  __shared__ float sm[AW * GF], sl[AW * GF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
+  const int c_begin = rx * cpw;
+  const int c_end = (c_begin + cpw) < nchunks ? (c_begin + cpw) : nchunks;
+
+  for (int i = tid; i < 256 * 4 * 2 / 16; i += AW * 64)
+    reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
+  {
+    const int64_t t0 = (int64_t)c_begin * FC;
+    const int nt0 = (T - t0) < FC ? (int)(T - t0) : FC;
+    attn_chunk_load(kc, vc, kn, vn, slab0 + t0, nt0, bufs, w, lane);
+  }
+
+  // rotated, scaled queries of the group's heads: sm_q[h][i] = qscale sum_j Pi[i][j] q[h][j],
+  // computed in the second chunk buffer, which is not loaded before the chunk loop
+  float* sm_q = reinterpret_cast<float*>(bufs + CB_BYTES);
+  {
+    float* qin = sm_q + GF * D;  // raw queries
+    for (int i = tid; i < G * D; i += AW * 64) qin[i] = (float)q[((int64_t)b * Hq + (int64_t)g * G) * D + i];
+    __syncthreads();
+    for (int o = tid; o < G * D; o += AW * 64) {
+      const int h = o / D, i = o % D;
+      float a = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < D; j++) a = fmaf(pi32[i * D + j], qin[h * D + j], a);
+      sm_q[o] = a * qscale;
+    }
+    __syncthreads();
+  }
+  const int col = lane & 15, grp = lane >> 4, hd = col & 7;
+  const bool hi_col = col < 8;
+  // B operand of QK: column col = head hd, hi part (col < 8) or lo part; k = 8 grp + j is
+  // dimension 32 s + 8 grp + j.
+  half8 qb[2];
+  {
+    const float* qr = sm_q + (hd < G ? hd : 0) * D;
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float v = hd < G ? qr[32 * s + 8 * grp + j] : 0.f;
+        const _Float16 hv = (_Float16)v;
+        qb[s][j] = hi_col ? hv : (_Float16)(v - (float)hv);
+      }
+  }
+
+  const float NEG = -__builtin_huge_valf();
+  float m_run = NEG, l_run = 0.f;
+  f32x4 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces are in LDS
+  __syncthreads();
+  for (int c = c_begin; c < c_end; c++) {
+    const char* cur = bufs + ((c - c_begin) & 1) * CB_BYTES;
+    if (c + 1 < c_end) {
+      const int64_t t1 = (int64_t)(c + 1) * FC;
+      const int nt1 = (T - t1) < FC ? (int)(T - t1) : FC;
+      attn_chunk_load(kc, vc, kn, vn, slab0 + t1, nt1, bufs + ((c + 1 - c_begin) & 1) * CB_BYTES, w, lane);
+    }
+    const int nt = (T - (int64_t)c * FC) < FC ? (int)(T - (int64_t)c * FC) : FC;
+
+    // The wave's 128 tokens of the chunk in two halves of 64: scores first, then
+    // one max / rescale, then the exponentials and PV.  Only a chunk that ends
+    // inside the wave's tokens needs token masks.
+    if (nt >= 128 * (w + 1))
+      attn_half_pair<false>(cur, cbL, qb, 128 * w, nt, col, grp, hi_col, m_run, l_run, O);
+    else
+      attn_half_pair<true>(cur, cbL, qb, 128 * w, nt, col, grp, hi_col, m_run, l_run, O);
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    __syncthreads();
+  }
+
+  // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
+  float l = l_run;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* so = reinterpret_cast<float*>(bufs);  // [AW][GF][D], the chunk buffers are no longer read
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float v = O[dt][i] + __shfl_xor(O[dt][i], 32);
+      if (grp < 2) so[(w * GF + 4 * grp + i) * D + 16 * dt + col] = v;
+    }
+  if (grp == 0 && col < GF) {
+    sm[w * GF + col] = m_run;
+    sl[w * GF + col] = l;
   }
   __syncthreads();
   {
-    const float NEG = -__builtin_huge_valf();
-    const int h = tid >> 4, d0 = (tid & 15) * 4;
+    const int h = tid >> 5, d0 = (tid & 31) * 2;
     if (h < G) {
       float M = NEG;
 #pragma unroll
-      for (int w = 0; w < AW; w++) M = fmaxf(M, sm[w * GMAX + h]);
+      for (int ww = 0; ww < AW; ww++) M = fmaxf(M, sm[ww * GF + h]);
       float wt[AW], Ls = 0.f;
 #pragma unroll
-      for (int w = 0; w < AW; w++) {
-        wt[w] = sm[w * GMAX + h] == NEG ? 0.f : __builtin_amdgcn_exp2f(sm[w * GMAX + h] - M);
-        Ls += sl[w * GMAX + h] * wt[w];
+      for (int ww = 0; ww < AW; ww++) {
+        wt[ww] = sm[ww * GF + h] == NEG ? 0.f : __builtin_amdgcn_exp2f(sm[ww * GF + h] - M);
+        Ls += sl[ww * GF + h] * wt[ww];
       }
-      float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nchunks + chunk) * REC;
+      float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nrec + rx) * REC;
       if (d0 == 0) {
         rec[0] = M;
         rec[1] = Ls;
       }
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
+      for (int e = 0; e < 2; e++) {
         float A = 0.f;
 #pragma unroll
-        for (int w = 0; w < AW; w++) A += so[(w * GMAX + h) * D + d0 + e] * wt[w];
+        for (int ww = 0; ww < AW; ww++) A += so[(ww * GF + h) * D + d0 + e] * wt[ww];
         rec[2 + d0 + e] = A;
       }
     }
   }
-}
-
-// Rotated, scaled queries for the fast path: qrot = (scale log2 e) Pi q, fp32.
-__global__ __launch_bounds__(64) void attn_prep(const _Float16* __restrict__ q, const float* __restrict__ pi32,
-                                                float qscale, float* __restrict__ qrot) {
-  __shared__ float qs[D];
-  const int64_t bh = blockIdx.x;
-  const int i = threadIdx.x;
-  qs[i] = (float)q[bh * D + i];
-  __syncthreads();
-  float a = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < D; j++) a = fmaf(pi32[i * D + j], qs[j], a);
-  qrot[bh * D + i] = a * qscale;
 }
 
 size_t attn_smem_bytes(int N, int K) {
@@ -554,11 +586,22 @@ size_t attn_smem_bytes(int N, int K) {
 }  // namespace
 
 #ifndef FQ_ONLY_K
-// k = 4 with 8-bit codes runs the chunk-resident kernel.
-bool attn_fast_path(const fq_codebook* cb, int64_t T) { return cb->k == 4 && cb->bits == 8 && T < ((int64_t)1 << 40); }
+// k = 4 with 8-bit codes, at most 8 query heads per KV head and T a multiple of 8
+// runs attn_k4b8.
+bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
+  return cb->k == 4 && cb->bits == 8 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
+}
 
-AttnPlan attn_plan(const fq_codebook* cb, int B, int Hkv, int64_t T) {
-  if (attn_fast_path(cb, T)) return AttnPlan{(int)((T + FCHUNK - 1) / FCHUNK), (int64_t)FCHUNK};
+AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
+  if (attn_fast_path(cb, Hq, Hkv, T)) {
+    // about 1024 persistent workgroups (4 per CU), each over cpw consecutive chunks
+    const int64_t fc = (T + FC - 1) / FC, slabs = (int64_t)B * Hkv;
+    int64_t cpw = fc * slabs / 1024;
+    if (cpw < 1) cpw = 1;
+    if (cpw > fc) cpw = fc;
+    const int64_t nrec = (fc + cpw - 1) / cpw;
+    return AttnPlan{(int)nrec, cpw * FC, (int)fc, (int)cpw, true};
+  }
   const int64_t per = (int64_t)AW * TILE;
   const int64_t groups = (int64_t)B * Hkv;
   const int64_t want = (2048 + groups - 1) / groups;
@@ -568,7 +611,7 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hkv, int64_t T) {
   int64_t tc = (T + nc - 1) / nc;
   tc = ((tc + per - 1) / per) * per;
   nc = (T + tc - 1) / tc;
-  return AttnPlan{(int)nc, tc};
+  return AttnPlan{(int)nc, tc, 0, 0, false};
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int nchunks) {
@@ -606,7 +649,7 @@ extern FQ_ATT_DECL(64);
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
                        float* out, void* workspace, hipStream_t s) {
-  const AttnPlan plan = attn_plan(cb, B, Hkv, T);
+  const AttnPlan plan = attn_plan(cb, B, Hq, Hkv, T);
   const float qscale = scale * 1.4426950408889634f;  // log2(e)
   const dim3 grid((unsigned)plan.nchunks, (unsigned)Hkv, (unsigned)B);
   const size_t sh = attn_smem_bytes(cb->N, cb->k);
@@ -615,21 +658,9 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* kn = reinterpret_cast<const _Float16*>(k_norms);
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
-  if (attn_fast_path(cb, T)) {
-    float* qrot = ws + (size_t)B * Hq * plan.nchunks * REC;
-    hipLaunchKernelGGL(attn_prep, dim3((unsigned)(B * Hq)), dim3(64), 0, s, qh, cb->pi32, qscale, qrot);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const bool nal = (T % 8) == 0;  // 8 consecutive norms of a chunk are one aligned 16-byte load
-#define FQ_FAST(NA)                                                                                           \
-  hipLaunchKernelGGL(attn_split_k4b8<NA>, grid, dim3(AW * 64), 0, s, qrot,                                    \
-                     reinterpret_cast<const uint32_t*>(k_codes), kn, reinterpret_cast<const uint32_t*>(v_codes), \
-                     vn, cb->cw16, cb->N, Hq, Hkv, T, plan.nchunks, ws)
-    if (nal)
-      FQ_FAST(true);
-    else
-      FQ_FAST(false);
-#undef FQ_FAST
+  if (plan.fast) {
+    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, cb->pi32, qscale, k_codes, kn, v_codes, vn,
+                       cb->cw16, Hq, Hkv, T, plan.fast_chunks, plan.cpw, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);

@@ -21,8 +21,11 @@
 //     256 ||c||^2 read from LDS.  A lane keeps the minimum of its 16 rows
 //     (v_min3 chains), the best and second-best such minimum and the best
 //     tile; the next tile's matrix op is issued before this one is reduced.
-//  4. Recovery: the lane recomputes its best tile's 16 scores in fp32 FMAs,
-//     the two lanes of a column merge.
+//  4. Recovery: per column, the half whose tile minimum won recomputes that
+//     tile's 16 rows in fp32 FMAs from the fp32 256 ||c||^2 (lane c takes
+//     column c of one tile of a pair, lane c + 32 the other tile's); the second
+//     best is the least of the recomputed runner-up, the winning half's other
+//     tiles and the other half's minimum.
 //  5. Certificate: every computed score is within
 //        E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 35840 sqrt(k) cmax u
 //                  + 2^-25 (1 + sqrt(k) cmax)),   u = 2^-24,
@@ -101,8 +104,7 @@ __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Flo
 // padding every tile maps to the same LDS banks, and the recovery's per-lane reads
 // (each lane in its own best tile) would all collide.
 __host__ __device__ constexpr size_t h16_lds_bytes(int K, int N, int waves) {
-  return (size_t)ROT_OPS * 16 + (size_t)(N + N / 32) * 16 + (K == 8 ? (size_t)(N + N / 8) * 4 : 0) +
-         (size_t)waves * WAVE_WORDS * 4;
+  return (size_t)ROT_OPS * 16 + (size_t)(N + N / 32) * 16 + (size_t)(N + N / 8) * 4 + (size_t)waves * WAVE_WORDS * 4;
 }
 __device__ inline int rslot(int n) { return n + (n >> 5); }
 __device__ inline int cslot(int n) { return n + 4 * (n >> 5); }
@@ -122,12 +124,12 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   uint4* recL = smem + ROT_OPS;
   float* c2L = reinterpret_cast<float*>(recL + N + N / 32);
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + (K == 8 ? N + N / 8 : 0)) + w * WAVE_WORDS;
+  uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + N + N / 8) + w * WAVE_WORDS;
   uint16_t* todoL = reinterpret_cast<uint16_t*>(spk + SPK_WORDS);
   for (int i = threadIdx.x; i < ROT_OPS; i += WAVES * 64) rotL[i] = rot16[i];
   for (int i = threadIdx.x; i < N; i += WAVES * 64) {
     recL[rslot(i)] = crec[i];
-    if constexpr (K == 8) c2L[cslot(i)] = cn2s[i];
+    c2L[cslot(i)] = cn2s[i];
   }
   __syncthreads();
 
@@ -272,73 +274,81 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       A = An;
     }
 
-    // ---- 4-5. recovery and certificate; uncertified blocks go to a list
-    uint32_t code[8];  // code | block index << 16, or ~0 when there is nothing to pack from this lane
+    // ---- 4-5. recovery and certificate; uncertified blocks go to a list.  Each
+    //      column needs one recompute, of the half whose tile minimum won: lane c
+    //      takes column c of tile 2p, lane c + 32 column c of tile 2p + 1.
+    uint32_t code[4];  // code | block index << 16, or ~0 when there is nothing to pack from this lane
     int ntodo = 0;
 #pragma unroll
-    for (int tb = 0; tb < 8; tb++) {
-      const int sigma = tb >> 1, hp = tb & 1;
-      // hi and lo of this column's block: one half is ours, the partner lane holds the other
+    for (int p = 0; p < 4; p++) {
+      const int tb = 2 * p + h;  // this lane's tile: slot sigma = p, partner offset hp = h
+      // statistics of this tile from both halves (the partner sends those of the tile it takes)
+      const float mm1 = h == 0 ? m1[2 * p] : m1[2 * p + 1];
+      const float mm2 = h == 0 ? m2[2 * p] : m2[2 * p + 1];
+      const int mtid = h == 0 ? tid[2 * p] : tid[2 * p + 1];
+      const float pm1 = __shfl_xor(h == 0 ? m1[2 * p + 1] : m1[2 * p], 32);
+      const float pm2 = __shfl_xor(h == 0 ? m2[2 * p + 1] : m2[2 * p], 32);
+      const int ptid = __shfl_xor(h == 0 ? tid[2 * p + 1] : tid[2 * p], 32);
+      const bool win = (mm1 < pm1) || (mm1 == pm1 && h == 0);
+      const int hw = win ? h : 1 - h;       // half (rows 4 hw + ..) holding the tile minimum
+      const int t0 = win ? mtid : ptid;     // its tile
+      const float m2w = win ? mm2 : pm2;    // its other tiles' minimum
+      const float m1l = win ? pm1 : mm1;    // minimum over the other half's rows
+      // hi and lo of this column's block: this lane's operand half plus the partner's
       float vp[K];
       {
-        uint32_t X[DW];
-#pragma unroll
-        for (int d = 0; d < DW; d++) X[d] = (uint32_t)__shfl_xor((int)bq[tb][d], 32);
+        uint32_t mine[DW], X[DW];
 #pragma unroll
         for (int d = 0; d < DW; d++) {
-          const uint32_t hw = h == 0 ? bq[tb][d] : X[d];
-          const uint32_t lw = h == 0 ? X[d] : bq[tb][d];
-          vp[2 * d] = h_lo(hw) + h_lo(lw);  // exact: the value the matrix core multiplied
-          vp[2 * d + 1] = h_hi(hw) + h_hi(lw);
+          mine[d] = h == 0 ? bq[2 * p][d] : bq[2 * p + 1][d];
+          X[d] = (uint32_t)__shfl_xor((int)(h == 0 ? bq[2 * p + 1][d] : bq[2 * p][d]), 32);
+        }
+#pragma unroll
+        for (int d = 0; d < DW; d++) {
+          const uint32_t hw_ = h == 0 ? mine[d] : X[d];
+          const uint32_t lw_ = h == 0 ? X[d] : mine[d];
+          vp[2 * d] = h_lo(hw_) + h_lo(lw_);  // exact: the value the matrix core multiplied
+          vp[2 * d + 1] = h_hi(hw_) + h_hi(lw_);
         }
       }
       float vn2 = 0.f;
 #pragma unroll
       for (int i = 0; i < K; i++) vn2 = fmaf(vp[i], vp[i], vn2);
-      const int t0 = tid[tb];
       float r1 = __builtin_huge_valf(), r2 = __builtin_huge_valf();
       int ri = 0;
 #pragma unroll
       for (int qq = 0; qq < 4; qq++) {
-        const int n0 = 32 * t0 + 8 * qq + 4 * h;  // rows n0 .. n0 + 3 of this lane
-        float4 c2v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if constexpr (K == 8) c2v = *reinterpret_cast<const float4*>(c2L + cslot(n0));
+        const int n0 = 32 * t0 + 8 * qq + 4 * hw;  // rows n0 .. n0 + 3 of the winning half
+        const float4 c2v = *reinterpret_cast<const float4*>(c2L + cslot(n0));  // fp32 256 ||c||^2
         const float c2a[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const uint4 rw = recL[rslot(n0 + e)];
           const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
-          float sc;
-          if constexpr (K == 4)
-            sc = h_lo(ww[2]) + h_hi(ww[2]);  // 256 ||c||^2 as stored (hi + lo, exact)
-          else
-            sc = c2a[e];
+          float sc = c2a[e];
 #pragma unroll
           for (int i = 0; i < K; i += 2) {
             sc = fmaf(h_lo(ww[i / 2]), vp[i], sc);
             sc = fmaf(h_hi(ww[i / 2]), vp[i + 1], sc);
           }
           r2 = __builtin_amdgcn_fmed3f(r1, r2, sc);
-          ri = sc < r1 ? (n0 + e) : ri;
+          ri = sc < r1 ? (4 * qq + e) : ri;  // row 8 qq + 4 hw + e of the tile
           r1 = fminf(r1, sc);
         }
       }
-      const float o1 = __shfl_xor(r1, 32), o2 = __shfl_xor(r2, 32), om = __shfl_xor(m2[tb], 32);
-      const int oi = __shfl_xor(ri, 32);
-      const bool other = (o1 < r1) || (o1 == r1 && oi < ri);
-      const float best = other ? o1 : r1;
-      const float second = fminf(fminf(fmaxf(r1, o1), fminf(r2, o2)), fminf(m2[tb], om));
-      // block of this column: slot sigma of lane o = c + 32 hp
-      const int o = c + 32 * hp;
-      const int vec = K == 4 ? (o & 15) : 16 * (sigma >> 1) + (o & 15);
-      const int bi = K == 4 ? 4 * (o >> 4) + sigma : 2 * (o >> 4) + (sigma & 1);
+      const uint32_t cbest = (uint32_t)(32 * t0 + 8 * (ri >> 2) + 4 * hw + (ri & 3));
+      const float second = fminf(r2, fminf(m2w, m1l));
+      // block of this column: slot p of lane o = c + 32 h
+      const int o = c + 32 * h;
+      const int vec = K == 4 ? (o & 15) : 16 * (p >> 1) + (o & 15);
+      const int bi = K == 4 ? 4 * (o >> 4) + p : 2 * (o >> 4) + (p & 1);
       const float yn = __builtin_sqrtf(vn2) * (1.01f / 512.0f);
-      const bool sure = (second - best) > 2.0f * (e_abs + e_rel * yn);
-      const bool mine = h == 0 && vec < nv;
-      code[tb] = (mine && sure) ? ((uint32_t)(other ? oi : ri) | ((uint32_t)(vec * (D / K) + bi) << 16)) : ~0u;
-      const uint64_t um = __ballot(mine && !sure);
+      const bool sure = (second - r1) > 2.0f * (e_abs + e_rel * yn);
+      const bool mine_ = vec < nv;
+      code[p] = (mine_ && sure) ? (cbest | ((uint32_t)(vec * (D / K) + bi) << 16)) : ~0u;
+      const uint64_t um = __ballot(mine_ && !sure);
       if (um) {
-        if (mine && !sure) {
+        if (mine_ && !sure) {
           const int pos = ntodo + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(um >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)um, 0u));
           todoL[pos] = (uint16_t)((tb << 8) | c);
@@ -352,10 +362,10 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
     for (int i = lane; i < words; i += 64) spk[i] = 0u;
     wave_lds_sync();
 #pragma unroll
-    for (int tb = 0; tb < 8; tb++) {
-      if (code[tb] != ~0u) {
-        const uint32_t cv = code[tb] & 0xffffu;
-        const int bo = (int)(code[tb] >> 16) * bits, sh = bo & 31;
+    for (int p = 0; p < 4; p++) {
+      if (code[p] != ~0u) {
+        const uint32_t cv = code[p] & 0xffffu;
+        const int bo = (int)(code[p] >> 16) * bits, sh = bo & 31;
         atomicOr(&spk[bo >> 5], cv << sh);
         if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
       }

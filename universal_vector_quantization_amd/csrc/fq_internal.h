@@ -69,13 +69,18 @@ hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const
 hipError_t launch_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                          int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
 
-// Split-K plan of the decode attention: number of chunks and tokens per chunk.
+// Split-K plan of the decode attention: partial records per (batch, query head) and
+// tokens per record; on the fast path also the 512-token chunks per slab and the
+// chunks one workgroup covers.
 struct AttnPlan {
   int nchunks;
   int64_t chunk_tokens;
+  int fast_chunks;
+  int cpw;
+  bool fast;
 };
-bool attn_fast_path(const fq_codebook* cb, int64_t T);
-AttnPlan attn_plan(const fq_codebook* cb, int B, int Hkv, int64_t T);
+bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
+AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
 size_t attn_workspace_bytes(int B, int Hq, int nchunks);
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
