@@ -14,8 +14,8 @@ Inputs are resident in HBM before timing starts.  The metric is KV vectors per
 second through the step (fp16-equivalent GB/s = vectors/s x 128 B).  Per-kernel
 times come from HIP events on the stream the library launches on.  The
 decode-attention workload (B=16, 32 query heads on 4 KV heads, T=32768) is
-timed separately with the last-level cache flushed before every launch, and
-reported against the HBM roofline.  The CPU oracle is timed on a bounded sample
+timed separately with L2 and the last-level cache evicted before every launch
+(a 512 MiB read), and reported against the HBM roofline.  The CPU oracle is timed on a bounded sample
 (rank 0, one GPU only).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -282,10 +282,13 @@ def main():
         aws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, Ta), dtype=torch.uint8, device=dev)
         kcs, vcs = ac[: cb.code_bytes(na)], ac[cb.code_bytes(na):]
         kns, vns = an[:na], an[na:]
-        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+        # Eviction between launches READS a 512 MiB buffer, leaving L2 and the 256 MB
+        # last-level cache full of clean lines of it; a write-based fill would leave
+        # dirty lines whose write-back lands inside the timed launch.
+        flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
         times = []
         for it in range(args.attn_iters + 3):
-            flush.fill_(it & 0xff)  # evict L2 and the 256 MB last-level cache
+            flush.max()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fq.fq_attn_decode(cb.handle, qa, kcs, kns, vcs, vns, B, Hq, Hkv, Ta, 0.125, ao, aws, stream)
@@ -296,7 +299,8 @@ def main():
         t_att = float(np.median(times)) / 1e3
         abytes = 2 * cb.code_bytes(na) + 2 * na * 2 + B * Hq * D * 2 + B * Hq * D * 4
         line["attn_b16_t32k"] = {
-            "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms, cache flushed per launch",
+            "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms, caches evicted (512 MiB read) "
+                        "before every launch",
             "us_per_step": t_att * 1e6, "hbm_bytes": abytes, "GBps": abytes / t_att / 1e9,
             "fp16_equiv_GBps": 2 * na * D * 2 / t_att / 1e9,
             "roofline": {"kernel": "attn_k4b8 (+ attn_combine: the events bracket the whole fq_attn_decode call)",

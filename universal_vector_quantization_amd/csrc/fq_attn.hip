@@ -245,33 +245,47 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
 }
 
 // Log-sum-exp merge of the chunk partials and the single inverse rotation.
-// Lane c < nchunks reads chunk c's statistics; the max and the weighted sum are
-// wave reductions; every lane then sums its own dim over the chunks.
+// Lanes take the chunks' statistics in parallel (max, weights, weighted sum); the
+// weights go to LDS; then every lane (one dimension) sums the chunks'
+// accumulators with the loads of 8 chunks in flight.
+constexpr int COMB_W = 1024;  // chunks whose weights are kept in LDS
 __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws, const float* __restrict__ pi32,
                                                    int nchunks, float* __restrict__ out) {
   __shared__ float ot[D];
-  __shared__ float wsh[256];
+  __shared__ float wsh[COMB_W];
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
+  const float NEG = -__builtin_huge_valf();
   const float* rec = ws + bh * nchunks * REC;
-  float M = -__builtin_huge_valf();
-  for (int c = lane; c < nchunks; c += 64) M = fmaxf(M, rec[c * REC]);
+  float M = NEG;
+  for (int c = lane; c < nchunks; c += 64) M = fmaxf(M, rec[(int64_t)c * REC]);
 #pragma unroll
   for (int s2 = 32; s2 >= 1; s2 >>= 1) M = fmaxf(M, __shfl_xor(M, s2));
   float Ls = 0.f;
   for (int c = lane; c < nchunks; c += 64) {
-    const float wgt = exp2f(rec[c * REC] - M);
-    if (c < 256) wsh[c] = wgt;
-    Ls += rec[c * REC + 1] * wgt;
+    const float mc = rec[(int64_t)c * REC];
+    const float wgt = mc == NEG ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+    if (c < COMB_W) wsh[c] = wgt;
+    Ls = fmaf(rec[(int64_t)c * REC + 1], wgt, Ls);
   }
 #pragma unroll
   for (int s2 = 32; s2 >= 1; s2 >>= 1) Ls += __shfl_xor(Ls, s2);
   __syncthreads();
+  auto weight = [&](int c) {
+    if (c < COMB_W) return wsh[c];
+    const float mc = rec[(int64_t)c * REC];
+    return mc == NEG ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+  };
   float A = 0.f;
-  for (int c = 0; c < nchunks; c++) {
-    const float wgt = c < 256 ? wsh[c] : exp2f(rec[c * REC] - M);
-    A = fmaf(rec[c * REC + 2 + lane], wgt, A);
+  int c = 0;
+  for (; c + 8 <= nchunks; c += 8) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = rec[(int64_t)(c + e) * REC + 2 + lane];
+#pragma unroll
+    for (int e = 0; e < 8; e++) A = fmaf(v[e], weight(c + e), A);
   }
+  for (; c < nchunks; c++) A = fmaf(rec[(int64_t)c * REC + 2 + lane], weight(c), A);
   ot[lane] = A / Ls;
   __syncthreads();
   float o = 0.f;
@@ -280,7 +294,6 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
   out[bh * D + lane] = o;
 }
 
-// ---------------------------------------------------------------------------
 // Fast path: k = 4 with 8-bit codes (N = 256), up to 8 query heads per KV head,
 // T a multiple of 8 (the attention workload's shape).  Differences from
 // attn_split:
@@ -294,15 +307,19 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
 //     address (token a', block) rows and receive 4 tokens of one dimension.
 //     The K order inside a 32-token tile is permuted (k = 8 grp + 4 a + i is
 //     token 16 a + 4 grp + i) so P' comes straight from the QK registers.
-//   * A wave computes all scores of its 128 tokens of a chunk first, so the
-//     running max and the rescaling happen once per chunk, not per tile.
-//   * A workgroup is persistent over `cpw` consecutive chunks of one (batch,
-//     KV head) slab and double-buffers them in LDS with direct global-to-LDS
-//     loads; it writes one partial record per query head.
-constexpr int FC = 512;  // tokens per chunk
+//   * The running max and the rescaling happen once per 64 tokens.
+//   * Every wave streams its own 128-token sub-chunks (codes and norms, 4.5 KiB)
+//     through a private double buffer filled by direct global-to-LDS loads and
+//     waits only for its own loads: no workgroup barrier inside the stream.
+//   * The workgroup merges its waves into one partial record per query head;
+//     attn_combine merges the records.  (Merging inside the kernel would need a
+//     device-scope fence per workgroup, which on this multi-die part writes back
+//     and invalidates the die's L2 and costs far more than a second launch.)
+constexpr int SC = 128;  // tokens per wave sub-chunk
 constexpr int GF = 8;    // query heads per KV head on the fast path
-constexpr int CB_KC = 0, CB_VC = FC * 16, CB_KN = 2 * FC * 16, CB_VN = 2 * FC * 16 + FC * 2;
-constexpr int CB_BYTES = 2 * FC * 16 + 4 * FC;  // 18432
+constexpr int SC_KC = 0, SC_VC = SC * 16, SC_KN = 2 * SC * 16, SC_VN = 2 * SC * 16 + SC * 2;
+constexpr int SC_BYTES = 2 * SC * 16 + 4 * SC;  // 4608
+constexpr int WG_TOKENS_UNIT = AW * SC;         // 512: workgroup token ranges are multiples of this
 
 typedef short short4_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_ lds_s4;
@@ -322,52 +339,48 @@ __device__ inline float swap8(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, true));
 }
 
-// Codes and norms of chunk `c` of the slab into LDS buffer `dst`: 18 pieces of
-// 1 KiB (8 of K codes, 8 of V codes, K norms, V norms); lane i of a piece
-// moves bytes 16 i .. 16 i + 15, and only bytes of tokens below `nt` are read.
-__device__ inline void attn_chunk_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                                       const _Float16* __restrict__ kn, const _Float16* __restrict__ vn,
-                                       int64_t tok0, int nt, char* dst, int w, int lane) {
-  for (int p = w; p < 18; p += AW) {
-    const uint8_t* src;
-    int first;  // first token of the lane's 16 bytes
-    if (p < 16) {
-      const int t = 64 * (p & 7) + lane;
-      src = ((p < 8) ? kc : vc) + (tok0 + t) * 16;
-      first = t;
-    } else {
-      src = reinterpret_cast<const uint8_t*>(((p == 16) ? kn : vn) + tok0 + 8 * lane);
-      first = 8 * lane;  // T % 8 == 0, so the 8 norms are all valid or all past the end
-    }
-    if (first < nt) __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst + p * 1024), 16, 0, 0);
+// Codes and norms of the nt tokens starting at slab token tok0 into the wave's
+// buffer: always 6 load instructions (token indices past nt are clamped to the
+// last valid token, whose bytes land in slots the compute masks), so a wave can
+// wait for exactly the older sub-chunk with vmcnt(6).  nt is a multiple of 8.
+__device__ inline void attn_sub_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                     const _Float16* __restrict__ kn, const _Float16* __restrict__ vn, int64_t tok0,
+                                     int nt, char* dst, int lane) {
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const int t = (64 * p + lane) < nt ? (64 * p + lane) : nt - 1;
+    lds_dma16(kc + (tok0 + t) * 16, dst + SC_KC + p * 1024);
+    lds_dma16(vc + (tok0 + t) * 16, dst + SC_VC + p * 1024);
   }
+  const int t2 = (2 * lane) < nt ? 2 * lane : nt - 2;  // two norms per lane
+  lds_dma4(kn + tok0 + t2, dst + SC_KN);
+  lds_dma4(vn + tok0 + t2, dst + SC_VN);
 }
 
-// One wave's 128 tokens [tw, tw + 128) of the chunk in LDS `cur`, as two halves
-// of 64 tokens: scores first, then one max / rescale, then the exponentials and
+// One wave's sub-chunk (tokens 0 .. 127 of `cur`, nt valid) as two halves of
+// 64 tokens: scores first, then one max / rescale, then the exponentials and
 // PV.  MASK: tokens at or past `nt` are excluded.
 template <bool MASK>
-__device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float16* __restrict__ cbL,
-                                      const half8 (&qb)[2], int tw, int nt, int col, int grp, bool hi_col,
-                                      float& m_run, float& l_run, f32x4 (&O)[4]) {
+__device__ inline void attn_sub(const char* __restrict__ cur, const _Float16* __restrict__ cbL, const half8 (&qb)[2],
+                                int nt, int col, int grp, bool hi_col, float& m_run, float& l_run, f32x4 (&O)[4]) {
   const float NEG = -__builtin_huge_valf();
 #pragma unroll 1
   for (int hf = 0; hf < 2; hf++) {
-    // ---- scores: L[u][a][i] is token tw + 64 hf + 32 u + 16 a + 4 grp + i
+    // ---- scores: L[u][a][i] is token 64 hf + 32 u + 16 a + 4 grp + i
     float L[2][2][4];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
-      const int tb = tw + 64 * hf + 32 * u;
+      const int tb = 64 * hf + 32 * u;
 #pragma unroll
       for (int a = 0; a < 2; a++) {
-        const uint32_t* rec = reinterpret_cast<const uint32_t*>(cur + CB_KC + (tb + 16 * a + col) * 16);
+        const uint32_t* rec = reinterpret_cast<const uint32_t*>(cur + SC_KC + (tb + 16 * a + col) * 16);
         const uint32_t w0 = rec[grp >> 1], w1 = rec[2 + (grp >> 1)];
         const int sh = (grp & 1) * 16;
         const half8 k0 = gather2(cbL, __builtin_amdgcn_ubfe(w0, sh, 8), __builtin_amdgcn_ubfe(w0, sh + 8, 8));
         const half8 k1 = gather2(cbL, __builtin_amdgcn_ubfe(w1, sh, 8), __builtin_amdgcn_ubfe(w1, sh + 8, 8));
         f32x4 S = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
         S = mfma16(k1, qb[1], S);
-        const uint2 nw = *reinterpret_cast<const uint2*>(cur + CB_KN + 2 * (tb + 16 * a + 4 * grp));
+        const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_KN + 2 * (tb + 16 * a + 4 * grp));
         const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -386,7 +399,7 @@ __device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float
         mx = fmaxf(fmaxf(mx, fmaxf(L[u][a][0], L[u][a][1])), fmaxf(L[u][a][2], L[u][a][3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (MASK && mx == NEG) continue;  // no tokens of the wave here (uniform)
+    if (MASK && mx == NEG) continue;  // no valid tokens here (uniform)
     const float m_new = fmaxf(m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
     l_run *= alpha;
@@ -402,11 +415,11 @@ __device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float
     // ---- P' = p nu_v (hi in rows 0..7, lo in rows 8..15) and PV
 #pragma unroll
     for (int u = 0; u < 2; u++) {
-      const int tb = tw + 64 * hf + 32 * u;
+      const int tb = 64 * hf + 32 * u;
       uint32_t Pw[4];  // P' as 4 packed fp16 pairs: element 4 a + i
 #pragma unroll
       for (int a = 0; a < 2; a++) {
-        const uint2 nw = *reinterpret_cast<const uint2*>(cur + CB_VN + 2 * (tb + 16 * a + 4 * grp));
+        const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_VN + 2 * (tb + 16 * a + 4 * grp));
         const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
         float pv[4];
 #pragma unroll
@@ -431,7 +444,7 @@ __device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float
       short4_ vt[2][4];
 #pragma unroll
       for (int a = 0; a < 2; a++) {
-        const uint4 rw = *reinterpret_cast<const uint4*>(cur + CB_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16);
+        const uint4 rw = *reinterpret_cast<const uint4*>(cur + SC_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16);
         const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
         const int sh = 8 * (col & 3);
 #pragma unroll
@@ -450,11 +463,11 @@ __device__ inline void attn_half_pair(const char* __restrict__ cur, const _Float
 
 __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q, const float* __restrict__ pi32,
                                                         float qscale, const uint8_t* __restrict__ kc,
-                                                     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
-                                                     const _Float16* __restrict__ vn,
-                                                     const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
-                                                     int nchunks, int cpw, int nrec, float* __restrict__ ws) {
-  __shared__ __align__(16) char bufs[2 * CB_BYTES];
+                                                        const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
+                                                        const _Float16* __restrict__ vn,
+                                                        const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
+                                                        int64_t wg_tokens, int nrec, float* __restrict__ ws) {
+  __shared__ __align__(16) char wbuf[AW * 2 * SC_BYTES];
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ float sm[AW * GF], sl[AW * GF];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -462,22 +475,23 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   const int rx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
-  const int c_begin = rx * cpw;
-  const int c_end = (c_begin + cpw) < nchunks ? (c_begin + cpw) : nchunks;
+  const int64_t t_begin = (int64_t)rx * wg_tokens;
+  const int64_t t_end = (t_begin + wg_tokens) < T ? (t_begin + wg_tokens) : T;
+  const int nsub = (int)((t_end - t_begin + SC - 1) / SC);
+  char* mybuf = wbuf + w * 2 * SC_BYTES;
 
+  // first sub-chunk of every wave on its way
+  if (w < nsub) {
+    const int64_t s0 = t_begin + (int64_t)w * SC;
+    attn_sub_load(kc, vc, kn, vn, slab0 + s0, (t_end - s0) < SC ? (int)(t_end - s0) : SC, mybuf, lane);
+  }
   for (int i = tid; i < 256 * 4 * 2 / 16; i += AW * 64)
     reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
+  // rotated, scaled queries of the group's heads: qs[h][i] = qscale sum_j Pi[i][j] q[h][j],
+  // computed in wave 0's second buffer, which no load touches before the barrier below
+  float* qs = reinterpret_cast<float*>(wbuf + SC_BYTES);
   {
-    const int64_t t0 = (int64_t)c_begin * FC;
-    const int nt0 = (T - t0) < FC ? (int)(T - t0) : FC;
-    attn_chunk_load(kc, vc, kn, vn, slab0 + t0, nt0, bufs, w, lane);
-  }
-
-  // rotated, scaled queries of the group's heads: sm_q[h][i] = qscale sum_j Pi[i][j] q[h][j],
-  // computed in the second chunk buffer, which is not loaded before the chunk loop
-  float* sm_q = reinterpret_cast<float*>(bufs + CB_BYTES);
-  {
-    float* qin = sm_q + GF * D;  // raw queries
+    float* qin = qs + GF * D;  // raw queries
     for (int i = tid; i < G * D; i += AW * 64) qin[i] = (float)q[((int64_t)b * Hq + (int64_t)g * G) * D + i];
     __syncthreads();
     for (int o = tid; o < G * D; o += AW * 64) {
@@ -485,7 +499,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       float a = 0.f;
 #pragma unroll 8
       for (int j = 0; j < D; j++) a = fmaf(pi32[i * D + j], qin[h * D + j], a);
-      sm_q[o] = a * qscale;
+      qs[o] = a * qscale;
     }
     __syncthreads();
   }
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   // dimension 32 s + 8 grp + j.
   half8 qb[2];
   {
-    const float* qr = sm_q + (hd < G ? hd : 0) * D;
+    const float* qr = qs + (hd < G ? hd : 0) * D;
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
@@ -505,40 +519,39 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
         qb[s][j] = hi_col ? hv : (_Float16)(v - (float)hv);
       }
   }
+  __syncthreads();  // qs is read; wave 0 may now load into its second buffer
 
-  const float NEG = -__builtin_huge_valf();
-  float m_run = NEG, l_run = 0.f;
+  float m_run = -__builtin_huge_valf(), l_run = 0.f;
   f32x4 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces are in LDS
-  __syncthreads();
-  for (int c = c_begin; c < c_end; c++) {
-    const char* cur = bufs + ((c - c_begin) & 1) * CB_BYTES;
-    if (c + 1 < c_end) {
-      const int64_t t1 = (int64_t)(c + 1) * FC;
-      const int nt1 = (T - t1) < FC ? (int)(T - t1) : FC;
-      attn_chunk_load(kc, vc, kn, vn, slab0 + t1, nt1, bufs + ((c + 1 - c_begin) & 1) * CB_BYTES, w, lane);
+  int k = 0;
+  for (int j = w; j < nsub; j += AW, k++) {
+    const int64_t s0 = t_begin + (int64_t)j * SC;
+    const int nt = (t_end - s0) < SC ? (int)(t_end - s0) : SC;
+    const int jn = j + AW;
+    if (jn < nsub) {
+      const int64_t s1 = t_begin + (int64_t)jn * SC;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): reads of the buffer being refilled are done
+      attn_sub_load(kc, vc, kn, vn, slab0 + s1, (t_end - s1) < SC ? (int)(t_end - s1) : SC,
+                    mybuf + ((k + 1) & 1) * SC_BYTES, lane);
+      __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6): everything but the 6 loads just issued
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     }
-    const int nt = (T - (int64_t)c * FC) < FC ? (int)(T - (int64_t)c * FC) : FC;
-
-    // The wave's 128 tokens of the chunk in two halves of 64: scores first, then
-    // one max / rescale, then the exponentials and PV.  Only a chunk that ends
-    // inside the wave's tokens needs token masks.
-    if (nt >= 128 * (w + 1))
-      attn_half_pair<false>(cur, cbL, qb, 128 * w, nt, col, grp, hi_col, m_run, l_run, O);
+    const char* cur = mybuf + (k & 1) * SC_BYTES;
+    if (nt == SC)
+      attn_sub<false>(cur, cbL, qb, nt, col, grp, hi_col, m_run, l_run, O);
     else
-      attn_half_pair<true>(cur, cbL, qb, 128 * w, nt, col, grp, hi_col, m_run, l_run, O);
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-    __syncthreads();
+      attn_sub<true>(cur, cbL, qb, nt, col, grp, hi_col, m_run, l_run, O);
   }
 
   // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
   float l = l_run;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  float* so = reinterpret_cast<float*>(bufs);  // [AW][GF][D], the chunk buffers are no longer read
+  __syncthreads();                            // every wave is done with its buffers
+  float* so = reinterpret_cast<float*>(wbuf);  // [AW][GF][D]
 #pragma unroll
   for (int dt = 0; dt < 4; dt++)
 #pragma unroll
@@ -551,6 +564,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     sl[w * GF + col] = l;
   }
   __syncthreads();
+  const float NEG = -__builtin_huge_valf();
   {
     const int h = tid >> 5, d0 = (tid & 31) * 2;
     if (h < G) {
@@ -579,6 +593,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   }
 }
 
+
 size_t attn_smem_bytes(int N, int K) {
   return (size_t)((N * K * 2 + 15) & ~15) + sizeof(float) * (GMAX * D + 2 * AW * GMAX + AW * GMAX * D);
 }
@@ -594,13 +609,13 @@ bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
 
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   if (attn_fast_path(cb, Hq, Hkv, T)) {
-    // about 1024 persistent workgroups (4 per CU), each over cpw consecutive chunks
-    const int64_t fc = (T + FC - 1) / FC, slabs = (int64_t)B * Hkv;
-    int64_t cpw = fc * slabs / 1024;
-    if (cpw < 1) cpw = 1;
-    if (cpw > fc) cpw = fc;
-    const int64_t nrec = (fc + cpw - 1) / cpw;
-    return AttnPlan{(int)nrec, cpw * FC, (int)fc, (int)cpw, true};
+    // about 1024 workgroups (4 per CU), each over a multiple of 512 consecutive tokens
+    const int64_t units = (T + WG_TOKENS_UNIT - 1) / WG_TOKENS_UNIT, slabs = (int64_t)B * Hkv;
+    int64_t upw = units * slabs / 1024;
+    if (upw < 1) upw = 1;
+    if (upw > units) upw = units;
+    const int64_t nrec = (units + upw - 1) / upw;
+    return AttnPlan{(int)nrec, upw * WG_TOKENS_UNIT, (int)units, (int)upw, true};
   }
   const int64_t per = (int64_t)AW * TILE;
   const int64_t groups = (int64_t)B * Hkv;
@@ -660,7 +675,7 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   hipError_t e;
   if (plan.fast) {
     hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, cb->pi32, qscale, k_codes, kn, v_codes, vn,
-                       cb->cw16, Hq, Hkv, T, plan.fast_chunks, plan.cpw, plan.nchunks, ws);
+                       cb->cw16, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);

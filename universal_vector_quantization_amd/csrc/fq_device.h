@@ -39,4 +39,23 @@ __device__ inline uint32_t load_code(const uint8_t* __restrict__ p, int64_t bito
   return (v >> sh) & ((1u << bits) - 1u);
 }
 
+// Direct global-to-LDS loads: lane i moves its 16 (or 4) bytes from `gptr` to
+// LDS address lds + 16 i (4 i).  Written as inline assembly on purpose: the
+// compiler's wait insertion treats such a load as a write to all of LDS and puts
+// a full vmcnt(0) before the next LDS read, which serialises any double buffer.
+// Callers wait for these loads explicitly (s_waitcnt vmcnt); nothing else in the
+// calling kernels uses M0.
+typedef __attribute__((address_space(3))) void fq_lds_void;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void lds_dma16(const void* gptr, char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(fq_lds_void*)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
+}
+__device__ inline void lds_dma4(const void* gptr, char* lds) {
+  const uint32_t la = (uint32_t)(uintptr_t)(fq_lds_void*)lds;
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 }  // namespace fq

@@ -40,7 +40,6 @@ constexpr int SCR_DW = 2 * 64 * 2 + 16;        // per wave: x and y (fp64) of a 
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline float min16(const f32x16& v) {
   float m = fminf(fminf(v[0], v[1]), v[2]);
@@ -75,7 +74,7 @@ __device__ inline void load_chunk(const uint8_t* __restrict__ rec, int ch, int n
                                   int lane) {
   const uint8_t* src = rec + (size_t)ch * CHUNKB;
   for (int p = w; p * 1024 < nchunk_bytes; p += WAVES)
-    __builtin_amdgcn_global_load_lds(src + p * 1024 + lane * 16, (lds_void*)(dst + p * 1024), 16, 0, 0);
+    lds_dma16(src + p * 1024 + lane * 16, dst + p * 1024);
 }
 
 constexpr size_t full_lds_bytes() { return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4; }
