@@ -251,12 +251,19 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
 constexpr int COMB_W = 1024;  // chunks whose weights are kept in LDS
 __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws, const float* __restrict__ pi32,
                                                    int nchunks, float* __restrict__ out) {
+  constexpr int PRE = 16;  // accumulators of the first chunks, loaded before anything waits
   __shared__ float ot[D];
   __shared__ float wsh[COMB_W];
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
   const float NEG = -__builtin_huge_valf();
   const float* rec = ws + bh * nchunks * REC;
+  float v[PRE];
+#pragma unroll
+  for (int e = 0; e < PRE; e++) v[e] = e < nchunks ? rec[(int64_t)e * REC + 2 + lane] : 0.f;
+  float pc[D];  // column `lane` of Pi
+#pragma unroll
+  for (int j = 0; j < D; j++) pc[j] = pi32[j * D + lane];
   float M = NEG;
   for (int c = lane; c < nchunks; c += 64) M = fmaxf(M, rec[(int64_t)c * REC]);
 #pragma unroll
@@ -277,20 +284,23 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
     return mc == NEG ? 0.f : __builtin_amdgcn_exp2f(mc - M);
   };
   float A = 0.f;
-  int c = 0;
+#pragma unroll
+  for (int e = 0; e < PRE; e++)
+    if (e < nchunks) A = fmaf(v[e], weight(e), A);
+  int c = PRE;
   for (; c + 8 <= nchunks; c += 8) {
-    float v[8];
+    float t[8];
 #pragma unroll
-    for (int e = 0; e < 8; e++) v[e] = rec[(int64_t)(c + e) * REC + 2 + lane];
+    for (int e = 0; e < 8; e++) t[e] = rec[(int64_t)(c + e) * REC + 2 + lane];
 #pragma unroll
-    for (int e = 0; e < 8; e++) A = fmaf(v[e], weight(c + e), A);
+    for (int e = 0; e < 8; e++) A = fmaf(t[e], weight(c + e), A);
   }
   for (; c < nchunks; c++) A = fmaf(rec[(int64_t)c * REC + 2 + lane], weight(c), A);
   ot[lane] = A / Ls;
   __syncthreads();
   float o = 0.f;
-#pragma unroll 8
-  for (int j = 0; j < D; j++) o = fmaf(pi32[j * D + lane], ot[j], o);
+#pragma unroll
+  for (int j = 0; j < D; j++) o = fmaf(pc[j], ot[j], o);
   out[bh * D + lane] = o;
 }
 
@@ -357,46 +367,75 @@ __device__ inline void attn_sub_load(const uint8_t* __restrict__ kc, const uint8
   lds_dma4(vn + tok0 + t2, dst + SC_VN);
 }
 
+// Value of lane l ^ 8 (row_ror:8 within each 16-lane row).
+__device__ inline uint32_t ror8u(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true); }
+// Lanes 8..15 of each row take lane l - 8's `src`, lanes 0..7 keep `keep`.
+__device__ inline uint32_t from_lo_partner(uint32_t keep, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xf, 0xc, false);
+}
+// Lanes 0..7 of each row take lane l + 8's `src`, lanes 8..15 keep `keep`.
+__device__ inline uint32_t from_hi_partner(uint32_t keep, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xf, 0x3, false);
+}
+
 // One wave's sub-chunk (tokens 0 .. 127 of `cur`, nt valid) as two halves of
 // 64 tokens: scores first, then one max / rescale, then the exponentials and
 // PV.  MASK: tokens at or past `nt` are excluded.
+//
+// Layouts inside a 32-token group starting at tb (lane = 16 grp + col):
+//   QK tile a (tokens tb + 16 a + 0..15): A row col = token tb + 16 a + col; its
+//   k = 8 grp + j is dimension 16 grp + 8 s + j for matrix op s, i.e. codes
+//   4 grp + 2 s and 4 grp + 2 s + 1 = bytes 2 s, 2 s + 1 of the token's record
+//   dword grp.  Output column col = head col & 7, query hi part (col < 8) or lo
+//   part, rows 4 grp + i.
+//   After the hi + lo recombination a lane holds whole scores of head col & 7
+//   for tokens tb + 16 ah + 4 grp + i, ah = 0 in lanes col < 8 (tile 0) and 1
+//   in lanes col >= 8 (tile 1): every score is computed once.
+//   PV: k = 8 grp + 4 a + i is token tb + 16 a + 4 grp + i; P' rows 0..7 are
+//   the hi parts of heads 0..7, rows 8..15 the lo parts.  Value operand dt,
+//   lane c = 4 a' + b: the lane addresses token tb + 16 a + 4 grp + c / 4 and
+//   the block whose code is byte dt of record dword c % 4 (block 4 (c % 4) + dt),
+//   and receives dimension 16 a' + 4 dt + b of 4 tokens; output column c of
+//   accumulator dt is dimension 16 (c / 4) + 4 dt + c % 4.
 template <bool MASK>
 __device__ inline void attn_sub(const char* __restrict__ cur, const _Float16* __restrict__ cbL, const half8 (&qb)[2],
                                 int nt, int col, int grp, bool hi_col, float& m_run, float& l_run, f32x4 (&O)[4]) {
   const float NEG = -__builtin_huge_valf();
+  const int ah = hi_col ? 0 : 1;
+  const int own_tok = 16 * ah + 4 * grp;  // first of the lane's 4 tokens in a 32-token group
 #pragma unroll 1
   for (int hf = 0; hf < 2; hf++) {
-    // ---- scores: L[u][a][i] is token 64 hf + 32 u + 16 a + 4 grp + i
-    float L[2][2][4];
+    // ---- scores: L[u][i] is token 64 hf + 32 u + own_tok + i, head col & 7
+    float L[2][4];
 #pragma unroll
     for (int u = 0; u < 2; u++) {
       const int tb = 64 * hf + 32 * u;
+      f32x4 S[2];
 #pragma unroll
       for (int a = 0; a < 2; a++) {
-        const uint32_t* rec = reinterpret_cast<const uint32_t*>(cur + SC_KC + (tb + 16 * a + col) * 16);
-        const uint32_t w0 = rec[grp >> 1], w1 = rec[2 + (grp >> 1)];
-        const int sh = (grp & 1) * 16;
-        const half8 k0 = gather2(cbL, __builtin_amdgcn_ubfe(w0, sh, 8), __builtin_amdgcn_ubfe(w0, sh + 8, 8));
-        const half8 k1 = gather2(cbL, __builtin_amdgcn_ubfe(w1, sh, 8), __builtin_amdgcn_ubfe(w1, sh + 8, 8));
-        f32x4 S = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-        S = mfma16(k1, qb[1], S);
-        const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_KN + 2 * (tb + 16 * a + 4 * grp));
-        const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
+        const uint32_t w = reinterpret_cast<const uint32_t*>(cur + SC_KC + (tb + 16 * a + col) * 16)[grp];
+        const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
+        const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
+        S[a] = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+        S[a] = mfma16(k1, qb[1], S[a]);
+      }
+      const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_KN + 2 * (tb + own_tok));
+      const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float st = S[i] + swap8(S[i]);
-          L[u][a][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
-          if constexpr (MASK) L[u][a][i] = (tb + 16 * a + 4 * grp + i) < nt ? L[u][a][i] : NEG;
-        }
+      for (int i = 0; i < 4; i++) {
+        // own part: tile 0 in hi lanes, tile 1 in lo lanes; the partner lane (col ^ 8)
+        // sends the other part of the same score
+        const float mine = hi_col ? S[0][i] : S[1][i];
+        const float send = hi_col ? S[1][i] : S[0][i];
+        const float st = mine + __builtin_bit_cast(float, ror8u(__builtin_bit_cast(uint32_t, send)));
+        L[u][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
+        if constexpr (MASK) L[u][i] = (tb + own_tok + i) < nt ? L[u][i] : NEG;
       }
     }
     // ---- max per head over these 64 tokens and rescaling of the running state
-    float mx = NEG;
-#pragma unroll
-    for (int u = 0; u < 2; u++)
-#pragma unroll
-      for (int a = 0; a < 2; a++)
-        mx = fmaxf(fmaxf(mx, fmaxf(L[u][a][0], L[u][a][1])), fmaxf(L[u][a][2], L[u][a][3]));
+    float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
+                     fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
+    mx = fmaxf(mx, swap8(mx));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (MASK && mx == NEG) continue;  // no valid tokens here (uniform)
@@ -412,44 +451,42 @@ __device__ inline void attn_sub(const char* __restrict__ cur, const _Float16* __
     }
     m_run = m_new;
 
-    // ---- P' = p nu_v (hi in rows 0..7, lo in rows 8..15) and PV
+    // ---- P' = p nu_v split hi + lo, exchanged with the partner lane, and PV
 #pragma unroll
     for (int u = 0; u < 2; u++) {
       const int tb = 64 * hf + 32 * u;
-      uint32_t Pw[4];  // P' as 4 packed fp16 pairs: element 4 a + i
+      const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_VN + 2 * (tb + own_tok));
+      const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
+      float pv[4];
 #pragma unroll
-      for (int a = 0; a < 2; a++) {
-        const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_VN + 2 * (tb + 16 * a + 4 * grp));
-        const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
-        float pv[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const float p = __builtin_amdgcn_exp2f(L[u][a][i] - m_new);  // 0 for masked tokens
-          l_run += p;
-          pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
-          if constexpr (MASK) pv[i] = (tb + 16 * a + 4 * grp + i) < nt ? pv[i] : 0.f;
-        }
-        // hi rounds toward zero (any rounding works: lo takes the exact remainder)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[i], pv[i + 1]));
-          const float ra = __builtin_fmaf((float)hlo(hw), -1.0f, pv[i]);
-          const float rb = __builtin_fmaf((float)hhi(hw), -1.0f, pv[i + 1]);
-          const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
-          Pw[2 * a + i / 2] = hi_col ? hw : lw;
-        }
+      for (int i = 0; i < 4; i++) {
+        const float p = __builtin_amdgcn_exp2f(L[u][i] - m_new);  // 0 for masked tokens
+        l_run += p;
+        pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
+        if constexpr (MASK) pv[i] = (tb + own_tok + i) < nt ? pv[i] : 0.f;
       }
-      const half8 P = __builtin_bit_cast(half8, uint4{Pw[0], Pw[1], Pw[2], Pw[3]});
-      // value operands: this lane addresses token tb + 16 a + 4 grp + col / 4, block 4 dt + col % 4
+      // hi rounds toward zero (any rounding works: lo takes the exact remainder)
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        hw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2 * e], pv[2 * e + 1]));
+        const float ra = __builtin_fmaf((float)hlo(hw[e]), -1.0f, pv[2 * e]);
+        const float rb = __builtin_fmaf((float)hhi(hw[e]), -1.0f, pv[2 * e + 1]);
+        lw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+      }
+      // rows < 8 (hi lanes): hi parts of tile 0 (own) and tile 1 (from lane col + 8);
+      // rows >= 8 (lo lanes): lo parts of tile 0 (from lane col - 8) and tile 1 (own)
+      const uint32_t P0 = from_lo_partner(hw[0], lw[0]), P1 = from_lo_partner(hw[1], lw[1]);
+      const uint32_t P2 = from_hi_partner(lw[0], hw[0]), P3 = from_hi_partner(lw[1], hw[1]);
+      const half8 P = __builtin_bit_cast(half8, uint4{P0, P1, P2, P3});
       short4_ vt[2][4];
 #pragma unroll
       for (int a = 0; a < 2; a++) {
-        const uint4 rw = *reinterpret_cast<const uint4*>(cur + SC_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16);
-        const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
-        const int sh = 8 * (col & 3);
+        const uint32_t w =
+            reinterpret_cast<const uint32_t*>(cur + SC_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16)[col & 3];
 #pragma unroll
         for (int dt = 0; dt < 4; dt++)
-          vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + __builtin_amdgcn_ubfe(ww[dt], sh, 8) * 4));
+          vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + ((w >> (8 * dt)) & 0xffu) * 4));
       }
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
@@ -461,7 +498,7 @@ __device__ inline void attn_sub(const char* __restrict__ cur, const _Float16* __
   }
 }
 
-__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q, const float* __restrict__ pi32,
+__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q, const float* __restrict__ pit32,
                                                         float qscale, const uint8_t* __restrict__ kc,
                                                         const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
                                                         const _Float16* __restrict__ vn,
@@ -488,25 +525,29 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   for (int i = tid; i < 256 * 4 * 2 / 16; i += AW * 64)
     reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
   // rotated, scaled queries of the group's heads: qs[h][i] = qscale sum_j Pi[i][j] q[h][j],
-  // computed in wave 0's second buffer, which no load touches before the barrier below
+  // computed in wave 0's second buffer, which no load touches before the barrier below;
+  // lanes run over i, so the transposed rotation is read coalesced
   float* qs = reinterpret_cast<float*>(wbuf + SC_BYTES);
   {
     float* qin = qs + GF * D;  // raw queries
     for (int i = tid; i < G * D; i += AW * 64) qin[i] = (float)q[((int64_t)b * Hq + (int64_t)g * G) * D + i];
     __syncthreads();
-    for (int o = tid; o < G * D; o += AW * 64) {
-      const int h = o / D, i = o % D;
-      float a = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < D; j++) a = fmaf(pi32[i * D + j], qin[h * D + j], a);
-      qs[o] = a * qscale;
+    const int i = lane, h0 = w;  // heads h0 and h0 + AW
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 16
+    for (int j = 0; j < D; j++) {
+      const float p = pit32[j * D + i];
+      a0 = fmaf(p, qin[h0 * D + j], a0);
+      a1 = fmaf(p, qin[(h0 + AW) * D + j], a1);
     }
+    if (h0 < G) qs[h0 * D + i] = a0 * qscale;
+    if (h0 + AW < G) qs[(h0 + AW) * D + i] = a1 * qscale;
     __syncthreads();
   }
   const int col = lane & 15, grp = lane >> 4, hd = col & 7;
   const bool hi_col = col < 8;
   // B operand of QK: column col = head hd, hi part (col < 8) or lo part; k = 8 grp + j is
-  // dimension 32 s + 8 grp + j.
+  // dimension 16 grp + 8 s + j.
   half8 qb[2];
   {
     const float* qr = qs + (hd < G ? hd : 0) * D;
@@ -514,7 +555,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     for (int s = 0; s < 2; s++)
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const float v = hd < G ? qr[32 * s + 8 * grp + j] : 0.f;
+        const float v = hd < G ? qr[16 * grp + 8 * s + j] : 0.f;
         const _Float16 hv = (_Float16)v;
         qb[s][j] = hi_col ? hv : (_Float16)(v - (float)hv);
       }
@@ -547,7 +588,8 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   }
 
   // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
-  float l = l_run;
+  float l = l_run;  // lanes col and col ^ 8 summed different tokens of the same head
+  l += swap8(l);
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   __syncthreads();                            // every wave is done with its buffers
@@ -557,7 +599,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const float v = O[dt][i] + __shfl_xor(O[dt][i], 32);
-      if (grp < 2) so[(w * GF + 4 * grp + i) * D + 16 * dt + col] = v;
+      if (grp < 2) so[(w * GF + 4 * grp + i) * D + 16 * (col >> 2) + 4 * dt + (col & 3)] = v;
     }
   if (grp == 0 && col < GF) {
     sm[w * GF + col] = m_run;
@@ -674,7 +716,7 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
   if (plan.fast) {
-    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, cb->pi32, qscale, k_codes, kn, v_codes, vn,
+    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, cb->pit32, qscale, k_codes, kn, v_codes, vn,
                        cb->cw16, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
