@@ -85,8 +85,8 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
   float* sl = sm + AW * GMAX;                            // [AW][GMAX]
   float* so = sl + AW * GMAX;                            // [AW][GMAX][64]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = fq_tid(), lane = tid & 63, wave = tid >> 6;
+  const int chunk = fq_bid_x(), g = fq_bid_y(), b = fq_bid_z();
   const int G = Hq / Hkv;
   const int B = (D / K) * bits;
 
@@ -254,8 +254,8 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
   constexpr int PRE = 16;  // accumulators of the first chunks, loaded before anything waits
   __shared__ float ot[D];
   __shared__ float wsh[COMB_W];
-  const int64_t bh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int64_t bh = fq_bid_x();
+  const int lane = fq_tid();
   const float NEG = -__builtin_huge_valf();
   const float* rec = ws + bh * nchunks * REC;
   float v[PRE];
@@ -264,12 +264,20 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
   float pc[D];  // column `lane` of Pi
 #pragma unroll
   for (int j = 0; j < D; j++) pc[j] = pi32[j * D + lane];
-  float M = NEG;
-  for (int c = lane; c < nchunks; c += 64) M = fmaxf(M, rec[(int64_t)c * REC]);
+  // max and sum of chunk `lane` (the common case has at most 64 chunks: one round trip)
+  const float m0 = lane < nchunks ? rec[(int64_t)lane * REC] : NEG;
+  const float l0 = lane < nchunks ? rec[(int64_t)lane * REC + 1] : 0.f;
+  float M = m0;
+  for (int c = lane + 64; c < nchunks; c += 64) M = fmaxf(M, rec[(int64_t)c * REC]);
 #pragma unroll
   for (int s2 = 32; s2 >= 1; s2 >>= 1) M = fmaxf(M, __shfl_xor(M, s2));
-  float Ls = 0.f;
-  for (int c = lane; c < nchunks; c += 64) {
+  float Ls;
+  {
+    const float wgt = m0 == NEG ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+    if (lane < COMB_W) wsh[lane] = wgt;
+    Ls = l0 * wgt;
+  }
+  for (int c = lane + 64; c < nchunks; c += 64) {
     const float mc = rec[(int64_t)c * REC];
     const float wgt = mc == NEG ? 0.f : __builtin_amdgcn_exp2f(mc - M);
     if (c < COMB_W) wsh[c] = wgt;
@@ -308,28 +316,33 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
 // T a multiple of 8 (the attention workload's shape).  Differences from
 // attn_split:
 //   * Query hi and lo parts sit in different MFMA columns (heads in 0..7, their
-//     lo parts in 8..15), so QK takes 4 matrix ops per 32 tokens; one DPP add
-//     (lane col + lane col ^ 8) recombines them.
+//     lo parts in 8..15) of QK; partner lanes (col, col ^ 8) hold the two parts
+//     of different 16-token tiles and recombine them with one DPP add, so every
+//     score and every exponential is computed once.
 //   * PV puts P' hi in rows 0..7 and lo in rows 8..15 (summed once at the end)
 //     and reads the value operand transposed straight from the LDS codebook
 //     with ds_read_tr16_b64: lane 4a + b of a 16-lane group receives element b
 //     of the 8-byte rows addressed by lanes a, a+4, a+8, a+12, so lanes
-//     address (token a', block) rows and receive 4 tokens of one dimension.
+//     address (token, block) rows and receive 4 tokens of one dimension.
 //     The K order inside a 32-token tile is permuted (k = 8 grp + 4 a + i is
 //     token 16 a + 4 grp + i) so P' comes straight from the QK registers.
-//   * The running max and the rescaling happen once per 64 tokens.
-//   * Every wave streams its own 128-token sub-chunks (codes and norms, 4.5 KiB)
-//     through a private double buffer filled by direct global-to-LDS loads and
-//     waits only for its own loads: no workgroup barrier inside the stream.
+//   * Every wave streams its own 64-token units (codes and norms, 2.25 KiB)
+//     through 4 private LDS buffers filled by direct global-to-LDS loads issued
+//     3 units ahead; it waits only for its own loads.
+//   * Software pipeline: iteration h computes the scores and the running max of
+//     unit h + 1 while it exponentiates unit h and accumulates its PV, so the
+//     two dependency chains (LDS gathers -> QK -> cross-lane max, and
+//     exp -> hi/lo split -> DPP exchange -> PV) overlap inside one wave.
 //   * The workgroup merges its waves into one partial record per query head;
 //     attn_combine merges the records.  (Merging inside the kernel would need a
 //     device-scope fence per workgroup, which on this multi-die part writes back
 //     and invalidates the die's L2 and costs far more than a second launch.)
-constexpr int SC = 128;  // tokens per wave sub-chunk
+constexpr int UT = 64;  // tokens per wave unit
+constexpr int NBUF = 4;  // unit buffers per wave
 constexpr int GF = 8;    // query heads per KV head on the fast path
-constexpr int SC_KC = 0, SC_VC = SC * 16, SC_KN = 2 * SC * 16, SC_VN = 2 * SC * 16 + SC * 2;
-constexpr int SC_BYTES = 2 * SC * 16 + 4 * SC;  // 4608
-constexpr int WG_TOKENS_UNIT = AW * SC;         // 512: workgroup token ranges are multiples of this
+constexpr int U_KC = 0, U_VC = UT * 16, U_KN = 2 * UT * 16, U_VN = 2 * UT * 16 + UT * 2;
+constexpr int U_BYTES = 2 * UT * 16 + 4 * UT;  // 2304
+constexpr int WG_TOKENS_UNIT = 2 * AW * UT;    // 512: workgroup token ranges are multiples of this
 
 typedef short short4_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_ lds_s4;
@@ -348,27 +361,6 @@ __device__ inline _Float16 hhi(uint32_t w) { return __builtin_bit_cast(_Float16,
 __device__ inline float swap8(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, true));
 }
-
-// Codes and norms of the nt tokens starting at slab token tok0 into the wave's
-// buffer: always 6 load instructions (token indices past nt are clamped to the
-// last valid token, whose bytes land in slots the compute masks), so a wave can
-// wait for exactly the older sub-chunk with vmcnt(6).  nt is a multiple of 8.
-__device__ inline void attn_sub_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
-                                     const _Float16* __restrict__ kn, const _Float16* __restrict__ vn, int64_t tok0,
-                                     int nt, char* dst, int lane) {
-#pragma unroll
-  for (int p = 0; p < 2; p++) {
-    const int t = (64 * p + lane) < nt ? (64 * p + lane) : nt - 1;
-    lds_dma16(kc + (tok0 + t) * 16, dst + SC_KC + p * 1024);
-    lds_dma16(vc + (tok0 + t) * 16, dst + SC_VC + p * 1024);
-  }
-  const int t2 = (2 * lane) < nt ? 2 * lane : nt - 2;  // two norms per lane
-  lds_dma4(kn + tok0 + t2, dst + SC_KN);
-  lds_dma4(vn + tok0 + t2, dst + SC_VN);
-}
-
-// Value of lane l ^ 8 (row_ror:8 within each 16-lane row).
-__device__ inline uint32_t ror8u(uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, true); }
 // Lanes 8..15 of each row take lane l - 8's `src`, lanes 0..7 keep `keep`.
 __device__ inline uint32_t from_lo_partner(uint32_t keep, uint32_t src) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xf, 0xc, false);
@@ -378,213 +370,320 @@ __device__ inline uint32_t from_hi_partner(uint32_t keep, uint32_t src) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)keep, (int)src, 0x128, 0xf, 0x3, false);
 }
 
-// One wave's sub-chunk (tokens 0 .. 127 of `cur`, nt valid) as two halves of
-// 64 tokens: scores first, then one max / rescale, then the exponentials and
-// PV.  MASK: tokens at or past `nt` are excluded.
-//
-// Layouts inside a 32-token group starting at tb (lane = 16 grp + col):
+// Codes and norms of the nt tokens starting at slab token tok0 into a unit
+// buffer: always 3 load instructions (token indices past nt are clamped to the
+// last valid token, whose bytes land in slots whose scores are masked), so a
+// wave waits for an older unit with vmcnt(3 x younger units).  nt is a
+// positive multiple of 8.
+__device__ inline void attn_unit_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
+                                      const _Float16* __restrict__ kn, const _Float16* __restrict__ vn, int64_t tok0,
+                                      int nt, char* dst, int lane) {
+  const int t = lane < nt ? lane : nt - 1;
+  lds_dma16(kc + (tok0 + t) * 16, dst + U_KC);
+  lds_dma16(vc + (tok0 + t) * 16, dst + U_VC);
+  // lanes 0..31: key norms of tokens 2 l, 2 l + 1; lanes 32..63: value norms
+  const int l2 = 2 * (lane & 31), t2 = l2 < nt ? l2 : nt - 2;
+  lds_dma4(lane < 32 ? kn + tok0 + t2 : vn + tok0 + t2, dst + U_KN);
+}
+
+// Scores of one unit (stage A).  Layouts inside a 32-token group starting at
+// tb = 32 u (lane = 16 grp + col):
 //   QK tile a (tokens tb + 16 a + 0..15): A row col = token tb + 16 a + col; its
 //   k = 8 grp + j is dimension 16 grp + 8 s + j for matrix op s, i.e. codes
 //   4 grp + 2 s and 4 grp + 2 s + 1 = bytes 2 s, 2 s + 1 of the token's record
 //   dword grp.  Output column col = head col & 7, query hi part (col < 8) or lo
-//   part, rows 4 grp + i.
-//   After the hi + lo recombination a lane holds whole scores of head col & 7
-//   for tokens tb + 16 ah + 4 grp + i, ah = 0 in lanes col < 8 (tile 0) and 1
-//   in lanes col >= 8 (tile 1): every score is computed once.
-//   PV: k = 8 grp + 4 a + i is token tb + 16 a + 4 grp + i; P' rows 0..7 are
-//   the hi parts of heads 0..7, rows 8..15 the lo parts.  Value operand dt,
-//   lane c = 4 a' + b: the lane addresses token tb + 16 a + 4 grp + c / 4 and
-//   the block whose code is byte dt of record dword c % 4 (block 4 (c % 4) + dt),
-//   and receives dimension 16 a' + 4 dt + b of 4 tokens; output column c of
-//   accumulator dt is dimension 16 (c / 4) + 4 dt + c % 4.
+//   part, rows 4 grp + i.  After the recombination the lane holds whole scores
+//   of head col & 7 for tokens tb + own_tok + i (own_tok = 16 ah + 4 grp, ah =
+//   0 in lanes col < 8 and 1 in lanes col >= 8).
+// Returns the unit's max per head (over all lanes of the head); MASK: tokens at
+// or past nt score -inf.
 template <bool MASK>
-__device__ inline void attn_sub(const char* __restrict__ cur, const _Float16* __restrict__ cbL, const half8 (&qb)[2],
-                                int nt, int col, int grp, bool hi_col, float& m_run, float& l_run, f32x4 (&O)[4]) {
+__device__ inline float attn_scores(const char* __restrict__ cur, const _Float16* __restrict__ cbL,
+                                    const half8 (&qb)[2], int nt, int col, int grp, bool hi_col, int own_tok,
+                                    float (&L)[2][4]) {
   const float NEG = -__builtin_huge_valf();
-  const int ah = hi_col ? 0 : 1;
-  const int own_tok = 16 * ah + 4 * grp;  // first of the lane's 4 tokens in a 32-token group
-#pragma unroll 1
-  for (int hf = 0; hf < 2; hf++) {
-    // ---- scores: L[u][i] is token 64 hf + 32 u + own_tok + i, head col & 7
-    float L[2][4];
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int tb = 64 * hf + 32 * u;
-      f32x4 S[2];
+  for (int u = 0; u < 2; u++) {
+    const int tb = 32 * u;
+    f32x4 S[2];
 #pragma unroll
-      for (int a = 0; a < 2; a++) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(cur + SC_KC + (tb + 16 * a + col) * 16)[grp];
-        const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
-        const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
-        S[a] = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
-        S[a] = mfma16(k1, qb[1], S[a]);
-      }
-      const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_KN + 2 * (tb + own_tok));
-      const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        // own part: tile 0 in hi lanes, tile 1 in lo lanes; the partner lane (col ^ 8)
-        // sends the other part of the same score
-        const float mine = hi_col ? S[0][i] : S[1][i];
-        const float send = hi_col ? S[1][i] : S[0][i];
-        const float st = mine + __builtin_bit_cast(float, ror8u(__builtin_bit_cast(uint32_t, send)));
-        L[u][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
-        if constexpr (MASK) L[u][i] = (tb + own_tok + i) < nt ? L[u][i] : NEG;
-      }
+    for (int a = 0; a < 2; a++) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(cur + U_KC + (tb + 16 * a + col) * 16)[grp];
+      const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
+      const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
+      S[a] = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      S[a] = mfma16(k1, qb[1], S[a]);
     }
-    // ---- max per head over these 64 tokens and rescaling of the running state
-    float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
-                     fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
-    mx = fmaxf(mx, swap8(mx));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (MASK && mx == NEG) continue;  // no valid tokens here (uniform)
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run is -inf
-    l_run *= alpha;
-    // accumulator rows 4 grp + i belong to head 4 (grp & 1) + i
+    const uint2 nw = *reinterpret_cast<const uint2*>(cur + U_KN + 2 * (tb + own_tok));
+    const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const float ai = __shfl(alpha, 4 * (grp & 1) + i);
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) O[dt][i] *= ai;
+      // own part: tile 0 in hi lanes, tile 1 in lo lanes; the partner lane (col ^ 8)
+      // sends the other part of the same score
+      const float mine = hi_col ? S[0][i] : S[1][i];
+      const float send = hi_col ? S[1][i] : S[0][i];
+      const float st = mine + swap8(send);
+      L[u][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
+      if constexpr (MASK) L[u][i] = (tb + own_tok + i) < nt ? L[u][i] : NEG;
     }
-    m_run = m_new;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
+                   fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
+  mx = fmaxf(mx, swap8(mx));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
 
-    // ---- P' = p nu_v split hi + lo, exchanged with the partner lane, and PV
+// Stage B of one unit: p = 2^(L - m), l += p, P' = p nu_v split hi + lo and
+// exchanged with the partner lane, O += V^T P'.  Masked tokens have p = 0 and
+// clamped (finite) codes and norms, so they add nothing.  Value operand dt,
+// lane c = 4 a' + b: the lane addresses token tb + 16 a + 4 grp + c / 4 and the
+// block whose code is byte dt of record dword c % 4 (block 4 (c % 4) + dt), and
+// receives dimension 16 a' + 4 dt + b of 4 tokens; output column c of
+// accumulator dt is dimension 16 (c / 4) + 4 dt + c % 4.
+__device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __restrict__ cbL, int col, int grp,
+                               int own_tok, const float (&L)[2][4], float m, float& l_run, f32x4 (&O)[4]) {
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int tb = 64 * hf + 32 * u;
-      const uint2 nw = *reinterpret_cast<const uint2*>(cur + SC_VN + 2 * (tb + own_tok));
-      const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
-      float pv[4];
+  for (int u = 0; u < 2; u++) {
+    const int tb = 32 * u;
+    const uint2 nw = *reinterpret_cast<const uint2*>(cur + U_VN + 2 * (tb + own_tok));
+    const _Float16 vv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
+    float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = __builtin_amdgcn_exp2f(L[u][i] - m_new);  // 0 for masked tokens
-        l_run += p;
-        pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
-        if constexpr (MASK) pv[i] = (tb + own_tok + i) < nt ? pv[i] : 0.f;
-      }
-      // hi rounds toward zero (any rounding works: lo takes the exact remainder)
-      uint32_t hw[2], lw[2];
+    for (int i = 0; i < 4; i++) {
+      const float p = __builtin_amdgcn_exp2f(L[u][i] - m);
+      l_run += p;
+      pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
+    }
+    // hi rounds toward zero (any rounding works: lo takes the exact remainder)
+    uint32_t hw[2], lw[2];
 #pragma unroll
-      for (int e = 0; e < 2; e++) {
-        hw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2 * e], pv[2 * e + 1]));
-        const float ra = __builtin_fmaf((float)hlo(hw[e]), -1.0f, pv[2 * e]);
-        const float rb = __builtin_fmaf((float)hhi(hw[e]), -1.0f, pv[2 * e + 1]);
-        lw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
-      }
-      // rows < 8 (hi lanes): hi parts of tile 0 (own) and tile 1 (from lane col + 8);
-      // rows >= 8 (lo lanes): lo parts of tile 0 (from lane col - 8) and tile 1 (own)
-      const uint32_t P0 = from_lo_partner(hw[0], lw[0]), P1 = from_lo_partner(hw[1], lw[1]);
-      const uint32_t P2 = from_hi_partner(lw[0], hw[0]), P3 = from_hi_partner(lw[1], hw[1]);
-      const half8 P = __builtin_bit_cast(half8, uint4{P0, P1, P2, P3});
-      short4_ vt[2][4];
+    for (int e = 0; e < 2; e++) {
+      hw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2 * e], pv[2 * e + 1]));
+      const float ra = __builtin_fmaf((float)hlo(hw[e]), -1.0f, pv[2 * e]);
+      const float rb = __builtin_fmaf((float)hhi(hw[e]), -1.0f, pv[2 * e + 1]);
+      lw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
+    }
+    // rows < 8 (hi lanes): hi parts of tile 0 (own) and tile 1 (from lane col + 8);
+    // rows >= 8 (lo lanes): lo parts of tile 0 (from lane col - 8) and tile 1 (own)
+    const uint32_t P0 = from_lo_partner(hw[0], lw[0]), P1 = from_lo_partner(hw[1], lw[1]);
+    const uint32_t P2 = from_hi_partner(lw[0], hw[0]), P3 = from_hi_partner(lw[1], hw[1]);
+    const half8 P = __builtin_bit_cast(half8, uint4{P0, P1, P2, P3});
+    short4_ vt[2][4];
 #pragma unroll
-      for (int a = 0; a < 2; a++) {
-        const uint32_t w =
-            reinterpret_cast<const uint32_t*>(cur + SC_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16)[col & 3];
+    for (int a = 0; a < 2; a++) {
+      const uint32_t w =
+          reinterpret_cast<const uint32_t*>(cur + U_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16)[col & 3];
 #pragma unroll
-        for (int dt = 0; dt < 4; dt++)
-          vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + ((w >> (8 * dt)) & 0xffu) * 4));
-      }
+      for (int dt = 0; dt < 4; dt++)
+        vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + ((w >> (8 * dt)) & 0xffu) * 4));
+    }
 #pragma unroll
-      for (int dt = 0; dt < 4; dt++) {
-        const short4_ v0 = vt[0][dt], v1 = vt[1][dt];
-        const half8 V = __builtin_bit_cast(half8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        O[dt] = mfma16(P, V, O[dt]);
-      }
+    for (int dt = 0; dt < 4; dt++) {
+      const short4_ v0 = vt[0][dt], v1 = vt[1][dt];
+      const half8 V = __builtin_bit_cast(half8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      O[dt] = mfma16(P, V, O[dt]);
     }
   }
 }
 
-__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q, const float* __restrict__ pit32,
-                                                        float qscale, const uint8_t* __restrict__ kc,
+// Running-max update after a unit's max mx: the new max, the factor for the
+// lane's own sum and the factors for the accumulator rows 4 grp + i (head
+// 4 (grp & 1) + i).
+__device__ inline void attn_rescale_factors(float m_old, float mx, int grp, float& m_new, float& a_own,
+                                            float (&a_row)[4]) {
+  m_new = fmaxf(m_old, mx);
+  a_own = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 while m_old is -inf
+#pragma unroll
+  for (int i = 0; i < 4; i++) a_row[i] = __shfl(a_own, 4 * (grp & 1) + i);
+}
+
+// Rotated, scaled queries of one (batch, KV head) group as the QK B operands of
+// attn_k4b8: qs[h][i] = qscale sum_j Pi[i][j] q[h][j] for the group's G heads, then
+// lane (col, grp) gets, for s = 0, 1, the 8 values qs[col & 7][16 grp + 8 s + j]
+// as fp16 hi parts (col < 8) or lo parts (col >= 8; zeros for heads >= G).
+// Written once per group to qop[group][lane][s] (16 bytes each).
+__global__ __launch_bounds__(256) void attn_prep(const _Float16* __restrict__ q, const float* __restrict__ pit32,
+                                                 float qscale, int Hq, int Hkv, uint4* __restrict__ qop) {
+  __shared__ float qin[GF * D], qs[GF * D];
+  const int tid = fq_tid(), lane = tid & 63, w = tid >> 6;
+  const int grpi = fq_bid_x();  // b * Hkv + g
+  const int G = Hq / Hkv;
+  const _Float16* qg = q + (int64_t)grpi * G * D;  // heads g G .. g G + G - 1 of batch b are contiguous
+  // every load is issued before anything waits: column `lane` of Pi^T (coalesced), then the queries
+  float pt[D];
+#pragma unroll
+  for (int j = 0; j < D; j++) pt[j] = pit32[j * D + lane];
+  for (int i = tid; i < G * D; i += 256) qin[i] = (float)qg[i];
+  __syncthreads();
+  float a0 = 0.f, a1 = 0.f;  // heads w and w + 4, output i = lane
+#pragma unroll
+  for (int j = 0; j < D; j++) {
+    a0 = fmaf(pt[j], qin[w * D + j], a0);
+    a1 = fmaf(pt[j], qin[(w + 4) * D + j], a1);
+  }
+  if (w < G) qs[w * D + lane] = a0 * qscale;
+  if (w + 4 < G) qs[(w + 4) * D + lane] = a1 * qscale;
+  __syncthreads();
+  if (tid < 128) {
+    const int l = tid & 63, s = tid >> 6, col = l & 15, grp = l >> 4, hd = col & 7;
+    half8 v8;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float v = hd < G ? qs[hd * D + 16 * grp + 8 * s + j] : 0.f;
+      const _Float16 hv = (_Float16)v;
+      v8[j] = col < 8 ? hv : (_Float16)(v - (float)hv);
+    }
+    qop[((int64_t)grpi * 64 + l) * 2 + s] = __builtin_bit_cast(uint4, v8);
+  }
+}
+
+__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const uint4* __restrict__ qop, const uint8_t* __restrict__ kc,
                                                         const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
                                                         const _Float16* __restrict__ vn,
                                                         const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
                                                         int64_t wg_tokens, int nrec, float* __restrict__ ws) {
-  __shared__ __align__(16) char wbuf[AW * 2 * SC_BYTES];
+  __shared__ __align__(16) char wbuf[AW * NBUF * U_BYTES];
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ float sm[AW * GF], sl[AW * GF];
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = fq_tid(), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rx = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int rx = fq_bid_x(), g = fq_bid_y(), b = fq_bid_z();
   const int G = Hq / Hkv;
   const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
   const int64_t t_begin = (int64_t)rx * wg_tokens;
   const int64_t t_end = (t_begin + wg_tokens) < T ? (t_begin + wg_tokens) : T;
-  const int nsub = (int)((t_end - t_begin + SC - 1) / SC);
-  char* mybuf = wbuf + w * 2 * SC_BYTES;
+  // this wave's units: workgroup units w, w + AW, w + 2 AW, ...
+  const int nu_wg = (int)((t_end - t_begin + UT - 1) / UT);
+  const int nu = nu_wg > w ? (nu_wg - w + AW - 1) / AW : 0;
+  char* mybuf = wbuf + w * NBUF * U_BYTES;
+  auto unit_tok0 = [&](int h) { return t_begin + (int64_t)(w + AW * h) * UT; };
+  auto unit_nt = [&](int h) {
+    const int64_t r = t_end - unit_tok0(h);
+    return r < UT ? (int)r : UT;
+  };
+  auto load_unit = [&](int h) {
+    attn_unit_load(kc, vc, kn, vn, slab0 + unit_tok0(h), unit_nt(h), mybuf + (h & (NBUF - 1)) * U_BYTES, lane);
+  };
 
-  // first sub-chunk of every wave on its way
-  if (w < nsub) {
-    const int64_t s0 = t_begin + (int64_t)w * SC;
-    attn_sub_load(kc, vc, kn, vn, slab0 + s0, (t_end - s0) < SC ? (int)(t_end - s0) : SC, mybuf, lane);
-  }
-  for (int i = tid; i < 256 * 4 * 2 / 16; i += AW * 64)
-    reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
-  // rotated, scaled queries of the group's heads: qs[h][i] = qscale sum_j Pi[i][j] q[h][j],
-  // computed in wave 0's second buffer, which no load touches before the barrier below;
-  // lanes run over i, so the transposed rotation is read coalesced
-  float* qs = reinterpret_cast<float*>(wbuf + SC_BYTES);
-  {
-    float* qin = qs + GF * D;  // raw queries
-    for (int i = tid; i < G * D; i += AW * 64) qin[i] = (float)q[((int64_t)b * Hq + (int64_t)g * G) * D + i];
-    __syncthreads();
-    const int i = lane, h0 = w;  // heads h0 and h0 + AW
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll 16
-    for (int j = 0; j < D; j++) {
-      const float p = pit32[j * D + i];
-      a0 = fmaf(p, qin[h0 * D + j], a0);
-      a1 = fmaf(p, qin[(h0 + AW) * D + j], a1);
-    }
-    if (h0 < G) qs[h0 * D + i] = a0 * qscale;
-    if (h0 + AW < G) qs[(h0 + AW) * D + i] = a1 * qscale;
-    __syncthreads();
-  }
-  const int col = lane & 15, grp = lane >> 4, hd = col & 7;
+  // The small operands go first, through the same direct-to-LDS path as the stream, so
+  // that every wait below is an explicit count (the compiler does not see these loads and
+  // would otherwise wait for the whole stream before touching a register it loaded):
+  // waves 0 and 1 move the 2 KiB codebook, waves 2 and 3 the group's 2 KiB of query
+  // operands into wave 2's last buffer, which the stream reaches only after the barrier
+  // that follows their use.
+  char* qst = wbuf + (3 * NBUF - 1) * U_BYTES;
+  if (w < 2)
+    lds_dma16(reinterpret_cast<const char*>(cw16) + w * 1024 + lane * 16, reinterpret_cast<char*>(cbL) + w * 1024);
+  else
+    lds_dma16(reinterpret_cast<const char*>(qop + ((int64_t)b * Hkv + g) * 128) + (w - 2) * 1024 + lane * 16,
+              qst + (w - 2) * 1024);
+  const int pre = nu < NBUF - 1 ? nu : NBUF - 1;
+  for (int h = 0; h < pre; h++) load_unit(h);
+  if (pre == 3)
+    __builtin_amdgcn_s_waitcnt(0x3f79);  // vmcnt(9): the small operand landed
+  else if (pre == 2)
+    __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6)
+  else if (pre == 1)
+    __builtin_amdgcn_s_waitcnt(0x3f73);  // vmcnt(3)
+  else
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+  __syncthreads();  // codebook and query operands are in place
+  const int col = lane & 15, grp = lane >> 4;
   const bool hi_col = col < 8;
-  // B operand of QK: column col = head hd, hi part (col < 8) or lo part; k = 8 grp + j is
-  // dimension 16 grp + 8 s + j.
+  const int own_tok = 16 * (hi_col ? 0 : 1) + 4 * grp;
+  // B operand of QK: column col = head col & 7, hi part (col < 8) or lo part; k = 8 grp + j
+  // is dimension 16 grp + 8 s + j
   half8 qb[2];
-  {
-    const float* qr = qs + (hd < G ? hd : 0) * D;
-#pragma unroll
-    for (int s = 0; s < 2; s++)
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float v = hd < G ? qr[16 * grp + 8 * s + j] : 0.f;
-        const _Float16 hv = (_Float16)v;
-        qb[s][j] = hi_col ? hv : (_Float16)(v - (float)hv);
-      }
-  }
-  __syncthreads();  // qs is read; wave 0 may now load into its second buffer
+  qb[0] = *reinterpret_cast<const half8*>(qst + lane * 32);
+  qb[1] = *reinterpret_cast<const half8*>(qst + lane * 32 + 16);
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __syncthreads();  // the staging buffer is free again
 
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
   f32x4 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int k = 0;
-  for (int j = w; j < nsub; j += AW, k++) {
-    const int64_t s0 = t_begin + (int64_t)j * SC;
-    const int nt = (t_end - s0) < SC ? (int)(t_end - s0) : SC;
-    const int jn = j + AW;
-    if (jn < nsub) {
-      const int64_t s1 = t_begin + (int64_t)jn * SC;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): reads of the buffer being refilled are done
-      attn_sub_load(kc, vc, kn, vn, slab0 + s1, (t_end - s1) < SC ? (int)(t_end - s1) : SC,
-                    mybuf + ((k + 1) & 1) * SC_BYTES, lane);
-      __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6): everything but the 6 loads just issued
+  auto buf = [&](int h) -> const char* { return mybuf + (h & (NBUF - 1)) * U_BYTES; };
+  // pipeline state: scores Lc of unit h, its running max m_run, and the factors that
+  // move O and l_run from the previous max to m_run
+  float Lc[2][4], a_own = 0.f, a_row[4] = {0.f, 0.f, 0.f, 0.f};
+  if (nu > 0) {
+    if (pre == 3)
+      __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6): unit 0 landed
+    else if (pre == 2)
+      __builtin_amdgcn_s_waitcnt(0x3f73);  // vmcnt(3)
+    else
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    const float mx = unit_nt(0) == UT ? attn_scores<false>(buf(0), cbL, qb, UT, col, grp, hi_col, own_tok, Lc)
+                                      : attn_scores<true>(buf(0), cbL, qb, unit_nt(0), col, grp, hi_col, own_tok, Lc);
+    attn_rescale_factors(m_run, mx, grp, m_run, a_own, a_row);
+  }
+  // B(h) from scores Lcur at the current max, then the factors for unit h + 1 (max mxn)
+  auto finish_unit = [&](int h, float mxn, const float (&Lcur)[2][4]) {
+    l_run *= a_own;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
+    attn_pv(buf(h), cbL, col, grp, own_tok, Lcur, m_run, l_run, O);
+    attn_rescale_factors(m_run, mxn, grp, m_run, a_own, a_row);
+  };
+  // one steady-state iteration: unit h + 1 is full; its scores (into Lnxt) overlap unit h's PV
+  auto step = [&](int h, const float (&Lcur)[2][4], float (&Lnxt)[2][4]) {
+    if (h + 3 < nu) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): reads of unit h - 1's buffer are done
+      load_unit(h + 3);
+      __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6): unit h + 1 landed
+    } else if (h + 2 < nu) {
+      __builtin_amdgcn_s_waitcnt(0x3f73);  // vmcnt(3)
     } else {
       __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     }
-    const char* cur = mybuf + (k & 1) * SC_BYTES;
-    if (nt == SC)
-      attn_sub<false>(cur, cbL, qb, nt, col, grp, hi_col, m_run, l_run, O);
-    else
-      attn_sub<true>(cur, cbL, qb, nt, col, grp, hi_col, m_run, l_run, O);
+    const float mxn = attn_scores<false>(buf(h + 1), cbL, qb, UT, col, grp, hi_col, own_tok, Lnxt);
+    finish_unit(h, mxn, Lcur);
+  };
+  auto steady = [&](int h) { return h + 1 < nu && unit_nt(h + 1) == UT; };
+  int h = 0;
+  {
+    // unrolled twice so the two score arrays swap roles without copies
+    float Lb[2][4];
+    bool in_b = false;
+    while (true) {
+      if (!steady(h)) break;
+      step(h, Lc, Lb);
+      h++;
+      if (!steady(h)) {
+        in_b = true;
+        break;
+      }
+      step(h, Lb, Lc);
+      h++;
+    }
+    if (in_b)
+#pragma unroll
+      for (int u = 0; u < 2; u++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) Lc[u][i] = Lb[u][i];
+  }
+  if (h + 1 < nu) {  // unit h + 1 is the wave's last unit and is partial; all its loads were issued
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+    float Ln[2][4];
+    const float mxn = attn_scores<true>(buf(h + 1), cbL, qb, unit_nt(h + 1), col, grp, hi_col, own_tok, Ln);
+    finish_unit(h, mxn, Lc);
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) Lc[u][i] = Ln[u][i];
+    h++;
+  }
+  if (nu > 0) {  // the last unit's PV
+    l_run *= a_own;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
+    attn_pv(buf(h), cbL, col, grp, own_tok, Lc, m_run, l_run, O);
   }
 
   // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
@@ -608,18 +707,18 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   __syncthreads();
   const float NEG = -__builtin_huge_valf();
   {
-    const int h = tid >> 5, d0 = (tid & 31) * 2;
-    if (h < G) {
+    const int hh = tid >> 5, d0 = (tid & 31) * 2;
+    if (hh < G) {
       float M = NEG;
 #pragma unroll
-      for (int ww = 0; ww < AW; ww++) M = fmaxf(M, sm[ww * GF + h]);
+      for (int ww = 0; ww < AW; ww++) M = fmaxf(M, sm[ww * GF + hh]);
       float wt[AW], Ls = 0.f;
 #pragma unroll
       for (int ww = 0; ww < AW; ww++) {
-        wt[ww] = sm[ww * GF + h] == NEG ? 0.f : __builtin_amdgcn_exp2f(sm[ww * GF + h] - M);
-        Ls += sl[ww * GF + h] * wt[ww];
+        wt[ww] = sm[ww * GF + hh] == NEG ? 0.f : __builtin_amdgcn_exp2f(sm[ww * GF + hh] - M);
+        Ls += sl[ww * GF + hh] * wt[ww];
       }
-      float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nrec + rx) * REC;
+      float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + hh) * nrec + rx) * REC;
       if (d0 == 0) {
         rec[0] = M;
         rec[1] = Ls;
@@ -628,13 +727,12 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       for (int e = 0; e < 2; e++) {
         float A = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < AW; ww++) A += so[(ww * GF + h) * D + d0 + e] * wt[ww];
+        for (int ww = 0; ww < AW; ww++) A += so[(ww * GF + hh) * D + d0 + e] * wt[ww];
         rec[2 + d0 + e] = A;
       }
     }
   }
 }
-
 
 size_t attn_smem_bytes(int N, int K) {
   return (size_t)((N * K * 2 + 15) & ~15) + sizeof(float) * (GMAX * D + 2 * AW * GMAX + AW * GMAX * D);
@@ -671,9 +769,13 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   return AttnPlan{(int)nc, tc, 0, 0, false};
 }
 
-size_t attn_workspace_bytes(int B, int Hq, int nchunks) {
-  // chunk partial records, then the rotated queries of the fast path
-  return (size_t)B * (size_t)Hq * ((size_t)nchunks * REC + D) * sizeof(float);
+size_t attn_records_bytes(int B, int Hq, int nchunks) {
+  return (((size_t)B * (size_t)Hq * (size_t)nchunks * REC * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks) {
+  // chunk partial records, then the query operands of the fast path (2 KiB per group)
+  return attn_records_bytes(B, Hq, nchunks) + (size_t)B * (size_t)Hkv * 128 * sizeof(uint4);
 }
 #endif
 
@@ -716,7 +818,11 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
   if (plan.fast) {
-    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, cb->pit32, qscale, k_codes, kn, v_codes, vn,
+    uint4* qop = reinterpret_cast<uint4*>(reinterpret_cast<char*>(workspace) + attn_records_bytes(B, Hq, plan.nchunks));
+    hipLaunchKernelGGL(attn_prep, dim3((unsigned)(B * Hkv)), dim3(256), 0, s, qh, cb->pit32, qscale, Hq, Hkv, qop);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qop, k_codes, kn, v_codes, vn,
                        cb->cw16, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(WG) void decode_valu(const uint8_t* __restrict__ co
                                                   int64_t n, const float* __restrict__ cw,
                                                   const float* __restrict__ pi32, int bits, void* __restrict__ out) {
   constexpr int NB = D / K;
-  const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+  const int64_t i = (int64_t)fq_bid_x() * WG + fq_tid();
   if (i >= n) return;
   const int B = NB * bits;
 

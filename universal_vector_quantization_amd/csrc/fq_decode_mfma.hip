@@ -50,16 +50,16 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restr
                                                           const half8* __restrict__ dec_a, int N, int bits,
                                                           void* __restrict__ out) {
   __shared__ __align__(16) _Float16 cbL[LDS_CB_HALFS];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = fq_tid() & 63, w = fq_tid() >> 6;
   const int col = lane & 31, h = lane >> 5;
   const bool in_lds = N * K <= LDS_CB_HALFS;
   if (in_lds) {
-    for (int i = threadIdx.x; i < N * K * 2 / 16; i += WAVES * 64)
+    for (int i = fq_tid(); i < N * K * 2 / 16; i += WAVES * 64)
       reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
     __syncthreads();
   }
   const _Float16* cb = in_lds ? cbL : cw16;
-  const int64_t v = ((int64_t)blockIdx.x * WAVES + w) * 32 + col;
+  const int64_t v = ((int64_t)fq_bid_x() * WAVES + w) * 32 + col;
   const bool valid = v < n;
   const int B = (D / K) * bits;
 

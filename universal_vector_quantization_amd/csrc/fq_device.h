@@ -6,6 +6,21 @@
 
 namespace fq {
 
+// Work-item and workgroup indices read straight from the hardware registers, and
+// the x size of the grid in workgroups from the dispatch packet (grid_size_x, in
+// work-items, is the 32-bit word at byte 12).  The HIP index variables go through
+// library functions that are not inlined into kernels built without IEEE mode,
+// which turns every index into an opaque call result held in vector registers.
+__device__ inline int fq_tid() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ inline int fq_bid_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
+__device__ inline int fq_bid_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
+__device__ inline int fq_bid_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
+__device__ inline int fq_ngroups_x(int wg_size) {
+  typedef const __attribute__((address_space(4))) uint32_t fq_const_u32;
+  fq_const_u32* pkt = (fq_const_u32*)__builtin_amdgcn_dispatch_ptr();
+  return (int)(pkt[3] / (uint32_t)wg_size);
+}
+
 // Round a double to the nearest fp16 value, ties to even, in one step (no
 // detour through fp32, whose double rounding can differ).  Returns the fp16
 // bit pattern; |v| >= 65520 gives +-inf, NaN gives a quiet NaN.
@@ -44,16 +59,16 @@ __device__ inline uint32_t load_code(const uint8_t* __restrict__ p, int64_t bito
 // compiler's wait insertion treats such a load as a write to all of LDS and puts
 // a full vmcnt(0) before the next LDS read, which serialises any double buffer.
 // Callers wait for these loads explicitly (s_waitcnt vmcnt); nothing else in the
-// calling kernels uses M0.
+// calling kernels uses M0.  `lds` must be the same in every lane of the wave.
 typedef __attribute__((address_space(3))) void fq_lds_void;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void lds_dma16(const void* gptr, char* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(fq_lds_void*)lds;
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(fq_lds_void*)lds);
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
 }
 __device__ inline void lds_dma4(const void* gptr, char* lds) {
-  const uint32_t la = (uint32_t)(uintptr_t)(fq_lds_void*)lds;
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(fq_lds_void*)lds);
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
 }
 #pragma clang diagnostic pop

@@ -58,9 +58,9 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
   constexpr int PK_WORDS = 2 * NB * 16;  // 64 lanes * B bits / 32, for bits <= 16
   __shared__ uint32_t pk[WG / 64][PK_WORDS];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t i = (int64_t)blockIdx.x * WG + threadIdx.x;
+  const int lane = fq_tid() & 63;
+  const int wave = fq_tid() >> 6;
+  const int64_t i = (int64_t)fq_bid_x() * WG + fq_tid();
   const bool valid = i < n;
   const int B = NB * bits;
 

@@ -86,8 +86,8 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms) {
   extern __shared__ uint4 smem[];
   char* buf0 = reinterpret_cast<char*>(smem);
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(fq_tid() >> 6));
+  const int lane = fq_tid() & 63;
   const int c = lane & 31, h = lane >> 5;
   uint32_t* scr = reinterpret_cast<uint32_t*>(buf0 + 2 * CHUNKB) + w * SCR_DW;
   double* xs = reinterpret_cast<double*>(scr);  // 64 fp64
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
   const int NT = N / 32;
   const int nch = (NT + CT - 1) / CT;
 
-  for (int64_t base = (int64_t)blockIdx.x * WAVES; base < ngroups; base += (int64_t)gridDim.x * WAVES) {
+  for (int64_t base = (int64_t)fq_bid_x() * WAVES; base < ngroups; base += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
     const int64_t g = base + w;
     const int64_t v0 = g * 32;
     const int nv = g < ngroups ? (int)((n - v0) < 32 ? (n - v0) : 32) : 0;

@@ -123,22 +123,22 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   uint4* rotL = smem;
   uint4* recL = smem + ROT_OPS;
   float* c2L = reinterpret_cast<float*>(recL + N + N / 32);
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int w = __builtin_amdgcn_readfirstlane((int)(fq_tid() >> 6));
   uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + N + N / 8) + w * WAVE_WORDS;
   uint16_t* todoL = reinterpret_cast<uint16_t*>(spk + SPK_WORDS);
-  for (int i = threadIdx.x; i < ROT_OPS; i += WAVES * 64) rotL[i] = rot16[i];
-  for (int i = threadIdx.x; i < N; i += WAVES * 64) {
+  for (int i = fq_tid(); i < ROT_OPS; i += WAVES * 64) rotL[i] = rot16[i];
+  for (int i = fq_tid(); i < N; i += WAVES * 64) {
     recL[rslot(i)] = crec[i];
     c2L[cslot(i)] = cn2s[i];
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
+  const int lane = fq_tid() & 63;
   const int c = lane & 31, h = lane >> 5, q = lane >> 4, vl = lane & 15;
   const int NT = N / 32;
   const _Float16* cbh = reinterpret_cast<const _Float16*>(recL);  // record n: halfs 8 rslot(n) .. + 7
 
-  for (int64_t g = (int64_t)blockIdx.x * WAVES + w; g < ngroups; g += (int64_t)gridDim.x * WAVES) {
+  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
     const int64_t v0 = g * VG;
     const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
 

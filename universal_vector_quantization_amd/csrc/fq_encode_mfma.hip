@@ -82,14 +82,14 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
   __shared__ __align__(16) _Float16 cwL[CBL * 4];
   __shared__ __align__(16) float cn2L[CBL];
   if constexpr (K == 4) {
-    for (int i = threadIdx.x; i < N; i += WAVES * 64) {
+    for (int i = fq_tid(); i < N; i += WAVES * 64) {
       cn2L[i] = cn2s[i];
       *reinterpret_cast<uint2*>(cwL + 4 * i) = *reinterpret_cast<const uint2*>(cw16 + 4 * i);
     }
     __syncthreads();
   }
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = fq_tid() & 63, w = fq_tid() >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int NT = N / 32;
   const int B = NB * bits;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
   char* xs = xtile[w];
   const double u = 5.9604644775390625e-08;
 
-  for (int64_t g = (int64_t)blockIdx.x * WAVES + w; g < ngroups; g += (int64_t)gridDim.x * WAVES) {
+  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
     const int64_t v0 = g * VG;
     const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
 

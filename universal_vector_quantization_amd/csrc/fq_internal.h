@@ -82,7 +82,7 @@ struct AttnPlan {
 };
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
-size_t attn_workspace_bytes(int B, int Hq, int nchunks);
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
                        float* out, void* workspace, hipStream_t s);
