@@ -185,6 +185,35 @@ def test_decode_random_codes(dev, k, N, n, norm_dtype, out_dtype):
     assert max_rel_rows(got, ref) <= TOL
 
 
+@pytest.mark.parametrize("k,N,n,norm_dtype,out_dtype", [
+    (4, 256, 1_000_000 + 7, np.float16, np.float16),
+    (4, 256, 600_000 + 17, np.float32, np.float32),
+    (8, 4096, 700_000 + 1, np.float16, np.float32),
+    (2, 16, 500_000 + 31, np.float16, np.float16),
+])
+def test_decode_large_sampled(dev, k, N, n, norm_dtype, out_dtype):
+    # Batches large enough that every wave of the persistent decoder walks many groups
+    # (steady state of its load ring) plus a ragged tail, checked on sampled rows:
+    # both ends, the last whole group and random ones.
+    cb, cw, rot = codebook(k, N)
+    bits = oc.code_bits(N)
+    B = (D // k) * bits
+    store = workloads.random_code_store((n * B + 7) // 8, 60 + k)
+    if (n * B) % 8:
+        store[-1] &= (1 << ((n * B) % 8)) - 1
+    norms = workloads.random_norms(n, 70 + k, norm_dtype)
+    print(f"[decode large] k={k} N={N} n={n}", flush=True)
+    got = gpu_decode(cb, store, norms, dev, out_dtype)
+    rng = np.random.default_rng(3)
+    full = (n // 32) * 32
+    idx = np.unique(np.concatenate([rng.choice(n, 3000, replace=False), np.arange(96), np.arange(n - 96, n),
+                                    np.arange(full - 40, full + 8)]))
+    idx = idx[idx < n]
+    codes = unpack_sampled(store, idx, D // k, bits)
+    ref = oc.decode(codes, norms[idx], rot, cw)
+    assert max_rel_rows(got[idx], ref) <= TOL
+
+
 def test_decode_of_oracle_encode_roundtrip(dev):
     cb, cw, rot = codebook(4, 256)
     x = workloads.gpt2_small_kv()[:8192]

@@ -8,7 +8,40 @@
 
 #include "fq_internal.h"
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #define FQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace fq {
+
+hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int device, int64_t* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, size_t, int>, int64_t> cache;
+  const auto key = std::make_tuple(kernel, block, lds, device);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, lds);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return e;
+  const int64_t r = (int64_t)(per_cu < 1 ? 1 : per_cu) * (cus < 1 ? 1 : cus);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    cache[key] = r;
+  }
+  *out = r;
+  return hipSuccess;
+}
+
+}  // namespace fq
 
 namespace {
 

@@ -7,9 +7,17 @@
 // exact fp16 operand; Pi^T is split into fp16 hi + lo (22 bits), accumulation
 // is fp32.  Lane l owns vector l % 32 and, per 16-dim k-step, 8 consecutive
 // input dims (whole codewords for k <= 8), which it gathers from the codebook
-// (LDS copy when it fits, else the fp16 copy in global memory).  The result
-// rows a lane holds are 4 runs of 4 consecutive output dims per 32-dim tile,
-// written as 8-byte (fp16) or 16-byte (fp32) stores.
+// (LDS copy when it fits, else the fp16 copy in global memory).
+//
+// Workgroups are persistent: each loads the codebook into LDS and every wave
+// keeps the 16 Pi^T operands in registers, then walks 32-vector groups with the
+// next PF groups' records and norms already in flight.  Records that are whole
+// 32-bit words (B a multiple of 32) arrive in one load per lane.  The result rows
+// a lane holds are scattered over the 32 vectors, so they pass through a padded
+// LDS tile and leave as 16-byte stores that cover 8 (fp16) or 4 (fp32) whole
+// output vectors per instruction.
+#include <type_traits>
+
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -18,113 +26,405 @@ namespace {
 
 constexpr int D = kD;
 constexpr int WAVES = 4;
-constexpr int LDS_CB_HALFS = 16384;  // 32 KiB: codebooks up to N*k = 16384 live in LDS
+constexpr int LDS_CB_HALFS = 16384;  // codebooks up to N*k = 16384 (32 KiB) live in LDS
+constexpr int PF = 4;                // groups whose records are in flight ahead of the one decoded
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Input dims [d0, d0 + 8) of the vector whose record starts at bit `rec`.
+// Output staging row of one vector: 64 values plus 4 of padding (bank spread).
+template <bool OF16>
+constexpr int stage_row_bytes() {
+  return OF16 ? 68 * 2 : 68 * 4;
+}
+
+// `bits`-wide code starting at bit `bo` (a compile-time offset) of a record held
+// in registers.
+template <int RW>
+__device__ inline uint32_t code_at(const uint32_t (&w)[RW], int bo, int bits) {
+  const int wi = bo >> 5, sh = bo & 31;
+  uint32_t v = w[wi] >> sh;
+  if (sh + bits > 32 && wi + 1 < RW) v |= w[wi + 1] << (32 - sh);
+  return v & ((1u << bits) - 1u);
+}
+
+// Input dims [d0, d0 + 8) from a codebook copy `cb` (LDS or global), for the
+// codes of blocks d0 / K ... (K >= 8: one code; else 8 / K codes).
 template <int K>
-__device__ inline half8 gather8(const _Float16* __restrict__ cb, const uint8_t* __restrict__ codes, int64_t rec,
-                                int d0, int bits) {
+__device__ inline half8 gather_codes(const _Float16* __restrict__ cb, const uint32_t (&c)[8 / K > 0 ? 8 / K : 1],
+                                     int d0) {
   half8 r;
   if constexpr (K >= 8) {
-    const uint32_t code = load_code(codes, rec + (int64_t)(d0 / K) * bits, bits);
-    r = *reinterpret_cast<const half8*>(cb + (size_t)code * K + (d0 % K));
+    r = *reinterpret_cast<const half8*>(cb + (size_t)c[0] * K + (d0 % K));
+  } else if constexpr (K == 4) {
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const half4 v = *reinterpret_cast<const half4*>(cb + (size_t)c[p] * 4);
+#pragma unroll
+      for (int t = 0; t < 4; t++) r[4 * p + t] = v[t];
+    }
   } else {
 #pragma unroll
-    for (int p = 0; p < 8 / K; p++) {
-      const uint32_t code = load_code(codes, rec + (int64_t)(d0 / K + p) * bits, bits);
+    for (int p = 0; p < 8 / K; p++)
 #pragma unroll
-      for (int t = 0; t < K; t++) r[p * K + t] = cb[(size_t)code * K + t];
-    }
+      for (int t = 0; t < K; t++) r[p * K + t] = cb[(size_t)c[p] * K + t];
   }
   return r;
 }
 
-template <int K, bool NF16, bool OF16>
+// Scale the accumulators by the norm, pass them through the wave's padded staging
+// tile and store the first `nv` of the 32 vectors: rows 8 q + 4 h + i of tile r
+// are output dims 32 r + 8 q + 4 h + i of vector col, and each 16-byte store
+// covers 8 (fp16) or 4 (fp32) consecutive whole output vectors.
+template <bool OF16>
+__device__ inline void stage_and_store(const f32x16 (&acc)[2], float nu, char* stage, int col, int h, int lane,
+                                       char* out_g, int nv) {
+  constexpr int ROWB = stage_row_bytes<OF16>();
+#pragma unroll
+  for (int r = 0; r < 2; r++)
+#pragma unroll
+    for (int qd = 0; qd < 4; qd++) {
+      const int o = 32 * r + 8 * qd + 4 * h;
+      if constexpr (OF16) {
+        half4 hv;
+#pragma unroll
+        for (int i = 0; i < 4; i++) hv[i] = (_Float16)(acc[r][4 * qd + i] * nu);
+        *reinterpret_cast<half4*>(stage + col * ROWB + o * 2) = hv;
+      } else {
+        *reinterpret_cast<float4*>(stage + col * ROWB + o * 4) =
+            make_float4(acc[r][4 * qd] * nu, acc[r][4 * qd + 1] * nu, acc[r][4 * qd + 2] * nu, acc[r][4 * qd + 3] * nu);
+      }
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the tile is written (the wave reads it back)
+  constexpr int CHUNKS = OF16 ? 8 : 16;  // 16-byte chunks per output vector
+  constexpr int VPP = 64 / CHUNKS;       // vectors per pass
+#pragma unroll
+  for (int ps = 0; ps < 32 / VPP; ps++) {
+    const int vl = ps * VPP + lane / CHUNKS, ch = lane % CHUNKS;
+    const uint4 val = *reinterpret_cast<const uint4*>(stage + vl * ROWB + ch * 16);
+    if (nv == 32 || vl < nv) reinterpret_cast<uint4*>(out_g + vl * (OF16 ? 128 : 256))[ch] = val;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the tile is read before the next group writes it
+}
+
+// s_waitcnt vmcnt(N) that is also a compiler memory barrier.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __asm__ volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Decode of whole 32-vector groups whose records are RW whole words.  Every wave
+// keeps the records and norms of its next PF groups in a private LDS ring, filled
+// by direct global-to-LDS loads (REC_DMA + 1 per group, always issued, clamped to
+// the last group) ahead of use; the output leaves through the staging tile as
+// STORES 16-byte stores per group.  With these fixed counts the wait for a slot is
+// an exact vmcnt, and no compiler-inserted wait ever covers the ring.
+template <int K, bool NF16, bool OF16, int RW, bool CBL>
+struct StreamShape {
+  static constexpr int ROWB = stage_row_bytes<OF16>();
+  static constexpr int REC_BYTES = 32 * RW * 4;
+  static constexpr int SLOT_BYTES = (REC_BYTES + 32 * (NF16 ? 2 : 4) + 15) & ~15;
+  static constexpr int REC_DMA = RW % 4 == 0 ? (8 * RW + 63) / 64 : (32 * RW + 63) / 64;
+  static constexpr int LOADS = REC_DMA + 1;
+  static constexpr int STORES = OF16 ? 4 : 8;
+  static constexpr int WAIT_STEADY = (PF - 1) * LOADS + PF * STORES;
+  static size_t lds_bytes(int N) {
+    const size_t cb = CBL ? (size_t)((N * K * 2 + 15) & ~15) : 0;
+    return cb + (size_t)WAVES * (32 * ROWB + PF * SLOT_BYTES);
+  }
+};
+
+template <int K, bool NF16, bool OF16, int RW, bool CBL>
+__global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __restrict__ codes,
+                                                            const void* __restrict__ norms, int64_t ngroups,
+                                                            const _Float16* __restrict__ cw16,
+                                                            const half8* __restrict__ dec_a, int N, int bits,
+                                                            void* __restrict__ out) {
+  typedef StreamShape<K, NF16, OF16, RW, CBL> S;
+  constexpr int NC = 8 / K > 0 ? 8 / K : 1;
+  constexpr int BITS = RW * K / 2;  // (64 / K) blocks of BITS bits fill RW words
+  static_assert((D / K) * BITS == 32 * RW, "whole-word records");
+  (void)bits;
+  constexpr int ROWB = S::ROWB;
+  extern __shared__ uint4 smem[];
+  const int tid = fq_tid(), lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, h = lane >> 5;
+  const int cb_bytes = CBL ? ((N * K * 2 + 15) & ~15) : 0;
+  char* stage = reinterpret_cast<char*>(smem) + cb_bytes + w * 32 * ROWB;
+  char* ring = reinterpret_cast<char*>(smem) + cb_bytes + WAVES * 32 * ROWB + w * PF * S::SLOT_BYTES;
+
+  half8 da[2][4][2];  // Pi^T operands (hi, lo) of both 32-row tiles and all 4 k-steps
+#pragma unroll
+  for (int r = 0; r < 2; r++)
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int p = 0; p < 2; p++) da[r][s][p] = dec_a[((r * 4 + s) * 2 + p) * 64 + lane];
+  if constexpr (CBL)
+    for (int i = tid; i < cb_bytes / 16; i += WAVES * 64) smem[i] = reinterpret_cast<const uint4*>(cw16)[i];
+  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the operands are in registers before any ring load
+  if constexpr (CBL) __syncthreads();
+  const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
+
+  const int64_t step = (int64_t)fq_ngroups_x(WAVES * 64) * WAVES;
+  int64_t g = (int64_t)fq_bid_x() * WAVES + w;
+  if (g >= ngroups) return;
+  int64_t left = (ngroups - 1 - g) / step + 1;  // groups of this wave
+
+  auto issue = [&](int sl, int64_t gg) {
+    gg = gg < ngroups ? gg : ngroups - 1;
+    char* dst = ring + sl * S::SLOT_BYTES;
+    const char* rsrc = reinterpret_cast<const char*>(codes) + gg * S::REC_BYTES;
+    // records: REC_BYTES in 16-byte (RW % 4 == 0) or 4-byte pieces, 64 lanes per instruction,
+    // lanes past the end of the group masked off
+    constexpr int PIECE = RW % 4 == 0 ? 16 : 4;
+#pragma unroll
+    for (int p = 0; p < S::REC_DMA; p++) {
+      constexpr int TOTAL = S::REC_BYTES / PIECE;
+      if (64 * p + lane < TOTAL) {
+        if constexpr (PIECE == 16)
+          lds_dma16(rsrc + (64 * p + lane) * 16, dst + p * 1024);
+        else
+          lds_dma4(rsrc + (64 * p + lane) * 4, dst + p * 256);
+      }
+    }
+    // norms: 32 x 2 or 32 x 4 bytes in 4-byte pieces
+    constexpr int NPIECES = 32 * (NF16 ? 2 : 4) / 4;
+    const char* nsrc = reinterpret_cast<const char*>(norms) + gg * 32 * (NF16 ? 2 : 4);
+    if (lane < NPIECES) lds_dma4(nsrc + lane * 4, dst + S::REC_BYTES);
+  };
+#pragma unroll
+  for (int i = 0; i < PF; i++) issue(i, g + i * step);
+
+  auto body = [&](auto slot_c, auto wait_c) {
+    constexpr int sl = decltype(slot_c)::value;
+    wait_vmcnt<decltype(wait_c)::value>();
+    const char* src = ring + sl * S::SLOT_BYTES;
+    uint32_t rc[RW];
+    {
+      const uint32_t* rp = reinterpret_cast<const uint32_t*>(src) + col * RW;
+#pragma unroll
+      for (int i = 0; i < RW; i++) rc[i] = rp[i];
+    }
+    float nu;
+    if constexpr (NF16)
+      nu = (float)reinterpret_cast<const _Float16*>(src + S::REC_BYTES)[col];
+    else
+      nu = reinterpret_cast<const float*>(src + S::REC_BYTES)[col];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the slot is read before it is refilled
+    issue(sl, g + PF * step);
+    f32x16 acc[2];
+#pragma unroll
+    for (int r = 0; r < 2; r++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[r][e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      uint32_t c[NC];  // codes of this lane's input dims 16 s + 8 h .. + 7
+#pragma unroll
+      for (int p = 0; p < NC; p++) {
+        const uint32_t c0 = code_at<RW>(rc, ((16 * s) / K + p) * BITS, BITS);
+        const uint32_t c1 = code_at<RW>(rc, ((16 * s + 8) / K + p) * BITS, BITS);
+        c[p] = h ? c1 : c0;
+      }
+      const half8 yb = gather_codes<K>(cb, c, 16 * s + 8 * h);
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[r][s][0], yb, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[r][s][1], yb, acc[r], 0, 0, 0);
+      }
+    }
+    stage_and_store<OF16>(acc, nu, stage, col, h, lane, reinterpret_cast<char*>(out) + g * 32 * (OF16 ? 128 : 256),
+                          32);
+  };
+  typedef std::integral_constant<int, 0> C0;
+  typedef std::integral_constant<int, 1> C1;
+  typedef std::integral_constant<int, 2> C2;
+  typedef std::integral_constant<int, 3> C3;
+  static_assert(PF == 4, "the unrolled bodies below assume 4 slots");
+  constexpr int L = S::LOADS, T = S::STORES;
+  // first PF groups: fewer stores are younger than their slot
+  body(C0{}, std::integral_constant<int, 3 * L>{});
+  if (--left == 0) return;
+  g += step;
+  body(C1{}, std::integral_constant<int, 3 * L + T>{});
+  if (--left == 0) return;
+  g += step;
+  body(C2{}, std::integral_constant<int, 3 * L + 2 * T>{});
+  if (--left == 0) return;
+  g += step;
+  body(C3{}, std::integral_constant<int, 3 * L + 3 * T>{});
+  if (--left == 0) return;
+  g += step;
+  typedef std::integral_constant<int, S::WAIT_STEADY> CW;
+  while (true) {
+    body(C0{}, CW{});
+    if (--left == 0) return;
+    g += step;
+    body(C1{}, CW{});
+    if (--left == 0) return;
+    g += step;
+    body(C2{}, CW{});
+    if (--left == 0) return;
+    g += step;
+    body(C3{}, CW{});
+    if (--left == 0) return;
+    g += step;
+  }
+}
+
+// Generic decoder: any record length (codes read bit-wise from global memory) and
+// partial groups; one group per wave step, no prefetch.  Used for non-word records
+// and for the last n mod 32 vectors of the stream decoder's input.
+template <int K, bool NF16, bool OF16, bool CBL>
 __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restrict__ codes,
                                                           const void* __restrict__ norms, int64_t n,
                                                           const _Float16* __restrict__ cw16,
                                                           const half8* __restrict__ dec_a, int N, int bits,
                                                           void* __restrict__ out) {
-  __shared__ __align__(16) _Float16 cbL[LDS_CB_HALFS];
-  const int lane = fq_tid() & 63, w = fq_tid() >> 6;
+  constexpr int NC = 8 / K > 0 ? 8 / K : 1;
+  constexpr int ROWB = stage_row_bytes<OF16>();
+  extern __shared__ uint4 smem[];
+  const int tid = fq_tid(), lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, h = lane >> 5;
-  const bool in_lds = N * K <= LDS_CB_HALFS;
-  if (in_lds) {
-    for (int i = fq_tid(); i < N * K * 2 / 16; i += WAVES * 64)
-      reinterpret_cast<uint4*>(cbL)[i] = reinterpret_cast<const uint4*>(cw16)[i];
-    __syncthreads();
-  }
-  const _Float16* cb = in_lds ? cbL : cw16;
-  const int64_t v = ((int64_t)fq_bid_x() * WAVES + w) * 32 + col;
-  const bool valid = v < n;
-  const int B = (D / K) * bits;
-
-  float nu = 0.f;
-  if (valid) {
-    if constexpr (NF16)
-      nu = (float)reinterpret_cast<const _Float16*>(norms)[v];
-    else
-      nu = reinterpret_cast<const float*>(norms)[v];
-  }
-  f32x16 acc[2];
+  const int cb_bytes = CBL ? ((N * K * 2 + 15) & ~15) : 0;
+  char* stage = reinterpret_cast<char*>(smem) + cb_bytes + w * 32 * ROWB;
+  half8 da[2][4][2];
 #pragma unroll
   for (int r = 0; r < 2; r++)
 #pragma unroll
-    for (int e = 0; e < 16; e++) acc[r][e] = 0.f;
+    for (int s = 0; s < 4; s++)
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
-    half8 yb = {};
-    if (valid) yb = gather8<K>(cb, codes, v * B, 16 * s + 8 * h, bits);
-#pragma unroll
-    for (int r = 0; r < 2; r++) {
-      const half8 ahi = dec_a[((r * 4 + s) * 2 + 0) * 64 + lane];
-      const half8 alo = dec_a[((r * 4 + s) * 2 + 1) * 64 + lane];
-      acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi, yb, acc[r], 0, 0, 0);
-      acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo, yb, acc[r], 0, 0, 0);
-    }
+      for (int p = 0; p < 2; p++) da[r][s][p] = dec_a[((r * 4 + s) * 2 + p) * 64 + lane];
+  if constexpr (CBL) {
+    for (int i = tid; i < cb_bytes / 16; i += WAVES * 64) smem[i] = reinterpret_cast<const uint4*>(cw16)[i];
+    __syncthreads();
   }
-  if (!valid) return;
+  const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
+  const int B = (D / K) * bits;
+  const int64_t ngroups = (n + 31) / 32;
+  const int64_t step = (int64_t)fq_ngroups_x(WAVES * 64) * WAVES;
+  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += step) {
+    const int64_t v = g * 32 + col;
+    const int64_t vv = v < n ? v : n - 1;  // invalid lanes decode a valid record, never stored
+    float nu;
+    if constexpr (NF16)
+      nu = (float)reinterpret_cast<const _Float16*>(norms)[vv];
+    else
+      nu = reinterpret_cast<const float*>(norms)[vv];
+    f32x16 acc[2];
 #pragma unroll
-  for (int r = 0; r < 2; r++) {
+    for (int r = 0; r < 2; r++)
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      const int o = 32 * r + 8 * q + 4 * h;  // rows 8q + 4h + i of tile r
-      if constexpr (OF16) {
-        half4 hv;
+      for (int e = 0; e < 16; e++) acc[r][e] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; i++) hv[i] = (_Float16)(acc[r][4 * q + i] * nu);
-        *reinterpret_cast<half4*>(reinterpret_cast<_Float16*>(out) + v * D + o) = hv;
-      } else {
-        float4 fv = make_float4(acc[r][4 * q] * nu, acc[r][4 * q + 1] * nu, acc[r][4 * q + 2] * nu,
-                                acc[r][4 * q + 3] * nu);
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + v * D + o) = fv;
+    for (int s = 0; s < 4; s++) {
+      uint32_t c[NC];
+#pragma unroll
+      for (int p = 0; p < NC; p++) c[p] = load_code(codes, vv * B + (int64_t)((16 * s + 8 * h) / K + p) * bits, bits);
+      const half8 yb = gather_codes<K>(cb, c, 16 * s + 8 * h);
+#pragma unroll
+      for (int r = 0; r < 2; r++) {
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[r][s][0], yb, acc[r], 0, 0, 0);
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_f16(da[r][s][1], yb, acc[r], 0, 0, 0);
       }
     }
+    const int64_t nv = n - g * 32;
+    stage_and_store<OF16>(acc, nu, stage, col, h, lane, reinterpret_cast<char*>(out) + g * 32 * (OF16 ? 128 : 256),
+                          nv < 32 ? (int)nv : 32);
   }
 }
 
+template <bool OF16>
+size_t generic_lds_bytes(int N, int K, bool cbl) {
+  const size_t cb = cbl ? (size_t)((N * K * 2 + 15) & ~15) : 0;
+  return cb + (size_t)WAVES * 32 * stage_row_bytes<OF16>();
+}
+
+// Persistent grid: the workgroups that fit at once, at most one per `work` units.
+template <typename KernelT>
+hipError_t persistent_grid(const fq_codebook* cb, KernelT kernel, size_t lds, int64_t work, int64_t* wgs) {
+  int64_t resident = 0;
+  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kernel), WAVES * 64, lds, cb->device, &resident);
+  if (e != hipSuccess) return e;
+  *wgs = work < resident ? work : resident;
+  if (*wgs < 1) *wgs = 1;
+  return hipSuccess;
+}
+
+template <int K, bool NF, bool OF, bool CBL>
+hipError_t launch_generic(const fq_codebook* cb, const uint8_t* codes, const void* norms, int64_t n, void* out,
+                          hipStream_t s) {
+  const size_t lds = generic_lds_bytes<OF>(cb->N, K, CBL);
+  int64_t wgs = 0;
+  hipError_t e = persistent_grid(cb, decode_mfma<K, NF, OF, CBL>, lds, ((n + 31) / 32 + WAVES - 1) / WAVES, &wgs);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_mfma<K, NF, OF, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes, norms, n,
+                     cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out);
+  return hipGetLastError();
+}
+
+// RW > 0: the whole groups go to decode_stream, the last n mod 32 vectors to the
+// generic kernel; RW = 0: everything to the generic kernel.
+template <int K, bool NF, bool OF, int RW, bool CBL>
+hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* norms, int64_t n, void* out,
+                      hipStream_t s) {
+  int64_t done = 0;
+  if constexpr (RW > 0) {
+    typedef StreamShape<K, NF, OF, RW, CBL> S;
+    const int64_t ngroups = n / 32;
+    if (ngroups > 0) {
+      const size_t lds = S::lds_bytes(cb->N);
+      int64_t wgs = 0;
+      hipError_t e = persistent_grid(cb, decode_stream<K, NF, OF, RW, CBL>, lds, (ngroups + WAVES - 1) / WAVES, &wgs);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((decode_stream<K, NF, OF, RW, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes,
+                         norms, ngroups, cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      done = ngroups * 32;
+    }
+  }
+  if (done == n) return hipSuccess;
+  const int B = (D / K) * cb->bits;  // done is a multiple of 32, so done B bits are whole bytes
+  return launch_generic<K, NF, OF, CBL>(cb, codes + done * B / 8,
+                                        reinterpret_cast<const char*>(norms) + done * (NF ? 2 : 4), n - done,
+                                        reinterpret_cast<char*>(out) + done * (OF ? 128 : 256), s);
+}
+
+template <int K, int RW, bool CBL>
+hipError_t launch_cbl(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype nd, int64_t n,
+                      void* out, fq_dtype od, hipStream_t s) {
+  if (nd == FQ_F16 && od == FQ_F16) return launch_one<K, true, true, RW, CBL>(cb, codes, norms, n, out, s);
+  if (nd == FQ_F16) return launch_one<K, true, false, RW, CBL>(cb, codes, norms, n, out, s);
+  if (od == FQ_F16) return launch_one<K, false, true, RW, CBL>(cb, codes, norms, n, out, s);
+  return launch_one<K, false, false, RW, CBL>(cb, codes, norms, n, out, s);
+}
+
+template <int K, int RW>
+hipError_t launch_rw(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype nd, int64_t n,
+                     void* out, fq_dtype od, hipStream_t s) {
+  if (cb->N * K <= LDS_CB_HALFS) return launch_cbl<K, RW, true>(cb, codes, norms, nd, n, out, od, s);
+  return launch_cbl<K, RW, false>(cb, codes, norms, nd, n, out, od, s);
+}
+
+// Whole-word record lengths are specialised: k = 2, N = 16 and k = 4, N = 256
+// (4 words), k = 8, N = 4096 (3 words); everything else reads codes bit-wise.
 template <int K>
 hipError_t launch_k(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype nd, int64_t n,
                     void* out, fq_dtype od, hipStream_t s) {
-  const dim3 grid((unsigned)((n + WAVES * 32 - 1) / (WAVES * 32))), block(WAVES * 64);
-  const half8* da = reinterpret_cast<const half8*>(cb->dec_a);
-#define FQ_DM(NF, OF)                                                                                      \
-  hipLaunchKernelGGL((decode_mfma<K, NF, OF>), grid, block, 0, s, codes, norms, n, cb->cw16, da, cb->N,   \
-                     cb->bits, out)
-  if (nd == FQ_F16 && od == FQ_F16)
-    FQ_DM(true, true);
-  else if (nd == FQ_F16)
-    FQ_DM(true, false);
-  else if (od == FQ_F16)
-    FQ_DM(false, true);
-  else
-    FQ_DM(false, false);
-#undef FQ_DM
-  return hipGetLastError();
+  const int B = (D / K) * cb->bits;
+  if constexpr (K == 2 || K == 4) {
+    if (B == 128) return launch_rw<K, 4>(cb, codes, norms, nd, n, out, od, s);
+  }
+  if constexpr (K == 8) {
+    if (B == 96) return launch_rw<K, 3>(cb, codes, norms, nd, n, out, od, s);
+  }
+  return launch_rw<K, 0>(cb, codes, norms, nd, n, out, od, s);
 }
 
 }  // namespace

@@ -315,13 +315,12 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
 template <bool NF16>
 hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
   const size_t lds = full_lds_bytes();
-  int per_cu = 0, cus = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_full<NF16>, WAVES * 64, lds);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cb->device);
+  int64_t resident = 0;
+  const hipError_t e =
+      resident_workgroups(reinterpret_cast<const void*>(encode_full<NF16>), WAVES * 64, lds, cb->device, &resident);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (n + 31) / 32;
   int64_t wgs = (ngroups + WAVES - 1) / WAVES;
-  const int64_t resident = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
   if (wgs > resident) wgs = resident;
   hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),

@@ -435,24 +435,14 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   }
 }
 
-// Workgroups that stay resident at once (persistent grid size), per instantiation.
-template <int K, bool NF16>
-hipError_t resident_wgs(const fq_codebook* cb, size_t lds, int64_t* out) {
-  int per_cu = 0, cus = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, encode_h16<K, NF16>, Shape<K>::WAVES * 64, lds);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, cb->device);
-  if (e != hipSuccess) return e;
-  *out = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
-  return hipSuccess;
-}
-
 template <int K, bool NF16>
 hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int VG = 16 * Shape<K>::NSUB;
   const size_t lds = h16_lds_bytes(K, cb->N, WAVES);
   int64_t resident = 0;
-  const hipError_t e = resident_wgs<K, NF16>(cb, lds, &resident);
+  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(encode_h16<K, NF16>), WAVES * 64, lds,
+                                           cb->device, &resident);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (n + VG - 1) / VG;
   int64_t wgs = (ngroups + WAVES - 1) / WAVES;

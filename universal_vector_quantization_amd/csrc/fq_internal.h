@@ -83,6 +83,11 @@ struct AttnPlan {
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
+
+// Workgroups of `kernel` (block threads, lds bytes of dynamic LDS) resident at once on
+// `device`: per-CU occupancy times the CU count, at least 1.  Cached per (kernel, block,
+// lds, device) so that launches do not pay for the occupancy query.
+hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int device, int64_t* out);
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
                        float* out, void* workspace, hipStream_t s);
