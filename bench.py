@@ -75,7 +75,7 @@ def measured_traffic(kernel: str, src: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(budget_s: float = 20.0):
+def cpu_baseline(budget_s: float = 12.0):
     """The oracle as it stands, on a bounded sample of the same step."""
     import workloads
     from oracle import attention as oatt
@@ -91,7 +91,11 @@ def cpu_baseline(budget_s: float = 20.0):
 
     cw, rot = fq.load_artifact(4, 256)
     x = workloads.gpt2_small_kv()
-    n_s = 2048
+    # size the sample from a 2048-vector calibration so the encode takes about budget_s
+    t0 = time.perf_counter()
+    oc.encode(x[:2048], rot, cw, np.float16)
+    t_cal = time.perf_counter() - t0
+    n_s = int(min(len(x), max(2048, 2048 * budget_s / max(t_cal, 1e-3))) // 2048 * 2048)
     t0 = time.perf_counter()
     enc = oc.encode(x[:n_s], rot, cw, np.float16)
     t_enc = time.perf_counter() - t0
