@@ -81,7 +81,6 @@ void release(fq_codebook* cb) {
   (void)hipFree(cb->cn2);
   (void)hipFree(cb->pi64t);
   (void)hipFree(cb->pi32);
-  (void)hipFree(cb->pit32);
   (void)hipFree(cb->amfma);
   (void)hipFree(cb->cinit);
   (void)hipFree(cb->cn2s);
@@ -318,12 +317,10 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   _Float16* h16 = new (std::nothrow) _Float16[cw16_bytes / 2]();
   float* hcn2 = new (std::nothrow) float[N];
   double* hpi64t = new (std::nothrow) double[d * d];
-  float* hpit32 = new (std::nothrow) float[d * d];
-  if (!h16 || !hcn2 || !hpi64t || !hpit32) {
+  if (!h16 || !hcn2 || !hpi64t) {
     delete[] h16;
     delete[] hcn2;
     delete[] hpi64t;
-    delete[] hpit32;
     delete cb;
     return FQ_ERR_HIP;
   }
@@ -350,31 +347,25 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
     cb->h16_eabs = nextafterf((float)abs_, INFINITY);
   }
   for (int i = 0; i < d; i++)
-    for (int j = 0; j < d; j++) {
-      hpi64t[j * d + i] = (double)rotation[i * d + j];
-      hpit32[j * d + i] = rotation[i * d + j];
-    }
+    for (int j = 0; j < d; j++) hpi64t[j * d + i] = (double)rotation[i * d + j];
 
   fq_status st = FQ_OK;
   if (hipMalloc(&cb->cw, nk * sizeof(float)) != hipSuccess || hipMalloc(&cb->cw16, cw16_bytes) != hipSuccess ||
       hipMalloc(&cb->cn2, N * sizeof(float)) != hipSuccess ||
       hipMalloc(&cb->pi64t, (size_t)d * d * sizeof(double)) != hipSuccess ||
-      hipMalloc(&cb->pi32, (size_t)d * d * sizeof(float)) != hipSuccess ||
-      hipMalloc(&cb->pit32, (size_t)d * d * sizeof(float)) != hipSuccess)
+      hipMalloc(&cb->pi32, (size_t)d * d * sizeof(float)) != hipSuccess)
     st = FQ_ERR_HIP;
   if (st == FQ_OK &&
       (hipMemcpy(cb->cw, codewords, nk * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
        hipMemcpy(cb->cw16, h16, cw16_bytes, hipMemcpyHostToDevice) != hipSuccess ||
        hipMemcpy(cb->cn2, hcn2, N * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
        hipMemcpy(cb->pi64t, hpi64t, (size_t)d * d * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
-       hipMemcpy(cb->pi32, rotation, (size_t)d * d * sizeof(float), hipMemcpyHostToDevice) != hipSuccess ||
-       hipMemcpy(cb->pit32, hpit32, (size_t)d * d * sizeof(float), hipMemcpyHostToDevice) != hipSuccess))
+       hipMemcpy(cb->pi32, rotation, (size_t)d * d * sizeof(float), hipMemcpyHostToDevice) != hipSuccess))
     st = FQ_ERR_HIP;
   if (st == FQ_OK) st = upload_mfma_operands(cb, codewords, rotation, hcn2);
   delete[] h16;
   delete[] hcn2;
   delete[] hpi64t;
-  delete[] hpit32;
   if (st != FQ_OK) {
     release(cb);
     return st;

@@ -498,47 +498,9 @@ __device__ inline void attn_rescale_factors(float m_old, float mx, int grp, floa
   for (int i = 0; i < 4; i++) a_row[i] = __shfl(a_own, 4 * (grp & 1) + i);
 }
 
-// Rotated, scaled queries of one (batch, KV head) group as the QK B operands of
-// attn_k4b8: qs[h][i] = qscale sum_j Pi[i][j] q[h][j] for the group's G heads, then
-// lane (col, grp) gets, for s = 0, 1, the 8 values qs[col & 7][16 grp + 8 s + j]
-// as fp16 hi parts (col < 8) or lo parts (col >= 8; zeros for heads >= G).
-// Written once per group to qop[group][lane][s] (16 bytes each).
-__global__ __launch_bounds__(256) void attn_prep(const _Float16* __restrict__ q, const float* __restrict__ pit32,
-                                                 float qscale, int Hq, int Hkv, uint4* __restrict__ qop) {
-  __shared__ float qin[GF * D], qs[GF * D];
-  const int tid = fq_tid(), lane = tid & 63, w = tid >> 6;
-  const int grpi = fq_bid_x();  // b * Hkv + g
-  const int G = Hq / Hkv;
-  const _Float16* qg = q + (int64_t)grpi * G * D;  // heads g G .. g G + G - 1 of batch b are contiguous
-  // every load is issued before anything waits: column `lane` of Pi^T (coalesced), then the queries
-  float pt[D];
-#pragma unroll
-  for (int j = 0; j < D; j++) pt[j] = pit32[j * D + lane];
-  for (int i = tid; i < G * D; i += 256) qin[i] = (float)qg[i];
-  __syncthreads();
-  float a0 = 0.f, a1 = 0.f;  // heads w and w + 4, output i = lane
-#pragma unroll
-  for (int j = 0; j < D; j++) {
-    a0 = fmaf(pt[j], qin[w * D + j], a0);
-    a1 = fmaf(pt[j], qin[(w + 4) * D + j], a1);
-  }
-  if (w < G) qs[w * D + lane] = a0 * qscale;
-  if (w + 4 < G) qs[(w + 4) * D + lane] = a1 * qscale;
-  __syncthreads();
-  if (tid < 128) {
-    const int l = tid & 63, s = tid >> 6, col = l & 15, grp = l >> 4, hd = col & 7;
-    half8 v8;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const float v = hd < G ? qs[hd * D + 16 * grp + 8 * s + j] : 0.f;
-      const _Float16 hv = (_Float16)v;
-      v8[j] = col < 8 ? hv : (_Float16)(v - (float)hv);
-    }
-    qop[((int64_t)grpi * 64 + l) * 2 + s] = __builtin_bit_cast(uint4, v8);
-  }
-}
-
-__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const uint4* __restrict__ qop, const uint8_t* __restrict__ kc,
+__global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q,
+                                                        const uint4* __restrict__ rot16, float qscale,
+                                                        const uint8_t* __restrict__ kc,
                                                         const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
                                                         const _Float16* __restrict__ vn,
                                                         const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
@@ -566,39 +528,65 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const uint4* __restrict_
     attn_unit_load(kc, vc, kn, vn, slab0 + unit_tok0(h), unit_nt(h), mybuf + (h & (NBUF - 1)) * U_BYTES, lane);
   };
 
-  // The small operands go first, through the same direct-to-LDS path as the stream, so
-  // that every wait below is an explicit count (the compiler does not see these loads and
-  // would otherwise wait for the whole stream before touching a register it loaded):
-  // waves 0 and 1 move the 2 KiB codebook, waves 2 and 3 the group's 2 KiB of query
-  // operands into wave 2's last buffer, which the stream reaches only after the barrier
-  // that follows their use.
-  char* qst = wbuf + (3 * NBUF - 1) * U_BYTES;
+  // The codebook (waves 0 and 1) and the first units go first, through the direct-to-LDS
+  // path, so that every wait in the stream is an explicit count.
   if (w < 2)
     lds_dma16(reinterpret_cast<const char*>(cw16) + w * 1024 + lane * 16, reinterpret_cast<char*>(cbL) + w * 1024);
-  else
-    lds_dma16(reinterpret_cast<const char*>(qop + ((int64_t)b * Hkv + g) * 128) + (w - 2) * 1024 + lane * 16,
-              qst + (w - 2) * 1024);
+  // units 0 and 1 now, unit 2 after the rotation (whose compiler-inserted wait covers
+  // every load issued before it)
   const int pre = nu < NBUF - 1 ? nu : NBUF - 1;
-  for (int h = 0; h < pre; h++) load_unit(h);
-  if (pre == 3)
-    __builtin_amdgcn_s_waitcnt(0x3f79);  // vmcnt(9): the small operand landed
-  else if (pre == 2)
-    __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6)
-  else if (pre == 1)
-    __builtin_amdgcn_s_waitcnt(0x3f73);  // vmcnt(3)
-  else
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-  __syncthreads();  // codebook and query operands are in place
-  const int col = lane & 15, grp = lane >> 4;
+  const int pre_early = pre < 2 ? pre : 2;
+  for (int h = 0; h < pre_early; h++) load_unit(h);
+  const int col = lane & 15, grp = lane >> 4, hd = col & 7;
   const bool hi_col = col < 8;
   const int own_tok = 16 * (hi_col ? 0 : 1) + 4 * grp;
+  // Query rotation on the matrix core: wave w computes row tile w of (1024 Pi) q^T for the
+  // group's heads with the split rotation operands of the codebook handle (hi + mid parts;
+  // the lo part is 2^-22 of them and is left out), B = the raw fp16 queries (exact).  The
+  // operand's row permutation leaves coordinates 16 grp + 4 w + i of head col & 7 in lane
+  // (col, grp); they go through LDS (wave 2's last buffer, which the stream reaches only
+  // after the barriers below) so every lane can build its QK B operand.  These loads are
+  // compiler-visible; the compiler's wait for them also covers the older stream loads
+  // above (codebook, units 0 and 1), which the first steps need anyway.
+  float* qs = reinterpret_cast<float*>(wbuf + (3 * NBUF - 1) * U_BYTES);  // [GF][D]
+  static_assert(GF * D * (int)sizeof(float) <= U_BYTES, "query staging");
+  {
+    half8 ra[2][2], qin[2];
+#pragma unroll
+    for (int s = 0; s < 2; s++) {
+#pragma unroll
+      for (int part = 0; part < 2; part++)
+        ra[s][part] = __builtin_bit_cast(half8, rot16[((s * 4 + w) * 3 + part) * 64 + lane]);
+      qin[s] = hd < G ? __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(
+                            q + ((int64_t)b * Hq + (int64_t)g * G + hd) * D + 32 * s + 8 * grp))
+                      : half8{};
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int part = 0; part < 2; part++) acc = mfma16(ra[s][part], qin[s], acc);
+    if (hi_col) {
+      const float sc = qscale * (1.0f / 1024.0f);
+#pragma unroll
+      for (int i = 0; i < 4; i++) qs[hd * D + 16 * grp + 4 * w + i] = acc[i] * sc;
+    }
+  }
+  __syncthreads();  // codebook in place, rotated queries staged
   // B operand of QK: column col = head col & 7, hi part (col < 8) or lo part; k = 8 grp + j
   // is dimension 16 grp + 8 s + j
   half8 qb[2];
-  qb[0] = *reinterpret_cast<const half8*>(qst + lane * 32);
-  qb[1] = *reinterpret_cast<const half8*>(qst + lane * 32 + 16);
+#pragma unroll
+  for (int s = 0; s < 2; s++)
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const float v = hd < G ? qs[hd * D + 16 * grp + 8 * s + j] : 0.f;
+      const _Float16 hv = (_Float16)v;
+      qb[s][j] = hi_col ? hv : (_Float16)(v - (float)hv);
+    }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   __syncthreads();  // the staging buffer is free again
+  for (int h = pre_early; h < pre; h++) load_unit(h);
 
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
   f32x4 O[4];
@@ -744,7 +732,7 @@ size_t attn_smem_bytes(int N, int K) {
 // k = 4 with 8-bit codes, at most 8 query heads per KV head and T a multiple of 8
 // runs attn_k4b8.
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
-  return cb->k == 4 && cb->bits == 8 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
+  return cb->k == 4 && cb->bits == 8 && cb->rot16 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
 }
 
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
@@ -774,8 +762,8 @@ size_t attn_records_bytes(int B, int Hq, int nchunks) {
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks) {
-  // chunk partial records, then the query operands of the fast path (2 KiB per group)
-  return attn_records_bytes(B, Hq, nchunks) + (size_t)B * (size_t)Hkv * 128 * sizeof(uint4);
+  (void)Hkv;  // chunk partial records only
+  return attn_records_bytes(B, Hq, nchunks);
 }
 #endif
 
@@ -818,11 +806,8 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
   if (plan.fast) {
-    uint4* qop = reinterpret_cast<uint4*>(reinterpret_cast<char*>(workspace) + attn_records_bytes(B, Hq, plan.nchunks));
-    hipLaunchKernelGGL(attn_prep, dim3((unsigned)(B * Hkv)), dim3(256), 0, s, qh, cb->pit32, qscale, Hq, Hkv, qop);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qop, k_codes, kn, v_codes, vn,
+    hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, reinterpret_cast<const uint4*>(cb->rot16), qscale,
+                       k_codes, kn, v_codes, vn,
                        cb->cw16, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

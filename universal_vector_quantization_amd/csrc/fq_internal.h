@@ -18,7 +18,6 @@ struct fq_codebook {
   float* cn2;       // [N] fp32 ||c_n||^2, rounded to nearest from an fp64 sum
   double* pi64t;    // [d][d] Pi transposed, fp64: pi64t[j*d + i] = Pi[i][j]
   float* pi32;      // [d][d] Pi row-major, fp32
-  float* pit32;     // [d][d] Pi transposed, fp32: pit32[j*d + i] = Pi[i][j]
   float cmax;       // max_n ||c_n||, rounded up
   float c2max;      // max_n ||c_n||^2, rounded up
   // Operands of the matrix-core encoder (k = 4 or 8, N a multiple of 32; else null):
