@@ -16,8 +16,6 @@
 // a lane holds are scattered over the 32 vectors, so they pass through a padded
 // LDS tile and leave as 16-byte stores that cover 8 (fp16) or 4 (fp32) whole
 // output vectors per instruction.
-#include <type_traits>
-
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -141,7 +139,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
                                                             const void* __restrict__ norms, int64_t ngroups,
                                                             const _Float16* __restrict__ cw16,
                                                             const half8* __restrict__ dec_a, int N, int bits,
-                                                            void* __restrict__ out) {
+                                                            void* __restrict__ out, int nwg) {
   typedef StreamShape<K, NF16, OF16, RW, CBL> S;
   constexpr int NC = 8 / K > 0 ? 8 / K : 1;
   constexpr int BITS = RW * K / 2;  // (64 / K) blocks of BITS bits fill RW words
@@ -169,7 +167,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
   if constexpr (CBL) __syncthreads();
   const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
 
-  const int64_t step = (int64_t)fq_ngroups_x(WAVES * 64) * WAVES;
+  const int64_t step = (int64_t)nwg * WAVES;
   int64_t g = (int64_t)fq_bid_x() * WAVES + w;
   if (g >= ngroups) return;
   int64_t left = (ngroups - 1 - g) / step + 1;  // groups of this wave
@@ -199,15 +197,27 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
 #pragma unroll
   for (int i = 0; i < PF; i++) issue(i, g + i * step);
 
-  auto body = [&](auto slot_c, auto wait_c) {
-    constexpr int sl = decltype(slot_c)::value;
-    wait_vmcnt<decltype(wait_c)::value>();
+  // One copy of the loop body (a kernel that runs only a few groups per wave would
+  // otherwise execute several cold copies of it from the instruction cache).  Step i
+  // reads slot i mod PF; younger operations when it waits: the later prologue groups'
+  // loads plus the stores and loads of the steps before it, S::WAIT_STEADY from step PF on.
+  constexpr int L = S::LOADS, T = S::STORES;
+  static_assert(PF == 4, "one wait case per prologue slot");
+  for (int i = 0;; i++) {
+    switch (i < PF ? i : PF) {
+      case 0: wait_vmcnt<(PF - 1) * L>(); break;
+      case 1: wait_vmcnt<(PF - 1) * L + T>(); break;
+      case 2: wait_vmcnt<(PF - 1) * L + 2 * T>(); break;
+      case 3: wait_vmcnt<(PF - 1) * L + 3 * T>(); break;
+      default: wait_vmcnt<S::WAIT_STEADY>(); break;
+    }
+    const int sl = i & (PF - 1);
     const char* src = ring + sl * S::SLOT_BYTES;
     uint32_t rc[RW];
     {
       const uint32_t* rp = reinterpret_cast<const uint32_t*>(src) + col * RW;
 #pragma unroll
-      for (int i = 0; i < RW; i++) rc[i] = rp[i];
+      for (int e = 0; e < RW; e++) rc[e] = rp[e];
     }
     float nu;
     if constexpr (NF16)
@@ -239,38 +249,6 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
     }
     stage_and_store<OF16>(acc, nu, stage, col, h, lane, reinterpret_cast<char*>(out) + g * 32 * (OF16 ? 128 : 256),
                           32);
-  };
-  typedef std::integral_constant<int, 0> C0;
-  typedef std::integral_constant<int, 1> C1;
-  typedef std::integral_constant<int, 2> C2;
-  typedef std::integral_constant<int, 3> C3;
-  static_assert(PF == 4, "the unrolled bodies below assume 4 slots");
-  constexpr int L = S::LOADS, T = S::STORES;
-  // first PF groups: fewer stores are younger than their slot
-  body(C0{}, std::integral_constant<int, 3 * L>{});
-  if (--left == 0) return;
-  g += step;
-  body(C1{}, std::integral_constant<int, 3 * L + T>{});
-  if (--left == 0) return;
-  g += step;
-  body(C2{}, std::integral_constant<int, 3 * L + 2 * T>{});
-  if (--left == 0) return;
-  g += step;
-  body(C3{}, std::integral_constant<int, 3 * L + 3 * T>{});
-  if (--left == 0) return;
-  g += step;
-  typedef std::integral_constant<int, S::WAIT_STEADY> CW;
-  while (true) {
-    body(C0{}, CW{});
-    if (--left == 0) return;
-    g += step;
-    body(C1{}, CW{});
-    if (--left == 0) return;
-    g += step;
-    body(C2{}, CW{});
-    if (--left == 0) return;
-    g += step;
-    body(C3{}, CW{});
     if (--left == 0) return;
     g += step;
   }
@@ -284,7 +262,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restr
                                                           const void* __restrict__ norms, int64_t n,
                                                           const _Float16* __restrict__ cw16,
                                                           const half8* __restrict__ dec_a, int N, int bits,
-                                                          void* __restrict__ out) {
+                                                          void* __restrict__ out, int nwg) {
   constexpr int NC = 8 / K > 0 ? 8 / K : 1;
   constexpr int ROWB = stage_row_bytes<OF16>();
   extern __shared__ uint4 smem[];
@@ -307,7 +285,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restr
   const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
   const int B = (D / K) * bits;
   const int64_t ngroups = (n + 31) / 32;
-  const int64_t step = (int64_t)fq_ngroups_x(WAVES * 64) * WAVES;
+  const int64_t step = (int64_t)nwg * WAVES;
   for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += step) {
     const int64_t v = g * 32 + col;
     const int64_t vv = v < n ? v : n - 1;  // invalid lanes decode a valid record, never stored
@@ -364,7 +342,7 @@ hipError_t launch_generic(const fq_codebook* cb, const uint8_t* codes, const voi
   hipError_t e = persistent_grid(cb, decode_mfma<K, NF, OF, CBL>, lds, ((n + 31) / 32 + WAVES - 1) / WAVES, &wgs);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_mfma<K, NF, OF, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes, norms, n,
-                     cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out);
+                     cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out, (int)wgs);
   return hipGetLastError();
 }
 
@@ -383,7 +361,8 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
       hipError_t e = persistent_grid(cb, decode_stream<K, NF, OF, RW, CBL>, lds, (ngroups + WAVES - 1) / WAVES, &wgs);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL((decode_stream<K, NF, OF, RW, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes,
-                         norms, ngroups, cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out);
+                         norms, ngroups, cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out,
+                         (int)wgs);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       done = ngroups * 32;

@@ -6,20 +6,16 @@
 
 namespace fq {
 
-// Work-item and workgroup indices read straight from the hardware registers, and
-// the x size of the grid in workgroups from the dispatch packet (grid_size_x, in
-// work-items, is the 32-bit word at byte 12).  The HIP index variables go through
-// library functions that are not inlined into kernels built without IEEE mode,
-// which turns every index into an opaque call result held in vector registers.
+// Work-item and workgroup indices read straight from the hardware registers.  The
+// HIP index variables go through library functions that are not inlined into
+// kernels built without IEEE mode, which turns every index into an opaque call
+// result held in vector registers.  Grid sizes are passed as kernel arguments:
+// reading them from the dispatch packet (host memory) in every wave costs
+// several microseconds at the start of a kernel.
 __device__ inline int fq_tid() { return (int)__builtin_amdgcn_workitem_id_x(); }
 __device__ inline int fq_bid_x() { return (int)__builtin_amdgcn_workgroup_id_x(); }
 __device__ inline int fq_bid_y() { return (int)__builtin_amdgcn_workgroup_id_y(); }
 __device__ inline int fq_bid_z() { return (int)__builtin_amdgcn_workgroup_id_z(); }
-__device__ inline int fq_ngroups_x(int wg_size) {
-  typedef const __attribute__((address_space(4))) uint32_t fq_const_u32;
-  fq_const_u32* pkt = (fq_const_u32*)__builtin_amdgcn_dispatch_ptr();
-  return (int)(pkt[3] / (uint32_t)wg_size);
-}
 
 // Round a double to the nearest fp16 value, ties to even, in one step (no
 // detour through fp32, whose double rounding can differ).  Returns the fp16

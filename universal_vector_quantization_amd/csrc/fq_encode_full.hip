@@ -83,7 +83,7 @@ template <bool NF16>
 __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rotA,
     const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64, int N, int bits,
-    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
   extern __shared__ uint4 smem[];
   char* buf0 = reinterpret_cast<char*>(smem);
   const int w = __builtin_amdgcn_readfirstlane((int)(fq_tid() >> 6));
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
   const int NT = N / 32;
   const int nch = (NT + CT - 1) / CT;
 
-  for (int64_t base = (int64_t)fq_bid_x() * WAVES; base < ngroups; base += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
+  for (int64_t base = (int64_t)fq_bid_x() * WAVES; base < ngroups; base += (int64_t)nwg * WAVES) {
     const int64_t g = base + w;
     const int64_t v0 = g * 32;
     const int nv = g < ngroups ? (int)((n - v0) < 32 ? (n - v0) : 32) : 0;
@@ -325,7 +325,7 @@ hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t*
   hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),
                      reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms);
+                     cb->h16_erel, codes, norms, (int)wgs);
   return hipGetLastError();
 }
 

@@ -113,7 +113,7 @@ template <int K, bool NF16>
 __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
     const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
-    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int NSUB = Shape<K>::NSUB;
   constexpr int VG = 16 * NSUB;    // vectors per group
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   const int NT = N / 32;
   const _Float16* cbh = reinterpret_cast<const _Float16*>(recL);  // record n: halfs 8 rslot(n) .. + 7
 
-  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
+  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)nwg * WAVES) {
     const int64_t v0 = g * VG;
     const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
 
@@ -450,7 +450,7 @@ hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* 
   hipLaunchKernelGGL((encode_h16<K, NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot16),
                      reinterpret_cast<const uint4*>(cb->crec), cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms);
+                     cb->h16_erel, codes, norms, (int)wgs);
   return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
     const float* __restrict__ cinit, const float* __restrict__ cn2s, const float* __restrict__ cw,
     const _Float16* __restrict__ cw16,
     const double* __restrict__ pi64m, const double* __restrict__ pi64, int N, int bits, float cmax, float c2max,
-    uint8_t* __restrict__ codes, void* __restrict__ norms) {
+    uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
   constexpr int NB = D / K;        // blocks per vector
   constexpr int VG = 256 / NB;     // vectors per group
   constexpr int NSUB = VG / 16;    // 16-vector rotation sub-groups
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
   char* xs = xtile[w];
   const double u = 5.9604644775390625e-08;
 
-  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)fq_ngroups_x(WAVES * 64) * WAVES) {
+  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)nwg * WAVES) {
     const int64_t v0 = g * VG;
     const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
 
@@ -391,7 +391,7 @@ hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_d
   hipLaunchKernelGGL((encode_mfma<KK, XF, NF>), grid, block, 0, s, x, n, ngroups,                               \
                      reinterpret_cast<const half8*>(cb->amfma), cb->cinit, cb->cn2s, cb->cw, cb->cw16, cb->pi64m,  \
                      cb->pi64,                                                                                 \
-                     cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms)
+                     cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms, (int)wgs)
 #define FQ_EM_K(KK)            \
   if (xf && nf)                \
     FQ_EM(KK, true, true);     \
