@@ -34,12 +34,14 @@
  *     norm dtype directly from fp64 (fp16 overflow stores +inf).  nu = 0 gives
  *     the all-smallest-norm codes and decodes to exactly 0.
  *   - Memory: every bulk pointer is caller-owned device memory on the device
- *     that was current at fq_codebook_load, 16-byte aligned.  Inputs are only
+ *     that was current at fq_codebook_load, 16-byte aligned (the int64 slot
+ *     and int32 length arrays: 8- and 4-byte aligned).  Inputs are only
  *     read, outputs only written.  Nothing here allocates except
  *     fq_codebook_load.
- *   - Asynchrony: fq_encode, fq_decode and fq_attn_decode only enqueue work on
- *     `stream` (a hipStream_t; NULL is the default stream) and return; they
- *     never synchronise and never read results back.
+ *   - Asynchrony: fq_encode, fq_encode_scatter, fq_decode, fq_attn_decode and
+ *     fq_attn_decode_varlen only enqueue work on `stream` (a hipStream_t; NULL
+ *     is the default stream) and return; they never synchronise and never read
+ *     results back.
  *   - Errors: arguments are checked on the host before any launch and return
  *     FQ_ERR_ARG / FQ_ERR_UNSUPPORTED / FQ_ERR_WORKSPACE with nothing enqueued;
  *     a failed launch returns FQ_ERR_HIP.  No call aborts or throws.  n = 0 (or
@@ -96,6 +98,26 @@ int64_t fq_code_bytes(const fq_codebook* cb, int64_t n);
 fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                     void* norms, fq_dtype norm_dtype, void* stream);
 
+/* Encode n vectors into chosen records of an existing code store: the append
+ * step of a growing cache (FibQuant summary §1 and §5: every record has a fixed
+ * size and address, so one record is rewritten without touching the others).
+ * Vector i is encoded exactly as fq_encode would encode it; its record is
+ * written to record slots[i] of a store of `capacity` records and its norm to
+ * norms[slots[i]].
+ *   x:        device [n][d] in x_dtype, row-major.
+ *   slots:    device int64 [n], 8-byte aligned.  A slot outside [0, capacity)
+ *             skips that vector (nothing is written for it), e.g. a finished
+ *             sequence.  Slots within one call must be distinct; two equal
+ *             slots leave an unspecified mix of the two records.
+ *   codes:    device, fq_code_bytes(cb, capacity) bytes; records not named in
+ *             slots are left untouched.
+ *   norms:    device [capacity] in norm_dtype.
+ * Records must be whole bytes (bits per vector a multiple of 8, so no byte is
+ * shared by two records); otherwise FQ_ERR_UNSUPPORTED. */
+fq_status fq_encode_scatter(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                            const int64_t* slots, int64_t capacity, uint8_t* codes, void* norms,
+                            fq_dtype norm_dtype, void* stream);
+
 /* Decode n vectors (FibQuant summary §2.3 decoder): x_out = nu * Pi^T concat(c).
  *   codes:  device, fq_code_bytes(cb, n) bytes.  norms: device [n] in norm_dtype.
  *   x_out:  device [n][d] in out_dtype, each value rounded once (RNE) from an
@@ -125,6 +147,21 @@ size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, in
 fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,
                          float scale, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fq_attn_decode over a growing cache (FibQuant summary §5): each slab holds
+ * room for T keys (the capacity; all layouts and the workspace as above, sized
+ * by T) and batch b attends only to its first L_b = min(max(lens[b], 0), T)
+ * keys, the ones written so far:
+ *     out[b][h] = sum_{j < L_b} softmax_j(scale * q[b][h] . k_j) v_j,
+ * and out[b][h] = 0 when L_b = 0.  Keys at or past L_b are never used, so
+ * their codes and norms may hold anything.
+ *   lens: device int32 [B], 4-byte aligned (read on the device; the host never
+ *         waits for it).
+ * T = 0 (or B = 0) is a no-op, as for fq_attn_decode. */
+fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                                const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq,
+                                int Hkv, int64_t T, float scale, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* fq_status_string(fq_status st);

@@ -168,6 +168,29 @@ def unpack_codes(buf: np.ndarray, n: int, m: int, bits: int) -> np.ndarray:
     return (b << np.arange(bits)).sum(axis=1).reshape(n, m)
 
 
+def write_records(codes: np.ndarray, norms: np.ndarray, new_codes: np.ndarray, new_norms: np.ndarray,
+                  slots) -> tuple[np.ndarray, np.ndarray]:
+    """The append step on a fixed-address store (FibQuant summary §1: each record has a
+    fixed size and place, so one record changes without touching the others; §5: the
+    decode loop adds one token per step).  codes [capacity, m] and norms [capacity] are
+    the store; new vector i (codes new_codes[i], norm new_norms[i]) replaces record
+    slots[i]; a slot outside [0, capacity) writes nothing.  Slots must be distinct.
+    Returns new arrays; the inputs are not modified."""
+    out_c = np.array(codes, copy=True)
+    out_n = np.array(norms, copy=True)
+    cap = out_c.shape[0]
+    used = set()
+    for i, s in enumerate(np.asarray(slots, dtype=np.int64).tolist()):
+        if not 0 <= s < cap:
+            continue
+        if s in used:
+            raise ValueError(f"slot {s} given twice")
+        used.add(s)
+        out_c[s] = new_codes[i]
+        out_n[s] = new_norms[i]
+    return out_c, out_n
+
+
 # ---------------------------------------------------------------- decode
 def decode(codes: np.ndarray, norms: np.ndarray, rotation: np.ndarray, codebook: np.ndarray) -> np.ndarray:
     """x̂ = ν · Πᵀ concat(c_code) in fp64 from stored norms (FibQuant summary §2.3)."""

@@ -27,9 +27,9 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == sorted(["fq_attn_decode", "fq_attn_workspace_bytes", "fq_code_bytes",
-                                  "fq_codebook_free", "fq_codebook_load", "fq_decode", "fq_encode",
-                                  "fq_status_string"])
+    assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_varlen", "fq_attn_workspace_bytes",
+                                  "fq_code_bytes", "fq_codebook_free", "fq_codebook_load", "fq_decode",
+                                  "fq_encode", "fq_encode_scatter", "fq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -57,6 +57,10 @@ def test_null_handle_paths_without_gpu(L):
     assert L.fq_attn_workspace_bytes(None, 1, 8, 1, 10) == 0
     assert L.fq_attn_decode(None, vp(16), vp(16), vp(16), vp(16), vp(16), 1, 8, 1, 10, 0.125, vp(16), vp(16),
                             1 << 20, None) == fq.FQ_ERR_ARG
+    assert L.fq_encode_scatter(None, vp(16), fq.FQ_F16, 1, vp(16), 10, vp(16), vp(16), fq.FQ_F16,
+                               None) == fq.FQ_ERR_ARG
+    assert L.fq_attn_decode_varlen(None, vp(16), vp(16), vp(16), vp(16), vp(16), vp(16), 1, 8, 1, 10, 0.125,
+                                   vp(16), vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
     L.fq_codebook_free(None)  # ignored
 
 

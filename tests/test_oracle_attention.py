@@ -85,3 +85,59 @@ def test_against_pure_python_loops_with_grouping():
             z = math.fsum(e)
             ref = [math.fsum(e[t] / z * vs[t][i] for t in range(T)) for i in range(D)]
             assert np.max(np.abs(out[b, h] - np.array(ref))) < 1e-11
+
+
+# ------------------------------------------------------------------ growing cache (per-batch lengths)
+def _python_attention_row(q, kc, kn, vc, vn, L, scale=0.125):
+    """Pure-Python loops over the first L keys of one (batch, KV head) slab; 0 when L = 0."""
+    if L == 0:
+        return [0.0] * D
+    pi = PI.astype(np.float64)
+    cb = CB.astype(np.float64)
+
+    def dec(codes, nu):
+        yh = [float(cb[codes[j // 4], j % 4]) for j in range(D)]
+        return [float(nu) * math.fsum(pi[r, i] * yh[r] for r in range(D)) for i in range(D)]
+
+    ks = [dec(kc[t], kn[t]) for t in range(L)]
+    vs = [dec(vc[t], vn[t]) for t in range(L)]
+    s = [scale * math.fsum(float(q[i]) * ks[t][i] for i in range(D)) for t in range(L)]
+    mx = max(s)
+    e = [math.exp(v - mx) for v in s]
+    z = math.fsum(e)
+    return [math.fsum(e[t] / z * vs[t][i] for t in range(L)) for i in range(D)]
+
+
+def test_lengths_against_pure_python_loops():
+    # Each batch sees only its first L_b keys; keys past L_b carry values that would
+    # change the result if they were read (huge norms).
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, T = 4, 4, 2, 6
+    kc, kn, vc, vn = _rand_cache(rng, B, Hkv, T)
+    lengths = np.array([0, 1, 4, 6])
+    for b in range(B):
+        kn[b, :, lengths[b]:] = 60000.0
+        vn[b, :, lengths[b]:] = 60000.0
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    out = attention(q, kc, kn, vc, vn, PI, CB, 0.125, lengths=lengths)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            ref = _python_attention_row(q[b, h], kc[b, g], kn[b, g], vc[b, g], vn[b, g], int(lengths[b]))
+            assert np.max(np.abs(out[b, h] - np.array(ref))) < 1e-11
+    assert np.all(out[0] == 0.0)
+
+
+def test_lengths_clamp_and_full_length_is_the_plain_call():
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, T = 3, 2, 1, 5
+    kc, kn, vc, vn = _rand_cache(rng, B, Hkv, T)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    full = attention(q, kc, kn, vc, vn, PI, CB, 0.125)
+    assert np.array_equal(attention(q, kc, kn, vc, vn, PI, CB, 0.125, lengths=[T, T + 9, 10 ** 6]), full)
+    neg = attention(q, kc, kn, vc, vn, PI, CB, 0.125, lengths=[-4, 0, T])
+    assert np.all(neg[:2] == 0.0) and np.array_equal(neg[2], full[2])
+    one = attention(q, kc, kn, vc, vn, PI, CB, 0.125, lengths=[1, 1, 1])
+    for b in range(B):  # one key: the output is exactly that key's value
+        v0 = decode(vc[b, 0, :1], vn[b, 0, :1], PI, CB)[0]
+        assert np.array_equal(one[b, 0], v0) and np.array_equal(one[b, 1], v0)

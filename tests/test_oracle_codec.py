@@ -240,3 +240,37 @@ def test_reported_end_to_end_mse_iid_workload(cb2):
     xh = codec.round_output(codec.decode(enc.codes, enc.norms, PI, cb2), np.float32).astype(np.float64)
     nmse = np.sum((x - xh) ** 2) / np.sum(x ** 2)
     assert 0.0625 < nmse < 0.1175  # between the Gaussian D(R) at b=2 and scalar Lloyd-Max at b=2
+
+
+# ------------------------------------------------------------------ append path (record writes)
+def test_write_records_token_by_token_equals_batch_encode(cb2):
+    # §1 fixed addresses: a record depends on its own vector only, so appending
+    # vectors one at a time in any order builds the same store as one batch encode,
+    # and records never named stay as they were.
+    x = workloads.gpt2_small_kv()[:40].astype(np.float32)
+    cap, m = 50, D // 2
+    rng = np.random.default_rng(8)
+    store_c = rng.integers(0, 16, size=(cap, m))
+    store_n = rng.standard_normal(cap).astype(np.float32)
+    for i in rng.permutation(40):
+        e = codec.encode(x[i:i + 1], PI, cb2, np.float32)
+        store_c, store_n = codec.write_records(store_c, store_n, e.codes, e.norms, [i])
+    full = codec.encode(x, PI, cb2, np.float32)
+    assert np.array_equal(store_c[:40], full.codes)
+    assert np.array_equal(store_n[:40].view(np.uint32), full.norms.view(np.uint32))
+    rng2 = np.random.default_rng(8)
+    assert np.array_equal(store_c[40:], rng2.integers(0, 16, size=(cap, m))[40:])
+    packed = codec.pack_codes(store_c, 4)
+    assert np.array_equal(codec.unpack_codes(packed, 40, m, 4), full.codes)
+
+
+def test_write_records_skips_out_of_range_and_rejects_duplicates():
+    c = np.arange(12).reshape(4, 3)
+    n = np.arange(4, dtype=np.float32)
+    new_c, new_n = np.full((4, 3), 99), np.full(4, -1.0, dtype=np.float32)
+    oc_, on_ = codec.write_records(c, n, new_c, new_n, [-1, 4, 7, 2])
+    assert np.array_equal(oc_[[0, 1, 3]], c[[0, 1, 3]]) and np.all(oc_[2] == 99)
+    assert np.array_equal(on_, np.array([0, 1, -1, 3], dtype=np.float32))
+    assert np.array_equal(c, np.arange(12).reshape(4, 3))  # inputs untouched
+    with pytest.raises(ValueError):
+        codec.write_records(c, n, new_c, new_n, [1, 1, -1, -1])

@@ -19,7 +19,8 @@ import numpy as np
 __all__ = [
     "FQ_OK", "FQ_ERR_ARG", "FQ_ERR_UNSUPPORTED", "FQ_ERR_WORKSPACE", "FQ_ERR_HIP", "FQ_F32", "FQ_F16",
     "FQError", "lib", "library_path", "fq_status_string", "fq_codebook_load", "fq_codebook_free", "fq_code_bytes",
-    "fq_encode", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode", "Codebook", "load_artifact",
+    "fq_encode", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
+    "fq_attn_decode_varlen", "Codebook", "load_artifact",
     "artifact_dir",
 ]
 
@@ -55,11 +56,16 @@ def lib() -> ctypes.CDLL:
         L.fq_code_bytes.argtypes, L.fq_code_bytes.restype = [vp, i64], i64
         L.fq_encode.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp]
         L.fq_encode.restype = i32
+        L.fq_encode_scatter.argtypes = [vp, vp, i32, i64, vp, i64, vp, vp, i32, vp]
+        L.fq_encode_scatter.restype = i32
         L.fq_decode.argtypes = [vp, vp, vp, i32, i64, vp, i32, vp]
         L.fq_decode.restype = i32
         L.fq_attn_workspace_bytes.argtypes, L.fq_attn_workspace_bytes.restype = [vp, i32, i32, i32, i64], sz
         L.fq_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp, sz, vp]
         L.fq_attn_decode.restype = i32
+        L.fq_attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp,
+                                            sz, vp]
+        L.fq_attn_decode_varlen.restype = i32
         _lib = L
     return _lib
 
@@ -124,6 +130,19 @@ def fq_encode(cb: int, x, codes, norms, stream=None) -> None:
                                         _dtype_code(norms), _stream(stream)))
 
 
+def fq_encode_scatter(cb: int, x, slots, capacity: int, codes, norms, stream=None) -> None:
+    """x: [n, 64] fp16/fp32; slots: int64 [n] record slots (outside [0, capacity) = skip);
+    codes: uint8 store of `capacity` records; norms: [capacity] fp16/fp32."""
+    import torch
+
+    n = x.shape[0] if x.dim() else 0
+    if slots.dtype != torch.int64 or slots.numel() != n:
+        raise ValueError("slots must be int64 [n]")
+    _check("fq_encode_scatter", lib().fq_encode_scatter(cb, _ptr(x), _dtype_code(x), n, _ptr(slots), int(capacity),
+                                                        _ptr(codes), _ptr(norms), _dtype_code(norms),
+                                                        _stream(stream)))
+
+
 def fq_decode(cb: int, codes, norms, x_out, stream=None) -> None:
     """codes: uint8 store; norms: [n]; x_out: [n, 64] fp16/fp32 (written)."""
     n = x_out.shape[0]
@@ -143,6 +162,22 @@ def fq_attn_decode(cb: int, q, k_codes, k_norms, v_codes, v_norms, B: int, Hq: i
     _check("fq_attn_decode", lib().fq_attn_decode(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
                                                   _ptr(v_norms), B, Hq, Hkv, T, float(scale), _ptr(out), ws_ptr,
                                                   ws_bytes, _stream(stream)))
+
+
+def fq_attn_decode_varlen(cb: int, q, k_codes, k_norms, v_codes, v_norms, lens, B: int, Hq: int, Hkv: int, T: int,
+                          scale: float, out, workspace, stream=None) -> None:
+    """As fq_attn_decode over a cache of capacity T; batch b attends to its first lens[b] keys
+    (lens: int32 [B] device tensor)."""
+    import torch
+
+    if lens.dtype != torch.int32 or lens.numel() != B:
+        raise ValueError("lens must be int32 [B]")
+    ws_ptr = None if workspace is None else _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fq_attn_decode_varlen",
+           lib().fq_attn_decode_varlen(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+                                       _ptr(lens), B, Hq, Hkv, T, float(scale), _ptr(out), ws_ptr, ws_bytes,
+                                       _stream(stream)))
 
 
 # --------------------------------------------------------------- artifacts

@@ -390,7 +390,26 @@ FQ_EXPORT fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_d
   if (n > ((int64_t)1 << 40)) return FQ_ERR_UNSUPPORTED;
   const fq_status ds = check_device(cb);
   if (ds != FQ_OK) return ds;
-  return fq::launch_encode(cb, x, x_dtype, n, codes, norms, norm_dtype, (hipStream_t)stream) == hipSuccess
+  return fq::launch_encode(cb, x, x_dtype, n, codes, norms, norm_dtype, nullptr, 0, (hipStream_t)stream) ==
+                 hipSuccess
+             ? FQ_OK
+             : FQ_ERR_HIP;
+}
+
+FQ_EXPORT fq_status fq_encode_scatter(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
+                                      const int64_t* slots, int64_t capacity, uint8_t* codes, void* norms,
+                                      fq_dtype norm_dtype, void* stream) {
+  if (!cb || n < 0 || capacity < 0 || !valid_dtype(x_dtype) || !valid_dtype(norm_dtype)) return FQ_ERR_ARG;
+  if (cb->B % 8 != 0) return FQ_ERR_UNSUPPORTED;  // records must not share bytes
+  if (n == 0) return FQ_OK;
+  if (!x || !slots || !codes || !norms) return FQ_ERR_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(norms) || (reinterpret_cast<uintptr_t>(slots) & 7) != 0)
+    return FQ_ERR_ARG;
+  if (n > ((int64_t)1 << 40) || capacity > ((int64_t)1 << 40)) return FQ_ERR_UNSUPPORTED;
+  const fq_status ds = check_device(cb);
+  if (ds != FQ_OK) return ds;
+  return fq::launch_encode(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, capacity, (hipStream_t)stream) ==
+                 hipSuccess
              ? FQ_OK
              : FQ_ERR_HIP;
 }
@@ -426,9 +445,10 @@ FQ_EXPORT size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, i
   return fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_plan(cb, B, Hq, Hkv, T).nchunks);
 }
 
-FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
-                                   const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,
-                                   float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                      const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
+                      int64_t T, float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
   const fq_status ss = attn_check_sizes(cb, B, Hq, Hkv, T);
   if (ss != FQ_OK) return ss;
   if (!isfinite(scale)) return FQ_ERR_ARG;
@@ -443,8 +463,25 @@ FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const u
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FQ_ERR_WORKSPACE;
   const fq_status ds = check_device(cb);
   if (ds != FQ_OK) return ds;
-  return fq::launch_attn(cb, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv, T, scale, out, workspace,
+  return fq::launch_attn(cb, q, k_codes, k_norms, v_codes, v_norms, lens, B, Hq, Hkv, T, scale, out, workspace,
                          (hipStream_t)stream) == hipSuccess
              ? FQ_OK
              : FQ_ERR_HIP;
+}
+}  // namespace
+
+FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                                   const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,
+                                   float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_decode(cb, q, k_codes, k_norms, v_codes, v_norms, nullptr, B, Hq, Hkv, T, scale, out, workspace,
+                     workspace_bytes, stream);
+}
+
+FQ_EXPORT fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint8_t* k_codes,
+                                          const void* k_norms, const uint8_t* v_codes, const void* v_norms,
+                                          const int32_t* lens, int B, int Hq, int Hkv, int64_t T, float scale,
+                                          float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && T > 0 && (!lens || (reinterpret_cast<uintptr_t>(lens) & 3) != 0)) return FQ_ERR_ARG;
+  return attn_decode(cb, q, k_codes, k_norms, v_codes, v_norms, lens, B, Hq, Hkv, T, scale, out, workspace,
+                     workspace_bytes, stream);
 }

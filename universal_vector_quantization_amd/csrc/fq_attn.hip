@@ -40,6 +40,13 @@ __device__ inline f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Keys batch b attends to: all T, or its valid length clamped to [0, T].
+__device__ inline int64_t valid_keys(const int32_t* __restrict__ lens, int b, int64_t T) {
+  if (!lens) return T;
+  const int64_t L = lens[b];
+  return L < 0 ? 0 : (L < T ? L : T);
+}
+
 // Dims [dim0, dim0+8) of the concatenated codewords of vector `vec`.
 template <int K>
 __device__ inline half8 gather8(const _Float16* __restrict__ cbL, const uint8_t* __restrict__ codes, int64_t vec,
@@ -75,8 +82,8 @@ template <int K>
 __global__ __launch_bounds__(AW * 64) void attn_split(
     const _Float16* __restrict__ q, const uint8_t* __restrict__ kc, const _Float16* __restrict__ kn,
     const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn, const _Float16* __restrict__ cw16,
-    const float* __restrict__ pi32, int N, int bits, int Hq, int Hkv, int64_t T, int64_t Tc, int nchunks,
-    float qscale, float* __restrict__ ws) {
+    const float* __restrict__ pi32, int N, int bits, int Hq, int Hkv, int64_t T, const int32_t* __restrict__ lens,
+    int64_t Tc, int nchunks, float qscale, float* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int cbBytes = (N * K * 2 + 15) & ~15;
   _Float16* cbL = reinterpret_cast<_Float16*>(smem);
@@ -120,8 +127,9 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
     }
   }
 
+  const int64_t Tb = valid_keys(lens, b, T);
   const int64_t c0 = (int64_t)chunk * Tc;
-  const int64_t c1 = (c0 + Tc) < T ? (c0 + Tc) : T;
+  const int64_t c1 = (c0 + Tc) < Tb ? (c0 + Tc) : Tb;
   const int64_t base = ((int64_t)b * Hkv + g) * T;
   const float NEG = -__builtin_huge_valf();
   float m = NEG, l = 0.f;
@@ -225,7 +233,7 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
       float wt[AW], Ls = 0.f;
 #pragma unroll
       for (int w = 0; w < AW; w++) {
-        wt[w] = exp2f(sm[w * GMAX + h] - M);
+        wt[w] = sm[w * GMAX + h] == NEG ? 0.f : exp2f(sm[w * GMAX + h] - M);  // a wave with no keys adds nothing
         Ls += sl[w * GMAX + h] * wt[w];
       }
       float* rec = ws + (((int64_t)b * Hq + (int64_t)g * G + h) * nchunks + chunk) * REC;
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
     for (int e = 0; e < 8; e++) A = fmaf(t[e], weight(c + e), A);
   }
   for (; c < nchunks; c++) A = fmaf(rec[(int64_t)c * REC + 2 + lane], weight(c), A);
-  ot[lane] = A / Ls;
+  ot[lane] = Ls > 0.f ? A / Ls : 0.f;  // no keys at all (a zero valid length): output 0
   __syncthreads();
   float o = 0.f;
 #pragma unroll
@@ -373,8 +381,10 @@ __device__ inline uint32_t from_hi_partner(uint32_t keep, uint32_t src) {
 // Codes and norms of the nt tokens starting at slab token tok0 into a unit
 // buffer: always 3 load instructions (token indices past nt are clamped to the
 // last valid token, whose bytes land in slots whose scores are masked), so a
-// wave waits for an older unit with vmcnt(3 x younger units).  nt is a
-// positive multiple of 8.
+// wave waits for an older unit with vmcnt(3 x younger units).  Norms move in
+// pairs: an odd nt also brings the norm of token nt, which lies inside the slab
+// (slab lengths are even) but past the valid keys, so its scores are masked and
+// its value weight is forced to 0.
 __device__ inline void attn_unit_load(const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
                                       const _Float16* __restrict__ kn, const _Float16* __restrict__ vn, int64_t tok0,
                                       int nt, char* dst, int lane) {
@@ -382,7 +392,8 @@ __device__ inline void attn_unit_load(const uint8_t* __restrict__ kc, const uint
   lds_dma16(kc + (tok0 + t) * 16, dst + U_KC);
   lds_dma16(vc + (tok0 + t) * 16, dst + U_VC);
   // lanes 0..31: key norms of tokens 2 l, 2 l + 1; lanes 32..63: value norms
-  const int l2 = 2 * (lane & 31), t2 = l2 < nt ? l2 : nt - 2;
+  const int nl = (nt + 1) & ~1;
+  const int l2 = 2 * (lane & 31), t2 = l2 < nl ? l2 : nl - 2;
   lds_dma4(lane < 32 ? kn + tok0 + t2 : vn + tok0 + t2, dst + U_KN);
 }
 
@@ -435,14 +446,15 @@ __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16
 }
 
 // Stage B of one unit: p = 2^(L - m), l += p, P' = p nu_v split hi + lo and
-// exchanged with the partner lane, O += V^T P'.  Masked tokens have p = 0 and
-// clamped (finite) codes and norms, so they add nothing.  Value operand dt,
+// exchanged with the partner lane, O += V^T P'.  Masked tokens have p = 0; with
+// MASK their value weight is set to 0 outright (their norm may be any bits).  Value operand dt,
 // lane c = 4 a' + b: the lane addresses token tb + 16 a + 4 grp + c / 4 and the
 // block whose code is byte dt of record dword c % 4 (block 4 (c % 4) + dt), and
 // receives dimension 16 a' + 4 dt + b of 4 tokens; output column c of
 // accumulator dt is dimension 16 (c / 4) + 4 dt + c % 4.
+template <bool MASK>
 __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __restrict__ cbL, int col, int grp,
-                               int own_tok, const float (&L)[2][4], float m, float& l_run, f32x4 (&O)[4]) {
+                               int own_tok, int nt, const float (&L)[2][4], float m, float& l_run, f32x4 (&O)[4]) {
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const int tb = 32 * u;
@@ -454,6 +466,7 @@ __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __r
       const float p = __builtin_amdgcn_exp2f(L[u][i] - m);
       l_run += p;
       pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
+      if constexpr (MASK) pv[i] = (tb + own_tok + i) < nt ? pv[i] : 0.f;
     }
     // hi rounds toward zero (any rounding works: lo takes the exact remainder)
     uint32_t hw[2], lw[2];
@@ -504,7 +517,8 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
                                                         const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
                                                         const _Float16* __restrict__ vn,
                                                         const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
-                                                        int64_t wg_tokens, int nrec, float* __restrict__ ws) {
+                                                        const int32_t* __restrict__ lens, int64_t wg_tokens, int nrec,
+                                                        float* __restrict__ ws) {
   __shared__ __align__(16) char wbuf[AW * NBUF * U_BYTES];
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ float sm[AW * GF], sl[AW * GF];
@@ -513,8 +527,10 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   const int rx = fq_bid_x(), g = fq_bid_y(), b = fq_bid_z();
   const int G = Hq / Hkv;
   const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
+  const int64_t Tb = valid_keys(lens, b, T);
   const int64_t t_begin = (int64_t)rx * wg_tokens;
-  const int64_t t_end = (t_begin + wg_tokens) < T ? (t_begin + wg_tokens) : T;
+  int64_t t_end = (t_begin + wg_tokens) < Tb ? (t_begin + wg_tokens) : Tb;
+  if (t_end < t_begin) t_end = t_begin;  // past the valid keys: an empty record
   // this wave's units: workgroup units w, w + AW, w + 2 AW, ...
   const int nu_wg = (int)((t_end - t_begin + UT - 1) / UT);
   const int nu = nu_wg > w ? (nu_wg - w + AW - 1) / AW : 0;
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
-    attn_pv(buf(h), cbL, col, grp, own_tok, Lcur, m_run, l_run, O);
+    attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lcur, m_run, l_run, O);
     attn_rescale_factors(m_run, mxn, grp, m_run, a_own, a_row);
   };
   // one steady-state iteration: unit h + 1 is full; its scores (into Lnxt) overlap unit h's PV
@@ -665,13 +681,17 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       for (int i = 0; i < 4; i++) Lc[u][i] = Ln[u][i];
     h++;
   }
-  if (nu > 0) {  // the last unit's PV
+  if (nu > 0) {  // the last unit's PV (the only unit that can be partial)
     l_run *= a_own;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
-    attn_pv(buf(h), cbL, col, grp, own_tok, Lc, m_run, l_run, O);
+    const int ntl = unit_nt(h);
+    if (ntl == UT)
+      attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lc, m_run, l_run, O);
+    else
+      attn_pv<true>(buf(h), cbL, col, grp, own_tok, ntl, Lc, m_run, l_run, O);
   }
 
   // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
@@ -772,16 +792,17 @@ size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks) {
 template <int K>
 hipError_t launch_attn_split_k(dim3 grid, size_t sh, hipStream_t s, const _Float16* q, const uint8_t* kc,
                                const _Float16* kn, const uint8_t* vc, const _Float16* vn, const fq_codebook* cb,
-                               int Hq, int Hkv, int64_t T, int64_t Tc, int nchunks, float qscale, float* ws) {
+                               int Hq, int Hkv, int64_t T, const int32_t* lens, int64_t Tc, int nchunks,
+                               float qscale, float* ws) {
   hipLaunchKernelGGL((attn_split<K>), grid, dim3(AW * 64), sh, s, q, kc, kn, vc, vn, cb->cw16, cb->pi32, cb->N,
-                     cb->bits, Hq, Hkv, T, Tc, nchunks, qscale, ws);
+                     cb->bits, Hq, Hkv, T, lens, Tc, nchunks, qscale, ws);
   return hipGetLastError();
 }
 
 #define FQ_ATT_DECL(KK)                                                                                        \
   template hipError_t launch_attn_split_k<KK>(dim3, size_t, hipStream_t, const _Float16*, const uint8_t*,      \
                                               const _Float16*, const uint8_t*, const _Float16*, const fq_codebook*, \
-                                              int, int, int64_t, int64_t, int, float, float*)
+                                              int, int, int64_t, const int32_t*, int64_t, int, float, float*)
 #ifdef FQ_ONLY_K
 FQ_ATT_DECL(FQ_ONLY_K);
 #else
@@ -794,8 +815,8 @@ extern FQ_ATT_DECL(32);
 extern FQ_ATT_DECL(64);
 
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
-                       const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
-                       float* out, void* workspace, hipStream_t s) {
+                       const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
+                       int64_t T, float scale, float* out, void* workspace, hipStream_t s) {
   const AttnPlan plan = attn_plan(cb, B, Hq, Hkv, T);
   const float qscale = scale * 1.4426950408889634f;  // log2(e)
   const dim3 grid((unsigned)plan.nchunks, (unsigned)Hkv, (unsigned)B);
@@ -808,15 +829,15 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   if (plan.fast) {
     hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, reinterpret_cast<const uint4*>(cb->rot16), qscale,
                        k_codes, kn, v_codes, vn,
-                       cb->cw16, Hq, Hkv, T, plan.chunk_tokens, plan.nchunks, ws);
+                       cb->cw16, Hq, Hkv, T, lens, plan.chunk_tokens, plan.nchunks, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);
     return hipGetLastError();
   }
 #define FQ_ATT(KK)                                                                                                \
-  e = launch_attn_split_k<KK>(grid, sh, s, qh, k_codes, kn, v_codes, vn, cb, Hq, Hkv, T, plan.chunk_tokens,       \
-                              plan.nchunks, qscale, ws)
+  e = launch_attn_split_k<KK>(grid, sh, s, qh, k_codes, kn, v_codes, vn, cb, Hq, Hkv, T, lens,                  \
+                              plan.chunk_tokens, plan.nchunks, qscale, ws)
   switch (cb->k) {
     case 1: FQ_ATT(1); break;
     case 2: FQ_ATT(2); break;

@@ -50,6 +50,38 @@ __device__ inline uint32_t load_code(const uint8_t* __restrict__ p, int64_t bito
   return (v >> sh) & ((1u << bits) - 1u);
 }
 
+// Scattered stores (one new token per sequence appended to a fixed-address cache):
+// vector v of a launch goes to record slots[v] of a code store of `cap` records, or to
+// record v when slots is null.  A slot outside [0, cap) gives -1: the vector is not stored.
+__device__ inline int64_t out_slot(const int64_t* __restrict__ slots, int64_t cap, int64_t v) {
+  if (!slots) return v;
+  const int64_t s = slots[v];
+  return (s >= 0 && s < cap) ? s : -1;
+}
+
+// Copies the nv records of a group packed in LDS (record r is bytes [r rb, (r + 1) rb) of
+// src, rb = record bytes) to their slots.  Records are whole bytes, so no byte of the
+// store is shared between records: plain stores, dwords when rb is a multiple of 4, else
+// bytes.  Called by every lane of a wave.
+__device__ inline void scatter_records(const uint32_t* src, int nv, int rb, const int64_t* __restrict__ slots,
+                                       int64_t cap, int64_t v0, uint8_t* __restrict__ codes, int lane) {
+  if ((rb & 3) == 0) {
+    const int rw = rb >> 2;
+    for (int t = lane; t < nv * rw; t += 64) {
+      const int r = t / rw, w = t - r * rw;
+      const int64_t s = out_slot(slots, cap, v0 + r);
+      if (s >= 0) reinterpret_cast<uint32_t*>(codes)[s * rw + w] = src[r * rw + w];
+    }
+  } else {
+    const uint8_t* sb = reinterpret_cast<const uint8_t*>(src);
+    for (int t = lane; t < nv * rb; t += 64) {
+      const int r = t / rb, c = t - r * rb;
+      const int64_t s = out_slot(slots, cap, v0 + r);
+      if (s >= 0) codes[s * rb + c] = sb[r * rb + c];
+    }
+  }
+}
+
 // Direct global-to-LDS loads: lane i moves its 16 (or 4) bytes from `gptr` to
 // LDS address lds + 16 i (4 i).  Written as inline assembly on purpose: the
 // compiler's wait insertion treats such a load as a write to all of LDS and puts

@@ -53,7 +53,8 @@ template <int K, bool XF16, bool NF16>
 __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, int64_t n,
                                                   const float* __restrict__ cw, const float* __restrict__ cn2,
                                                   const double* __restrict__ pi64t, int N, int bits, float cmax,
-                                                  float c2max, uint8_t* __restrict__ codes, void* __restrict__ norms) {
+                                                  float c2max, uint8_t* __restrict__ codes, void* __restrict__ norms,
+                                                  const int64_t* __restrict__ slots, int64_t cap) {
   constexpr int NB = D / K;
   constexpr int PK_WORDS = 2 * NB * 16;  // 64 lanes * B bits / 32, for bits <= 16
   __shared__ uint32_t pk[WG / 64][PK_WORDS];
@@ -135,11 +136,12 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
   if (!valid) unsure = 0;
 
   // ---- norm store (fp64 -> storage dtype, one rounding)
-  if (valid) {
+  const int64_t slot = valid ? out_slot(slots, cap, i) : -1;
+  if (slot >= 0) {
     if constexpr (NF16)
-      reinterpret_cast<uint16_t*>(norms)[i] = f64_to_f16_bits(nu);
+      reinterpret_cast<uint16_t*>(norms)[slot] = f64_to_f16_bits(nu);
     else
-      reinterpret_cast<float*>(norms)[i] = (float)nu;
+      reinterpret_cast<float*>(norms)[slot] = (float)nu;
   }
 
   // ---- pack this wave's 64 records (64*B bits, dword aligned) through LDS
@@ -198,7 +200,9 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
   }
   __syncthreads();
   const int64_t v0 = i - lane;
-  if (v0 < n) {
+  if (slots) {
+    if (v0 < n) scatter_records(pk[wave], (n - v0) < 64 ? (int)(n - v0) : 64, B / 8, slots, cap, v0, codes, lane);
+  } else if (v0 < n) {
     const int64_t nv = (n - v0) < 64 ? (n - v0) : 64;
     const int64_t nbytes = (nv * B + 7) / 8;
     uint8_t* dst = codes + (v0 / 64) * (int64_t)(8 * B);
@@ -215,12 +219,12 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
 // unit (compiled with -DFQ_ONLY_K=K) so the build can run in parallel.
 template <int K>
 hipError_t launch_encode_k(const fq_codebook* cb, const void* x, fq_dtype xd, int64_t n, uint8_t* codes,
-                           void* norms, fq_dtype nd, hipStream_t s) {
+                           void* norms, fq_dtype nd, const int64_t* slots, int64_t cap, hipStream_t s) {
   const dim3 grid((unsigned)((n + WG - 1) / WG)), block(WG);
   const bool xf16 = xd == FQ_F16, nf16 = nd == FQ_F16;
 #define FQ_ENC(XF, NF)                                                                                          \
   hipLaunchKernelGGL((encode_valu<K, XF, NF>), grid, block, 0, s, x, n, cb->cw, cb->cn2, cb->pi64t, cb->N,     \
-                     cb->bits, cb->cmax, cb->c2max, codes, norms)
+                     cb->bits, cb->cmax, cb->c2max, codes, norms, slots, cap)
   if (xf16 && nf16)
     FQ_ENC(true, true);
   else if (xf16)
@@ -235,41 +239,41 @@ hipError_t launch_encode_k(const fq_codebook* cb, const void* x, fq_dtype xd, in
 
 #ifdef FQ_ONLY_K
 template hipError_t launch_encode_k<FQ_ONLY_K>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*, void*,
-                                               fq_dtype, hipStream_t);
+                                               fq_dtype, const int64_t*, int64_t, hipStream_t);
 #else
 extern template hipError_t launch_encode_k<1>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<2>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<4>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<8>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<16>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<32>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 extern template hipError_t launch_encode_k<64>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
-                                                 void*, fq_dtype, hipStream_t);
+                                                 void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
-                         void* norms, fq_dtype norm_dtype, hipStream_t s) {
+                         void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
   if (!cb->force_valu && !cb->force_mfma64 && x_dtype == FQ_F16 && encode_h16_supported(cb))
-    return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, s);
+    return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
   if (!cb->force_valu && x_dtype == FQ_F16 && encode_full_supported(cb))
-    return launch_encode_full(cb, x, n, codes, norms, norm_dtype, s);
+    return launch_encode_full(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
   if (!cb->force_valu && cb->amfma) {
-    const hipError_t e = launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    const hipError_t e = launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
     if (e != hipErrorNotSupported) return e;
   }
   switch (cb->k) {
-    case 1: return launch_encode_k<1>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 2: return launch_encode_k<2>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 4: return launch_encode_k<4>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 8: return launch_encode_k<8>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 16: return launch_encode_k<16>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 32: return launch_encode_k<32>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
-    case 64: return launch_encode_k<64>(cb, x, x_dtype, n, codes, norms, norm_dtype, s);
+    case 1: return launch_encode_k<1>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 2: return launch_encode_k<2>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 4: return launch_encode_k<4>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 8: return launch_encode_k<8>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 16: return launch_encode_k<16>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 32: return launch_encode_k<32>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case 64: return launch_encode_k<64>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -83,7 +83,8 @@ template <bool NF16>
 __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rotA,
     const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64, int N, int bits,
-    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
+    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
+    const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   extern __shared__ uint4 smem[];
   char* buf0 = reinterpret_cast<char*>(smem);
   const int w = __builtin_amdgcn_readfirstlane((int)(fq_tid() >> 6));
@@ -128,10 +129,13 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     sq += shfl_xor_f64(sq, 32);
     const double nu = sqrt(sq);
     if (h == 0 && valid) {
-      if constexpr (NF16)
-        reinterpret_cast<uint16_t*>(norms)[v0 + c] = f64_to_f16_bits(nu);
-      else
-        reinterpret_cast<float*>(norms)[v0 + c] = (float)nu;
+      const int64_t sv = out_slot(slots, cap, v0 + c);
+      if (sv >= 0) {
+        if constexpr (NF16)
+          reinterpret_cast<uint16_t*>(norms)[sv] = f64_to_f16_bits(nu);
+        else
+          reinterpret_cast<float*>(norms)[sv] = (float)nu;
+      }
     }
     const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
 
@@ -300,7 +304,9 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       wave_lds_sync();
     }
     wave_lds_sync();
-    if (nv > 0) {
+    if (slots) {
+      scatter_records(spk, nv, bits / 8, slots, cap, v0, codes, lane);
+    } else if (nv > 0) {
       const int nbytes = (nv * bits + 7) / 8;
       uint8_t* dst = codes + g * (int64_t)(4 * bits);  // group g starts at bit g * 32 * bits
       const int nfull = nbytes / 4;
@@ -313,7 +319,8 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
 }
 
 template <bool NF16>
-hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
+hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                       const int64_t* slots, int64_t cap, hipStream_t s) {
   const size_t lds = full_lds_bytes();
   int64_t resident = 0;
   const hipError_t e =
@@ -325,7 +332,7 @@ hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t*
   hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),
                      reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms, (int)wgs);
+                     cb->h16_erel, codes, norms, slots, cap, (int)wgs);
   return hipGetLastError();
 }
 
@@ -337,10 +344,10 @@ bool encode_full_supported(const fq_codebook* cb) {
 }
 
 hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
-                              fq_dtype norm_dtype, hipStream_t s) {
+                              fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
   if (!encode_full_supported(cb)) return hipErrorNotSupported;
-  return norm_dtype == FQ_F16 ? launch_full<true>(cb, x, n, codes, norms, s)
-                              : launch_full<false>(cb, x, n, codes, norms, s);
+  return norm_dtype == FQ_F16 ? launch_full<true>(cb, x, n, codes, norms, slots, cap, s)
+                              : launch_full<false>(cb, x, n, codes, norms, slots, cap, s);
 }
 
 }  // namespace fq

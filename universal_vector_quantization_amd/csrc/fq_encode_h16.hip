@@ -109,11 +109,14 @@ __host__ __device__ constexpr size_t h16_lds_bytes(int K, int N, int waves) {
 __device__ inline int rslot(int n) { return n + (n >> 5); }
 __device__ inline int cslot(int n) { return n + 4 * (n >> 5); }
 
-template <int K, bool NF16>
+// SC: records and norms go to the slots given per vector (an instantiation of its own,
+// so the contiguous kernel keeps its register allocation).
+template <int K, bool NF16, bool SC>
 __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
     const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
-    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
+    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
+    const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int NSUB = Shape<K>::NSUB;
   constexpr int VG = 16 * NSUB;    // vectors per group
@@ -168,10 +171,13 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       s += shfl_xor_f64(s, 32);
       const double nu = sqrt(s);
       if (q == 0 && vec < nv) {
-        if constexpr (NF16)
-          reinterpret_cast<uint16_t*>(norms)[v0 + vec] = f64_to_f16_bits(nu);
-        else
-          reinterpret_cast<float*>(norms)[v0 + vec] = (float)nu;
+        const int64_t sv = SC ? out_slot(slots, cap, v0 + vec) : v0 + vec;
+        if (sv >= 0) {
+          if constexpr (NF16)
+            reinterpret_cast<uint16_t*>(norms)[sv] = f64_to_f16_bits(nu);
+          else
+            reinterpret_cast<float*>(norms)[sv] = (float)nu;
+        }
       }
       const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
 
@@ -423,7 +429,9 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       }
     }
     wave_lds_sync();
-    {
+    if constexpr (SC) {
+      scatter_records(spk, nv, (D / K) * bits / 8, slots, cap, v0, codes, lane);
+    } else {
       const int64_t nbytes = ((int64_t)nv * (D / K) * bits + 7) / 8;
       uint8_t* dst = codes + g * (int64_t)(32 * bits);  // group g starts at bit g * 256 * bits
       const int nfull = (int)(nbytes / 4);
@@ -435,22 +443,23 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   }
 }
 
-template <int K, bool NF16>
-hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, hipStream_t s) {
+template <int K, bool NF16, bool SC>
+hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
+                      const int64_t* slots, int64_t cap, hipStream_t s) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int VG = 16 * Shape<K>::NSUB;
   const size_t lds = h16_lds_bytes(K, cb->N, WAVES);
   int64_t resident = 0;
-  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(encode_h16<K, NF16>), WAVES * 64, lds,
+  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(encode_h16<K, NF16, SC>), WAVES * 64, lds,
                                            cb->device, &resident);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (n + VG - 1) / VG;
   int64_t wgs = (ngroups + WAVES - 1) / WAVES;
   if (wgs > resident) wgs = resident;
-  hipLaunchKernelGGL((encode_h16<K, NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
+  hipLaunchKernelGGL((encode_h16<K, NF16, SC>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot16),
                      reinterpret_cast<const uint4*>(cb->crec), cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms, (int)wgs);
+                     cb->h16_erel, codes, norms, slots, cap, (int)wgs);
   return hipGetLastError();
 }
 
@@ -464,11 +473,15 @@ bool encode_h16_supported(const fq_codebook* cb) {
 }
 
 hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
-                             fq_dtype norm_dtype, hipStream_t s) {
+                             fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
   if (!encode_h16_supported(cb)) return hipErrorNotSupported;
   const bool nf = norm_dtype == FQ_F16;
-  if (cb->k == 4) return nf ? launch_h16<4, true>(cb, x, n, codes, norms, s) : launch_h16<4, false>(cb, x, n, codes, norms, s);
-  return nf ? launch_h16<8, true>(cb, x, n, codes, norms, s) : launch_h16<8, false>(cb, x, n, codes, norms, s);
+#define FQ_H16(KK, NF) \
+  (slots ? launch_h16<KK, NF, true>(cb, x, n, codes, norms, slots, cap, s) \
+         : launch_h16<KK, NF, false>(cb, x, n, codes, norms, slots, cap, s))
+  if (cb->k == 4) return nf ? FQ_H16(4, true) : FQ_H16(4, false);
+  return nf ? FQ_H16(8, true) : FQ_H16(8, false);
+#undef FQ_H16
 }
 
 }  // namespace fq

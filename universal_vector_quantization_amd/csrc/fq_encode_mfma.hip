@@ -65,7 +65,7 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
     const float* __restrict__ cinit, const float* __restrict__ cn2s, const float* __restrict__ cw,
     const _Float16* __restrict__ cw16,
     const double* __restrict__ pi64m, const double* __restrict__ pi64, int N, int bits, float cmax, float c2max,
-    uint8_t* __restrict__ codes, void* __restrict__ norms, int nwg) {
+    uint8_t* __restrict__ codes, void* __restrict__ norms, const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   constexpr int NB = D / K;        // blocks per vector
   constexpr int VG = 256 / NB;     // vectors per group
   constexpr int NSUB = VG / 16;    // 16-vector rotation sub-groups
@@ -134,11 +134,12 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
         const int vl = lane / LPV;
         const double nu = sqrt(s);
         sinv[w][vl] = nu > 0.0 ? 1.0 / nu : 0.0;
-        if (vl < nv) {
+        const int64_t sv = vl < nv ? out_slot(slots, cap, v0 + vl) : -1;
+        if (sv >= 0) {
           if constexpr (NF16)
-            reinterpret_cast<uint16_t*>(norms)[v0 + vl] = f64_to_f16_bits(nu);
+            reinterpret_cast<uint16_t*>(norms)[sv] = f64_to_f16_bits(nu);
           else
-            reinterpret_cast<float*>(norms)[v0 + vl] = (float)nu;
+            reinterpret_cast<float*>(norms)[sv] = (float)nu;
         }
       }
     }
@@ -363,7 +364,9 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
       }
     }
     wave_lds_sync();
-    {
+    if (slots) {
+      scatter_records(spk[w], nv, B / 8, slots, cap, v0, codes, lane);
+    } else {
       const int64_t nbytes = ((int64_t)nv * B + 7) / 8;
       uint8_t* dst = codes + g * (int64_t)(32 * bits);  // group g starts at bit g * 256 * bits
       const int nfull = (int)(nbytes / 4);
@@ -378,7 +381,8 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
 }  // namespace
 
 hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
-                              void* norms, fq_dtype norm_dtype, hipStream_t s) {
+                              void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap,
+                              hipStream_t s) {
   if (!cb->amfma || !(cb->k == 4 || cb->k == 8) || cb->N % 32 != 0 || (cb->k == 4 && cb->N > 1024))
     return hipErrorNotSupported;
   const int VG = 256 / (kD / cb->k);
@@ -391,7 +395,7 @@ hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_d
   hipLaunchKernelGGL((encode_mfma<KK, XF, NF>), grid, block, 0, s, x, n, ngroups,                               \
                      reinterpret_cast<const half8*>(cb->amfma), cb->cinit, cb->cn2s, cb->cw, cb->cw16, cb->pi64m,  \
                      cb->pi64,                                                                                 \
-                     cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms, (int)wgs)
+                     cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms, slots, cap, (int)wgs)
 #define FQ_EM_K(KK)            \
   if (xf && nf)                \
     FQ_EM(KK, true, true);     \

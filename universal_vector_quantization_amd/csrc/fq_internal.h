@@ -51,19 +51,22 @@ namespace fq {
 
 constexpr int kD = 64;
 
+// Encoder launchers.  With slots == null vector v goes to record v of the code store;
+// otherwise to record slots[v] of a store of `cap` records (slots outside [0, cap) are
+// skipped), which needs whole-byte records.
 // Matrix-core encoder; returns hipErrorNotSupported when the codebook shape is not covered.
 hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
-                              void* norms, fq_dtype norm_dtype, hipStream_t s);
+                              void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 // Matrix-core encoder for fp16 input (fp16-split rotation); see encode_h16_supported.
 bool encode_h16_supported(const fq_codebook* cb);
 hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
-                             fq_dtype norm_dtype, hipStream_t s);
+                             fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 // Matrix-core encoder for k = d = 64 and fp16 input; see encode_full_supported.
 bool encode_full_supported(const fq_codebook* cb);
 hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
-                              fq_dtype norm_dtype, hipStream_t s);
+                              fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
-                         void* norms, fq_dtype norm_dtype, hipStream_t s);
+                         void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                               int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
@@ -87,8 +90,10 @@ size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
 // `device`: per-CU occupancy times the CU count, at least 1.  Cached per (kernel, block,
 // lds, device) so that launches do not pay for the occupancy query.
 hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int device, int64_t* out);
+// lens == null: every batch attends to all T keys; else batch b to its first
+// min(max(lens[b], 0), T) keys.
 hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
-                       const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
-                       float* out, void* workspace, hipStream_t s);
+                       const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
+                       int64_t T, float scale, float* out, void* workspace, hipStream_t s);
 
 }  // namespace fq
