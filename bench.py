@@ -15,7 +15,10 @@ second through the step (fp16-equivalent GB/s = vectors/s x 128 B).  Per-kernel
 times come from HIP events on the stream the library launches on.  The
 decode-attention workload (B=16, 32 query heads on 4 KV heads, T=32768) is
 timed separately with L2 and the last-level cache evicted before every launch
-(a 512 MiB read), and reported against the HBM roofline.  The CPU oracle is timed on a bounded sample
+(a 512 MiB read), and reported against the HBM roofline.  On the same cache a
+decode loop is timed as well: per step the new token's K and V are encoded into
+their slots (fq_encode_scatter) and attention runs over each sequence's valid
+length (fq_attn_decode_varlen).  The CPU oracle is timed on a bounded sample
 (rank 0, one GPU only).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -52,6 +55,7 @@ def parse():
     ap.add_argument("--attn-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-workload", action="store_true")
+    ap.add_argument("--no-decode-loop", action="store_true", help="skip the append + varlen attention timing")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -312,7 +316,55 @@ def main():
                          "frac": abytes / t_att / 1e9 / HBM_PEAK_GBPS,
                          "traffic": measured_traffic("attn_k4b8", "fq_attn.hip")},
         }
-        del flush
+
+        # ------------------------------------------------------------ decode loop over the same cache
+        # One decode step per sequence: the new token's K and V go to slot len_b of their
+        # (batch, KV head) slab (fq_encode_scatter), then attention runs over len_b + 1
+        # keys (fq_attn_decode_varlen).  Lengths start spread over [T/2, T - iters) and
+        # grow by one per step; slots and lengths of every step are on the device
+        # before timing, and the caches are evicted before every step.
+        if not args.no_decode_loop:
+            iters = args.attn_iters
+            rng = np.random.default_rng(106)
+            len0 = rng.integers(Ta // 2, Ta - iters - 4, size=B)
+            base = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None, :]) * Ta  # [B, Hkv] slab starts
+            slots_all = torch.from_numpy(np.stack([(base + (len0 + it)[:, None]).reshape(-1)
+                                                   for it in range(iters + 3)]).astype(np.int64)).to(dev)
+            lens_all = torch.from_numpy(np.stack([len0 + it + 1 for it in range(iters + 3)]).astype(np.int32)).to(dev)
+            newk = torch.from_numpy(np.ascontiguousarray(kv_np[0, :, :, :iters + 3].transpose(2, 0, 1, 3))
+                                    .reshape(iters + 3, B * Hkv, D)).to(dev)
+            newv = torch.from_numpy(np.ascontiguousarray(kv_np[1, :, :, :iters + 3].transpose(2, 0, 1, 3))
+                                    .reshape(iters + 3, B * Hkv, D)).to(dev)
+            flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+            t_app, t_var = [], []
+            for it in range(iters + 3):
+                flush.max()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(stream)
+                fq.fq_encode_scatter(cb.handle, newk[it], slots_all[it], na, kcs, kns, stream)
+                fq.fq_encode_scatter(cb.handle, newv[it], slots_all[it], na, vcs, vns, stream)
+                e[1].record(stream)
+                fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, lens_all[it], B, Hq, Hkv, Ta, 0.125, ao,
+                                         aws, stream)
+                e[2].record(stream)
+                torch.cuda.synchronize()
+                if it >= 3:
+                    t_app.append(e[0].elapsed_time(e[1]))
+                    t_var.append(e[1].elapsed_time(e[2]))
+            t_a, t_v = float(np.median(t_app)) / 1e3, float(np.median(t_var)) / 1e3
+            keys = int(lens_all[3:].sum().item()) * Hkv / iters  # keys read per step, all slabs
+            vbytes = keys * (16 + 16 + 2 + 2) + B * Hq * D * 2 + B * Hq * D * 4
+            line["decode_loop_b16_t32k"] = {
+                "workload": "B=16, Hq=32, Hkv=4, cache capacity T=32768, per-batch lengths uniform in [T/2, T); per "
+                            "step: 64 new K and 64 new V vectors encoded into their slots, then attention over each "
+                            "batch's valid keys; caches evicted before every step",
+                "us_per_step": (t_a + t_v) * 1e6, "breakdown_us": {"append": t_a * 1e6, "attention": t_v * 1e6},
+                "keys_per_step": keys, "hbm_bytes_attention": vbytes,
+                "roofline": {"kernel": "attn_k4b8 with per-batch lengths (+ attn_combine)", "bound": "hbm",
+                             "achieved": vbytes / t_v / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": vbytes / t_v / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+            }
+            del flush
 
     if not args.no_workloads:
         line["workloads"] = workload_timings(fq, workloads, dev, stream)
