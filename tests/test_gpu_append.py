@@ -54,20 +54,25 @@ def _poison_past(norms_bkt, lens):
 
 
 # ------------------------------------------------------------------ fq_encode_scatter
-@pytest.mark.parametrize("k,N,xdt,ndt", [
-    (4, 256, np.float16, np.float16),   # fp16 matrix-core encoder, 16-byte records
-    (4, 256, np.float32, np.float32),   # fp32-input matrix-core encoder
-    (8, 4096, np.float16, np.float16),  # 12-byte records
-    (2, 16, np.float32, np.float16),    # one-lane-per-vector encoder
-    (4, 32, np.float16, np.float32),    # 10-byte records: byte stores
-    (64, 256, np.float16, np.float16),  # k = d encoder, 1-byte records
+# Batches of at most 2048 vectors go to the small-batch encoder (one wave per vector)
+# where the codebook shape allows it; larger ones to the throughput encoders.
+@pytest.mark.parametrize("k,N,xdt,ndt,n", [
+    (4, 256, np.float16, np.float16, 300),    # small-batch encoder, 16-byte records
+    (4, 256, np.float16, np.float16, 5000),   # fp16 matrix-core encoder
+    (4, 256, np.float32, np.float32, 5000),   # fp32-input matrix-core encoder
+    (8, 4096, np.float16, np.float16, 300),   # 12-byte records (fp16 matrix-core encoder)
+    (2, 16, np.float32, np.float16, 300),     # small-batch encoder, k = 2
+    (2, 16, np.float32, np.float16, 5000),    # one-lane-per-vector encoder
+    (4, 32, np.float16, np.float32, 300),     # 10-byte records: byte stores (small batch)
+    (4, 32, np.float16, np.float32, 5000),    # 10-byte records: byte stores (matrix core)
+    (64, 256, np.float16, np.float16, 300),   # k = d encoder, 1-byte records
 ])
-def test_encode_scatter_parity(dev, k, N, xdt, ndt):
+def test_encode_scatter_parity(dev, k, N, xdt, ndt, n):
     import torch
 
     cb, cw, rot = codebook(k, N)
     bits, m = oc.code_bits(N), D // k
-    cap, n = 3001, 300
+    cap = max(3001, 2 * n + 1)
     x = workloads.gpt2_small_kv()[7000:7000 + n].astype(xdt)
     rng = np.random.default_rng(k * 7919 + N)
     slots = rng.choice(cap, n, replace=False).astype(np.int64)
@@ -99,7 +104,7 @@ def test_encode_scatter_parity(dev, k, N, xdt, ndt):
     assert oc.accepted(enc.y, cw, enc, other).all()
 
 
-@pytest.mark.parametrize("k,N,n", [(4, 256, 1007), (8, 4096, 777), (2, 16, 130)])
+@pytest.mark.parametrize("k,N,n", [(4, 256, 1007), (4, 256, 6007), (8, 4096, 777), (2, 16, 130)])
 def test_encode_scatter_identity_slots_equal_encode(dev, k, N, n):
     # slots 0..n-1 into a store of n records: byte-identical to fq_encode.
     import torch
@@ -288,3 +293,64 @@ def test_decode_loop_append_then_attend(dev, k, N, T):
         assert np.array_equal(got_n.view(np.uint16), s["on"].view(np.uint16))
         got_c = oc.unpack_codes(s["gc"].cpu().numpy(), cap, m, bits)
         assert not ((got_c != s["oc"]) & ~s["tie"]).any()
+
+
+def test_decode_step_as_graph_matches_eager(dev):
+    # The append + attention step captured once as a HIP graph and replayed with new
+    # vectors, slots and lengths in its fixed device buffers, eager work and
+    # synchronisations between replays: every replay's cache and output are
+    # bit-identical to the same step run eagerly on a twin cache.
+    import torch
+
+    cb, _, _ = codebook(4, 256)
+    B, Hq, Hkv, T = 3, 8, 2, 264
+    cap = 2 * B * Hkv * T  # K records then V records
+    c0 = workloads.random_code_store(cb.code_bytes(cap), 91)
+    n0 = workloads.random_norms(cap, 92)
+    ga, gn = to_dev(c0, dev), to_dev(n0, dev)
+    ea, en = to_dev(c0, dev), to_dev(n0, dev)
+    half = cb.code_bytes(cap // 2)
+    src = workloads.gpt2_small_kv()
+    rng = np.random.default_rng(93)
+    q = to_dev(rng.standard_normal((B, Hq, D)).astype(np.float16), dev)
+    wsb = fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, T)
+    ws_g = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out_g = torch.zeros((B, Hq, D), dtype=torch.float32, device=dev)
+    out_e = torch.zeros((B, Hq, D), dtype=torch.float32, device=dev)
+    x_buf = torch.zeros((2 * B * Hkv, D), dtype=torch.float16, device=dev)
+    s_buf = torch.full((2 * B * Hkv,), -1, dtype=torch.int64, device=dev)
+    l_buf = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    def step(codes, norms, out, ws, x, s, l, stream):
+        fq.fq_encode_scatter(cb.handle, x, s, cap, codes, norms, stream)
+        fq.fq_attn_decode_varlen(cb.handle, q, codes[:half], norms[:cap // 2], codes[half:], norms[cap // 2:], l,
+                                 B, Hq, Hkv, T, 0.125, out, ws, stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture (slots -1: nothing written)
+        step(ga, gn, out_g, ws_g, x_buf, s_buf, l_buf, side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(ga, gn, out_g, ws_g, x_buf, s_buf, l_buf, torch.cuda.current_stream())
+    lens = np.array([0, 7, 40])
+    base = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None, :]) * T
+    for it in range(6):
+        slots = np.concatenate([(base + lens[:, None]).reshape(-1)] * 2) + np.repeat([0, cap // 2], B * Hkv)
+        lens = lens + 1
+        x = to_dev(src[it * 2 * B * Hkv:(it + 1) * 2 * B * Hkv], dev)
+        s = to_dev(slots.astype(np.int64), dev)
+        l = to_dev(lens.astype(np.int32), dev)
+        x_buf.copy_(x)
+        s_buf.copy_(s)
+        l_buf.copy_(l)
+        graph.replay()
+        torch.cuda.synchronize()
+        step(ea, en, out_e, ws_e, x, s, l, None)  # eager twin
+        torch.cuda.synchronize()
+        assert torch.equal(ga, ea) and torch.equal(gn.view(torch.int16), en.view(torch.int16)), f"replay {it}: cache"
+        assert torch.equal(out_g.view(torch.int32), out_e.view(torch.int32)), f"replay {it}: output"
+        assert torch.isfinite(out_g).all()

@@ -258,6 +258,9 @@ extern template hipError_t launch_encode_k<64>(const fq_codebook*, const void*, 
 
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
+  // a few vectors (the decode loop's append): latency of one launch is what counts
+  if (!cb->force_valu && !cb->force_mfma64 && n <= SMALL_ENCODE_MAX && encode_small_supported(cb))
+    return launch_encode_small(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
   if (!cb->force_valu && !cb->force_mfma64 && x_dtype == FQ_F16 && encode_h16_supported(cb))
     return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
   if (!cb->force_valu && x_dtype == FQ_F16 && encode_full_supported(cb))

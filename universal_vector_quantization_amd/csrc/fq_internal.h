@@ -65,6 +65,12 @@ hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, ui
 bool encode_full_supported(const fq_codebook* cb);
 hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
                               fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
+// Small-batch encoder (one wave per vector, fp64 search) for at most SMALL_ENCODE_MAX
+// vectors; see encode_small_supported.
+constexpr int64_t SMALL_ENCODE_MAX = 2048;
+bool encode_small_supported(const fq_codebook* cb);
+hipError_t launch_encode_small(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
+                               void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
