@@ -18,7 +18,9 @@ timed separately with L2 and the last-level cache evicted before every launch
 (a 512 MiB read), and reported against the HBM roofline.  On the same cache a
 decode loop is timed as well: per step the new token's K and V are encoded into
 their slots (fq_encode_scatter) and attention runs over each sequence's valid
-length (fq_attn_decode_varlen).  The CPU oracle is timed on a bounded sample
+length (fq_attn_decode_varlen).  Along the rate axis (frozen initial codebooks
+from b = 4 down to 0.22 bits per coordinate) the same tensor's encode, decode
+and attention are timed as well.  The CPU oracle is timed on a bounded sample
 (rank 0, one GPU only).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -56,6 +58,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-attn-workload", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true", help="skip the append + varlen attention timing")
+    ap.add_argument("--no-rate-axis", action="store_true", help="skip the rate-axis timings")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -166,6 +169,67 @@ def workload_timings(fq, workloads, dev, stream, reps: int = 5):
         cb.close()
         del x, codes, norms, xr
         torch.cuda.empty_cache()
+    return out
+
+
+# Rate-axis points (k, N) with frozen initial codebooks: b = log2(N) / k from 4 down to 0.22.
+RATE_AXIS = [(1, 16), (2, 32), (2, 128), (4, 1024), (4, 16384), (16, 1024), (32, 512), (64, 16384)]
+
+
+def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
+    """Encode, decode and decode-attention time along the rate axis on the
+    GPT-2-small-shaped tensor (294,912 fp16 vectors; event-timed, median of
+    ``reps``, inputs resident).  Attention: one query per (layer, head) over the
+    just-encoded halves (B = 12, Hq = Hkv = 12, T = 1024), where the codebook fits
+    in LDS."""
+    import torch
+
+    x = torch.from_numpy(workloads.gpt2_small_kv()).to(dev)
+    n = x.shape[0]
+    L, H, T = workloads.GPT2_L, workloads.GPT2_H, workloads.GPT2_T
+    q = torch.from_numpy(workloads.gpt2_small_queries()).to(dev)
+    ao = torch.empty((L, H, D), dtype=torch.float32, device=dev)
+    out = {}
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts)) / 1e3
+
+    for k, N in RATE_AXIS:
+        try:
+            cb = fq.Codebook.from_artifact(k, N, initial=True)
+        except FileNotFoundError:
+            out[f"k{k}_N{N}"] = {"skipped": "codebook artifact missing"}
+            continue
+        bits = N.bit_length() - 1
+        codes = torch.empty(cb.code_bytes(n), dtype=torch.uint8, device=dev)
+        norms = torch.empty(n, dtype=torch.float16, device=dev)
+        xr = torch.empty_like(x)
+        t_e = timed(lambda: fq.fq_encode(cb.handle, x, codes, norms, stream))
+        t_d = timed(lambda: fq.fq_decode(cb.handle, codes, norms, xr, stream))
+        dbytes = cb.code_bytes(n) + 2 * n + 2 * D * n  # codes + norms read, fp16 output written
+        rec = {"b": bits / k, "record_bits": (D // k) * bits, "encode_us": t_e * 1e6, "encode_vec_per_s": n / t_e,
+               "encode_cmp_frac": (D // k) * N * n / t_e / 1e12 / CMP_PEAK_T, "decode_us": t_d * 1e6,
+               "decode_GBps": dbytes / t_d / 1e9, "decode_hbm_frac": dbytes / t_d / 1e9 / HBM_PEAK_GBPS}
+        if k * N <= 16384:
+            half = cb.code_bytes(n // 2)
+            ws = torch.empty(max(fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T), 16), dtype=torch.uint8,
+                             device=dev)
+            t_a = timed(lambda: fq.fq_attn_decode(cb.handle, q, codes[:half], norms[: n // 2], codes[half:],
+                                                  norms[n // 2:], L, H, H, T, 0.125, ao, ws, stream))
+            abytes = cb.code_bytes(n) + 2 * n + L * H * D * 6
+            rec.update({"attention_us": t_a * 1e6, "attention_GBps": abytes / t_a / 1e9})
+        out[f"k{k}_N{N}"] = rec
+        cb.close()
+        del codes, norms, xr
     return out
 
 
@@ -399,6 +463,8 @@ def main():
 
     if not args.no_workloads:
         line["workloads"] = workload_timings(fq, workloads, dev, stream)
+    if not args.no_rate_axis:
+        line["rate_axis"] = rate_axis_timings(fq, workloads, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     cb.close()

@@ -8,7 +8,13 @@ sha256 so the tests can detect drift.  Lloyd uses multithreaded BLAS, so a
 rebuild on another machine may differ in the last bits; the committed files are
 the reference.
 
-Usage:  python -m oracle.build_codebooks [--only k,N] [--out DIR]
+Rate-axis points away from the workloads (FibQuant summary §3.3: a dense rate
+axis) are frozen as the construction's *initial* codebooks (companded radii and
+spiral / Roberts directions on the fp16 grid, no Lloyd refinement): the codec
+is exact for any fp16-exact codebook, and these serve its parity tests and
+throughput measurements, not its distortion.
+
+Usage:  python -m oracle.build_codebooks [--only k,N] [--initial] [--out DIR]
 """
 from __future__ import annotations
 
@@ -20,7 +26,7 @@ import time
 
 import numpy as np
 
-from .codebook import build_codebook
+from .codebook import build_codebook, initial_codebook, to_fp16_grid
 from .rotation import shared_rotation
 
 D = 64
@@ -31,12 +37,14 @@ SPECS = [
     (8, 4096, 203, None, 60),
     (64, 4096, 204, 64 * 4096, 30),
 ]
+# (k, N) rate-axis points frozen as initial codebooks.
+RATE_AXIS = [(1, 16), (2, 32), (2, 128), (4, 1024), (4, 16384), (16, 1024), (32, 512), (64, 16384)]
 DEFAULT_OUT = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "universal_vector_quantization_amd", "codebooks")
 
 
-def codebook_filename(k: int, N: int, d: int = D) -> str:
-    return f"fq_d{d}_k{k}_n{N}.npz"
+def codebook_filename(k: int, N: int, d: int = D, initial: bool = False) -> str:
+    return f"fq_d{d}_k{k}_n{N}{'_init' if initial else ''}.npz"
 
 
 def sha256_file(path: str) -> str:
@@ -50,7 +58,9 @@ def manifest_entry(path: str) -> dict:
     """Manifest record of one artifact, read back from the file itself."""
     z = np.load(path, allow_pickle=False)
     e = {"sha256": sha256_file(path), "d": int(z["d"])}
-    if "codewords" in z.files:
+    if "codewords" in z.files and "initial" in z.files:
+        e.update({"k": int(z["k"]), "N": int(z["N"]), "initial": True})
+    elif "codewords" in z.files:
         k, N = int(z["k"]), int(z["N"])
         e.update({"k": k, "N": N, "seed": int(z["seed"]), "samples": int(z["samples"]),
                   "restarts": int(z["restarts"]), "valid_mse": float(z["valid_mse"]),
@@ -78,9 +88,19 @@ def main() -> None:
     ap.add_argument("--out", default=DEFAULT_OUT)
     ap.add_argument("--no-rotation", action="store_true")
     ap.add_argument("--manifest-only", action="store_true")
+    ap.add_argument("--initial", action="store_true", help="write the rate-axis initial codebooks only")
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
     if args.manifest_only:
+        write_manifest(args.out)
+        return
+    if args.initial:
+        for k, N in RATE_AXIS:
+            if args.only and args.only != f"{k},{N}":
+                continue
+            cw = to_fp16_grid(initial_codebook(D, k, N)).astype(np.float32)
+            np.savez(os.path.join(args.out, codebook_filename(k, N, initial=True)), codewords=cw, d=D, k=k, N=N,
+                     initial=True)
         write_manifest(args.out)
         return
     if not args.no_rotation:

@@ -3,10 +3,10 @@
 decode, scattered encode and decode attention at (k, N) points away from the
 four workload codebooks, against the CPU oracle.
 
-The codec is exact for any fp16-exact codebook, so these tests use the
-construction's initial codebook (companded radii and spiral / Roberts
-directions, rounded to the fp16 grid) without the Lloyd refinement; the
-refinement changes codeword values, not what the kernels compute.
+The codec is exact for any fp16-exact codebook, so these tests use the frozen
+rate-axis artifacts: the construction's initial codebooks (companded radii and
+spiral / Roberts directions, rounded to the fp16 grid) without the Lloyd
+refinement, which changes codeword values, not what the kernels compute.
 
 Bars as for the workload codebooks: codes equal the oracle's outside its
 near-ties (accepted codes inside), norms bit-exact, decoded vectors and
@@ -18,9 +18,8 @@ import universal_vector_quantization_amd as fq
 import workloads
 from oracle import attention as oatt
 from oracle import codec as oc
-from oracle.codebook import initial_codebook, to_fp16_grid
 
-from gpu_util import D, artifact_or_skip, check_encode, device, gpu_decode, gpu_encode, max_rel_rows, to_dev
+from gpu_util import D, check_encode, device, gpu_decode, gpu_encode, max_rel_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -49,8 +48,10 @@ _cbs = {}
 
 def codebook(k, N):
     if (k, N) not in _cbs:
-        cw = to_fp16_grid(initial_codebook(D, k, N)).astype(np.float32)
-        _, rot = artifact_or_skip(4, 256)
+        try:
+            cw, rot = fq.load_artifact(k, N, initial=True)
+        except FileNotFoundError:
+            pytest.skip(f"rate-axis artifact k={k} N={N} not built")
         _cbs[(k, N)] = (fq.Codebook(cw, rot), cw, rot)
     return _cbs[(k, N)]
 

@@ -217,8 +217,19 @@ def test_artifact_codebooks_fp16_exact_distinct_idempotent():
         nz = np.abs(c[c != 0])
         assert nz.size == 0 or nz.min() >= 2 ** -14
         assert len(np.unique(c, axis=0)) == e["N"]
+        if e["N"] * e["N"] * e["k"] > 2 ** 30:
+            continue  # k = d, N = 16384: the all-pairs search would dominate the CPU suite
         code, d1, d2, nt = nearest_codewords(c.astype(np.float64), c)
         assert np.array_equal(code, np.arange(e["N"])) and not nt.any()
+
+
+def test_initial_artifacts_rebuild_identically():
+    # the rate-axis artifacts are the deterministic initial construction, frozen
+    for name, e in _artifacts().items():
+        if not e.get("initial"):
+            continue
+        c = np.load(os.path.join(ART, name))["codewords"]
+        assert np.array_equal(c, cbm.to_fp16_grid(cbm.initial_codebook(64, e["k"], e["N"])).astype(np.float32)), name
 
 
 def test_artifact_rotation_is_seed0_haar():

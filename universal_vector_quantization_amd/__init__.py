@@ -184,10 +184,11 @@ def fq_attn_decode_varlen(cb: int, q, k_codes, k_norms, v_codes, v_norms, lens, 
 artifact_dir = os.path.join(_PKG, "codebooks")
 
 
-def load_artifact(k: int, N: int, d: int = 64):
-    """(codewords fp32 [N, k], rotation fp32 [d, d]) from the frozen artifact files."""
+def load_artifact(k: int, N: int, d: int = 64, initial: bool = False):
+    """(codewords fp32 [N, k], rotation fp32 [d, d]) from the frozen artifact files;
+    initial=True: the rate-axis codebooks frozen before any Lloyd refinement."""
     man = json.load(open(os.path.join(artifact_dir, "MANIFEST.json")))
-    name = f"fq_d{d}_k{k}_n{N}.npz"
+    name = f"fq_d{d}_k{k}_n{N}{'_init' if initial else ''}.npz"
     if name not in man:
         raise FileNotFoundError(f"no codebook artifact {name}")
     cw = np.load(os.path.join(artifact_dir, name), allow_pickle=False)["codewords"]
@@ -205,8 +206,8 @@ class Codebook:
         self.handle = fq_codebook_load(self.d, self.k, self.N, codewords, rotation)
 
     @classmethod
-    def from_artifact(cls, k: int, N: int, d: int = 64) -> "Codebook":
-        return cls(*load_artifact(k, N, d))
+    def from_artifact(cls, k: int, N: int, d: int = 64, initial: bool = False) -> "Codebook":
+        return cls(*load_artifact(k, N, d, initial))
 
     def code_bytes(self, n: int) -> int:
         return fq_code_bytes(self.handle, n)
