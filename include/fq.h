@@ -163,6 +163,47 @@ fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint
                                 int Hkv, int64_t T, float scale, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ---- Codebook construction on the GPU (FibQuant summary §2.2: the codebook is
+ * built offline by Lloyd-Max iterations on samples of the canonical block source
+ * of §2.1 / §3.1, i.e. k-blocks of points uniform on the unit sphere S^{d-1}).
+ *
+ * Generalised Lloyd in fp64 from each of `restarts` starting codebooks:
+ *   assignment: every training block y goes to the codeword minimising
+ *     ||c||^2 - 2 y.c (lowest index on equal values); its error ||y - c||^2;
+ *   update: every codeword becomes the mean of its cell; empty cells, in
+ *     increasing index order, are re-seeded at the training blocks with the
+ *     largest errors (decreasing error, lowest index on equal errors);
+ *   stop: no assignment changed, or the training MSE fell by no more than
+ *     rel_tol of itself, or max_iter updates were made.
+ * The refined codebook with the lowest validation MSE is kept (the first on
+ * equal values) and rounded to the fp16 grid (round to nearest even straight
+ * from fp64; |v| < 2^-14 becomes 0), which makes it loadable by
+ * fq_codebook_load.  Cell sums are accumulated in 64-bit fixed point, so a
+ * build is bit-reproducible on one device.
+ *   k:         block length, a power of two <= 64.  N: 1 <= N <= 65536.
+ *   train:     device fp64 [m_train][k]; valid: device fp64 [m_valid][k]
+ *              (coordinates in [-1, 1]; both < 2^31 rows).
+ *   starts:    device fp64 [restarts][N][k] starting codebooks.
+ *   codewords: device fp32 [N][k] out (fp16-exact values), 16-byte aligned.
+ *   codewords64: device fp64 [N][k] out, the kept codebook before rounding
+ *              (may be NULL).
+ *   restart_valid_mse: host [restarts] out, validation MSE per block of each
+ *              refined codebook before rounding (may be NULL);
+ *   valid_mse: host out, validation MSE of the rounded codebook (may be NULL);
+ *   history:   host [max_iter + 1] out, training MSE of the kept run after
+ *              every assignment (may be NULL); history_len: host out (may be
+ *              NULL).
+ *   workspace: device, fq_codebook_train_workspace_bytes(...) bytes.
+ * fp64 arrays are 8-byte aligned.  Unlike the codec calls this one blocks: it
+ * synchronises `stream` after every assignment to decide whether to stop, and
+ * returns when the build is done. */
+size_t fq_codebook_train_workspace_bytes(int k, int N, int64_t m_train, int64_t m_valid);
+fq_status fq_codebook_train(int k, int N, const double* train, int64_t m_train, const double* valid,
+                            int64_t m_valid, const double* starts, int restarts, int max_iter, double rel_tol,
+                            float* codewords, double* codewords64, double* restart_valid_mse, double* valid_mse,
+                            double* history, int* history_len, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* fq_status_string(fq_status st);
 

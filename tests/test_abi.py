@@ -29,6 +29,7 @@ def L():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_varlen", "fq_attn_workspace_bytes",
                                   "fq_code_bytes", "fq_codebook_free", "fq_codebook_load", "fq_decode",
+                                  "fq_codebook_train", "fq_codebook_train_workspace_bytes",
                                   "fq_encode", "fq_encode_scatter", "fq_status_string"])
 
 
@@ -61,6 +62,17 @@ def test_null_handle_paths_without_gpu(L):
                                None) == fq.FQ_ERR_ARG
     assert L.fq_attn_decode_varlen(None, vp(16), vp(16), vp(16), vp(16), vp(16), vp(16), 1, 8, 1, 10, 0.125,
                                    vp(16), vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
+    assert L.fq_codebook_train_workspace_bytes(3, 16, 100, 100) == 0  # k not a power of two
+    assert L.fq_codebook_train_workspace_bytes(4, 16, 100, 100) > 0
+    dbl = ctypes.c_double
+    L.fq_codebook_train.argtypes = [ctypes.c_int, ctypes.c_int, vp, ctypes.c_int64, vp, ctypes.c_int64, vp,
+                                    ctypes.c_int, ctypes.c_int, dbl, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    assert L.fq_codebook_train(4, 16, None, 100, vp(16), 100, vp(16), 1, 10, 1e-6, vp(16), None, None, None, None,
+                               None, vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
+    assert L.fq_codebook_train(4, 16, vp(16), 100, vp(16), 100, vp(16), 1, 10, -1.0, vp(16), None, None, None,
+                               None, None, vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
+    assert L.fq_codebook_train(4, 16, vp(16), 100, vp(16), 100, vp(16), 1, 10, 1e-6, vp(16), None, None, None,
+                               None, None, vp(16), 16, None) == fq.FQ_ERR_WORKSPACE
     L.fq_codebook_free(None)  # ignored
 
 

@@ -1,0 +1,125 @@
+"""GPU parity of the codebook construction (fq_codebook_train; FibQuant summary
+§2.2: Lloyd-Max refinement of the deterministic start on samples of the
+canonical block source) against the oracle's construction.
+
+Bars: one Lloyd step from the same start and samples gives the oracle's
+assignment exactly (the samples are continuous draws, so fp64 near-ties have
+probability ~0) and its cell means within 1e-10 (the GPU sums cells in 64-bit
+fixed point, quantum <= 2^-39 per sample); training MSE within 1e-12 relative;
+a full multi-restart build reproduces the frozen, oracle-built workload
+codebooks exactly.  Also the source-coding sweep of §4.1 on the canonical
+source: at every integer rate the vector codes beat the scalar code (shape only:
+the pages print no numbers for it)."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import universal_vector_quantization_amd as fq
+from oracle import codebook as ocb
+from oracle.codec import code_bits
+from oracle.rotation import haar_rotation
+from oracle.source import sample_canonical
+
+from gpu_util import D, device, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _gpu_train(dev, train, valid, starts, max_iter, rel_tol):
+    import torch
+
+    R, N, k = starts.shape
+    cw = torch.empty((N, k), dtype=torch.float32, device=dev)
+    c64 = torch.empty((N, k), dtype=torch.float64, device=dev)
+    res = fq.fq_codebook_train(to_dev(train, dev), to_dev(valid, dev), to_dev(starts, dev), max_iter, rel_tol, cw,
+                               c64)
+    torch.cuda.synchronize()
+    res["codewords"] = cw.cpu().numpy()
+    res["codewords64"] = c64.cpu().numpy()
+    return res
+
+
+@pytest.mark.parametrize("k,N,m", [(1, 16, 100_000), (2, 16, 100_000), (4, 256, 100_000), (8, 256, 70_000),
+                                   (64, 64, 20_000)])
+def test_one_lloyd_step_matches_oracle(dev, k, N, m):
+    rng = np.random.default_rng(1000 + k)
+    train = sample_canonical(D, k, m, rng)
+    init = ocb.initial_codebook(D, k, N)
+    print(f"[lloyd step] k={k} N={N} m={m}", flush=True)
+    got = _gpu_train(dev, train, train[:1000], init[None], 1, 0.0)
+    c1, hist, idx = ocb.lloyd(init, train, max_iter=1, rel_tol=0.0)
+    assert np.max(np.abs(got["codewords64"] - c1)) <= 1e-10
+    assert len(got["history"]) == len(hist)
+    assert np.allclose(got["history"], hist, rtol=1e-12, atol=0)
+
+
+def test_empty_cells_are_reseeded_like_the_oracle(dev):
+    # Six codewords far outside the unit ball get no samples: the update re-seeds
+    # them, in increasing index order, at the worst-served samples.
+    k, N, m = 4, 64, 20_000
+    rng = np.random.default_rng(77)
+    train = sample_canonical(D, k, m, rng)
+    init = ocb.initial_codebook(D, k, N)
+    far = [3, 10, 11, 40, 41, 63]
+    init[far] = 5.0 + np.arange(len(far))[:, None]
+    got = _gpu_train(dev, train, train[:500], init[None], 2, 0.0)
+    c2, hist, _ = ocb.lloyd(init, train, max_iter=2, rel_tol=0.0)
+    assert np.max(np.abs(got["codewords64"] - c2)) <= 1e-10
+    assert np.allclose(got["history"], hist, rtol=1e-12, atol=0)
+
+
+def _oracle_inputs(k, N, seed, samples=None):
+    """The training and validation draws and the restart starts exactly as the
+    oracle's build_codebook makes them."""
+    rng = np.random.default_rng(seed)
+    m = samples if samples is not None else max(256 * N, 100_000)
+    train = sample_canonical(D, k, m, rng)
+    valid = sample_canonical(D, k, m, rng)
+    c0 = ocb.initial_codebook(D, k, N)
+    starts = np.stack([c0 @ (np.eye(k) if r == 0 else haar_rotation(k, seed * 1000 + r)).T for r in range(3)])
+    return train, valid, starts
+
+
+@pytest.mark.parametrize("k,N,seed,max_iter", [(2, 16, 201, 100), (4, 256, 202, 100)])
+def test_build_reproduces_frozen_workload_codebook(dev, k, N, seed, max_iter):
+    art = os.path.join(os.path.dirname(fq.__file__), "codebooks")
+    man = json.load(open(os.path.join(art, "MANIFEST.json")))[f"fq_d64_k{k}_n{N}.npz"]
+    frozen = np.load(os.path.join(art, f"fq_d64_k{k}_n{N}.npz"))["codewords"]
+    train, valid, starts = _oracle_inputs(k, N, seed)
+    print(f"[codebook build] k={k} N={N} seed={seed} m={len(train)}", flush=True)
+    got = _gpu_train(dev, train, valid, starts, max_iter, 1e-6)
+    assert np.array_equal(got["codewords"], frozen)
+    assert np.allclose(got["restart_valid_mse"], man["restart_valid_mse"], rtol=1e-10, atol=0)
+    assert abs(got["valid_mse"] - man["valid_mse"]) <= 1e-10 * man["valid_mse"]
+    assert len(got["history"]) - 1 == man["iterations"]
+
+
+def test_source_coding_sweep_vector_codes_beat_scalar(dev):
+    # Normalised validation MSE of GPU-built codebooks at b = 1, 2, 3 bits per
+    # coordinate for k = 1 (scalar), 2 and 4 (N = 2^(k b)).  At b = 1 the 2-D code
+    # with N = 4 can only tie the scalar one (the square is already the best
+    # 4-point code of a near-Gaussian pair), so the strict claim is checked for k = 4
+    # at every rate and for k = 2 from b = 2 on.
+    nmse = {}
+    for b in (1, 2, 3):
+        for k in (1, 2, 4):
+            N = 2 ** (k * b)
+            train, valid, starts = _oracle_inputs(k, N, 300 + 10 * b + k)
+            got = _gpu_train(dev, train, valid, starts, 100, 1e-6)
+            nmse[(k, b)] = got["valid_mse"] / (k / D)
+            print(f"[sweep] b={b} k={k} N={N} normalised MSE {nmse[(k, b)]:.5f}", flush=True)
+    for b in (1, 2, 3):
+        assert nmse[(4, b)] < nmse[(1, b)]
+        assert nmse[(2, b)] <= nmse[(1, b)] * (1 + 1e-3)
+        if b >= 2:
+            assert nmse[(2, b)] < nmse[(1, b)]
+        assert nmse[(1, b)] < (0.5 if b == 1 else 1.0)  # a useful code at all
+    for k in (1, 2, 4):
+        assert nmse[(k, 1)] > nmse[(k, 2)] > nmse[(k, 3)]  # more bits, less distortion

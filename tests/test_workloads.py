@@ -38,3 +38,15 @@ def test_workload_table():
     assert w.WORKLOADS["tinyllama_kv"].n == 5767168
     assert w.WORKLOADS["fullvec_kv"].n == 1048576
     assert w.WORKLOADS["attn_b16_t32k"].n == 2 * w.ATTN_B * w.ATTN_HKV * w.ATTN_T
+
+
+def test_canonical_blocks_agree_with_the_oracle_source():
+    # two implementations of the same draw (uniform points on the sphere, first k
+    # coordinates): the generator here and the oracle's own
+    from oracle.source import sample_canonical
+
+    for k in (1, 4, 64):
+        a = w.canonical_blocks(64, k, 1000, 7)
+        b = sample_canonical(64, k, 1000, np.random.default_rng(7))
+        assert a.shape == (1000, k) and np.array_equal(a, b)
+    assert np.allclose(np.sum(w.canonical_blocks(64, 64, 10, 1) ** 2, axis=1), 1.0)

@@ -20,7 +20,8 @@ __all__ = [
     "FQ_OK", "FQ_ERR_ARG", "FQ_ERR_UNSUPPORTED", "FQ_ERR_WORKSPACE", "FQ_ERR_HIP", "FQ_F32", "FQ_F16",
     "FQError", "lib", "library_path", "fq_status_string", "fq_codebook_load", "fq_codebook_free", "fq_code_bytes",
     "fq_encode", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
-    "fq_attn_decode_varlen", "Codebook", "load_artifact",
+    "fq_attn_decode_varlen", "fq_codebook_train_workspace_bytes", "fq_codebook_train", "Codebook",
+    "load_artifact",
     "artifact_dir",
 ]
 
@@ -66,6 +67,12 @@ def lib() -> ctypes.CDLL:
         L.fq_attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp,
                                             sz, vp]
         L.fq_attn_decode_varlen.restype = i32
+        L.fq_codebook_train_workspace_bytes.argtypes = [i32, i32, i64, i64]
+        L.fq_codebook_train_workspace_bytes.restype = sz
+        dbl = ctypes.c_double
+        L.fq_codebook_train.argtypes = [i32, i32, vp, i64, vp, i64, vp, i32, i32, dbl, vp, vp, vp, vp, vp, vp, vp,
+                                        sz, vp]
+        L.fq_codebook_train.restype = i32
         _lib = L
     return _lib
 
@@ -178,6 +185,36 @@ def fq_attn_decode_varlen(cb: int, q, k_codes, k_norms, v_codes, v_norms, lens, 
            lib().fq_attn_decode_varlen(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
                                        _ptr(lens), B, Hq, Hkv, T, float(scale), _ptr(out), ws_ptr, ws_bytes,
                                        _stream(stream)))
+
+
+def fq_codebook_train_workspace_bytes(k: int, N: int, m_train: int, m_valid: int) -> int:
+    return int(lib().fq_codebook_train_workspace_bytes(k, N, m_train, m_valid))
+
+
+def fq_codebook_train(train, valid, starts, max_iter: int, rel_tol: float, codewords, codewords64=None,
+                      workspace=None, stream=None) -> dict:
+    """Generalised Lloyd on the GPU.  train [m_train, k] / valid [m_valid, k] fp64, starts
+    [restarts, N, k] fp64 device tensors; codewords fp32 [N, k] (written).  Returns the
+    per-restart validation MSE, the rounded codebook's validation MSE and the kept run's
+    training-MSE history (host values the call produced)."""
+    import torch
+
+    R, N, k = starts.shape
+    mt, mv = train.shape[0], valid.shape[0]
+    if train.shape[1] != k or valid.shape[1] != k or codewords.shape != (N, k):
+        raise ValueError("shape mismatch")
+    if workspace is None:
+        workspace = torch.empty(max(fq_codebook_train_workspace_bytes(k, N, mt, mv), 16), dtype=torch.uint8,
+                                device=train.device)
+    rmse = (ctypes.c_double * R)()
+    vmse = ctypes.c_double()
+    hist = (ctypes.c_double * (max_iter + 1))()
+    hlen = ctypes.c_int()
+    _check("fq_codebook_train", lib().fq_codebook_train(
+        k, N, _ptr(train), mt, _ptr(valid), mv, _ptr(starts), R, max_iter, float(rel_tol), _ptr(codewords),
+        _ptr(codewords64), rmse, ctypes.byref(vmse), hist, ctypes.byref(hlen), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return {"restart_valid_mse": list(rmse), "valid_mse": vmse.value, "history": list(hist)[: hlen.value]}
 
 
 # --------------------------------------------------------------- artifacts

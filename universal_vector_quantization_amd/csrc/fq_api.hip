@@ -477,6 +477,40 @@ FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const u
                      workspace_bytes, stream);
 }
 
+namespace {
+bool train_sizes_ok(int k, int N, int64_t m_train, int64_t m_valid) {
+  if (k < 1 || k > 64 || (k & (k - 1)) != 0) return false;
+  if (N < 1 || N > 65536) return false;
+  return m_train >= 1 && m_valid >= 1 && m_train <= INT32_MAX && m_valid <= INT32_MAX;
+}
+}  // namespace
+
+FQ_EXPORT size_t fq_codebook_train_workspace_bytes(int k, int N, int64_t m_train, int64_t m_valid) {
+  if (!train_sizes_ok(k, N, m_train, m_valid)) return 0;
+  return fq::train_workspace_bytes(k, N, m_train, m_valid);
+}
+
+FQ_EXPORT fq_status fq_codebook_train(int k, int N, const double* train, int64_t m_train, const double* valid,
+                                      int64_t m_valid, const double* starts, int restarts, int max_iter,
+                                      double rel_tol, float* codewords, double* codewords64,
+                                      double* restart_valid_mse, double* valid_mse, double* history,
+                                      int* history_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!train_sizes_ok(k, N, m_train, m_valid)) return FQ_ERR_ARG;
+  if (restarts < 1 || max_iter < 0 || !(rel_tol >= 0.0) || !isfinite(rel_tol)) return FQ_ERR_ARG;
+  if (!train || !valid || !starts || !codewords) return FQ_ERR_ARG;
+  auto al8 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7) == 0; };
+  if (!al8(train) || !al8(valid) || !al8(starts) || !aligned16(codewords) || (codewords64 && !al8(codewords64)))
+    return FQ_ERR_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fq::train_workspace_bytes(k, N, m_train, m_valid))
+    return FQ_ERR_WORKSPACE;
+  return fq::train_codebook(k, N, train, m_train, valid, m_valid, starts, restarts, max_iter, rel_tol, codewords,
+                            codewords64, restart_valid_mse, valid_mse, history, history_len, workspace,
+                            (hipStream_t)stream) == hipSuccess
+             ? FQ_OK
+             : FQ_ERR_HIP;
+}
+
 FQ_EXPORT fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint8_t* k_codes,
                                           const void* k_norms, const uint8_t* v_codes, const void* v_norms,
                                           const int32_t* lens, int B, int Hq, int Hkv, int64_t T, float scale,

@@ -102,4 +102,12 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
                        const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
                        int64_t T, float scale, float* out, void* workspace, hipStream_t s);
 
+// Codebook construction (generalised Lloyd over fp64 training blocks, several starts,
+// validation selection, fp16 grid); blocking: synchronises `s` every iteration.
+size_t train_workspace_bytes(int k, int N, int64_t m_train, int64_t m_valid);
+hipError_t train_codebook(int k, int N, const double* train, int64_t mt, const double* valid, int64_t mv,
+                          const double* starts, int restarts, int max_iter, double rel_tol, float* out, double* out64,
+                          double* restart_mse, double* valid_mse, double* history, int* history_len, void* ws,
+                          hipStream_t s);
+
 }  // namespace fq

@@ -137,3 +137,14 @@ def random_norms(n: int, seed: int, dtype=np.float16) -> np.ndarray:
     """Positive norms with the spread of the Student-t workloads: 8 * exp(0.5 z)."""
     rng = np.random.default_rng(seed)
     return (8.0 * np.exp(0.5 * rng.standard_normal(n))).astype(dtype)
+
+
+def canonical_blocks(d: int, k: int, m: int, seed: int) -> np.ndarray:
+    """Training blocks for the codebook construction: the first k coordinates of m
+    points uniform on the unit sphere S^{d-1}, drawn as normalised standard
+    Gaussian d-vectors (fp64 [m, k]).  A draw of the source, not a step of the
+    codec."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((m, d))
+    g /= np.sqrt(np.sum(g * g, axis=1, keepdims=True))
+    return g[:, :k].copy()
