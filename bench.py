@@ -20,7 +20,8 @@ decode loop is timed as well: per step the new token's K and V are encoded into
 their slots (fq_encode_scatter) and attention runs over each sequence's valid
 length (fq_attn_decode_varlen).  Along the rate axis (frozen initial codebooks
 from b = 4 down to 0.22 bits per coordinate) the same tensor's encode, decode
-and attention are timed as well.  The CPU oracle is timed on a bounded sample
+and attention are timed as well, and so is the codebook construction
+(fq_codebook_train) at larger shapes.  The CPU oracle is timed on a bounded sample
 (rank 0, one GPU only).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -59,6 +60,7 @@ def parse():
     ap.add_argument("--no-attn-workload", action="store_true")
     ap.add_argument("--no-decode-loop", action="store_true", help="skip the append + varlen attention timing")
     ap.add_argument("--no-rate-axis", action="store_true", help="skip the rate-axis timings")
+    ap.add_argument("--no-build", action="store_true", help="skip the codebook-construction timings")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -230,6 +232,48 @@ def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
         out[f"k{k}_N{N}"] = rec
         cb.close()
         del codes, norms, xr
+    return out
+
+
+# Codebook-construction shapes: (k, N, training blocks); starts are the frozen initial codebooks.
+BUILD_SHAPES = [(4, 1024, 262144), (4, 16384, 1048576), (64, 16384, 262144)]
+FP64_VALU_PEAK_T = 78.6  # dense fp64 vector FLOP/s of the MI355X, in T
+
+
+def build_timings(fq, workloads, dev, stream, iters: int = 5):
+    """fq_codebook_train at larger shapes: `iters` Lloyd updates from the frozen
+    initial codebook (rel_tol 0), 1024 validation blocks.  The assignment pass is
+    the work: m N (2k + 2) fp64 flops (dot product, score, compare) per pass, and a
+    call makes iters + 3 passes (one before the first update, one after each, two
+    validations of 1024 blocks)."""
+    import torch
+
+    out = {}
+    for k, N, m in BUILD_SHAPES:
+        try:
+            cw0, _ = fq.load_artifact(k, N, initial=True)
+        except FileNotFoundError:
+            out[f"k{k}_N{N}"] = {"skipped": "initial codebook artifact missing"}
+            continue
+        train = torch.from_numpy(workloads.canonical_blocks(D, k, m, 400 + k)).to(dev)
+        valid = torch.from_numpy(workloads.canonical_blocks(D, k, 1024, 500 + k)).to(dev)
+        starts = torch.from_numpy(cw0.astype(np.float64)[None]).to(dev)
+        cw = torch.empty((N, k), dtype=torch.float32, device=dev)
+        ws = torch.empty(fq.fq_codebook_train_workspace_bytes(k, N, m, 1024), dtype=torch.uint8, device=dev)
+        fq.fq_codebook_train(train, valid, starts, 1, 0.0, cw, workspace=ws, stream=stream)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = fq.fq_codebook_train(train, valid, starts, iters, 0.0, cw, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        t = time.perf_counter() - t0
+        passes = len(res["history"])  # training assignments; validation passes are 1024 blocks each
+        flops = passes * m * N * (2 * k + 2)
+        out[f"k{k}_N{N}"] = {"training_blocks": m, "updates": passes - 1, "seconds": t,
+                             "ms_per_update": t * 1e3 / max(passes - 1, 1),
+                             "assign_TFLOPs": flops / t / 1e12,
+                             "assign_frac_fp64_valu": flops / t / 1e12 / FP64_VALU_PEAK_T,
+                             "train_mse_first_last": [res["history"][0], res["history"][-1]]}
+        del train, valid, starts, cw, ws
     return out
 
 
@@ -465,6 +509,8 @@ def main():
         line["workloads"] = workload_timings(fq, workloads, dev, stream)
     if not args.no_rate_axis:
         line["rate_axis"] = rate_axis_timings(fq, workloads, dev, stream)
+    if not args.no_build:
+        line["codebook_build"] = build_timings(fq, workloads, dev, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     cb.close()

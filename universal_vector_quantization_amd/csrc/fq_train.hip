@@ -16,6 +16,12 @@
 // independent validation set is kept (the first on equal MSE) and rounded to the
 // fp16 grid (round to nearest even, |v| < 2^-14 flushed to 0).
 //
+// Assignment: one thread per S samples (held in registers), every codeword
+// visited in increasing index order.  For k <= 8 codeword tiles are staged in LDS
+// and each broadcast LDS read feeds S samples; for k >= 16 a codeword's values
+// are read with wave-uniform addresses (scalar cache, scalar registers), since
+// with one or two samples per thread an LDS read per FMA would saturate LDS.
+//
 // The assignment pass also accumulates the cell sums and counts for the next
 // update: sample coordinates are added as 64-bit fixed-point integers (scale
 // 2^s with m * 2^s < 2^62), so the sums do not depend on the order of the
@@ -35,8 +41,8 @@ constexpr int TW = 256;  // threads per workgroup
 
 template <int K>
 struct TrainShape {
-  static constexpr int S = K <= 8 ? 4 : (K <= 16 ? 2 : 1);  // samples per thread
-  static constexpr int TILE = K >= 32 ? 64 : 128;             // codewords per LDS tile
+  static constexpr int S = K <= 8 ? 4 : (K <= 32 ? 2 : 1);  // samples per thread
+  static constexpr int TILE = 128;                          // codewords per LDS tile (k <= 8)
 };
 
 // Assignment of samples [0, m) against codebook c [N][K] (fp64) with ||c||^2 in cn2.
@@ -52,9 +58,10 @@ __global__ __launch_bounds__(TW) void lloyd_assign(const double* __restrict__ y,
                                                    unsigned int* __restrict__ counts, double scale,
                                                    unsigned long long* __restrict__ esum, double escale) {
   typedef TrainShape<K> Sh;
-  constexpr int S = Sh::S, TILE = Sh::TILE;
-  __shared__ double tc[TILE * K];
-  __shared__ double tn[TILE];
+  constexpr int S = Sh::S;
+  constexpr int TILE = Sh::TILE;
+  __shared__ double tc[K <= 8 ? TILE * K : 1];
+  __shared__ double tn[K <= 8 ? TILE : 1];
   __shared__ double red[TW];
   const int tid = fq_tid();
   const int64_t base = (int64_t)fq_bid_x() * (TW * S);
@@ -75,29 +82,64 @@ __global__ __launch_bounds__(TW) void lloyd_assign(const double* __restrict__ y,
     best[s] = __builtin_huge_val();
     bi[s] = 0;
   }
-  for (int t0 = 0; t0 < N; t0 += TILE) {
-    const int nt = N - t0 < TILE ? N - t0 : TILE;
-    __syncthreads();
-    for (int e = tid; e < nt * K; e += TW) tc[e] = c[(int64_t)t0 * K + e];
-    for (int e = tid; e < nt; e += TW) tn[e] = cn2[t0 + e];
-    __syncthreads();
-    for (int r = 0; r < nt; r++) {
-      double dot[S];
+  if constexpr (K <= 8) {
+    // short codewords: tiles staged in LDS, every LDS read (the same address in
+    // every lane: a broadcast) feeding S samples
+    for (int t0 = 0; t0 < N; t0 += TILE) {
+      const int nt = N - t0 < TILE ? N - t0 : TILE;
+      __syncthreads();
+      for (int e = tid; e < nt * K; e += TW) tc[e] = c[(int64_t)t0 * K + e];
+      for (int e = tid; e < nt; e += TW) tn[e] = cn2[t0 + e];
+      __syncthreads();
+      for (int r = 0; r < nt; r++) {
+        double dot[S];
 #pragma unroll
-      for (int s = 0; s < S; s++) dot[s] = 0.0;
+        for (int s = 0; s < S; s++) dot[s] = 0.0;
+#pragma unroll
+        for (int j = 0; j < K; j++) {
+          const double cv = tc[r * K + j];
+#pragma unroll
+          for (int s = 0; s < S; s++) dot[s] = fma(ys[s][j], cv, dot[s]);
+        }
+        const double cn = tn[r];
+#pragma unroll
+        for (int s = 0; s < S; s++) {
+          const double sc = fma(-2.0, dot[s], cn);
+          if (sc < best[s]) {  // codewords in increasing order: the lowest index wins equal scores
+            best[s] = sc;
+            bi[s] = t0 + r;
+          }
+        }
+      }
+    }
+  } else {
+    // The codeword is the same for every lane: its values are read with uniform
+    // addresses, so they arrive through the scalar cache into scalar registers and
+    // feed the FMAs directly (no LDS traffic per FMA).
+    for (int n = 0; n < N; n++) {
+      const double* __restrict__ cr = c + (int64_t)n * K;
+      // P partial sums per sample: long dot products would otherwise be one chain of
+      // dependent FMAs
+      constexpr int P = 4;
+      double dot[S][P];
+#pragma unroll
+      for (int s = 0; s < S; s++)
+#pragma unroll
+        for (int q = 0; q < P; q++) dot[s][q] = 0.0;
 #pragma unroll
       for (int j = 0; j < K; j++) {
-        const double cv = tc[r * K + j];  // the same LDS address in every lane: a broadcast
+        const double cv = cr[j];
 #pragma unroll
-        for (int s = 0; s < S; s++) dot[s] = fma(ys[s][j], cv, dot[s]);
+        for (int s = 0; s < S; s++) dot[s][j % P] = fma(ys[s][j], cv, dot[s][j % P]);
       }
-      const double cn = tn[r];
+      const double cn = cn2[n];
 #pragma unroll
       for (int s = 0; s < S; s++) {
-        const double sc = fma(-2.0, dot[s], cn);
+        const double dt = (dot[s][0] + dot[s][1]) + (dot[s][2] + dot[s][3]);
+        const double sc = fma(-2.0, dt, cn);
         if (sc < best[s]) {  // codewords in increasing order: the lowest index wins equal scores
           best[s] = sc;
-          bi[s] = t0 + r;
+          bi[s] = n;
         }
       }
     }
