@@ -38,10 +38,11 @@
  *     and int32 length arrays: 8- and 4-byte aligned).  Inputs are only
  *     read, outputs only written.  Nothing here allocates except
  *     fq_codebook_load.
- *   - Asynchrony: fq_encode, fq_encode_scatter, fq_decode, fq_attn_decode and
- *     fq_attn_decode_varlen only enqueue work on `stream` (a hipStream_t; NULL
- *     is the default stream) and return; they never synchronise and never read
- *     results back.
+ *   - Asynchrony: fq_encode, fq_encode_scatter, fq_decode, fq_attn_decode,
+ *     fq_attn_decode_varlen and fq_attn_prefill only enqueue work on `stream`
+ *     (a hipStream_t; NULL is the default stream) and return; they never
+ *     synchronise and never read results back (fq_codebook_train is the
+ *     exception and says so).
  *   - Errors: arguments are checked on the host before any launch and return
  *     FQ_ERR_ARG / FQ_ERR_UNSUPPORTED / FQ_ERR_WORKSPACE with nothing enqueued;
  *     a failed launch returns FQ_ERR_HIP.  No call aborts or throws.  n = 0 (or
@@ -162,6 +163,23 @@ fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint
                                 const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq,
                                 int Hkv, int64_t T, float scale, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes fq_attn_prefill needs (0 for invalid sizes, T = 0, B = 0 or Sq = 0). */
+size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T);
+
+/* Multi-query (prefill) attention over a compressed cache (FibQuant summary §5):
+ * Sq queries per query head, each scored as in fq_attn_decode:
+ *     out[b][h][i] = sum_{j in K_i} softmax_j(scale * q[b][h][i] . k_j) v_j,
+ * K_i = all T keys, or with causal = 1 the keys 0 .. T - Sq + i (the queries
+ * are the last Sq positions of the cache; a query that sees no key gets 0).
+ *   q:   device fp16 [B][Hq][Sq][d].  out: device fp32 [B][Hq][Sq][d].
+ *   cache, grouping, workspace rules as for fq_attn_decode.
+ * Implemented for k = 4 with 8-bit codes (N = 256); other codebooks give
+ * FQ_ERR_UNSUPPORTED.  B * Hq * Sq < 2^31 and B * Hkv <= 65535. */
+fq_status fq_attn_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
+                          int causal, float scale, float* out, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ---- Codebook construction on the GPU (FibQuant summary §2.2: the codebook is
  * built offline by Lloyd-Max iterations on samples of the canonical block source

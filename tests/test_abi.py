@@ -27,7 +27,8 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_varlen", "fq_attn_workspace_bytes",
+    assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_varlen", "fq_attn_prefill",
+                                  "fq_attn_prefill_workspace_bytes", "fq_attn_workspace_bytes",
                                   "fq_code_bytes", "fq_codebook_free", "fq_codebook_load", "fq_decode",
                                   "fq_codebook_train", "fq_codebook_train_workspace_bytes",
                                   "fq_encode", "fq_encode_scatter", "fq_status_string"])
@@ -62,6 +63,9 @@ def test_null_handle_paths_without_gpu(L):
                                None) == fq.FQ_ERR_ARG
     assert L.fq_attn_decode_varlen(None, vp(16), vp(16), vp(16), vp(16), vp(16), vp(16), 1, 8, 1, 10, 0.125,
                                    vp(16), vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
+    assert L.fq_attn_prefill_workspace_bytes(None, 1, 8, 1, 4, 10) == 0
+    assert L.fq_attn_prefill(None, vp(16), vp(16), vp(16), vp(16), vp(16), 1, 8, 1, 4, 10, 1, 0.125, vp(16),
+                             vp(16), 1 << 20, None) == fq.FQ_ERR_ARG
     assert L.fq_codebook_train_workspace_bytes(3, 16, 100, 100) == 0  # k not a power of two
     assert L.fq_codebook_train_workspace_bytes(4, 16, 100, 100) > 0
     dbl = ctypes.c_double

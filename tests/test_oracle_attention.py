@@ -141,3 +141,37 @@ def test_lengths_clamp_and_full_length_is_the_plain_call():
     for b in range(B):  # one key: the output is exactly that key's value
         v0 = decode(vc[b, 0, :1], vn[b, 0, :1], PI, CB)[0]
         assert np.array_equal(one[b, 0], v0) and np.array_equal(one[b, 1], v0)
+
+
+# ------------------------------------------------------------------ prefill (several queries per head)
+def test_prefill_noncausal_is_decode_per_query():
+    from oracle.attention import prefill_attention
+
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, T, Sq = 2, 4, 2, 7, 3
+    kc, kn, vc, vn = _rand_cache(rng, B, Hkv, T)
+    q = rng.standard_normal((B, Hq, Sq, D)).astype(np.float16)
+    out = prefill_attention(q, kc, kn, vc, vn, PI, CB, 0.125, causal=False)
+    for i in range(Sq):
+        assert np.array_equal(out[:, :, i], attention(q[:, :, i], kc, kn, vc, vn, PI, CB, 0.125))
+
+
+def test_prefill_causal_against_pure_python_loops():
+    # query i sees keys 0 .. T - Sq + i; the last query sees every key, Sq = T makes
+    # query 0 see only key 0 (its output is exactly that value)
+    from oracle.attention import prefill_attention
+
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, T, Sq = 1, 2, 1, 5, 5
+    kc, kn, vc, vn = _rand_cache(rng, B, Hkv, T)
+    q = rng.standard_normal((B, Hq, Sq, D)).astype(np.float16)
+    out = prefill_attention(q, kc, kn, vc, vn, PI, CB, 0.125, causal=True)
+    for h in range(Hq):
+        for i in range(Sq):
+            ref = _python_attention_row(q[0, h, i], kc[0, 0], kn[0, 0], vc[0, 0], vn[0, 0], i + 1)
+            assert np.max(np.abs(out[0, h, i] - np.array(ref))) < 1e-11
+    v0 = decode(vc[0, 0, :1], vn[0, 0, :1], PI, CB)[0]
+    assert np.array_equal(out[0, 0, 0], v0)
+    # more queries than keys: the first Sq - T queries see nothing
+    out2 = prefill_attention(np.concatenate([q, q], axis=2), kc, kn, vc, vn, PI, CB, 0.125, causal=True)
+    assert np.all(out2[:, :, :5] == 0.0) and np.array_equal(out2[:, :, 5:], out)

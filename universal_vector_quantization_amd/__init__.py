@@ -20,7 +20,8 @@ __all__ = [
     "FQ_OK", "FQ_ERR_ARG", "FQ_ERR_UNSUPPORTED", "FQ_ERR_WORKSPACE", "FQ_ERR_HIP", "FQ_F32", "FQ_F16",
     "FQError", "lib", "library_path", "fq_status_string", "fq_codebook_load", "fq_codebook_free", "fq_code_bytes",
     "fq_encode", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
-    "fq_attn_decode_varlen", "fq_codebook_train_workspace_bytes", "fq_codebook_train", "Codebook",
+    "fq_attn_decode_varlen", "fq_attn_prefill_workspace_bytes", "fq_attn_prefill",
+    "fq_codebook_train_workspace_bytes", "fq_codebook_train", "Codebook",
     "load_artifact",
     "artifact_dir",
 ]
@@ -67,6 +68,11 @@ def lib() -> ctypes.CDLL:
         L.fq_attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp,
                                             sz, vp]
         L.fq_attn_decode_varlen.restype = i32
+        L.fq_attn_prefill_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i64]
+        L.fq_attn_prefill_workspace_bytes.restype = sz
+        L.fq_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, ctypes.c_float, vp, vp,
+                                      sz, vp]
+        L.fq_attn_prefill.restype = i32
         L.fq_codebook_train_workspace_bytes.argtypes = [i32, i32, i64, i64]
         L.fq_codebook_train_workspace_bytes.restype = sz
         dbl = ctypes.c_double
@@ -185,6 +191,20 @@ def fq_attn_decode_varlen(cb: int, q, k_codes, k_norms, v_codes, v_norms, lens, 
            lib().fq_attn_decode_varlen(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
                                        _ptr(lens), B, Hq, Hkv, T, float(scale), _ptr(out), ws_ptr, ws_bytes,
                                        _stream(stream)))
+
+
+def fq_attn_prefill_workspace_bytes(cb: int, B: int, Hq: int, Hkv: int, Sq: int, T: int) -> int:
+    return int(lib().fq_attn_prefill_workspace_bytes(cb, B, Hq, Hkv, Sq, T))
+
+
+def fq_attn_prefill(cb: int, q, k_codes, k_norms, v_codes, v_norms, B: int, Hq: int, Hkv: int, Sq: int, T: int,
+                    causal: bool, scale: float, out, workspace, stream=None) -> None:
+    """q fp16 [B, Hq, Sq, 64]; codes/norms of a [B, Hkv, T] cache; out fp32 [B, Hq, Sq, 64]."""
+    ws_ptr = None if workspace is None else _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("fq_attn_prefill", lib().fq_attn_prefill(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes),
+                                                    _ptr(v_norms), B, Hq, Hkv, Sq, T, 1 if causal else 0,
+                                                    float(scale), _ptr(out), ws_ptr, ws_bytes, _stream(stream)))
 
 
 def fq_codebook_train_workspace_bytes(k: int, N: int, m_train: int, m_valid: int) -> int:

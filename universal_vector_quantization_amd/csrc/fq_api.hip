@@ -477,6 +477,41 @@ FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const u
                      workspace_bytes, stream);
 }
 
+FQ_EXPORT size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T) {
+  if (attn_check_sizes(cb, B, Hq, Hkv, T) != FQ_OK || Sq <= 0 || T == 0 || B == 0) return 0;
+  if ((int64_t)B * Hq * Sq > ((int64_t)1 << 31) - 1) return 0;
+  const fq::PrefillPlan p = fq::prefill_plan(B, Hq, Hkv, Sq, T);
+  return ((size_t)B * Hq * Sq * p.nchunks * (2 + fq::kD) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+FQ_EXPORT fq_status fq_attn_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                                    const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq,
+                                    int64_t T, int causal, float scale, float* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  const fq_status ss = attn_check_sizes(cb, B, Hq, Hkv, T);
+  if (ss != FQ_OK) return ss;
+  if (Sq < 0 || (causal != 0 && causal != 1) || !isfinite(scale)) return FQ_ERR_ARG;
+  if (!fq::prefill_supported(cb)) return FQ_ERR_UNSUPPORTED;
+  if (B == 0 || Sq == 0) return FQ_OK;
+  if (!q || !out) return FQ_ERR_ARG;
+  if (T == 0) return FQ_OK;  // nothing to attend to
+  if ((int64_t)B * Hq * Sq > ((int64_t)1 << 31) - 1 || (int64_t)B * Hkv > 65535) return FQ_ERR_UNSUPPORTED;
+  if (fq::prefill_plan(B, Hq, Hkv, Sq, T).rblocks > 65535) return FQ_ERR_UNSUPPORTED;  // grid y
+  if (!k_codes || !k_norms || !v_codes || !v_norms) return FQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_norms) || !aligned16(v_codes) || !aligned16(v_norms) ||
+      !aligned16(out))
+    return FQ_ERR_ARG;
+  if (!workspace || !aligned16(workspace) ||
+      workspace_bytes < fq_attn_prefill_workspace_bytes(cb, B, Hq, Hkv, Sq, T))
+    return FQ_ERR_WORKSPACE;
+  const fq_status ds = check_device(cb);
+  if (ds != FQ_OK) return ds;
+  return fq::launch_prefill(cb, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv, Sq, T, causal, scale, out,
+                            workspace, (hipStream_t)stream) == hipSuccess
+             ? FQ_OK
+             : FQ_ERR_HIP;
+}
+
 namespace {
 bool train_sizes_ok(int k, int N, int64_t m_train, int64_t m_valid) {
   if (k < 1 || k > 64 || (k & (k - 1)) != 0) return false;

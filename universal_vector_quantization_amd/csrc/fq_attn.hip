@@ -777,6 +777,12 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   return AttnPlan{(int)nc, tc, 0, 0, false};
 }
 
+hipError_t launch_attn_combine(const float* ws, const float* pi32, int64_t rows, int nchunks, float* out,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows), dim3(64), 0, s, ws, pi32, nchunks, out);
+  return hipGetLastError();
+}
+
 size_t attn_records_bytes(int B, int Hq, int nchunks) {
   return (((size_t)B * (size_t)Hq * (size_t)nchunks * REC * sizeof(float)) + 255) & ~(size_t)255;
 }

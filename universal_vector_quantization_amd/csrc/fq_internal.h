@@ -102,6 +102,24 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
                        const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
                        int64_t T, float scale, float* out, void* workspace, hipStream_t s);
 
+// Log-sum-exp merge of `rows` rows of nchunks partial records each (m, l, acc[64] in the
+// rotated domain) and the inverse rotation: out[row][64].
+hipError_t launch_attn_combine(const float* ws, const float* pi32, int64_t rows, int nchunks, float* out,
+                               hipStream_t s);
+
+// Multi-query (prefill) attention: k = 4, 8-bit codes.  Split over keys into nchunks
+// ranges of chunk_tokens keys, 64 query rows per workgroup.
+struct PrefillPlan {
+  int nchunks;
+  int64_t chunk_tokens;
+  int rblocks;
+};
+PrefillPlan prefill_plan(int B, int Hq, int Hkv, int Sq, int64_t T);
+bool prefill_supported(const fq_codebook* cb);
+hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
+                          int causal, float scale, float* out, void* workspace, hipStream_t s);
+
 // Codebook construction (generalised Lloyd over fp64 training blocks, several starts,
 // validation selection, fp16 grid); blocking: synchronises `s` every iteration.
 size_t train_workspace_bytes(int k, int N, int64_t m_train, int64_t m_valid);

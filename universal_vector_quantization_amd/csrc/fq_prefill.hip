@@ -1,0 +1,276 @@
+// Multi-query (prefill) attention over a FibQuant-compressed cache (FibQuant
+// summary §5: fixed-address codes let decompression be fused into attention;
+// §2.3: k_j = nu_j Pi^T concat(c_j), so q . k_j = nu_j (Pi q) . concat(c_j)).
+//
+// Sq queries per query head attend to the T keys of their KV head's slab; with
+// the causal flag the queries are the slab's last Sq positions, so query i sees
+// keys 0 .. T - Sq + i.  Many query rows share every key, so the products run on
+// the matrix core (mfma_f32_16x16x32_f16) over codeword tiles decoded into LDS:
+//   * a workgroup takes 64 query rows of one (batch, KV head) slab (row r = head
+//     r / Sq of the group, query r % Sq) and a range of its keys; each of its 4
+//     waves owns 16 rows (the MFMA columns);
+//   * per 64-key unit every thread decodes one key's quarter record into LDS: K
+//     as [key][dim] fp16 (the A operand of S^T = K Qrot^T), V transposed as
+//     [dim][key] (the A operand of O^T += V^T P^T), norms as fp32;
+//   * the rotated, scaled query is split fp16 hi + lo (two products per K step:
+//     scores carry ~22 bits); P' = p * nu_v enters as one fp16 operand (relative
+//     rounding 2^-12 of each weight);
+//   * the key order inside a 32-key PV step is chosen so that the score
+//     registers of a lane are exactly its P^T operand (no shuffles): operand k
+//     index 8 h + j is key 4 h + j (j < 4) or 16 + 4 h + j - 4 of the step;
+//   * online softmax in base 2 per query column; the workgroup writes one
+//     partial record (m, l, acc[64], rotated domain) per row and key range, and
+//     the decode combine kernel merges the records and applies Pi^T.
+#include "fq_internal.h"
+#include "fq_device.h"
+
+namespace fq {
+namespace {
+
+constexpr int D = kD;
+constexpr int PW = 4;       // waves per workgroup
+constexpr int PU = 64;      // keys per unit
+constexpr int PROWS = 16 * PW;  // query rows per workgroup
+constexpr int REC_F = 2 + D;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline f32x4 mfma16(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Per-thread registers of one unit's records: key `lane / 4`, record dword `lane % 4`
+// of K and of V, and (threads < 64) the two norms of key `tid`.
+struct UnitRegs {
+  uint32_t kw, vw;
+  _Float16 kn, vn;
+};
+
+__global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
+    const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
+    const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
+    const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T, int Sq, int causal, int64_t chunk_tokens,
+    int nchunks, float* __restrict__ ws) {
+  __shared__ __align__(16) _Float16 cbL[256 * 4];
+  __shared__ __align__(16) _Float16 Kt[PU * D];  // [key][dim]
+  __shared__ __align__(16) _Float16 Vt[D * PU];  // [dim][key]
+  __shared__ float knL[PU], vnL[PU];
+  __shared__ float qscr[PW * 64 * 17];  // per-lane scratch of the query rotation (stride 17: no bank conflicts)
+  const int tid = fq_tid(), lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = fq_bid_x(), rb = fq_bid_y(), slab = fq_bid_z();
+  const int b = slab / Hkv, g = slab - b * Hkv;
+  const int G = Hq / Hkv, rows = G * Sq;
+  const int64_t slab0 = (int64_t)slab * T;
+  const int col = lane & 15, hq = lane >> 4;
+  // this lane's query row (an MFMA column)
+  const int r = rb * PROWS + 16 * w + col;
+  const bool row_ok = r < rows;
+  const int hl = row_ok ? r / Sq : 0, qi = row_ok ? r - hl * Sq : 0;
+  const int64_t lim = causal ? T - Sq + qi : T - 1;  // last key this row sees
+  // key range of the workgroup (causal: no row of the block sees past its last row's limit)
+  const int64_t t_begin = (int64_t)chunk * chunk_tokens;
+  int64_t t_end = t_begin + chunk_tokens < T ? t_begin + chunk_tokens : T;
+  if (causal) {
+    const int rlast = rb * PROWS + PROWS - 1 < rows - 1 ? rb * PROWS + PROWS - 1 : rows - 1;
+    // the largest query index among the block's rows
+    int imax = 0;
+    for (int rr = rb * PROWS; rr <= rlast && imax < Sq - 1; rr++) {
+      const int ii = rr % Sq;
+      imax = ii > imax ? ii : imax;
+    }
+    const int64_t kmax = T - Sq + imax + 1;
+    t_end = t_end < kmax ? t_end : kmax;
+  }
+
+  // codebook
+  for (int e = tid; e < 256 * 4 / 8; e += PW * 64)
+    reinterpret_cast<uint4*>(cbL)[e] = reinterpret_cast<const uint4*>(cw16)[e];
+
+  // B operands of QK: column col = query row r, k = 8 hq + j is dimension 32 s + 8 hq + j
+  // of the rotated query (Pi q) * scale * log2(e), split fp16 hi + lo
+  half8 qhi[2], qlo[2];
+  {
+    float qv[D];
+    const _Float16* qr = q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D;
+#pragma unroll
+    for (int e = 0; e < D; e++) qv[e] = row_ok ? (float)qr[e] : 0.0f;
+    // one rotated dimension per iteration (not unrolled: all 16 rows of Pi at once
+    // would not fit in registers); each lane parks its 16 values in its own LDS slots
+#pragma unroll 1
+    for (int jj = 0; jj < 16; jj++) {
+      const int d = 32 * (jj >> 3) + 8 * hq + (jj & 7);
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D; e++) a = __builtin_fmaf(pi32[d * D + e], qv[e], a);
+      qscr[tid * 17 + jj] = a * qscale;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; s++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float a = qscr[tid * 17 + 8 * s + j];
+        const _Float16 h = (_Float16)a;
+        qhi[s][j] = h;
+        qlo[s][j] = (_Float16)(a - (float)h);
+      }
+  }
+
+  const float NEG = -__builtin_huge_valf();
+  float m_run = NEG, l_run = 0.0f;
+  f32x4 O[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // unit loads (registers), one unit ahead
+  const int lk = tid >> 2, lp = tid & 3;
+  auto load_unit = [&](int64_t t0, UnitRegs& u) {
+    const int64_t nt = t_end - t0;
+    const int64_t key = slab0 + t0 + (lk < nt ? lk : nt - 1);
+    u.kw = reinterpret_cast<const uint32_t*>(kc + key * 16)[lp];
+    u.vw = reinterpret_cast<const uint32_t*>(vc + key * 16)[lp];
+    if (tid < PU) {
+      const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
+      u.kn = kn[kk];
+      u.vn = vn[kk];
+    }
+  };
+  UnitRegs cur{}, nxt{};
+  if (t_begin < t_end) load_unit(t_begin, cur);
+  __syncthreads();  // codebook in place
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += PU) {
+    // ---- decode the unit into LDS
+    __syncthreads();  // the previous unit's tiles are no longer read
+    {
+      const uint32_t kw = cur.kw, vw = cur.vw;
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const uint32_t kcode = (kw >> (8 * c)) & 0xffu, vcode = (vw >> (8 * c)) & 0xffu;
+        const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
+        *reinterpret_cast<half4*>(Kt + lk * D + d0) = *reinterpret_cast<const half4*>(cbL + kcode * 4);
+        const half4 vv = *reinterpret_cast<const half4*>(cbL + vcode * 4);
+#pragma unroll
+        for (int e = 0; e < 4; e++) Vt[(d0 + e) * PU + lk] = vv[e];
+      }
+      if (tid < PU) {
+        knL[tid] = (float)cur.kn;
+        vnL[tid] = (float)cur.vn;
+      }
+    }
+    if (t0 + PU < t_end) load_unit(t0 + PU, nxt);
+    __syncthreads();
+
+    const int64_t nt = t_end - t0;
+    const bool need_mask = nt < PU || (causal && t0 + PU - 1 > T - Sq);
+    // ---- S^T = K Qrot^T: tile a covers keys 16 a .. 16 a + 15; the lane holds keys
+    // 16 a + 4 hq + i of query column col
+    float sc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; a++) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        const half8 A = *reinterpret_cast<const half8*>(Kt + (16 * a + col) * D + 32 * s + 8 * hq);
+        acc = mfma16(A, qhi[s], acc);
+        acc = mfma16(A, qlo[s], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int kk = 16 * a + 4 * hq + i;
+        float v = acc[i] * knL[kk];
+        if (need_mask && (kk >= nt || t0 + kk > lim)) v = NEG;
+        sc[a][i] = row_ok ? v : NEG;
+      }
+    }
+    float mx = NEG;
+#pragma unroll
+    for (int a = 0; a < 4; a++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) mx = fmaxf(mx, sc[a][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == NEG ? 0.0f : m_new;  // a column with no key yet: nothing to scale
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 4; dt++) O[dt] *= alpha;
+    m_run = m_new;
+    // ---- O^T += V^T P'^T over two 32-key steps
+#pragma unroll
+    for (int st = 0; st < 2; st++) {
+      half8 P;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int a = 2 * st + (j >> 2), i = j & 3;
+        const float p = __builtin_amdgcn_exp2f(sc[a][i] - m_use);
+        l_run += p;
+        P[j] = (_Float16)(p * vnL[16 * a + 4 * hq + i]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; dt++) {
+        const _Float16* vrow = Vt + (16 * dt + col) * PU + 32 * st + 4 * hq;
+        const half4 lo4 = *reinterpret_cast<const half4*>(vrow);
+        const half4 hi4 = *reinterpret_cast<const half4*>(vrow + 16);
+        const half8 A = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        O[dt] = mfma16(A, P, O[dt]);
+      }
+    }
+    cur = nxt;
+  }
+
+  // ---- this row's partial record: O^T rows 16 dt + 4 hq + i of column col
+  float l = l_run;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const int64_t bh = ((int64_t)b * Hq + (int64_t)g * G + hl) * Sq + qi;
+  float* rec = ws + (bh * nchunks + chunk) * REC_F;
+  if (hq == 0) {
+    rec[0] = m_run;
+    rec[1] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; dt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) rec[2 + 16 * dt + 4 * hq + i] = O[dt][i];
+}
+
+}  // namespace
+
+PrefillPlan prefill_plan(int B, int Hq, int Hkv, int Sq, int64_t T) {
+  const int rows = (Hq / Hkv) * Sq;
+  const int rblocks = (rows + PROWS - 1) / PROWS;
+  const int64_t wgs = (int64_t)rblocks * B * Hkv;
+  int64_t nc = (1024 + wgs - 1) / wgs;
+  const int64_t most = (T + 511) / 512;
+  if (nc > most) nc = most;
+  if (nc < 1) nc = 1;
+  int64_t ct = (T + nc - 1) / nc;
+  ct = (ct + PU - 1) / PU * PU;
+  nc = (T + ct - 1) / ct;
+  return PrefillPlan{(int)nc, ct, rblocks};
+}
+
+bool prefill_supported(const fq_codebook* cb) { return cb->k == 4 && cb->bits == 8; }
+
+hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
+                          int causal, float scale, float* out, void* workspace, hipStream_t s) {
+  const PrefillPlan p = prefill_plan(B, Hq, Hkv, Sq, T);
+  const float qscale = scale * 1.4426950408889634f;  // log2(e)
+  hipLaunchKernelGGL(attn_prefill_k4b8, dim3((unsigned)p.nchunks, (unsigned)p.rblocks, (unsigned)(B * Hkv)),
+                     dim3(PW * 64), 0, s, reinterpret_cast<const _Float16*>(q), qscale, cb->pi32, k_codes,
+                     reinterpret_cast<const _Float16*>(k_norms), v_codes, reinterpret_cast<const _Float16*>(v_norms),
+                     cb->cw16, Hq, Hkv, T, Sq, causal, p.chunk_tokens, p.nchunks,
+                     reinterpret_cast<float*>(workspace));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_attn_combine(reinterpret_cast<const float*>(workspace), cb->pi32, (int64_t)B * Hq * Sq, p.nchunks,
+                             out, s);
+}
+
+}  // namespace fq
