@@ -20,7 +20,8 @@ decode loop is timed as well: per step the new token's K and V are encoded into
 their slots (fq_encode_scatter) and attention runs over each sequence's valid
 length (fq_attn_decode_varlen).  Along the rate axis (frozen initial codebooks
 from b = 4 down to 0.22 bits per coordinate) the same tensor's encode, decode
-and attention are timed as well, and so is the codebook construction
+and attention are timed as well, and so are prefill attention (64 causal
+queries per head on the 32k cache) and the codebook construction
 (fq_codebook_train) at larger shapes.  The CPU oracle is timed on a bounded sample
 (rank 0, one GPU only).
 
@@ -61,6 +62,7 @@ def parse():
     ap.add_argument("--no-decode-loop", action="store_true", help="skip the append + varlen attention timing")
     ap.add_argument("--no-rate-axis", action="store_true", help="skip the rate-axis timings")
     ap.add_argument("--no-build", action="store_true", help="skip the codebook-construction timings")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill attention timing")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -238,6 +240,7 @@ def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
 # Codebook-construction shapes: (k, N, training blocks); starts are the frozen initial codebooks.
 BUILD_SHAPES = [(4, 1024, 262144), (4, 16384, 1048576), (64, 16384, 262144)]
 FP64_VALU_PEAK_T = 78.6  # dense fp64 vector FLOP/s of the MI355X, in T
+FP16_MFMA_PEAK_T = 2500.0  # dense fp16 matrix FLOP/s of the MI355X, in T
 
 
 def build_timings(fq, workloads, dev, stream, iters: int = 5):
@@ -424,6 +427,42 @@ def main():
                          "frac": abytes / t_att / 1e9 / HBM_PEAK_GBPS,
                          "traffic": measured_traffic("attn_k4b8", "fq_attn.hip")},
         }
+
+        # ------------------------------------------------------------ prefill over the same cache
+        # 64 causal queries per head (a 64-token chunk appended to the 32k cache): useful
+        # work 4 * 64 flops per (query, visible key) pair (QK and PV); the kernel issues
+        # 1.5x that on the matrix core (the query enters as fp16 hi + lo).
+        if not args.no_prefill:
+            Sq = 64
+            qp = torch.from_numpy(np.random.default_rng(107).standard_normal((B, Hq, Sq, D)).astype(np.float16)).to(dev)
+            po = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
+            pws = torch.empty(fq.fq_attn_prefill_workspace_bytes(cb.handle, B, Hq, Hkv, Sq, Ta), dtype=torch.uint8,
+                              device=dev)
+            flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+            tp = []
+            for it in range(args.attn_iters + 3):
+                flush.max()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fq.fq_attn_prefill(cb.handle, qp, kcs, kns, vcs, vns, B, Hq, Hkv, Sq, Ta, True, 0.125, po, pws,
+                                   stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if it >= 3:
+                    tp.append(e0.elapsed_time(e1))
+            t_p = float(np.median(tp)) / 1e3
+            pairs = B * Hq * sum(Ta - Sq + i + 1 for i in range(Sq))
+            useful = 4.0 * D * pairs
+            line["prefill_b16_t32k_q64"] = {
+                "workload": "B=16, Hq=32, Hkv=4, T=32768, 64 causal queries per head (the last 64 positions), "
+                            "k=4, N=256 codes + fp16 norms, caches evicted before every launch",
+                "us_per_step": t_p * 1e6, "query_key_pairs": pairs,
+                "roofline": {"kernel": "attn_prefill_k4b8 (+ attn_combine)", "bound": "mfma",
+                             "achieved": useful / t_p / 1e12, "peak": FP16_MFMA_PEAK_T, "unit": "TFLOP/s",
+                             "frac": useful / t_p / 1e12 / FP16_MFMA_PEAK_T, "traffic": None,
+                             "issued_TFLOPs": 1.5 * useful / t_p / 1e12},
+            }
+            del flush
 
         # ------------------------------------------------------------ decode loop over the same cache
         # One decode step per sequence: the new token's K and V go to slot len_b of their

@@ -32,6 +32,10 @@ constexpr int PW = 4;       // waves per workgroup
 constexpr int PU = 64;      // keys per unit
 constexpr int PROWS = 16 * PW;  // query rows per workgroup
 constexpr int REC_F = 2 + D;
+// LDS row strides (halves): 128-byte rows would put the 16 rows one MFMA operand read
+// touches on the same banks; 144- and 136-byte rows spread them over all 64 banks
+constexpr int KS = D + 8;   // K tile [key][KS]
+constexpr int VS = PU + 4;  // V tile [dim][VS]
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -48,14 +52,14 @@ struct UnitRegs {
   _Float16 kn, vn;
 };
 
-__global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
+__global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
     const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
     const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T, int Sq, int causal, int64_t chunk_tokens,
     int nchunks, float* __restrict__ ws) {
   __shared__ __align__(16) _Float16 cbL[256 * 4];
-  __shared__ __align__(16) _Float16 Kt[PU * D];  // [key][dim]
-  __shared__ __align__(16) _Float16 Vt[D * PU];  // [dim][key]
+  __shared__ __align__(16) _Float16 Kt[PU * KS];  // [key][dim]
+  __shared__ __align__(16) _Float16 Vt[D * VS];   // [dim][key]
   __shared__ float knL[PU], vnL[PU];
   __shared__ float qscr[PW * 64 * 17];  // per-lane scratch of the query rotation (stride 17: no bank conflicts)
   const int tid = fq_tid(), lane = tid & 63;
@@ -94,9 +98,14 @@ __global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
   half8 qhi[2], qlo[2];
   {
     float qv[D];
-    const _Float16* qr = q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D;
+    // hl = qi = 0 for a row past the block's end: the address stays inside q
+    const uint4* qr = reinterpret_cast<const uint4*>(q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D);
 #pragma unroll
-    for (int e = 0; e < D; e++) qv[e] = row_ok ? (float)qr[e] : 0.0f;
+    for (int e8 = 0; e8 < D / 8; e8++) {
+      const half8 h8 = __builtin_bit_cast(half8, qr[e8]);
+#pragma unroll
+      for (int j = 0; j < 8; j++) qv[8 * e8 + j] = row_ok ? (float)h8[j] : 0.0f;
+    }
     // one rotated dimension per iteration (not unrolled: all 16 rows of Pi at once
     // would not fit in registers); each lane parks its 16 values in its own LDS slots
 #pragma unroll 1
@@ -150,10 +159,10 @@ __global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
       for (int c = 0; c < 4; c++) {
         const uint32_t kcode = (kw >> (8 * c)) & 0xffu, vcode = (vw >> (8 * c)) & 0xffu;
         const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
-        *reinterpret_cast<half4*>(Kt + lk * D + d0) = *reinterpret_cast<const half4*>(cbL + kcode * 4);
+        *reinterpret_cast<half4*>(Kt + lk * KS + d0) = *reinterpret_cast<const half4*>(cbL + kcode * 4);
         const half4 vv = *reinterpret_cast<const half4*>(cbL + vcode * 4);
 #pragma unroll
-        for (int e = 0; e < 4; e++) Vt[(d0 + e) * PU + lk] = vv[e];
+        for (int e = 0; e < 4; e++) Vt[(d0 + e) * VS + lk] = vv[e];
       }
       if (tid < PU) {
         knL[tid] = (float)cur.kn;
@@ -163,8 +172,16 @@ __global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
     if (t0 + PU < t_end) load_unit(t0 + PU, nxt);
     __syncthreads();
 
+    // keys of this unit the lane's row may see: kk <= bound (32-bit; -1 = none)
     const int64_t nt = t_end - t0;
-    const bool need_mask = nt < PU || (causal && t0 + PU - 1 > T - Sq);
+    const bool need_mask = nt < PU || (causal && t0 + PU - 1 > T - Sq) || !row_ok;
+    int bound = PU - 1;
+    if (need_mask) {
+      const int64_t bl = lim - t0, bn = nt - 1;
+      int64_t bb = bl < bn ? bl : bn;
+      bb = bb < -1 ? -1 : (bb > PU - 1 ? PU - 1 : bb);
+      bound = row_ok ? (int)bb : -1;
+    }
     // ---- S^T = K Qrot^T: tile a covers keys 16 a .. 16 a + 15; the lane holds keys
     // 16 a + 4 hq + i of query column col
     float sc[4][4];
@@ -173,17 +190,18 @@ __global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 2; s++) {
-        const half8 A = *reinterpret_cast<const half8*>(Kt + (16 * a + col) * D + 32 * s + 8 * hq);
+        const half8 A = *reinterpret_cast<const half8*>(Kt + (16 * a + col) * KS + 32 * s + 8 * hq);
         acc = mfma16(A, qhi[s], acc);
         acc = mfma16(A, qlo[s], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int kk = 16 * a + 4 * hq + i;
-        float v = acc[i] * knL[kk];
-        if (need_mask && (kk >= nt || t0 + kk > lim)) v = NEG;
-        sc[a][i] = row_ok ? v : NEG;
-      }
+      for (int i = 0; i < 4; i++) sc[a][i] = acc[i] * knL[16 * a + 4 * hq + i];
+    }
+    if (need_mask) {  // uniform: the last units of a range, the causal diagonal, short blocks
+#pragma unroll
+      for (int a = 0; a < 4; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) sc[a][i] = 16 * a + 4 * hq + i <= bound ? sc[a][i] : NEG;
     }
     float mx = NEG;
 #pragma unroll
@@ -212,7 +230,7 @@ __global__ __launch_bounds__(PW * 64) void attn_prefill_k4b8(
       }
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
-        const _Float16* vrow = Vt + (16 * dt + col) * PU + 32 * st + 4 * hq;
+        const _Float16* vrow = Vt + (16 * dt + col) * VS + 32 * st + 4 * hq;
         const half4 lo4 = *reinterpret_cast<const half4*>(vrow);
         const half4 hi4 = *reinterpret_cast<const half4*>(vrow + 16);
         const half8 A = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
