@@ -107,9 +107,15 @@ def cpu_baseline(budget_s: float = 12.0):
     oc.encode(x[:2048], rot, cw, np.float16)
     t_cal = time.perf_counter() - t0
     n_s = int(min(len(x), max(2048, 2048 * budget_s / max(t_cal, 1e-3))) // 2048 * 2048)
-    t0 = time.perf_counter()
-    enc = oc.encode(x[:n_s], rot, cw, np.float16)
-    t_enc = time.perf_counter() - t0
+    # the whole tensor encodes in less than the budget on a many-core host: repeat the
+    # timed encode (at most 5 times) until the budget is spent
+    reps, t_enc = 0, 0.0
+    while reps < 5 and (reps == 0 or t_enc < budget_s):
+        t0 = time.perf_counter()
+        enc = oc.encode(x[:n_s], rot, cw, np.float16)
+        t_enc += time.perf_counter() - t0
+        reps += 1
+    t_enc /= reps
     t0 = time.perf_counter()
     oc.round_output(oc.decode(enc.codes, enc.norms, rot, cw), np.float16)
     t_dec = time.perf_counter() - t0
@@ -126,9 +132,9 @@ def cpu_baseline(budget_s: float = 12.0):
     t_att = time.perf_counter() - t0
     per_vec = t_enc / n_s + t_dec / n_s + t_att / (2 * T)
     return {"value": 1.0 / per_vec, "unit": "vectors/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle encode+decode of the first {n_s} of the 294912 vectors plus attention of one "
-                      f"(layer, head) query over its {T} keys/values; per-vector times summed "
-                      f"(encode {t_enc:.2f}s, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
+            "sample": f"oracle encode (x{reps}) + decode of the first {n_s} of the 294912 vectors plus attention "
+                      f"of one (layer, head) query over its {T} keys/values; per-vector times summed "
+                      f"(encode {t_enc:.2f}s per pass, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
 
 
 def workload_timings(fq, workloads, dev, stream, reps: int = 5):
