@@ -442,7 +442,7 @@ fq_status attn_check_sizes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_
 
 FQ_EXPORT size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   if (attn_check_sizes(cb, B, Hq, Hkv, T) != FQ_OK || T == 0 || B == 0) return 0;
-  return fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_plan(cb, B, Hq, Hkv, T).nchunks);
+  return fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
 }
 
 namespace {
@@ -459,7 +459,7 @@ fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_cod
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_norms) || !aligned16(v_codes) || !aligned16(v_norms) ||
       !aligned16(out))
     return FQ_ERR_ARG;
-  const size_t need = fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_plan(cb, B, Hq, Hkv, T).nchunks);
+  const size_t need = fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FQ_ERR_WORKSPACE;
   const fq_status ds = check_device(cb);
   if (ds != FQ_OK) return ds;

@@ -47,6 +47,82 @@ __device__ inline int64_t valid_keys(const int32_t* __restrict__ lens, int b, in
   return L < 0 ? 0 : (L < T ? L : T);
 }
 
+// Balanced split of the fast kernel's workgroups under per-batch lengths.  Batch b's
+// slabs (one per KV head) hold u_b = ceil(L_b / 64) units of 64 keys (a wave's unit).
+// Of the W workgroups of the launch, every non-empty slab gets
+//     n_b = min(u_b, cap, 1 + floor(u_b W' / U))   (U = Hkv sum_b u_b, W' = W - Hkv #{b : u_b > 0})
+// pieces (cap: the records a (batch, head) has room for), so sum n <= W; piece p covers
+// units [p u_b / n_b, (p + 1) u_b / n_b).  The largest share is then within one unit of
+// the mean, whatever the lengths; a split over the slab capacity would leave the
+// workgroups of long slabs with all the work.  Every quantity is wave-uniform; each
+// wave computes it from lens on its own.
+constexpr int BAL_UNIT = 64;
+struct VarlenTotals {
+  int64_t U, Wp, cap;
+};
+
+__device__ inline int64_t bal_units(const int32_t* __restrict__ lens, int b, int64_t T) {
+  return (valid_keys(lens, b, T) + BAL_UNIT - 1) / BAL_UNIT;
+}
+
+__device__ inline int64_t bal_pieces(int64_t ub, const VarlenTotals& t) {
+  if (ub == 0) return 0;
+  int64_t n = 1 + ub * t.Wp / t.U;  // U >= ub > 0
+  n = n < ub ? n : ub;
+  return n < t.cap ? n : t.cap;
+}
+
+__device__ inline VarlenTotals varlen_totals(const int32_t* __restrict__ lens, int B, int Hkv, int64_t T, int64_t W,
+                                             int64_t cap, int lane) {
+  long long u = 0, e = 0;
+  for (int b = lane; b < B; b += 64) {
+    const int64_t ub = bal_units(lens, b, T);
+    u += ub;
+    e += ub > 0 ? 1 : 0;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    u += __shfl_xor(u, m);
+    e += __shfl_xor(e, m);
+  }
+  return VarlenTotals{(int64_t)Hkv * u, W - (int64_t)Hkv * e, cap};
+}
+
+// The piece of workgroup `wid`: batch, KV head, piece index, pieces and units of its
+// slab.  False when the workgroup has no piece.
+__device__ inline bool varlen_piece(const int32_t* __restrict__ lens, int B, int Hkv, int64_t T,
+                                    const VarlenTotals& t, int64_t wid, int lane, int& b, int& g, int& p, int64_t& n,
+                                    int64_t& u) {
+  int64_t base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int64_t ub = bb < B ? bal_units(lens, bb, T) : 0;
+    const int64_t nb = bal_pieces(ub, t);
+    const long long c = (long long)Hkv * nb;
+    long long incl = c;  // inclusive scan over the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const int64_t tot = __shfl(incl, 63);
+    if (wid < base + tot) {
+      const uint64_t hit = __ballot(base + incl > wid);
+      const int L = (int)__builtin_ctzll(hit);
+      const int64_t start = base + __shfl(incl - c, L);
+      n = __shfl((long long)nb, L);
+      u = __shfl((long long)ub, L);
+      const int64_t r = wid - start;
+      b = b0 + L;
+      g = (int)(r / n);
+      p = (int)(r - (int64_t)g * n);
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
 // Dims [dim0, dim0+8) of the concatenated codewords of vector `vec`.
 template <int K>
 __device__ inline half8 gather8(const _Float16* __restrict__ cbL, const uint8_t* __restrict__ codes, int64_t vec,
@@ -257,24 +333,37 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
 // weights go to LDS; then every lane (one dimension) sums the chunks'
 // accumulators with the loads of 8 chunks in flight.
 constexpr int COMB_W = 1024;  // chunks whose weights are kept in LDS
+// stride: records per (batch, query head); with nbh (the fast kernel's balanced split
+// under per-batch lengths) only the first nbh[batch] of them exist, else all `stride`.
 __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws, const float* __restrict__ pi32,
-                                                   int nchunks, float* __restrict__ out) {
+                                                   int stride, float* __restrict__ out,
+                                                   const int32_t* __restrict__ nbh, int Hq) {
   constexpr int PRE = 16;  // accumulators of the first chunks, loaded before anything waits
   __shared__ float ot[D];
   __shared__ float wsh[COMB_W];
   const int64_t bh = fq_bid_x();
   const int lane = fq_tid();
   const float NEG = -__builtin_huge_valf();
-  const float* rec = ws + bh * nchunks * REC;
+  const float* rec = ws + bh * stride * REC;
+  // The first records' loads go out together with the record count's; records past
+  // the count may hold anything and are dropped by selects below.
   float v[PRE];
 #pragma unroll
-  for (int e = 0; e < PRE; e++) v[e] = e < nchunks ? rec[(int64_t)e * REC + 2 + lane] : 0.f;
+  for (int e = 0; e < PRE; e++) v[e] = e < stride ? rec[(int64_t)e * REC + 2 + lane] : 0.f;
+  // max and sum of chunk `lane` (the common case has at most 64 chunks: one round trip)
+  float m0 = lane < stride ? rec[(int64_t)lane * REC] : NEG;
+  float l0 = lane < stride ? rec[(int64_t)lane * REC + 1] : 0.f;
   float pc[D];  // column `lane` of Pi
 #pragma unroll
   for (int j = 0; j < D; j++) pc[j] = pi32[j * D + lane];
-  // max and sum of chunk `lane` (the common case has at most 64 chunks: one round trip)
-  const float m0 = lane < nchunks ? rec[(int64_t)lane * REC] : NEG;
-  const float l0 = lane < nchunks ? rec[(int64_t)lane * REC + 1] : 0.f;
+  int nchunks = stride;
+  if (nbh) {
+    nchunks = nbh[bh / Hq];
+#pragma unroll
+    for (int e = 0; e < PRE; e++) v[e] = e < nchunks ? v[e] : 0.f;
+    m0 = lane < nchunks ? m0 : NEG;
+    l0 = lane < nchunks ? l0 : 0.f;
+  }
   float M = m0;
   for (int c = lane + 64; c < nchunks; c += 64) M = fmaxf(M, rec[(int64_t)c * REC]);
 #pragma unroll
@@ -516,21 +605,37 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
                                                         const uint8_t* __restrict__ kc,
                                                         const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc,
                                                         const _Float16* __restrict__ vn,
-                                                        const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T,
-                                                        const int32_t* __restrict__ lens, int64_t wg_tokens, int nrec,
-                                                        float* __restrict__ ws) {
+                                                        const _Float16* __restrict__ cw16, int B, int Hq, int Hkv,
+                                                        int64_t T, const int32_t* __restrict__ lens, int64_t wg_tokens,
+                                                        int nrec, int gx, float* __restrict__ ws,
+                                                        int32_t* __restrict__ nbh) {
   __shared__ __align__(16) char wbuf[AW * NBUF * U_BYTES];
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ float sm[AW * GF], sl[AW * GF];
   const int tid = fq_tid(), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rx = fq_bid_x(), g = fq_bid_y(), b = fq_bid_z();
+  int rx = fq_bid_x(), g = fq_bid_y(), b = fq_bid_z();
   const int G = Hq / Hkv;
+  int64_t t_begin, t_end;
+  if (lens) {
+    // balanced split over the valid keys (record index = piece index, stride nrec)
+    const int64_t W = (int64_t)gx * Hkv * B;
+    const VarlenTotals tt = varlen_totals(lens, B, Hkv, T, W, nrec, lane);
+    int64_t pn = 0, pu = 0;
+    const int64_t wid = ((int64_t)b * Hkv + g) * gx + rx;
+    // records per head of every batch, for the combine (workgroup i < B writes batch i's,
+    // empty batches included)
+    if (tid == 0 && wid < B) nbh[wid] = (int32_t)bal_pieces(bal_units(lens, (int)wid, T), tt);
+    if (!varlen_piece(lens, B, Hkv, T, tt, wid, lane, b, g, rx, pn, pu)) return;
+    const int64_t Lb = valid_keys(lens, b, T);
+    t_begin = BAL_UNIT * (rx * pu / pn);
+    t_end = BAL_UNIT * ((rx + 1) * pu / pn);
+    t_end = t_end < Lb ? t_end : Lb;
+  } else {
+    t_begin = (int64_t)rx * wg_tokens;
+    t_end = (t_begin + wg_tokens) < T ? (t_begin + wg_tokens) : T;
+  }
   const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
-  const int64_t Tb = valid_keys(lens, b, T);
-  const int64_t t_begin = (int64_t)rx * wg_tokens;
-  int64_t t_end = (t_begin + wg_tokens) < Tb ? (t_begin + wg_tokens) : Tb;
-  if (t_end < t_begin) t_end = t_begin;  // past the valid keys: an empty record
   // this wave's units: workgroup units w, w + AW, w + 2 AW, ...
   const int nu_wg = (int)((t_end - t_begin + UT - 1) / UT);
   const int nu = nu_wg > w ? (nu_wg - w + AW - 1) / AW : 0;
@@ -779,7 +884,8 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
 
 hipError_t launch_attn_combine(const float* ws, const float* pi32, int64_t rows, int nchunks, float* out,
                                hipStream_t s) {
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows), dim3(64), 0, s, ws, pi32, nchunks, out);
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)rows), dim3(64), 0, s, ws, pi32, nchunks, out,
+                     static_cast<const int32_t*>(nullptr), 1);
   return hipGetLastError();
 }
 
@@ -788,8 +894,15 @@ size_t attn_records_bytes(int B, int Hq, int nchunks) {
 }
 
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks) {
-  (void)Hkv;  // chunk partial records only
-  return attn_records_bytes(B, Hq, nchunks);
+  (void)Hkv;
+  // partial records, then one record count per batch (balanced split under lengths)
+  return attn_records_bytes(B, Hq, nchunks) + (((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255);
+}
+
+int attn_record_stride(const AttnPlan& p) {
+  // the fast path's balanced split under per-batch lengths uses up to one record per
+  // 512-key unit of a slab; sized for it in every case so one workspace serves both
+  return p.fast ? p.fast_chunks : p.nchunks;
 }
 #endif
 
@@ -833,12 +946,20 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   const _Float16* vn = reinterpret_cast<const _Float16*>(v_norms);
   hipError_t e;
   if (plan.fast) {
+    // without lengths the records of a (batch, head) are the grid's chunks; with them,
+    // the balanced split's pieces at a stride of one per 512-key unit
+    const int stride = lens ? plan.fast_chunks : plan.nchunks;
+    // batches' record counts after the records (balanced split only)
+    int32_t* nbh = lens ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) +
+                                                     attn_records_bytes(B, Hq, plan.fast_chunks))
+                        : nullptr;
     hipLaunchKernelGGL(attn_k4b8, grid, dim3(AW * 64), 0, s, qh, reinterpret_cast<const uint4*>(cb->rot16), qscale,
-                       k_codes, kn, v_codes, vn,
-                       cb->cw16, Hq, Hkv, T, lens, plan.chunk_tokens, plan.nchunks, ws);
+                       k_codes, kn, v_codes, vn, cb->cw16, B, Hq, Hkv, T, lens, plan.chunk_tokens, stride,
+                       plan.nchunks, ws, nbh);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);
+    hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, stride, out,
+                       static_cast<const int32_t*>(nbh), Hq);
     return hipGetLastError();
   }
 #define FQ_ATT(KK)                                                                                                \
@@ -856,7 +977,8 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
   }
 #undef FQ_ATT
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out);
+  hipLaunchKernelGGL(attn_combine, dim3((unsigned)(B * Hq)), dim3(64), 0, s, ws, cb->pi32, plan.nchunks, out,
+                     static_cast<const int32_t*>(nullptr), Hq);
   return hipGetLastError();
 }
 #endif

@@ -91,6 +91,8 @@ struct AttnPlan {
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
+// Partial records per (batch, query head) the workspace must hold for this plan.
+int attn_record_stride(const AttnPlan& p);
 
 // Workgroups of `kernel` (block threads, lds bytes of dynamic LDS) resident at once on
 // `device`: per-CU occupancy times the CU count, at least 1.  Cached per (kernel, block,
