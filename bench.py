@@ -289,7 +289,7 @@ def build_timings(fq, workloads, dev, stream, iters: int = 5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}), flush=True)
         sys.exit(2)
     import torch
 

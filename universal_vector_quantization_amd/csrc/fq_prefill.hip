@@ -39,16 +39,18 @@ constexpr int VS = PU + 4;  // V tile [dim][VS]
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline f32x4 mfma16(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Per-thread registers of one unit's records: key `lane / 4`, record dword `lane % 4`
-// of K and of V, and (threads < 64) the two norms of key `tid`.
+// Per-thread registers of one unit's records: threads 0..127 decode K, 128..255 V;
+// thread t of a half takes keys 2 (t / 4) and 2 (t / 4) + 1, record dword t % 4 of each,
+// and (threads < 64) the two norms of key `tid`.
 struct UnitRegs {
-  uint32_t kw, vw;
+  uint32_t w0, w1;
   _Float16 kn, vn;
 };
 
@@ -134,12 +136,15 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // unit loads (registers), one unit ahead
-  const int lk = tid >> 2, lp = tid & 3;
+  const bool vhalf = tid >= 128;  // wave-uniform: waves 2, 3 decode V
+  const int kp = (tid & 127) >> 2, lp = tid & 3;
+  const uint8_t* __restrict__ store = vhalf ? vc : kc;
   auto load_unit = [&](int64_t t0, UnitRegs& u) {
     const int64_t nt = t_end - t0;
-    const int64_t key = slab0 + t0 + (lk < nt ? lk : nt - 1);
-    u.kw = reinterpret_cast<const uint32_t*>(kc + key * 16)[lp];
-    u.vw = reinterpret_cast<const uint32_t*>(vc + key * 16)[lp];
+    const int64_t key0 = slab0 + t0 + (2 * kp < nt ? 2 * kp : nt - 1);
+    const int64_t key1 = slab0 + t0 + (2 * kp + 1 < nt ? 2 * kp + 1 : nt - 1);
+    u.w0 = reinterpret_cast<const uint32_t*>(store + key0 * 16)[lp];
+    u.w1 = reinterpret_cast<const uint32_t*>(store + key1 * 16)[lp];
     if (tid < PU) {
       const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
       u.kn = kn[kk];
@@ -154,15 +159,23 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
     // ---- decode the unit into LDS
     __syncthreads();  // the previous unit's tiles are no longer read
     {
-      const uint32_t kw = cur.kw, vw = cur.vw;
+      const uint32_t w0 = cur.w0, w1 = cur.w1;
 #pragma unroll
       for (int c = 0; c < 4; c++) {
-        const uint32_t kcode = (kw >> (8 * c)) & 0xffu, vcode = (vw >> (8 * c)) & 0xffu;
+        const half4 c0 = *reinterpret_cast<const half4*>(cbL + ((w0 >> (8 * c)) & 0xffu) * 4);
+        const half4 c1 = *reinterpret_cast<const half4*>(cbL + ((w1 >> (8 * c)) & 0xffu) * 4);
         const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
-        *reinterpret_cast<half4*>(Kt + lk * KS + d0) = *reinterpret_cast<const half4*>(cbL + kcode * 4);
-        const half4 vv = *reinterpret_cast<const half4*>(cbL + vcode * 4);
+        if (vhalf) {
+          // the two keys' values of one dimension are neighbours in the transposed tile
 #pragma unroll
-        for (int e = 0; e < 4; e++) Vt[(d0 + e) * VS + lk] = vv[e];
+          for (int e = 0; e < 4; e++) {
+            const half2_t pair = {c0[e], c1[e]};
+            *reinterpret_cast<half2_t*>(Vt + (d0 + e) * VS + 2 * kp) = pair;
+          }
+        } else {
+          *reinterpret_cast<half4*>(Kt + (2 * kp) * KS + d0) = c0;
+          *reinterpret_cast<half4*>(Kt + (2 * kp + 1) * KS + d0) = c1;
+        }
       }
       if (tid < PU) {
         knL[tid] = (float)cur.kn;
@@ -212,10 +225,12 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == NEG ? 0.0f : m_new;  // a column with no key yet: nothing to scale
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
+    if (__ballot(m_new > m_run)) {  // some column's max moved (rare after the first units)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 4; dt++) O[dt] *= alpha;
+      for (int dt = 0; dt < 4; dt++) O[dt] *= alpha;
+    }
     m_run = m_new;
     // ---- O^T += V^T P'^T over two 32-key steps
 #pragma unroll
