@@ -454,6 +454,13 @@ __device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, u
 __device__ inline _Float16 hlo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ inline _Float16 hhi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
+// A value that is the same in every lane, declared so (scalar registers).
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // value of lane (l ^ 8) within its 16-lane row
 __device__ inline float swap8(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, true));
@@ -495,8 +502,8 @@ __device__ inline void attn_unit_load(const uint8_t* __restrict__ kc, const uint
 //   part, rows 4 grp + i.  After the recombination the lane holds whole scores
 //   of head col & 7 for tokens tb + own_tok + i (own_tok = 16 ah + 4 grp, ah =
 //   0 in lanes col < 8 and 1 in lanes col >= 8).
-// Returns the unit's max per head (over all lanes of the head); MASK: tokens at
-// or past nt score -inf.
+// Returns the maximum of the lane's own 8 scores; MASK: tokens at or past nt
+// score -inf.
 template <bool MASK>
 __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16* __restrict__ cbL,
                                     const half8 (&qb)[2], int nt, int col, int grp, bool hi_col, int own_tok,
@@ -527,11 +534,15 @@ __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16
       if constexpr (MASK) L[u][i] = (tb + own_tok + i) < nt ? L[u][i] : NEG;
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
-                   fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
-  mx = fmaxf(mx, swap8(mx));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  return fmaxf(mx, __shfl_xor(mx, 32));
+  return fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
+               fmaxf(fmaxf(L[1][0], L[1][1]), fmaxf(L[1][2], L[1][3])));
+}
+
+// Maximum over the lanes of one head (col & 7): partner lanes and the 4 row groups.
+__device__ inline float head_max(float v) {
+  v = fmaxf(v, swap8(v));
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
 }
 
 // Stage B of one unit: p = 2^(L - m), l += p, P' = p nu_v split hi + lo and
@@ -589,9 +600,8 @@ __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __r
   }
 }
 
-// Running-max update after a unit's max mx: the new max, the factor for the
-// lane's own sum and the factors for the accumulator rows 4 grp + i (head
-// 4 (grp & 1) + i).
+// Offset update to m_new = max(m_old, mx): the factor for the lane's own sum and
+// the factors for the accumulator rows 4 grp + i (head 4 (grp & 1) + i).
 __device__ inline void attn_rescale_factors(float m_old, float mx, int grp, float& m_new, float& a_own,
                                             float (&a_row)[4]) {
   m_new = fmaxf(m_old, mx);
@@ -635,6 +645,13 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     t_begin = (int64_t)rx * wg_tokens;
     t_end = (t_begin + wg_tokens) < T ? (t_begin + wg_tokens) : T;
   }
+  // the slab and range are the same in every lane: keep them (and all unit addresses) in
+  // scalar registers
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  rx = __builtin_amdgcn_readfirstlane(rx);
+  t_begin = uniform64(t_begin);
+  t_end = uniform64(t_end);
   const int64_t slab0 = ((int64_t)b * Hkv + g) * T;
   // this wave's units: workgroup units w, w + AW, w + 2 AW, ...
   const int nu_wg = (int)((t_end - t_begin + UT - 1) / UT);
@@ -645,8 +662,21 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     const int64_t r = t_end - unit_tok0(h);
     return r < UT ? (int)r : UT;
   };
+  // A full unit's loads: codes from wave-uniform bases plus the lane's byte offset, norms
+  // from a per-lane pointer that advances by a constant; partial units clamp per lane.
+  const uint32_t voff16 = (uint32_t)lane * 16u;
+  const char* nptr0 =
+      reinterpret_cast<const char*>((lane < 32 ? kn : vn) + slab0 + t_begin + (int64_t)w * UT + 2 * (lane & 31));
   auto load_unit = [&](int h) {
-    attn_unit_load(kc, vc, kn, vn, slab0 + unit_tok0(h), unit_nt(h), mybuf + (h & (NBUF - 1)) * U_BYTES, lane);
+    char* dst = mybuf + (h & (NBUF - 1)) * U_BYTES;
+    if (unit_nt(h) == UT) {
+      const int64_t tok0 = slab0 + unit_tok0(h);
+      lds_dma16_s(kc + tok0 * 16, voff16, dst + U_KC);
+      lds_dma16_s(vc + tok0 * 16, voff16, dst + U_VC);
+      lds_dma4(nptr0 + (int64_t)h * (AW * UT * 2), dst + U_KN);
+    } else {
+      attn_unit_load(kc, vc, kn, vn, slab0 + unit_tok0(h), unit_nt(h), dst, lane);
+    }
   };
 
   // The codebook (waves 0 and 1) and the first units go first, through the direct-to-LDS
@@ -709,14 +739,27 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   __syncthreads();  // the staging buffer is free again
   for (int h = pre_early; h < pre; h++) load_unit(h);
 
+  // Softmax offset per head, lazily updated: exponentials are taken as 2^(L - m_run)
+  // with m_run at least TAU above every score seen when it was last set, and m_run
+  // moves only when a score exceeds it, so every weight is at most 1 and the wave
+  // rescales its accumulators only when some head's scores rise by more than TAU
+  // (after the first unit, rarely).  The decision is wave-uniform (one ballot); the
+  // cross-lane maximum is formed only then.
+  constexpr float TAU = 4.0f;
   float m_run = -__builtin_huge_valf(), l_run = 0.f;
   f32x4 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto buf = [&](int h) -> const char* { return mybuf + (h & (NBUF - 1)) * U_BYTES; };
-  // pipeline state: scores Lc of unit h, its running max m_run, and the factors that
-  // move O and l_run from the previous max to m_run
+  // pipeline state: scores Lc of unit h, the offset m_run, and (when pend) the factors
+  // that move O and l_run from the previous offset to m_run
   float Lc[2][4], a_own = 0.f, a_row[4] = {0.f, 0.f, 0.f, 0.f};
+  bool pend = false;
+  // offset update after a unit whose lanes' own maxima are lmx
+  auto update_offset = [&](float lmx) {
+    pend = __builtin_amdgcn_ballot_w64(lmx > m_run) != 0;
+    if (pend) attn_rescale_factors(m_run, head_max(lmx) + TAU, grp, m_run, a_own, a_row);
+  };
   if (nu > 0) {
     if (pre == 3)
       __builtin_amdgcn_s_waitcnt(0x3f76);  // vmcnt(6): unit 0 landed
@@ -726,17 +769,23 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     const float mx = unit_nt(0) == UT ? attn_scores<false>(buf(0), cbL, qb, UT, col, grp, hi_col, own_tok, Lc)
                                       : attn_scores<true>(buf(0), cbL, qb, unit_nt(0), col, grp, hi_col, own_tok, Lc);
-    attn_rescale_factors(m_run, mx, grp, m_run, a_own, a_row);
+    update_offset(mx);
   }
-  // B(h) from scores Lcur at the current max, then the factors for unit h + 1 (max mxn)
+  auto apply_factors = [&]() {
+    if (pend) {
+      l_run *= a_own;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
+    }
+  };
+  // B(h) from scores Lcur at the current offset, then the offset update for unit h + 1
+  // (lane maxima mxn)
   auto finish_unit = [&](int h, float mxn, const float (&Lcur)[2][4]) {
-    l_run *= a_own;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
+    apply_factors();
     attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lcur, m_run, l_run, O);
-    attn_rescale_factors(m_run, mxn, grp, m_run, a_own, a_row);
+    update_offset(mxn);
   };
   // one steady-state iteration: unit h + 1 is full; its scores (into Lnxt) overlap unit h's PV
   auto step = [&](int h, const float (&Lcur)[2][4], float (&Lnxt)[2][4]) {
@@ -787,11 +836,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     h++;
   }
   if (nu > 0) {  // the last unit's PV (the only unit that can be partial)
-    l_run *= a_own;
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int dt = 0; dt < 4; dt++) O[dt][i] *= a_row[i];
+    apply_factors();
     const int ntl = unit_nt(h);
     if (ntl == UT)
       attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lc, m_run, l_run, O);

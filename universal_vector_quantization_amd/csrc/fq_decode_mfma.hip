@@ -25,6 +25,14 @@ namespace {
 constexpr int D = kD;
 constexpr int WAVES = 4;
 constexpr int LDS_CB_HALFS = 16384;  // codebooks up to N*k = 16384 (32 KiB) live in LDS
+// The stream decoder also holds codebooks of up to 64 KiB (k = 8, N = 4096) in LDS, in
+// one workgroup per CU of 12 waves for fp16 output or 8 for fp32 output (136 / 146 KiB
+// of LDS with the waves' rings and staging tiles): gathered from L1 / L2 instead,
+// every 16-byte codeword read fills a whole cache line, and that path ran at a third
+// of the write bandwidth.
+constexpr int LDS_CB_HALFS_BIG = 32768;
+constexpr int LDS_MAX_BYTES = 160 * 1024;
+constexpr int waves_big(bool of16) { return of16 ? 12 : 8; }
 constexpr int PF = 4;                // groups whose records are in flight ahead of the one decoded
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -119,7 +127,7 @@ __device__ inline void wait_vmcnt() {
 // the last group) ahead of use; the output leaves through the staging tile as
 // STORES 16-byte stores per group.  With these fixed counts the wait for a slot is
 // an exact vmcnt, and no compiler-inserted wait ever covers the ring.
-template <int K, bool NF16, bool OF16, int RW, bool CBL>
+template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV>
 struct StreamShape {
   static constexpr int ROWB = stage_row_bytes<OF16>();
   static constexpr int REC_BYTES = 32 * RW * 4;
@@ -130,17 +138,17 @@ struct StreamShape {
   static constexpr int WAIT_STEADY = (PF - 1) * LOADS + PF * STORES;
   static size_t lds_bytes(int N) {
     const size_t cb = CBL ? (size_t)((N * K * 2 + 15) & ~15) : 0;
-    return cb + (size_t)WAVES * (32 * ROWB + PF * SLOT_BYTES);
+    return cb + (size_t)WV * (32 * ROWB + PF * SLOT_BYTES);
   }
 };
 
-template <int K, bool NF16, bool OF16, int RW, bool CBL>
-__global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __restrict__ codes,
+template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV>
+__global__ __launch_bounds__(WV * 64) void decode_stream(const uint8_t* __restrict__ codes,
                                                             const void* __restrict__ norms, int64_t ngroups,
                                                             const _Float16* __restrict__ cw16,
                                                             const half8* __restrict__ dec_a, int N, int bits,
                                                             void* __restrict__ out, int nwg) {
-  typedef StreamShape<K, NF16, OF16, RW, CBL> S;
+  typedef StreamShape<K, NF16, OF16, RW, CBL, WV> S;
   constexpr int NC = 8 / K > 0 ? 8 / K : 1;
   constexpr int BITS = RW * K / 2;  // (64 / K) blocks of BITS bits fill RW words
   static_assert((D / K) * BITS == 32 * RW, "whole-word records");
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
   const int col = lane & 31, h = lane >> 5;
   const int cb_bytes = CBL ? ((N * K * 2 + 15) & ~15) : 0;
   char* stage = reinterpret_cast<char*>(smem) + cb_bytes + w * 32 * ROWB;
-  char* ring = reinterpret_cast<char*>(smem) + cb_bytes + WAVES * 32 * ROWB + w * PF * S::SLOT_BYTES;
+  char* ring = reinterpret_cast<char*>(smem) + cb_bytes + WV * 32 * ROWB + w * PF * S::SLOT_BYTES;
 
   half8 da[2][4][2];  // Pi^T operands (hi, lo) of both 32-row tiles and all 4 k-steps
 #pragma unroll
@@ -162,13 +170,13 @@ __global__ __launch_bounds__(WAVES * 64) void decode_stream(const uint8_t* __res
 #pragma unroll
       for (int p = 0; p < 2; p++) da[r][s][p] = dec_a[((r * 4 + s) * 2 + p) * 64 + lane];
   if constexpr (CBL)
-    for (int i = tid; i < cb_bytes / 16; i += WAVES * 64) smem[i] = reinterpret_cast<const uint4*>(cw16)[i];
+    for (int i = tid; i < cb_bytes / 16; i += WV * 64) smem[i] = reinterpret_cast<const uint4*>(cw16)[i];
   __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the operands are in registers before any ring load
   if constexpr (CBL) __syncthreads();
   const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
 
-  const int64_t step = (int64_t)nwg * WAVES;
-  int64_t g = (int64_t)fq_bid_x() * WAVES + w;
+  const int64_t step = (int64_t)nwg * WV;
+  int64_t g = (int64_t)fq_bid_x() * WV + w;
   if (g >= ngroups) return;
   int64_t left = (ngroups - 1 - g) / step + 1;  // groups of this wave
 
@@ -323,11 +331,12 @@ size_t generic_lds_bytes(int N, int K, bool cbl) {
   return cb + (size_t)WAVES * 32 * stage_row_bytes<OF16>();
 }
 
-// Persistent grid: the workgroups that fit at once, at most one per `work` units.
+// Persistent grid: the workgroups of `block` threads that fit at once, at most one
+// per `work` units.
 template <typename KernelT>
-hipError_t persistent_grid(const fq_codebook* cb, KernelT kernel, size_t lds, int64_t work, int64_t* wgs) {
+hipError_t persistent_grid(const fq_codebook* cb, KernelT kernel, int block, size_t lds, int64_t work, int64_t* wgs) {
   int64_t resident = 0;
-  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kernel), WAVES * 64, lds, cb->device, &resident);
+  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(kernel), block, lds, cb->device, &resident);
   if (e != hipSuccess) return e;
   *wgs = work < resident ? work : resident;
   if (*wgs < 1) *wgs = 1;
@@ -339,7 +348,8 @@ hipError_t launch_generic(const fq_codebook* cb, const uint8_t* codes, const voi
                           hipStream_t s) {
   const size_t lds = generic_lds_bytes<OF>(cb->N, K, CBL);
   int64_t wgs = 0;
-  hipError_t e = persistent_grid(cb, decode_mfma<K, NF, OF, CBL>, lds, ((n + 31) / 32 + WAVES - 1) / WAVES, &wgs);
+  hipError_t e =
+      persistent_grid(cb, decode_mfma<K, NF, OF, CBL>, WAVES * 64, lds, ((n + 31) / 32 + WAVES - 1) / WAVES, &wgs);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_mfma<K, NF, OF, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes, norms, n,
                      cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out, (int)wgs);
@@ -347,22 +357,32 @@ hipError_t launch_generic(const fq_codebook* cb, const uint8_t* codes, const voi
 }
 
 // RW > 0: the whole groups go to decode_stream, the last n mod 32 vectors to the
-// generic kernel; RW = 0: everything to the generic kernel.
-template <int K, bool NF, bool OF, int RW, bool CBL>
+// generic kernel; RW = 0: everything to the generic kernel.  CBL: both hold the
+// codebook in LDS; BIG (with CBL false): the stream decoder holds it in LDS in
+// workgroups of waves_big(OF) waves, the generic kernel reads it from global memory.
+template <int K, bool NF, bool OF, int RW, bool CBL, bool BIG>
 hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* norms, int64_t n, void* out,
                       hipStream_t s) {
   int64_t done = 0;
   if constexpr (RW > 0) {
-    typedef StreamShape<K, NF, OF, RW, CBL> S;
+    constexpr bool SCBL = CBL || BIG;
+    constexpr int WV = BIG ? waves_big(OF) : WAVES;
+    typedef StreamShape<K, NF, OF, RW, SCBL, WV> S;
     const int64_t ngroups = n / 32;
     if (ngroups > 0) {
+      const auto kern = decode_stream<K, NF, OF, RW, SCBL, WV>;
       const size_t lds = S::lds_bytes(cb->N);
-      int64_t wgs = 0;
-      hipError_t e = persistent_grid(cb, decode_stream<K, NF, OF, RW, CBL>, lds, (ngroups + WAVES - 1) / WAVES, &wgs);
+      if (lds > (size_t)LDS_MAX_BYTES) return hipErrorInvalidConfiguration;
+      hipError_t e = hipSuccess;
+      if (lds > 65536)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL((decode_stream<K, NF, OF, RW, CBL>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, codes,
-                         norms, ngroups, cb->cw16, reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out,
-                         (int)wgs);
+      int64_t wgs = 0;
+      e = persistent_grid(cb, kern, WV * 64, lds, (ngroups + WV - 1) / WV, &wgs);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(WV * 64), lds, s, codes, norms, ngroups, cb->cw16,
+                         reinterpret_cast<const half8*>(cb->dec_a), cb->N, cb->bits, out, (int)wgs);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       done = ngroups * 32;
@@ -375,20 +395,24 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
                                         reinterpret_cast<char*>(out) + done * (OF ? 128 : 256), s);
 }
 
-template <int K, int RW, bool CBL>
+template <int K, int RW, bool CBL, bool BIG>
 hipError_t launch_cbl(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype nd, int64_t n,
                       void* out, fq_dtype od, hipStream_t s) {
-  if (nd == FQ_F16 && od == FQ_F16) return launch_one<K, true, true, RW, CBL>(cb, codes, norms, n, out, s);
-  if (nd == FQ_F16) return launch_one<K, true, false, RW, CBL>(cb, codes, norms, n, out, s);
-  if (od == FQ_F16) return launch_one<K, false, true, RW, CBL>(cb, codes, norms, n, out, s);
-  return launch_one<K, false, false, RW, CBL>(cb, codes, norms, n, out, s);
+  if (nd == FQ_F16 && od == FQ_F16) return launch_one<K, true, true, RW, CBL, BIG>(cb, codes, norms, n, out, s);
+  if (nd == FQ_F16) return launch_one<K, true, false, RW, CBL, BIG>(cb, codes, norms, n, out, s);
+  if (od == FQ_F16) return launch_one<K, false, true, RW, CBL, BIG>(cb, codes, norms, n, out, s);
+  return launch_one<K, false, false, RW, CBL, BIG>(cb, codes, norms, n, out, s);
 }
 
 template <int K, int RW>
 hipError_t launch_rw(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype nd, int64_t n,
                      void* out, fq_dtype od, hipStream_t s) {
-  if (cb->N * K <= LDS_CB_HALFS) return launch_cbl<K, RW, true>(cb, codes, norms, nd, n, out, od, s);
-  return launch_cbl<K, RW, false>(cb, codes, norms, nd, n, out, od, s);
+  if (cb->N * K <= LDS_CB_HALFS) return launch_cbl<K, RW, true, false>(cb, codes, norms, nd, n, out, od, s);
+  if constexpr (RW > 0) {
+    // (checked against LDS_MAX_BYTES at launch: 8 fp32-output waves need 146 KiB)
+    if (cb->N * K <= LDS_CB_HALFS_BIG) return launch_cbl<K, RW, false, true>(cb, codes, norms, nd, n, out, od, s);
+  }
+  return launch_cbl<K, RW, false, false>(cb, codes, norms, nd, n, out, od, s);
 }
 
 // Whole-word record lengths are specialised: k = 2, N = 16 and k = 4, N = 256

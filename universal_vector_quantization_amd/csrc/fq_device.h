@@ -95,6 +95,13 @@ __device__ inline void lds_dma16(const void* gptr, char* lds) {
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(fq_lds_void*)lds);
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
 }
+// Same as lds_dma16 with a wave-uniform base address (scalar registers) and a
+// per-lane 32-bit byte offset: no 64-bit address arithmetic per lane.
+__device__ inline void lds_dma16_s(const void* sbase, uint32_t voff, char* lds) {
+  const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(fq_lds_void*)lds);
+  __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(la)
+                   : "memory", "m0");
+}
 __device__ inline void lds_dma4(const void* gptr, char* lds) {
   const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(fq_lds_void*)lds);
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(gptr), "s"(la) : "memory", "m0");
