@@ -190,6 +190,8 @@ def test_decode_random_codes(dev, k, N, n, norm_dtype, out_dtype):
     (4, 256, 600_000 + 17, np.float32, np.float32),
     (8, 4096, 700_000 + 1, np.float16, np.float32),
     (2, 16, 500_000 + 31, np.float16, np.float16),
+    (64, 4096, 400_000 + 9, np.float16, np.float16),
+    (64, 4096, 50_000 + 3, np.float32, np.float32),
 ])
 def test_decode_large_sampled(dev, k, N, n, norm_dtype, out_dtype):
     # Batches large enough that every wave of the persistent decoder walks many groups

@@ -91,6 +91,7 @@ void release(fq_codebook* cb) {
   (void)hipFree(cb->crec);
   (void)hipFree(cb->rot32);
   (void)hipFree(cb->frec);
+  (void)hipFree(cb->dec_full);
   delete cb;
 }
 
@@ -185,6 +186,19 @@ fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const fl
   delete[] pr;
   delete[] pm;
   if (st == FQ_OK && k == 64 && N % 32 == 0) st = upload_full_operands(cb, codewords, rotation);
+  if (st == FQ_OK && k == d) {
+    // full-vector code: decoded unit vectors Pi^T c_n, summed in fp64 and rounded once to fp32
+    float* tab = new (std::nothrow) float[(size_t)N * d];
+    if (!tab) return FQ_ERR_HIP;
+    for (int n = 0; n < N; n++)
+      for (int o = 0; o < d; o++) {
+        double acc = 0.0;
+        for (int i = 0; i < d; i++) acc += (double)rotation[i * d + o] * (double)codewords[(size_t)n * d + i];
+        tab[(size_t)n * d + o] = (float)acc;
+      }
+    st = upload(&cb->dec_full, tab, (size_t)N * d);
+    delete[] tab;
+  }
   if (st != FQ_OK || !((k == 4 || k == 8) && N % 32 == 0)) return st;
 
   const int NT = N / 32;

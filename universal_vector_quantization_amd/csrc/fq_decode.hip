@@ -107,6 +107,8 @@ extern template hipError_t launch_decode_k<64>(const fq_codebook*, const uint8_t
 
 hipError_t launch_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                          int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s) {
+  if (!cb->force_valu_decode && cb->dec_full)
+    return launch_decode_full(cb, codes, norms, norm_dtype, n, x_out, out_dtype, s);
   if (!cb->force_valu_decode && cb->dec_a)
     return launch_decode_mfma(cb, codes, norms, norm_dtype, n, x_out, out_dtype, s);
   switch (cb->k) {

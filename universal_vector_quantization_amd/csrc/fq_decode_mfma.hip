@@ -325,6 +325,67 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restr
   }
 }
 
+// Full-vector code (k = d): the decoded unit vector of code c is row c of dec_full
+// (Pi^T c_n, fp32), so decoding is a gather of that row scaled by the norm, with no
+// rotation left to do.  Eight lanes per vector, 8 output dims each (two 16-byte table
+// loads; one 16-byte fp16 store or two fp32 ones); a workgroup takes FULL_PASSES x 32
+// consecutive vectors per step, every pass's loads issued before its first store, and
+// steps through the input at a stride of nwg steps.
+constexpr int FULL_PASSES = 4;
+constexpr int FULL_VEC_PER_STEP = 32 * FULL_PASSES;
+
+template <bool NF16, bool OF16>
+__global__ __launch_bounds__(256) void decode_full(const uint8_t* __restrict__ codes, const void* __restrict__ norms,
+                                                   int64_t n, int bits, const float* __restrict__ tab,
+                                                   void* __restrict__ out, int64_t nsteps, int nwg) {
+  const int tid = fq_tid();
+  const int sub = tid & 7;
+  for (int64_t st = fq_bid_x(); st < nsteps; st += nwg) {
+    const int64_t v0 = st * FULL_VEC_PER_STEP + (tid >> 3);
+    uint32_t c[FULL_PASSES];
+    float nu[FULL_PASSES];
+#pragma unroll
+    for (int p = 0; p < FULL_PASSES; p++) {
+      const int64_t v = v0 + 32 * p;
+      const int64_t vv = v < n ? v : n - 1;  // lanes past the end read a valid record, store nothing
+      c[p] = load_code(codes, vv * bits, bits);
+      if constexpr (NF16)
+        nu[p] = (float)reinterpret_cast<const _Float16*>(norms)[vv];
+      else
+        nu[p] = reinterpret_cast<const float*>(norms)[vv];
+    }
+    float4 a[FULL_PASSES], b[FULL_PASSES];
+#pragma unroll
+    for (int p = 0; p < FULL_PASSES; p++) {
+      const float4* row = reinterpret_cast<const float4*>(tab + (size_t)c[p] * D + 8 * sub);
+      a[p] = row[0];
+      b[p] = row[1];
+    }
+#pragma unroll
+    for (int p = 0; p < FULL_PASSES; p++) {
+      const int64_t v = v0 + 32 * p;
+      if (v >= n) continue;
+      const float u = nu[p];
+      if constexpr (OF16) {
+        half8 h;
+        h[0] = (_Float16)(a[p].x * u);
+        h[1] = (_Float16)(a[p].y * u);
+        h[2] = (_Float16)(a[p].z * u);
+        h[3] = (_Float16)(a[p].w * u);
+        h[4] = (_Float16)(b[p].x * u);
+        h[5] = (_Float16)(b[p].y * u);
+        h[6] = (_Float16)(b[p].z * u);
+        h[7] = (_Float16)(b[p].w * u);
+        reinterpret_cast<half8*>(out)[v * (D / 8) + sub] = h;
+      } else {
+        float4* o = reinterpret_cast<float4*>(out) + v * (D / 4) + 2 * sub;
+        o[0] = make_float4(a[p].x * u, a[p].y * u, a[p].z * u, a[p].w * u);
+        o[1] = make_float4(b[p].x * u, b[p].y * u, b[p].z * u, b[p].w * u);
+      }
+    }
+  }
+}
+
 template <bool OF16>
 size_t generic_lds_bytes(int N, int K, bool cbl) {
   const size_t cb = cbl ? (size_t)((N * K * 2 + 15) & ~15) : 0;
@@ -430,7 +491,32 @@ hipError_t launch_k(const fq_codebook* cb, const uint8_t* codes, const void* nor
   return launch_rw<K, 0>(cb, codes, norms, nd, n, out, od, s);
 }
 
+template <bool NF, bool OF>
+hipError_t launch_full(const fq_codebook* cb, const uint8_t* codes, const void* norms, int64_t n, void* out,
+                       hipStream_t s) {
+  const int64_t nsteps = (n + FULL_VEC_PER_STEP - 1) / FULL_VEC_PER_STEP;
+  int64_t wgs = 0;
+  // 8 resident waves per SIMD's worth of workgroups, each walking several steps
+  hipError_t e = resident_workgroups(reinterpret_cast<const void*>(decode_full<NF, OF>), 256, 0, cb->device, &wgs);
+  if (e != hipSuccess) return e;
+  wgs = nsteps < wgs ? nsteps : wgs;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL((decode_full<NF, OF>), dim3((unsigned)wgs), dim3(256), 0, s, codes, norms, n, cb->bits,
+                     cb->dec_full, out, nsteps, (int)wgs);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_decode_full(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
+                              int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s) {
+  if (!cb->dec_full || cb->k != D) return hipErrorNotSupported;
+  if (n <= 0) return hipSuccess;
+  if (norm_dtype == FQ_F16 && out_dtype == FQ_F16) return launch_full<true, true>(cb, codes, norms, n, x_out, s);
+  if (norm_dtype == FQ_F16) return launch_full<true, false>(cb, codes, norms, n, x_out, s);
+  if (out_dtype == FQ_F16) return launch_full<false, true>(cb, codes, norms, n, x_out, s);
+  return launch_full<false, false>(cb, codes, norms, n, x_out, s);
+}
 
 hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                               int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s) {

@@ -40,6 +40,8 @@ struct fq_codebook {
                     // mfma_f32_32x32x16_f16; row 8 a + 4 hh + b of tile r is coordinate 32 hh + 16 r + 4 a + b
   uint8_t* frec;    // [N / 32 tiles][32 rows][144 bytes], zero-padded to whole chunks of 8 tiles:
                     // 64 fp16 coordinates, then (rows 4 m only) 256 ||c||^2 of rows 4 m .. 4 m + 3 (fp32)
+  float* dec_full;  // k = d only: [N][d] Pi^T c_n in fp32 (rounded once from fp64), the decoded unit
+                    // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
   size_t max_lds;   // bytes of LDS one workgroup may use on the device
   bool force_valu;  // FQ_ENCODE_KERNEL=valu at load time: always use the one-lane-per-vector encoder
@@ -74,6 +76,9 @@ hipError_t launch_encode_small(const fq_codebook* cb, const void* x, fq_dtype x_
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
 hipError_t launch_decode_mfma(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
+                              int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
+// k = d decoder: gathers rows of dec_full (null dec_full: hipErrorNotSupported).
+hipError_t launch_decode_full(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                               int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
 hipError_t launch_decode(const fq_codebook* cb, const uint8_t* codes, const void* norms, fq_dtype norm_dtype,
                          int64_t n, void* x_out, fq_dtype out_dtype, hipStream_t s);
