@@ -137,6 +137,11 @@ def cpu_baseline(budget_s: float = 12.0):
                       f"(encode {t_enc:.2f}s per pass, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
 
 
+# decoder kernel whose HBM bytes per launch (rocprofv3 counters) each workload reports
+DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_stream_k4", "tinyllama_kv": "decode_stream_k8",
+                       "fullvec_kv": "decode_full_k64"}
+
+
 def workload_timings(fq, workloads, dev, stream, reps: int = 5):
     """Encode and decode time of every codec workload at full size (event-timed,
     median of ``reps`` launches; inputs resident, no cache flush)."""
@@ -171,7 +176,9 @@ def workload_timings(fq, workloads, dev, stream, reps: int = 5):
                 td.append(e[1].elapsed_time(e[2]))
         t_e, t_d = float(np.median(te)) / 1e3, float(np.median(td)) / 1e3
         vb = x.element_size() * D + norms.element_size() + cb.code_bytes(n) / n
+        dk = DECODE_TRAFFIC_KEYS.get(name)
         out[name] = {"n": n, "k": w.k, "N": w.N, "encode_us": t_e * 1e6, "decode_us": t_d * 1e6,
+                     "decode_traffic": measured_traffic(dk, "fq_decode_mfma.hip") if dk else None,
                      "encode_vec_per_s": n / t_e, "decode_vec_per_s": n / t_d,
                      "encode_GBps": n * vb / t_e / 1e9, "decode_GBps": n * vb / t_d / 1e9,
                      "decode_hbm_frac": n * vb / t_d / 1e9 / HBM_PEAK_GBPS,
