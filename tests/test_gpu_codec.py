@@ -314,6 +314,31 @@ def test_encode_exact_ties_take_lowest_index(dev, k):
     cb.close()
 
 
+@pytest.mark.parametrize("zero_every", [97, 2])
+def test_encode_full_vector_ties_queue_and_overflow(dev, zero_every):
+    # k = d = 64: codewords 3 and 5 are negatives of each other and the two shortest,
+    # so every zero vector is an exact tie that only the fp64 re-search settles (code
+    # 3).  Zeros every 97th vector: a few per 512-vector workgroup round, all through
+    # the workgroup's re-search queue; every 2nd vector: about 256 per round, past the
+    # queue's capacity, so most take the wave's own search.
+    N = 64
+    cw = _synthetic_codebook(D, N, 960)
+    cw[3] = cw[3] * np.float32(2.0 ** -6)
+    cw[3][np.abs(cw[3]) < 2.0 ** -14] = 0.0
+    cw[5] = -cw[3]
+    assert np.abs(cw[3]).max() > 0
+    _, rot = artifact_or_skip(4, 256)
+    cb = fq.Codebook(cw, rot)
+    x = workloads.gpt2_small_kv()[:3000].copy()
+    x[::zero_every] = 0
+    print(f"[full-vector ties] zero every {zero_every}", flush=True)
+    gc, gn = gpu_encode(cb, x, dev, np.float16)
+    check_encode(x, rot, cw, gc, gn, np.float16, D, N)
+    g = oc.unpack_codes(gc, len(x), 1, oc.code_bits(N))
+    assert (g[::zero_every] == 3).all()
+    cb.close()
+
+
 def test_encode_kernels_agree_on_full_gpt2s(dev):
     # Both encoders on the whole 294,912-vector workload: identical stores except
     # where the oracle calls the block a near-tie.

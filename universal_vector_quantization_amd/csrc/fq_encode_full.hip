@@ -22,8 +22,13 @@
 //     is certified with the same error bound as the k = 4 / 8 encoder:
 //     E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y|) + 35840 sqrt(k) cmax u
 //               + 2^-25 (1 + sqrt(k) cmax)); |y| <= 1 here.
-//  5. Uncertified vectors are searched again by the whole wave in fp64 with the
-//     direct distance (lowest index on exact ties).
+//  5. Uncertified vectors are searched again in fp64 with the direct distance
+//     (lowest index on exact ties) by the whole workgroup: each wave queues its
+//     vectors (y in fp64) in LDS, the workgroup streams the codebook through the
+//     chunk buffers once more, and every wave scores 16 codewords of each chunk
+//     for every queued vector (four lanes per codeword, 16 coordinates each).
+//     Searched by their own wave alone, one uncertified vector held up the
+//     workgroup's barriers for the length of a 4096-codeword fp64 scan.
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -37,6 +42,11 @@ constexpr int ROWB = 144;                      // bytes per codeword row: 64 fp1
 constexpr int TILEB = 32 * ROWB;               // 4608
 constexpr int CHUNKB = CT * TILEB;             // 36864
 constexpr int SCR_DW = 2 * 64 * 2 + 16;        // per wave: x and y (fp64) of a re-searched vector + codes
+constexpr int QMAX = 16;                       // queued re-searches per workgroup and round
+constexpr int QB = 4;                          // queued vectors scored per pass over the codebook
+// queue: y (fp64) per entry, owner (wave << 8 | column) per entry, per-wave best
+// (distance, index) per entry, and the count
+constexpr int Q_BYTES = QMAX * 64 * 8 + QMAX * 4 + QMAX * WAVES * 16 + 16;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -77,12 +87,12 @@ __device__ inline void load_chunk(const uint8_t* __restrict__ rec, int ch, int n
     lds_dma16(src + p * 1024 + lane * 16, dst + p * 1024);
 }
 
-constexpr size_t full_lds_bytes() { return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4; }
+constexpr size_t full_lds_bytes() { return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4 + Q_BYTES; }
 
 template <bool NF16>
 __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rotA,
-    const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64, int N, int bits,
+    const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64t, int N, int bits,
     float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
     const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   extern __shared__ uint4 smem[];
@@ -94,6 +104,12 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
   double* xs = reinterpret_cast<double*>(scr);  // 64 fp64
   double* ys = xs + 64;                          // 64 fp64
   uint32_t* spk = scr + 256;                     // 16 words: 32 codes x <= 16 bits
+  char* qbase = buf0 + 2 * CHUNKB + WAVES * SCR_DW * 4;
+  double* qy = reinterpret_cast<double*>(qbase);                          // [QMAX][64]
+  int* qown = reinterpret_cast<int*>(qbase + QMAX * 64 * 8);              // [QMAX]
+  double* qbd = reinterpret_cast<double*>(qbase + QMAX * 64 * 8 + QMAX * 4);  // [QMAX][WAVES]
+  int* qbi = reinterpret_cast<int*>(qbd + QMAX * WAVES);                  // [QMAX][WAVES]
+  int* qcnt = qbi + QMAX * WAVES;
   const int NT = N / 32;
   const int nch = (NT + CT - 1) / CT;
 
@@ -190,6 +206,7 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     f32x16 bestD;
 #pragma unroll
     for (int e = 0; e < 16; e++) bestD[e] = __builtin_huge_valf();
+    if (w == 0 && lane == 0) *qcnt = 0;  // read after the barriers below
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces of chunk 0 are in LDS
     __syncthreads();
     for (int ch = 0; ch < nch; ch++) {
@@ -255,7 +272,8 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       atomicOr(&spk[bo >> 5], code << sh);
       if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], code >> (32 - sh));
     }
-    // ---- 5. fp64 re-search of the uncertified vectors, one at a time
+    // ---- 5. fp64 re-search of the uncertified vectors: y of each goes to the workgroup's
+    //      queue (or, past QMAX entries, the wave searches alone)
     uint64_t todo = __ballot(h == 0 && valid && !sure);
     while (todo) {
       const int cc = __builtin_ctzll(todo);
@@ -269,8 +287,17 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       const double iv = nuf > 0.0 ? 1.0 / nuf : 0.0;
       wave_lds_sync();
       double yt = 0.0;  // coordinate `lane` of y
-      for (int j = 0; j < D; j++) yt = fma(pi64[lane * D + j], xs[j], yt);
-      ys[lane] = yt * iv;
+      for (int j = 0; j < D; j++) yt = fma(pi64t[j * D + lane], xs[j], yt);
+      yt *= iv;
+      int slot = 0;
+      if (lane == 0) slot = atomicAdd(qcnt, 1);
+      slot = __builtin_amdgcn_readfirstlane(__shfl(slot, 0));
+      if (slot < QMAX) {
+        qy[slot * 64 + lane] = yt;
+        if (lane == 0) qown[slot] = (w << 8) | cc;
+        continue;
+      }
+      ys[lane] = yt;
       wave_lds_sync();
       double bd = __builtin_huge_val();
       int bn = 0x7fffffff;
@@ -303,6 +330,103 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       }
       wave_lds_sync();
     }
+    __syncthreads();  // the queue is complete
+    const int nq0 = *qcnt;
+    const int nq = __builtin_amdgcn_readfirstlane(nq0 < QMAX ? nq0 : QMAX);
+    // Workgroup pass(es) over the codebook for the queued vectors, QB at a time: lane l
+    // of wave w scores codeword 16 w + l / 4 of every chunk over coordinates
+    // 16 (l % 4) .. + 15; the four partial sums are added in a fixed order.
+    for (int e0 = 0; e0 < nq; e0 += QB) {
+      const int ne = (nq - e0) < QB ? (nq - e0) : QB;
+      double bd[QB];
+      int bn[QB];
+#pragma unroll
+      for (int e = 0; e < QB; e++) {
+        bd[e] = __builtin_huge_val();
+        bn[e] = 0x7fffffff;
+      }
+      const int cl = 16 * w + (lane >> 2), q4 = lane & 3;
+      load_chunk(rec, 0, (NT < CT ? NT : CT) * TILEB, buf0, w, lane);
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+      __syncthreads();
+      for (int ch = 0; ch < nch; ch++) {
+        const char* cur = buf0 + (ch & 1) * CHUNKB;
+        if (ch + 1 < nch) {
+          const int nt1 = (NT - (ch + 1) * CT) < CT ? (NT - (ch + 1) * CT) : CT;
+          load_chunk(rec, ch + 1, nt1 * TILEB, buf0 + ((ch + 1) & 1) * CHUNKB, w, lane);
+        }
+        const int ntc = (NT - ch * CT) < CT ? (NT - ch * CT) : CT;
+        const bool ok = cl < 32 * ntc;  // rows past a partial last chunk hold stale bytes
+        const uint4* rowp = reinterpret_cast<const uint4*>(cur + (cl >> 5) * TILEB + (cl & 31) * ROWB + 32 * q4);
+        const uint4 r0 = rowp[0], r1 = rowp[1];
+        const uint32_t cwv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+        for (int e = 0; e < QB; e++) {
+          if (e < ne) {
+            const double* yq = qy + (e0 + e) * 64 + 16 * q4;
+            double pp = 0.0;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+              const double d0 = yq[2 * i] - (double)h_lo(cwv[i]);
+              const double d1 = yq[2 * i + 1] - (double)h_hi(cwv[i]);
+              pp = fma(d0, d0, pp);
+              pp = fma(d1, d1, pp);
+            }
+            const double p1 = shfl_xor_f64(pp, 1);
+            const double lo2 = (q4 & 1) ? p1 + pp : pp + p1;  // (q0 + q1) and (q2 + q3)
+            const double p2 = shfl_xor_f64(lo2, 2);
+            const double dd = (q4 & 2) ? p2 + lo2 : lo2 + p2;  // (q0 + q1) + (q2 + q3)
+            const int nn = ch * (CT * 32) + cl;
+            if (ok && dd < bd[e]) {
+              bd[e] = dd;
+              bn[e] = nn;
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
+        __syncthreads();
+      }
+      // best of the wave (lowest index on equal distances), then of the workgroup
+#pragma unroll
+      for (int e = 0; e < QB; e++) {
+        if (e < ne) {
+#pragma unroll
+          for (int m = 4; m <= 32; m <<= 1) {
+            const double od = shfl_xor_f64(bd[e], m);
+            const int on = __shfl_xor(bn[e], m);
+            if (od < bd[e] || (od == bd[e] && on < bn[e])) {
+              bd[e] = od;
+              bn[e] = on;
+            }
+          }
+          if (lane == 0) {
+            qbd[(e0 + e) * WAVES + w] = bd[e];
+            qbi[(e0 + e) * WAVES + w] = bn[e];
+          }
+        }
+      }
+      __syncthreads();
+      for (int e = 0; e < ne; e++) {
+        const int own = qown[e0 + e];
+        if ((own >> 8) == w && lane == 0) {
+          double b = qbd[(e0 + e) * WAVES];
+          int bi = qbi[(e0 + e) * WAVES];
+          for (int ww = 1; ww < WAVES; ww++) {
+            const double od = qbd[(e0 + e) * WAVES + ww];
+            const int on = qbi[(e0 + e) * WAVES + ww];
+            if (od < b || (od == b && on < bi)) {
+              b = od;
+              bi = on;
+            }
+          }
+          const uint32_t cv = (uint32_t)bi;
+          const int bo = (own & 0xff) * bits, sh = bo & 31;
+          atomicOr(&spk[bo >> 5], cv << sh);
+          if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
+        }
+      }
+      __syncthreads();  // chunk buffers and per-wave bests free again
+    }
     wave_lds_sync();
     if (slots) {
       scatter_records(spk, nv, bits / 8, slots, cap, v0, codes, lane);
@@ -331,7 +455,7 @@ hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t*
   if (wgs > resident) wgs = resident;
   hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),
-                     reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
+                     reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64t, cb->N, cb->bits, cb->h16_eabs,
                      cb->h16_erel, codes, norms, slots, cap, (int)wgs);
   return hipGetLastError();
 }
