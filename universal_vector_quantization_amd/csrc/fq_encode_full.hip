@@ -24,9 +24,9 @@
 //               + 2^-25 (1 + sqrt(k) cmax)); |y| <= 1 here.
 //  5. Uncertified vectors are searched again in fp64 with the direct distance
 //     (lowest index on exact ties) by the whole workgroup: each wave queues its
-//     vectors (y in fp64) in LDS, the workgroup streams the codebook through the
-//     chunk buffers once more, and every wave scores 16 codewords of each chunk
-//     for every queued vector (four lanes per codeword, 16 coordinates each).
+//     vectors (y in fp64) in LDS, then every wave scores its sixteenth of the
+//     codebook (fp16 records read straight from global memory, four lanes per
+//     codeword, 16 coordinates each) for up to four queued vectors per pass.
 //     Searched by their own wave alone, one uncertified vector held up the
 //     workgroup's barriers for the length of a 4096-codeword fp64 scan.
 #include "fq_device.h"
@@ -334,8 +334,8 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const int nq0 = *qcnt;
     const int nq = __builtin_amdgcn_readfirstlane(nq0 < QMAX ? nq0 : QMAX);
     // Workgroup pass(es) over the codebook for the queued vectors, QB at a time: lane l
-    // of wave w scores codeword 16 w + l / 4 of every chunk over coordinates
-    // 16 (l % 4) .. + 15; the four partial sums are added in a fixed order.
+    // of wave w scores codewords 256 i + 16 w + l / 4 over coordinates 16 (l % 4) .. + 15;
+    // the four partial sums are added in a fixed order.
     for (int e0 = 0; e0 < nq; e0 += QB) {
       const int ne = (nq - e0) < QB ? (nq - e0) : QB;
       double bd[QB];
@@ -346,45 +346,47 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
         bn[e] = 0x7fffffff;
       }
       const int cl = 16 * w + (lane >> 2), q4 = lane & 3;
-      load_chunk(rec, 0, (NT < CT ? NT : CT) * TILEB, buf0, w, lane);
-      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-      __syncthreads();
-      for (int ch = 0; ch < nch; ch++) {
-        const char* cur = buf0 + (ch & 1) * CHUNKB;
-        if (ch + 1 < nch) {
-          const int nt1 = (NT - (ch + 1) * CT) < CT ? (NT - (ch + 1) * CT) : CT;
-          load_chunk(rec, ch + 1, nt1 * TILEB, buf0 + ((ch + 1) & 1) * CHUNKB, w, lane);
+      const int nit = (N + 255) / 256;
+      // codeword it * 256 + cl: its 16 coordinates of this lane straight from the fp16
+      // records in global memory (four lanes read one row's 128 bytes), four rows in flight
+      for (int it0 = 0; it0 < nit; it0 += 4) {
+        uint4 rr[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int nn = (it0 + u) * 256 + cl;
+          const int nc = nn < N ? nn : N - 1;
+          const uint4* rowp = reinterpret_cast<const uint4*>(rec + (size_t)nc * ROWB + 32 * q4);
+          rr[u][0] = rowp[0];
+          rr[u][1] = rowp[1];
         }
-        const int ntc = (NT - ch * CT) < CT ? (NT - ch * CT) : CT;
-        const bool ok = cl < 32 * ntc;  // rows past a partial last chunk hold stale bytes
-        const uint4* rowp = reinterpret_cast<const uint4*>(cur + (cl >> 5) * TILEB + (cl & 31) * ROWB + 32 * q4);
-        const uint4 r0 = rowp[0], r1 = rowp[1];
-        const uint32_t cwv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
 #pragma unroll
-        for (int e = 0; e < QB; e++) {
-          if (e < ne) {
-            const double* yq = qy + (e0 + e) * 64 + 16 * q4;
-            double pp = 0.0;
+        for (int u = 0; u < 4; u++) {
+          const int nn = (it0 + u) * 256 + cl;
+          const uint32_t cwv[8] = {rr[u][0].x, rr[u][0].y, rr[u][0].z, rr[u][0].w,
+                                   rr[u][1].x, rr[u][1].y, rr[u][1].z, rr[u][1].w};
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-              const double d0 = yq[2 * i] - (double)h_lo(cwv[i]);
-              const double d1 = yq[2 * i + 1] - (double)h_hi(cwv[i]);
-              pp = fma(d0, d0, pp);
-              pp = fma(d1, d1, pp);
-            }
-            const double p1 = shfl_xor_f64(pp, 1);
-            const double lo2 = (q4 & 1) ? p1 + pp : pp + p1;  // (q0 + q1) and (q2 + q3)
-            const double p2 = shfl_xor_f64(lo2, 2);
-            const double dd = (q4 & 2) ? p2 + lo2 : lo2 + p2;  // (q0 + q1) + (q2 + q3)
-            const int nn = ch * (CT * 32) + cl;
-            if (ok && dd < bd[e]) {
-              bd[e] = dd;
-              bn[e] = nn;
+          for (int e = 0; e < QB; e++) {
+            if (e < ne) {
+              const double* yq = qy + (e0 + e) * 64 + 16 * q4;
+              double pp = 0.0;
+#pragma unroll
+              for (int i = 0; i < 8; i++) {
+                const double d0 = yq[2 * i] - (double)h_lo(cwv[i]);
+                const double d1 = yq[2 * i + 1] - (double)h_hi(cwv[i]);
+                pp = fma(d0, d0, pp);
+                pp = fma(d1, d1, pp);
+              }
+              const double p1 = shfl_xor_f64(pp, 1);
+              const double lo2 = (q4 & 1) ? p1 + pp : pp + p1;  // (q0 + q1) and (q2 + q3)
+              const double p2 = shfl_xor_f64(lo2, 2);
+              const double dd = (q4 & 2) ? p2 + lo2 : lo2 + p2;  // (q0 + q1) + (q2 + q3)
+              if (nn < N && dd < bd[e]) {
+                bd[e] = dd;
+                bn[e] = nn;
+              }
             }
           }
         }
-        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-        __syncthreads();
       }
       // best of the wave (lowest index on equal distances), then of the workgroup
 #pragma unroll
@@ -425,7 +427,7 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
           if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
         }
       }
-      __syncthreads();  // chunk buffers and per-wave bests free again
+      __syncthreads();  // per-wave bests free again
     }
     wave_lds_sync();
     if (slots) {
