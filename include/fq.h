@@ -76,7 +76,10 @@ typedef enum fq_dtype { FQ_F32 = 0, FQ_F16 = 1 } fq_dtype;
  *   codewords: host fp32 [N][k], fp16-representable values (see above).
  *   rotation:  host fp32 [d][d] row-major, y = Pi x.
  *   out:       receives the handle; free it with fq_codebook_free.
- * Synchronous.  Allocates under 2 MiB of device memory that the handle owns.
+ * Synchronous.  Allocates device memory that the handle owns: copies of the
+ * codebook in the kernels' layouts (about 7 N k bytes; for k = d about 800 N
+ * bytes, with the table of decoded unit vectors Pi^T c_n that the decoder
+ * gathers) plus about 200 KiB of rotation operands.
  * Returns FQ_ERR_ARG for bad sizes or values, FQ_ERR_UNSUPPORTED for d != 64,
  * FQ_ERR_HIP if an allocation or copy fails (nothing is leaked). */
 fq_status fq_codebook_load(int d, int k, int N, const float* codewords, const float* rotation,
