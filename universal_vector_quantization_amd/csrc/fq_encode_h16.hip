@@ -39,7 +39,8 @@
 //     second - best > 2E the winner is the exact unique minimiser.
 //  6. Uncertified blocks are listed in LDS and searched again, one at a time by
 //     the whole wave, in fp64 with the direct distance sum_t (y_t - c_t)^2
-//     (lowest index on exact ties).
+//     (lowest index on exact ties), after an fp32 screen that leaves (nearly
+//     always) one fp64 candidate per lane.
 //  7. Codes are assembled in LDS and written as whole dwords.
 #include "fq_device.h"
 #include "fq_internal.h"
@@ -398,18 +399,74 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
         for (int m = 32; m >= 1; m >>= 1) p += shfl_xor_f64(p, m);
         yb[i] = p * inv;
       }
+      // Large codebooks (16 or more codewords per lane) are screened in fp32 first
+      // (for smaller ones the screen costs more than it saves): every fp32 distance is
+      // within e of the fp64 one, so the fp64 minimiser and all its ties lie within 2 e
+      // of the smallest fp32 distance m.  When no lane holds two such candidates, each
+      // lane scores its one candidate in fp64; otherwise every codeword is scored in
+      // fp64.  e <= u (2 sqrt(d) |y_b| +
+      // (k + 2) d) for a distance d (rounding of y to fp32, of each difference and of
+      // each fused square-add) up to terms of order u^2 |y_b|^2, which the absolute
+      // 1e-12 covers; the bound is doubled again for slack.
       double bd = __builtin_huge_val();
       int bn = 0x7fffffff;
-      for (int nn = lane; nn < N; nn += 64) {
-        double dd = 0.0;
+      bool full_scan = N < 1024;
+      if (!full_scan) {
+        float yf[K];
+        float yn2 = 0.f;
 #pragma unroll
         for (int i = 0; i < K; i++) {
-          const double df = yb[i] - (double)cbh[8 * rslot(nn) + i];
-          dd = fma(df, df, dd);
+          yf[i] = (float)yb[i];
+          yn2 = fmaf(yf[i], yf[i], yn2);
         }
-        if (dd < bd) {
+        float f1 = __builtin_huge_valf(), f2 = __builtin_huge_valf();
+        int fi = 0x7fffffff;
+        for (int nn = lane; nn < N; nn += 64) {
+          const uint4 rw = *reinterpret_cast<const uint4*>(cbh + 8 * rslot(nn));
+          const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
+          float df = 0.f;
+#pragma unroll
+          for (int i = 0; i < K; i += 2) {
+            const float d0 = yf[i] - h_lo(ww[i / 2]);
+            const float d1 = yf[i + 1] - h_hi(ww[i / 2]);
+            df = fmaf(d0, d0, df);
+            df = fmaf(d1, d1, df);
+          }
+          f2 = fminf(f2, fmaxf(f1, df));
+          fi = df < f1 ? nn : fi;
+          f1 = fminf(f1, df);
+        }
+        float mf = f1;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mf = fminf(mf, __shfl_xor(mf, m));
+        const float dm = mf * 1.0001f + 1e-30f;
+        const float tol = 4.0f * 5.9604645e-8f * (2.0f * __builtin_sqrtf(dm) * __builtin_sqrtf(yn2) * 1.0001f +
+                                                  (float)(K + 2) * dm) + 1e-12f;
+        const bool cand = f1 <= mf + tol;
+        full_scan = __ballot(cand && f2 <= mf + tol) != 0;
+        if (!full_scan && cand) {
+          double dd = 0.0;
+#pragma unroll
+          for (int i = 0; i < K; i++) {
+            const double df = yb[i] - (double)cbh[8 * rslot(fi) + i];
+            dd = fma(df, df, dd);
+          }
           bd = dd;
-          bn = nn;
+          bn = fi;
+        }
+      }
+      if (full_scan) {
+        for (int nn = lane; nn < N; nn += 64) {
+          double dd = 0.0;
+#pragma unroll
+          for (int i = 0; i < K; i++) {
+            const double df = yb[i] - (double)cbh[8 * rslot(nn) + i];
+            dd = fma(df, df, dd);
+          }
+          if (dd < bd) {
+            bd = dd;
+            bn = nn;
+          }
         }
       }
 #pragma unroll
