@@ -170,6 +170,9 @@ def test_encode_n0_noop_and_bad_alignment(dev):
     (8, 4096, 5000 + 3, np.float16, np.float16),
     (64, 4096, 6000 + 1, np.float16, np.float16),
     (4, 256, 333, np.float32, np.float16),
+    (64, 4096, 777, np.float16, np.float32),
+    (64, 4096, 129, np.float32, np.float16),
+    (64, 4096, 1, np.float16, np.float16),
 ])
 def test_decode_random_codes(dev, k, N, n, norm_dtype, out_dtype):
     cb, cw, rot = codebook(k, N)
