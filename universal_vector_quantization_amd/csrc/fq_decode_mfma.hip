@@ -433,7 +433,11 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
     if (ngroups > 0) {
       const auto kern = decode_stream<K, NF, OF, RW, SCBL, WV>;
       const size_t lds = S::lds_bytes(cb->N);
-      if (lds > (size_t)LDS_MAX_BYTES) return hipErrorInvalidConfiguration;
+      if constexpr (BIG) {
+        // a device with less LDS per workgroup reads the codebook from L1 / L2 instead
+        if (lds > cb->max_lds || lds > (size_t)LDS_MAX_BYTES)
+          return launch_one<K, NF, OF, RW, false, false>(cb, codes, norms, n, out, s);
+      }
       hipError_t e = hipSuccess;
       if (lds > 65536)
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -470,7 +474,8 @@ hipError_t launch_rw(const fq_codebook* cb, const uint8_t* codes, const void* no
                      void* out, fq_dtype od, hipStream_t s) {
   if (cb->N * K <= LDS_CB_HALFS) return launch_cbl<K, RW, true, false>(cb, codes, norms, nd, n, out, od, s);
   if constexpr (RW > 0) {
-    // (checked against LDS_MAX_BYTES at launch: 8 fp32-output waves need 146 KiB)
+    // (checked against the device's LDS per workgroup at launch: 8 fp32-output waves
+    // need 146 KiB)
     if (cb->N * K <= LDS_CB_HALFS_BIG) return launch_cbl<K, RW, false, true>(cb, codes, norms, nd, n, out, od, s);
   }
   return launch_cbl<K, RW, false, false>(cb, codes, norms, nd, n, out, od, s);
