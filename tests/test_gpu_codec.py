@@ -367,6 +367,32 @@ def test_encode_kernels_agree_on_full_gpt2s(dev):
     cbv.close()
 
 
+@pytest.mark.parametrize("out_dtype", [np.float16, np.float32])
+def test_decode_cached_codebook_path_parity(dev, out_dtype):
+    # FQ_DECODE_KERNEL=cached at load time: the k = 8, N = 4096 stream decoder reads its
+    # 64 KiB codebook from L1 / L2, the path taken where LDS per workgroup is smaller.
+    import os
+
+    k, N, n = 8, 4096, 100_000 + 7
+    cw, rot = artifact_or_skip(k, N)
+    os.environ["FQ_DECODE_KERNEL"] = "cached"
+    try:
+        cbc = fq.Codebook(cw, rot)
+    finally:
+        del os.environ["FQ_DECODE_KERNEL"]
+    B = (D // k) * oc.code_bits(N)
+    store = workloads.random_code_store((n * B + 7) // 8, 95)
+    if (n * B) % 8:
+        store[-1] &= (1 << ((n * B) % 8)) - 1
+    norms = workloads.random_norms(n, 96, np.float16)
+    got = gpu_decode(cbc, store, norms, dev, out_dtype)
+    rng = np.random.default_rng(4)
+    idx = np.unique(np.concatenate([rng.choice(n, 3000, replace=False), np.arange(64), np.arange(n - 64, n)]))
+    ref = oc.decode(unpack_sampled(store, idx, D // k, oc.code_bits(N)), norms[idx], rot, cw)
+    assert max_rel_rows(got[idx], ref) <= TOL
+    cbc.close()
+
+
 @pytest.mark.parametrize("k,N,n", [(4, 256, 2000 + 5), (64, 4096, 1000 + 1), (2, 16, 777)])
 def test_decode_valu_kernel_parity(dev, k, N, n):
     # FQ_DECODE_KERNEL=valu at load time selects the one-lane-per-vector decoder.

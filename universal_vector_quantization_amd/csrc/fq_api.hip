@@ -317,6 +317,7 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
     cb->force_mfma64 = ek && strcmp(ek, "mfma64") == 0;
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
+    cb->force_cache_codebook = dk && strcmp(dk, "cached") == 0;
   }
   int lds_max = 0;
   if (hipGetDevice(&cb->device) != hipSuccess ||

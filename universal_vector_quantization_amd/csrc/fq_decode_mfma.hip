@@ -435,7 +435,7 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
       const size_t lds = S::lds_bytes(cb->N);
       if constexpr (BIG) {
         // a device with less LDS per workgroup reads the codebook from L1 / L2 instead
-        if (lds > cb->max_lds || lds > (size_t)LDS_MAX_BYTES)
+        if (lds > cb->max_lds || lds > (size_t)LDS_MAX_BYTES || cb->force_cache_codebook)
           return launch_one<K, NF, OF, RW, false, false>(cb, codes, norms, n, out, s);
       }
       hipError_t e = hipSuccess;

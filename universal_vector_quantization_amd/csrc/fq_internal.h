@@ -47,6 +47,8 @@ struct fq_codebook {
   bool force_valu;  // FQ_ENCODE_KERNEL=valu at load time: always use the one-lane-per-vector encoder
   bool force_mfma64;  // FQ_ENCODE_KERNEL=mfma64: the fp64-rotation matrix-core encoder for every input dtype
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
+  bool force_cache_codebook;  // FQ_DECODE_KERNEL=cached: the matrix-core decoders read codebooks of more
+                              // than 32 KiB from L1 / L2 (the path of devices with less LDS)
 };
 
 namespace fq {
