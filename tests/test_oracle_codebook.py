@@ -242,3 +242,99 @@ def test_artifact_k2_rebuilds_identically():
     z = np.load(os.path.join(ART, "fq_d64_k2_n16.npz"))
     cb = cbm.build_codebook(D, 2, 16, seed=int(z["seed"]), restarts=3, samples=int(z["samples"]), max_iter=100)
     assert np.array_equal(cb.codewords, z["codewords"])
+
+
+# ------------------------------------------------------------------ directions: uniformity on the sphere
+# A uniform point u on S^{k-1} has E[u] = 0, E[u uᵀ] = I/k, E[u_i⁴] = 3/(k(k+2)) and
+# u_i² ~ Beta(1/2, (k-1)/2) for every coordinate (textbook moments of the uniform
+# sphere law).  The Roberts-Kronecker directions (§2.2) are a low-discrepancy cover of
+# the sphere, so their empirical moments must approach those values; a map that skips
+# the inverse normal CDF (points of the positive orthant) or uses the cube [-1/2, 1/2)^k
+# (corners over-weighted) fails them.
+def _sphere_uniformity_violations(u, k):
+    out = []
+    N = len(u)
+    if not np.allclose(np.sum(u * u, axis=1), 1.0, atol=1e-12):
+        out.append("not unit length")
+    if np.abs(u.mean(axis=0)).max() > 0.01:
+        out.append("mean")
+    if np.abs(u.T @ u / N - np.eye(k) / k).max() > 0.01:
+        out.append("second moment")
+    if np.abs((u ** 4).mean(axis=0) / (3.0 / (k * (k + 2))) - 1.0).max() > 0.05:
+        out.append("fourth moment")
+    law = stats.beta(0.5, (k - 1) / 2.0)
+    if stats.kstest((u ** 2).reshape(-1), law.cdf).statistic > 0.02:
+        out.append("coordinate law")
+    return out
+
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_roberts_directions_uniform_on_sphere(k):
+    assert _sphere_uniformity_violations(cbm.roberts_directions(k, 4096), k) == []
+
+
+@pytest.mark.parametrize("k", [4, 8])
+def test_roberts_uniformity_pin_rejects_planted_mistakes(k, monkeypatch):
+    # Planted on the CPU, in the oracle: (1) the inverse normal map left out,
+    # (2) the Kronecker points only centred instead of mapped.
+    monkeypatch.setattr(cbm.special, "ndtri", lambda t: t)
+    assert "mean" in _sphere_uniformity_violations(cbm.roberts_directions(k, 4096), k)
+    monkeypatch.setattr(cbm.special, "ndtri", lambda t: t - 0.5)
+    assert "fourth moment" in _sphere_uniformity_violations(cbm.roberts_directions(k, 4096), k)
+
+
+def test_fibonacci_sphere_uniform_height_and_azimuth():
+    # Archimedes: a uniform point on S² has its height uniform on [-1, 1] and an
+    # azimuth uniform and independent of the height; the Fibonacci sphere puts
+    # height 1 - (2n+1)/N on the midpoints of N equal slices.
+    N = 2048
+    u = cbm.fibonacci_sphere_directions(N)
+    assert _sphere_uniformity_violations(u, 3) == []
+    assert stats.kstest(u[:, 2], stats.uniform(-1, 2).cdf).statistic <= 0.5 / N + 1e-12
+    az = np.mod(np.arctan2(u[:, 1], u[:, 0]), 2 * np.pi)
+    assert stats.kstest(az, stats.uniform(0, 2 * np.pi).cdf).statistic < 0.01
+    assert abs(stats.spearmanr(az, u[:, 2])[0]) < 0.05
+
+
+# ------------------------------------------------------------------ restart selection
+def _brute_force_mse(samples, c):
+    # mean over samples of min over codewords of the squared error, written out
+    best = np.full(len(samples), np.inf)
+    for cn in c:
+        best = np.minimum(best, np.sum((samples - cn[None, :]) ** 2, axis=1))
+    return float(best.mean())
+
+
+def _restart_candidates(init, k, seed, restarts):
+    from oracle.rotation import haar_rotation
+    return [init @ (np.eye(k) if r == 0 else haar_rotation(k, seed * 1000 + r)).T for r in range(restarts)]
+
+
+def _kept_restart_violations(cb, cands, mses):
+    out = []
+    if not np.allclose(cb.restart_valid_mse, mses, rtol=1e-12, atol=0):
+        out.append("restart validation MSEs")
+    if not np.array_equal(cb.codewords, cbm.to_fp16_grid(cands[int(np.argmin(mses))])):
+        out.append("kept codebook is not the lowest-validation-MSE restart")
+    return out
+
+
+def test_build_codebook_keeps_lowest_validation_mse_restart():
+    # §2.2 multi-restart refinement, reading: the restart with the lowest validation MSE
+    # is kept.  With max_iter = 0 every restart is its start rotated by its Haar matrix,
+    # so the candidates and their validation MSEs (brute force over an independent draw
+    # of the same seeded source) are known here without the oracle's selection code.
+    k, N, seed, m, R = 2, 5, 4242, 600, 4
+    init = np.array([[0.05, 0.0], [0.0, 0.12], [-0.2, 0.01], [0.03, -0.25], [0.3, 0.2]])
+    cb = cbm.build_codebook(D, k, N, seed=seed, restarts=R, samples=m, max_iter=0, init=init)
+    rng = np.random.default_rng(seed)
+    sample_canonical(D, k, m, rng)  # the training draw comes first
+    valid = sample_canonical(D, k, m, rng)
+    cands = _restart_candidates(init, k, seed, R)
+    mses = [_brute_force_mse(valid, c) for c in cands]
+    assert len(set(np.round(mses, 12))) == R and int(np.argmin(mses)) != int(np.argmax(mses))
+    assert _kept_restart_violations(cb, cands, mses) == []
+    # planted mistake (keep the worst restart): the same check must reject it
+    worst = cbm.Codebook(D, k, N, cbm.to_fp16_grid(cands[int(np.argmax(mses))]), seed, "companded", R, m,
+                         cb.valid_mse, list(mses), [])
+    assert "kept codebook is not the lowest-validation-MSE restart" in _kept_restart_violations(worst, cands, mses)
