@@ -1,29 +1,28 @@
 """Benchmark of the FibQuant hot path on one MI355X.
 
-A step is one pass of the whole hot path over the GPT-2-small-shaped KV
-workload (294,912 fp16 vectors = 12 layers x 12 heads x 1024 tokens x {K, V},
-d = 64, codebook k = 4, N = 256, b = 2 bits per coordinate):
+A step is one pass of the whole hot path (encode, decode, decode-fused
+attention) over the largest workloads:
 
-    fq_encode   all 294,912 vectors -> fixed-address codes + fp16 norms
-    fq_decode   all codes -> fp16 reconstructions
-    fq_attn_decode  one decode query per (layer, head) over the encoded cache
-                (layers act as the batch, 12 query heads on 12 KV heads,
-                T = 1024) straight from the codes
+    fq_encode       the TinyLlama-1.1B-shaped KV cache: 5,767,168 fp16 vectors
+                    (22 layers x 4 KV heads x {K, V} x batch 8 x 4096 tokens,
+                    d = 64), codebook k = 8, N = 4096 (b = 1.5 bits/coordinate)
+    fq_decode       all its codes -> fp16 reconstructions
+    fq_attn_decode  one decode step of batch 16, 32 query heads on 4 KV heads,
+                    context 32768, over a compressed cache (the attention
+                    workload's K and V draws encoded with k = 4, N = 256)
 
-Inputs are resident in HBM before timing starts.  The metric is KV vectors per
-second through the step (fp16-equivalent GB/s = vectors/s x 128 B).  Per-kernel
-times come from HIP events on the stream the library launches on.  The
-decode-attention workload (B=16, 32 query heads on 4 KV heads, T=32768) is
-timed separately with L2 and the last-level cache evicted before every launch
-(a 512 MiB read), and reported against the HBM roofline.  On the same cache a
-decode loop is timed as well: per step the new token's K and V are encoded into
-their slots (fq_encode_scatter) and attention runs over each sequence's valid
-length (fq_attn_decode_varlen).  Along the rate axis (frozen initial codebooks
-from b = 4 down to 0.22 bits per coordinate) the same tensor's encode, decode
-and attention are timed as well, and so are prefill attention (64 causal
-queries per head on the 32k cache) and the codebook construction
-(fq_codebook_train) at larger shapes.  The CPU oracle is timed on a bounded sample
-(rank 0, one GPU only).
+Inputs are resident in HBM before timing starts.  ``value`` is the TinyLlama
+cache's vectors per second through the step (fp16-equivalent GB/s = vectors/s x
+128 B).  Inside the timed steps nothing is evicted; every kernel of the step
+streams more than the 256 MB last-level cache except the decode's read of the
+80 MB of codes and norms the encode has just written.  The per-kernel figures
+(``breakdown_us``, ``roofline``, ``attn_b16_t32k``, ``workloads``) are medians of
+launches each preceded by an eviction of L2 and the last-level cache (a 512 MiB
+read), timed with HIP events on the stream the library launches on.  Also timed:
+the other codec workloads, a decode loop (append + attention over per-batch
+lengths), prefill attention, the rate axis (frozen initial codebooks from b = 4
+down to 0.22 bits per coordinate) and the codebook construction at larger
+shapes.  The CPU oracle is timed on a bounded sample (rank 0, one GPU only).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -49,6 +48,11 @@ HBM_PEAK_GBPS = 8000.0
 VALU_LANE_OPS = 256 * 64 * 2.4e9
 CMP_PEAK_T = 2 * VALU_LANE_OPS / 1e12
 D = 64
+
+
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -86,55 +90,94 @@ def measured_traffic(kernel: str, src: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The oracle as it stands, on a bounded sample of the same step."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(n_sample: int = 8192, n_single: int = 2048):
+    """The oracle as it stands on a bounded sample of the step, extrapolated to
+    the whole step: encode + decode of the first ``n_sample`` TinyLlama-shaped
+    vectors (all host threads), attention of one (batch, KV head) slab's 8 query
+    heads over its first ``n_sample`` keys, scaled to the step's 5,767,168 vectors
+    and 64 slabs of 32,768 keys; plus the same encode on ``n_single`` vectors with
+    one thread."""
     import workloads
     from oracle import attention as oatt
     from oracle import codec as oc
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     import universal_vector_quantization_amd as fq
 
-    cw, rot = fq.load_artifact(4, 256)
-    x = workloads.gpt2_small_kv()
-    # size the sample from a 2048-vector calibration so the encode takes about budget_s
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    cw, rot = fq.load_artifact(8, 4096)
+    w = workloads.WORKLOADS["tinyllama_kv"]
+    x = workloads.tinyllama_kv()[:n_sample]
     t0 = time.perf_counter()
-    oc.encode(x[:2048], rot, cw, np.float16)
-    t_cal = time.perf_counter() - t0
-    n_s = int(min(len(x), max(2048, 2048 * budget_s / max(t_cal, 1e-3))) // 2048 * 2048)
-    # the whole tensor encodes in less than the budget on a many-core host: repeat the
-    # timed encode (at most 5 times) until the budget is spent
-    reps, t_enc = 0, 0.0
-    while reps < 5 and (reps == 0 or t_enc < budget_s):
-        t0 = time.perf_counter()
-        enc = oc.encode(x[:n_s], rot, cw, np.float16)
-        t_enc += time.perf_counter() - t0
-        reps += 1
-    t_enc /= reps
+    enc = oc.encode(x, rot, cw, np.float16)
+    t_enc = time.perf_counter() - t0
     t0 = time.perf_counter()
     oc.round_output(oc.decode(enc.codes, enc.norms, rot, cw), np.float16)
     t_dec = time.perf_counter() - t0
-    # attention: one (layer, head) query over its 1024 keys and 1024 values
-    T = workloads.GPT2_T
-    kx = x[:T]
-    vx = x[len(x) // 2: len(x) // 2 + T]
-    ke = oc.encode(kx, rot, cw, np.float16)
-    ve = oc.encode(vx, rot, cw, np.float16)
-    q = workloads.gpt2_small_queries()[:1, :1]
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        oc.encode(x[:n_single], rot, cw, np.float16)
+        t_enc1 = time.perf_counter() - t0
+    cw4, _ = fq.load_artifact(4, 256)
+    G = workloads.ATTN_HQ // workloads.ATTN_HKV
+    q, kv = workloads.attention_inputs(B=1, Hkv=1, Hq=G)
+    T = n_sample
+    ke = oc.encode(kv[0, 0, 0, :T], rot, cw4, np.float16)
+    ve = oc.encode(kv[1, 0, 0, :T], rot, cw4, np.float16)
     t0 = time.perf_counter()
     oatt.attention(q, ke.codes.reshape(1, 1, T, 16), ke.norms.reshape(1, 1, T), ve.codes.reshape(1, 1, T, 16),
-                   ve.norms.reshape(1, 1, T), rot, cw, 0.125)
+                   ve.norms.reshape(1, 1, T), rot, cw4, 0.125)
     t_att = time.perf_counter() - t0
-    per_vec = t_enc / n_s + t_dec / n_s + t_att / (2 * T)
-    return {"value": 1.0 / per_vec, "unit": "vectors/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"oracle encode (x{reps}) + decode of the first {n_s} of the 294912 vectors plus attention "
-                      f"of one (layer, head) query over its {T} keys/values; per-vector times summed "
-                      f"(encode {t_enc:.2f}s per pass, decode {t_dec:.3f}s, attention {t_att:.3f}s)"}
+    slabs = workloads.ATTN_B * workloads.ATTN_HKV
+    t_att_step = t_att * slabs * workloads.ATTN_T / T
+    t_step = w.n * (t_enc + t_dec) / n_sample + t_att_step
+    t_step1 = w.n * (t_enc1 / n_single + t_dec / n_sample) + t_att_step
+    return {"value": w.n / t_step, "unit": "vectors/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count(),
+            "value_1_thread": w.n / t_step1,
+            "sample": f"oracle encode + decode of the first {n_sample} of the 5,767,168 TinyLlama-shaped vectors "
+                      f"(encode {t_enc:.2f} s, decode {t_dec:.3f} s) and attention of one (batch, KV head) slab's "
+                      f"{G} query heads over its first {T} keys ({t_att:.3f} s), extrapolated to the step (the whole "
+                      f"cache, {slabs} slabs of {workloads.ATTN_T} keys); one-thread figure: the encode of the first "
+                      f"{n_single} vectors ({t_enc1:.2f} s) in place of the all-thread encode",
+            "seconds_per_step_extrapolated": t_step}
+
+
+def evict_reader(dev):
+    """A 512 MiB buffer whose read (``.max()``) leaves L2 and the 256 MB last-level
+    cache holding only clean lines of it.  An eviction by writing would leave dirty
+    lines whose write-back lands inside the next timed launch."""
+    import torch
+
+    return torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
+
+
+def timed_evicted(fn, stream, flush, reps: int, warm: int = 2):
+    """Median event-timed duration (s) of ``fn`` over ``reps`` launches, each
+    preceded by an eviction of L2 and the last-level cache."""
+    import torch
+
+    ts = []
+    for r in range(reps + warm):
+        flush.max()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r >= warm:
+            ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts)) / 1e3
 
 
 # decoder kernel whose HBM bytes per launch (rocprofv3 counters) each workload reports
@@ -142,14 +185,15 @@ DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_stream_k4", "tinyllama_kv": "decode_s
                        "fullvec_kv": "decode_full_k64"}
 
 
-def workload_timings(fq, workloads, dev, stream, reps: int = 5):
-    """Encode and decode time of every codec workload at full size (event-timed,
-    median of ``reps`` launches; inputs resident, no cache flush)."""
+def workload_timings(fq, workloads, dev, stream, flush, reps: int = 5):
+    """Encode and decode time of the other codec workloads at full size (event-timed
+    medians of ``reps`` launches, each after an eviction of L2 and the last-level
+    cache)."""
     import torch
 
     out = {}
     gens = {"iid4096": lambda: workloads.iid_gaussian(4096, 101), "gpt2s_kv": workloads.gpt2_small_kv,
-            "tinyllama_kv": workloads.tinyllama_kv, "fullvec_kv": workloads.fullvec_kv}
+            "fullvec_kv": workloads.fullvec_kv}
     for name, gen in gens.items():
         w = workloads.WORKLOADS[name]
         try:
@@ -162,43 +206,48 @@ def workload_timings(fq, workloads, dev, stream, reps: int = 5):
         codes = torch.empty(cb.code_bytes(n), dtype=torch.uint8, device=dev)
         norms = torch.empty(n, dtype=torch.float16 if w.norm_dtype == "f16" else torch.float32, device=dev)
         xr = torch.empty_like(x)
-        te, td = [], []
-        for r in range(reps + 1):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record(stream)
-            fq.fq_encode(cb.handle, x, codes, norms, stream)
-            e[1].record(stream)
-            fq.fq_decode(cb.handle, codes, norms, xr, stream)
-            e[2].record(stream)
-            torch.cuda.synchronize()
-            if r:
-                te.append(e[0].elapsed_time(e[1]))
-                td.append(e[1].elapsed_time(e[2]))
-        t_e, t_d = float(np.median(te)) / 1e3, float(np.median(td)) / 1e3
-        vb = x.element_size() * D + norms.element_size() + cb.code_bytes(n) / n
-        dk = DECODE_TRAFFIC_KEYS.get(name)
-        out[name] = {"n": n, "k": w.k, "N": w.N, "encode_us": t_e * 1e6, "decode_us": t_d * 1e6,
-                     "decode_traffic": measured_traffic(dk, "fq_decode_mfma.hip") if dk else None,
-                     "encode_vec_per_s": n / t_e, "decode_vec_per_s": n / t_d,
-                     "encode_GBps": n * vb / t_e / 1e9, "decode_GBps": n * vb / t_d / 1e9,
-                     "decode_hbm_frac": n * vb / t_d / 1e9 / HBM_PEAK_GBPS,
-                     "encode_cmp_frac": (D // w.k) * w.N * n / t_e / 1e12 / CMP_PEAK_T}
+        t_e = timed_evicted(lambda: fq.fq_encode(cb.handle, x, codes, norms, stream), stream, flush, reps)
+        t_d = timed_evicted(lambda: fq.fq_decode(cb.handle, codes, norms, xr, stream), stream, flush, reps)
+        out[name] = codec_record(fq, cb, x, n, norms, w, t_e, t_d)
         cb.close()
         del x, codes, norms, xr
         torch.cuda.empty_cache()
     return out
 
 
+# decoder kernel whose HBM bytes per launch (rocprofv3 counters) each workload reports
+DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_stream_k4", "tinyllama_kv": "decode_stream_k8",
+                       "fullvec_kv": "decode_full_k64"}
+ENCODE_TRAFFIC_KEYS = {"gpt2s_kv": ("encode_h16_k4", "fq_encode_h16.hip"),
+                       "tinyllama_kv": ("encode_h16_k8", "fq_encode_h16.hip"),
+                       "fullvec_kv": ("encode_full_k64", "fq_encode_full.hip")}
+
+
+def codec_record(fq, cb, x, n, norms, w, t_e, t_d):
+    vb = x.element_size() * D + norms.element_size() + cb.code_bytes(n) / n  # algorithmic bytes per vector
+    dk = DECODE_TRAFFIC_KEYS.get(w.name)
+    ek = ENCODE_TRAFFIC_KEYS.get(w.name)
+    return {"n": n, "k": w.k, "N": w.N, "encode_kernel": fq.fq_encode_kernel(cb.handle, fq.FQ_F16 if
+                                                                              x.element_size() == 2 else fq.FQ_F32, n),
+            "encode_us": t_e * 1e6, "decode_us": t_d * 1e6,
+            "encode_vec_per_s": n / t_e, "decode_vec_per_s": n / t_d,
+            "encode_GBps": n * vb / t_e / 1e9, "decode_GBps": n * vb / t_d / 1e9,
+            "decode_hbm_frac": n * vb / t_d / 1e9 / HBM_PEAK_GBPS,
+            "encode_cmp_frac": (D // w.k) * w.N * n / t_e / 1e12 / CMP_PEAK_T,
+            "encode_traffic": measured_traffic(*ek) if ek else None,
+            "decode_traffic": measured_traffic(dk, "fq_decode_mfma.hip") if dk else None}
+
+
 # Rate-axis points (k, N) with frozen initial codebooks: b = log2(N) / k from 4 down to 0.22.
 RATE_AXIS = [(1, 16), (2, 32), (2, 128), (4, 1024), (4, 16384), (16, 1024), (32, 512), (64, 16384)]
 
 
-def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
+def rate_axis_timings(fq, workloads, dev, stream, flush, reps: int = 3):
     """Encode, decode and decode-attention time along the rate axis on the
-    GPT-2-small-shaped tensor (294,912 fp16 vectors; event-timed, median of
-    ``reps``, inputs resident).  Attention: one query per (layer, head) over the
-    just-encoded halves (B = 12, Hq = Hkv = 12, T = 1024), where the codebook fits
-    in LDS."""
+    GPT-2-small-shaped tensor (294,912 fp16 vectors; event-timed medians of
+    ``reps`` launches, each after an eviction of L2 and the last-level cache).
+    Attention: one query per (layer, head) over the just-encoded halves (B = 12,
+    Hq = Hkv = 12, T = 1024), where the attention kernels cover the codebook."""
     import torch
 
     x = torch.from_numpy(workloads.gpt2_small_kv()).to(dev)
@@ -209,16 +258,7 @@ def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
     out = {}
 
     def timed(fn):
-        ts = []
-        for r in range(reps + 1):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if r:
-                ts.append(e0.elapsed_time(e1))
-        return float(np.median(ts)) / 1e3
+        return timed_evicted(fn, stream, flush, reps, warm=1)
 
     for k, N in RATE_AXIS:
         try:
@@ -236,7 +276,7 @@ def rate_axis_timings(fq, workloads, dev, stream, reps: int = 3):
         rec = {"b": bits / k, "record_bits": (D // k) * bits, "encode_us": t_e * 1e6, "encode_vec_per_s": n / t_e,
                "encode_cmp_frac": (D // k) * N * n / t_e / 1e12 / CMP_PEAK_T, "decode_us": t_d * 1e6,
                "decode_GBps": dbytes / t_d / 1e9, "decode_hbm_frac": dbytes / t_d / 1e9 / HBM_PEAK_GBPS}
-        if k * N <= 16384:
+        if fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T) > 0:
             half = cb.code_bytes(n // 2)
             ws = torch.empty(max(fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T), 16), dtype=torch.uint8,
                              device=dev)
@@ -320,42 +360,65 @@ def main():
         print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
         return
 
-    # ---------------------------------------------------------------- headline workload
-    w = workloads.WORKLOADS["gpt2s_kv"]
+    flush = evict_reader(dev)
+    progress("generating the TinyLlama-shaped cache and the attention workload")
+
+    # ---------------------------------------------------------------- the step's inputs
+    # TinyLlama-shaped cache, k = 8, N = 4096
+    w = workloads.WORKLOADS["tinyllama_kv"]
     cb = fq.Codebook.from_artifact(w.k, w.N)
-    x_np = workloads.gpt2_small_kv(w.seed)
-    n = len(x_np)
-    x = torch.from_numpy(x_np).to(dev)
+    x = torch.from_numpy(workloads.tinyllama_kv(w.seed)).to(dev)
+    n = x.shape[0]
     codes = torch.empty(cb.code_bytes(n), dtype=torch.uint8, device=dev)
     norms = torch.empty(n, dtype=torch.float16, device=dev)
     xr = torch.empty_like(x)
-    L, H, T = workloads.GPT2_L, workloads.GPT2_H, workloads.GPT2_T
-    q = torch.from_numpy(workloads.gpt2_small_queries()).to(dev)
-    half_bytes = cb.code_bytes(n // 2)
-    k_codes, v_codes = codes[:half_bytes], codes[half_bytes:]
-    k_norms, v_norms = norms[: n // 2], norms[n // 2:]
-    attn_out = torch.empty((L, H, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T), 16), dtype=torch.uint8, device=dev)
+    # attention workload: K and V draws encoded with k = 4, N = 256 (not timed)
+    wa = workloads.WORKLOADS["attn_b16_t32k"]
+    cba = fq.Codebook.from_artifact(wa.k, wa.N)
+    B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+    qa_np, kv_np = workloads.attention_inputs()
+    na = B * Hkv * Ta
+    kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
+    ac = torch.empty(2 * cba.code_bytes(na), dtype=torch.uint8, device=dev)
+    an = torch.empty(2 * na, dtype=torch.float16, device=dev)
+    fq.fq_encode(cba.handle, kv, ac, an, stream)
+    del kv
+    qa = torch.from_numpy(qa_np).to(dev)
+    ao = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    aws = torch.empty(fq.fq_attn_workspace_bytes(cba.handle, B, Hq, Hkv, Ta), dtype=torch.uint8, device=dev)
+    kcs, vcs = ac[: cba.code_bytes(na)], ac[cba.code_bytes(na):]
+    kns, vns = an[:na], an[na:]
 
+    def enc():
+        fq.fq_encode(cb.handle, x, codes, norms, stream)
+
+    def dec():
+        fq.fq_decode(cb.handle, codes, norms, xr, stream)
+
+    def att():
+        fq.fq_attn_decode(cba.handle, qa, kcs, kns, vcs, vns, B, Hq, Hkv, Ta, 0.125, ao, aws, stream)
+
+    # ---------------------------------------------------------------- the timed steps
     ev = {k: [] for k in ("enc", "dec", "att")}
 
     def step(record: bool):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             e[0].record(stream)
-        fq.fq_encode(cb.handle, x, codes, norms, stream)
+        enc()
         if record:
             e[1].record(stream)
-        fq.fq_decode(cb.handle, codes, norms, xr, stream)
+        dec()
         if record:
             e[2].record(stream)
-        fq.fq_attn_decode(cb.handle, q, k_codes, k_norms, v_codes, v_norms, L, H, H, T, 0.125, attn_out, ws, stream)
+        att()
         if record:
             e[3].record(stream)
             ev["enc"].append((e[0], e[1]))
             ev["dec"].append((e[1], e[2]))
             ev["att"].append((e[2], e[3]))
 
+    progress("inputs resident; timing the steps")
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -364,209 +427,186 @@ def main():
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    in_step_us = {k: float(np.median([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in ev.items()}
     ms_step = elapsed * 1e3 / args.steps
     value = n * args.steps / elapsed
 
-    # dominant kernel roofline: the encoder's nearest-codeword search; every
-    # candidate score needs at least one comparison (two per three-input min)
+    # ---------------------------------------------------------------- each kernel after an eviction
+    progress(f"{args.steps} steps in {elapsed:.3f} s; timing each kernel after an eviction")
+    reps = args.attn_iters
+    t_e = timed_evicted(enc, stream, flush, reps)
+    t_d = timed_evicted(dec, stream, flush, reps)
+    t_a = timed_evicted(att, stream, flush, reps)
+    codec = codec_record(fq, cb, x, n, norms, w, t_e, t_d)
+    # dominant kernel: the encoder's nearest-codeword search.  The matrix core scores
+    # every candidate; what remains on the vector ALU is at least one comparison per
+    # candidate score, two per lane-op with a three-input minimum.
     cmp_per_vec = (D // w.k) * w.N
-    enc_s = ms["enc"] / 1e3
-    achieved = cmp_per_vec * n / enc_s / 1e12
-    enc_bytes = n * (D * 2 + 2) + cb.code_bytes(n)
-    dec_bytes = enc_bytes
-    att_bytes = 2 * cb.code_bytes(n // 2) + 2 * (n // 2) * 2 + L * H * D * 2 + L * H * D * 4
-    traffic = measured_traffic("encode_h16_k4", "fq_encode_h16.hip")
+    achieved = cmp_per_vec * n / t_e / 1e12
+    abytes = 2 * cba.code_bytes(na) + 2 * na * 2 + B * Hq * D * 2 + B * Hq * D * 4
     line = {
         "metric": METRIC, "value": value, "unit": "vectors/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "gpt2s_kv", "vectors": n, "layout": "[2 KV][12 layers][12 heads][1024 tokens][64]",
-                   "input_dtype": "f16", "d": D, "k": w.k, "N": w.N, "bits_per_coordinate": np.log2(w.N) / w.k,
-                   "step": "fq_encode + fq_decode + fq_attn_decode(B=12 layers, Hq=Hkv=12, T=1024)"},
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "tinyllama_kv", "vectors": n,
+                   "layout": "[22 layers][4 KV heads][K, V][8 batch x 4096 tokens][64]", "input_dtype": "f16",
+                   "d": D, "k": w.k, "N": w.N, "bits_per_coordinate": float(np.log2(w.N) / w.k),
+                   "step": "fq_encode + fq_decode of the TinyLlama-shaped cache, then fq_attn_decode(B=16, Hq=32, "
+                           "Hkv=4, T=32768; k=4, N=256 codes)"},
         "fp16_equiv_GBps": value * D * 2 / 1e9,
-        "breakdown_us": {"encode": ms["enc"] * 1e3, "decode": ms["dec"] * 1e3, "attention": ms["att"] * 1e3},
-        "breakdown_GBps": {"encode": enc_bytes / (ms["enc"] / 1e3) / 1e9,
-                           "decode": dec_bytes / (ms["dec"] / 1e3) / 1e9,
-                           "attention": att_bytes / (ms["att"] / 1e3) / 1e9},
-        "roofline": {"kernel": "encode_h16<k=4> (fq_encode, fp16 input)", "bound": "alu", "achieved": achieved,
-                     "peak": CMP_PEAK_T, "unit": "TFLOP/s", "frac": achieved / CMP_PEAK_T,
-                     "traffic": traffic,
-                     "work": f"{cmp_per_vec} candidate-score comparisons per vector ((d/k) N) x {n} vectors; "
-                             f"peak = 2 comparisons per VALU lane-op (three-input min) x 39.3 T lane-ops/s",
-                     # the same time against the VALU-search model (k/2 + 1 lane-ops per score: packed
-                     # FMAs plus a select), for comparison with designs that score on the VALU
-                     "frac_vs_valu_search_model": cmp_per_vec * (w.k / 2 + 1) * n / VALU_LANE_OPS / enc_s},
-    }
-
-    # ---------------------------------------------------------------- decode-attention workload
-    if not args.no_attn_workload:
-        B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
-        qa_np, kv_np = workloads.attention_inputs()
-        kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
-        na = B * Hkv * Ta
-        ac = torch.empty(2 * cb.code_bytes(na), dtype=torch.uint8, device=dev)
-        an = torch.empty(2 * na, dtype=torch.float16, device=dev)
-        fq.fq_encode(cb.handle, kv, ac, an, stream)
-        del kv
-        qa = torch.from_numpy(qa_np).to(dev)
-        ao = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-        aws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, Ta), dtype=torch.uint8, device=dev)
-        kcs, vcs = ac[: cb.code_bytes(na)], ac[cb.code_bytes(na):]
-        kns, vns = an[:na], an[na:]
-        # Eviction between launches READS a 512 MiB buffer, leaving L2 and the 256 MB
-        # last-level cache full of clean lines of it; a write-based fill would leave
-        # dirty lines whose write-back lands inside the timed launch.
-        flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
-        times = []
-        for it in range(args.attn_iters + 3):
-            flush.max()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fq.fq_attn_decode(cb.handle, qa, kcs, kns, vcs, vns, B, Hq, Hkv, Ta, 0.125, ao, aws, stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if it >= 3:
-                times.append(e0.elapsed_time(e1))
-        t_att = float(np.median(times)) / 1e3
-        abytes = 2 * cb.code_bytes(na) + 2 * na * 2 + B * Hq * D * 2 + B * Hq * D * 4
-        line["attn_b16_t32k"] = {
-            "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms, caches evicted (512 MiB read) "
-                        "before every launch",
-            "us_per_step": t_att * 1e6, "hbm_bytes": abytes, "GBps": abytes / t_att / 1e9,
-            "fp16_equiv_GBps": 2 * na * D * 2 / t_att / 1e9,
+        "in_step_us": in_step_us,
+        "breakdown_us": {"encode": t_e * 1e6, "decode": t_d * 1e6, "attention": t_a * 1e6,
+                         "note": "each kernel alone after an eviction of L2 and the last-level cache"},
+        "codec_evicted": codec,
+        "roofline": {"kernel": "encode_h16<k=8> (fq_encode, fp16 input)", "bound": "alu", "achieved": achieved,
+                     "peak": CMP_PEAK_T, "unit": "TOP/s", "frac": achieved / CMP_PEAK_T,
+                     "traffic": measured_traffic("encode_h16_k8", "fq_encode_h16.hip"),
+                     "work": f"{cmp_per_vec} candidate-score comparisons per vector ((d/k) N) x {n} vectors; peak = "
+                             f"2 comparisons per VALU lane-op (three-input min) x 39.3 T lane-ops/s",
+                     # the survey's model for this search: one VALU lane-op per candidate score
+                     "frac_vs_one_op_per_score": cmp_per_vec * n / VALU_LANE_OPS / t_e},
+        "attn_b16_t32k": {
+            "workload": "B=16, Hq=32, Hkv=4, T=32768, k=4, N=256 codes + fp16 norms (GPU encode of the attention "
+                        "workload's K and V draws), caches evicted before every launch",
+            "us_per_step": t_a * 1e6, "hbm_bytes": abytes, "GBps": abytes / t_a / 1e9,
+            "fp16_equiv_GBps": 2 * na * D * 2 / t_a / 1e9,
             "roofline": {"kernel": "attn_k4b8 (+ attn_combine: the events bracket the whole fq_attn_decode call)",
-                         "bound": "hbm", "achieved": abytes / t_att / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": abytes / t_att / 1e9 / HBM_PEAK_GBPS,
-                         "traffic": measured_traffic("attn_k4b8", "fq_attn.hip")},
+                         "bound": "hbm", "achieved": abytes / t_a / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": abytes / t_a / 1e9 / HBM_PEAK_GBPS,
+                         "traffic": measured_traffic("attn_k4b8", "fq_attn.hip")}},
+    }
+    del x, xr
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ prefill over the attention cache
+    # 64 causal queries per head (a 64-token chunk appended to the 32k cache): useful
+    # work 4 * 64 flops per (query, visible key) pair (QK and PV); the kernel issues
+    # 1.5x that on the matrix core (the query enters as fp16 hi + lo).
+    if not args.no_prefill:
+        progress("prefill")
+        Sq = 64
+        qp = torch.from_numpy(np.random.default_rng(107).standard_normal((B, Hq, Sq, D)).astype(np.float16)).to(dev)
+        po = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
+        pws = torch.empty(fq.fq_attn_prefill_workspace_bytes(cba.handle, B, Hq, Hkv, Sq, Ta), dtype=torch.uint8,
+                          device=dev)
+        t_p = timed_evicted(lambda: fq.fq_attn_prefill(cba.handle, qp, kcs, kns, vcs, vns, B, Hq, Hkv, Sq, Ta, True,
+                                                       0.125, po, pws, stream), stream, flush, args.attn_iters)
+        pairs = B * Hq * sum(Ta - Sq + i + 1 for i in range(Sq))
+        useful = 4.0 * D * pairs
+        line["prefill_b16_t32k_q64"] = {
+            "workload": "B=16, Hq=32, Hkv=4, T=32768, 64 causal queries per head (the last 64 positions), "
+                        "k=4, N=256 codes + fp16 norms, caches evicted before every launch",
+            "us_per_step": t_p * 1e6, "query_key_pairs": pairs,
+            "roofline": {"kernel": "attn_prefill_k4b8 (+ attn_combine)", "bound": "mfma",
+                         "achieved": useful / t_p / 1e12, "peak": FP16_MFMA_PEAK_T, "unit": "TFLOP/s",
+                         "frac": useful / t_p / 1e12 / FP16_MFMA_PEAK_T, "traffic": None,
+                         "issued_TFLOPs": 1.5 * useful / t_p / 1e12},
         }
+        del qp, po, pws
 
-        # ------------------------------------------------------------ prefill over the same cache
-        # 64 causal queries per head (a 64-token chunk appended to the 32k cache): useful
-        # work 4 * 64 flops per (query, visible key) pair (QK and PV); the kernel issues
-        # 1.5x that on the matrix core (the query enters as fp16 hi + lo).
-        if not args.no_prefill:
-            Sq = 64
-            qp = torch.from_numpy(np.random.default_rng(107).standard_normal((B, Hq, Sq, D)).astype(np.float16)).to(dev)
-            po = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
-            pws = torch.empty(fq.fq_attn_prefill_workspace_bytes(cb.handle, B, Hq, Hkv, Sq, Ta), dtype=torch.uint8,
-                              device=dev)
-            flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
-            tp = []
-            for it in range(args.attn_iters + 3):
-                flush.max()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fq.fq_attn_prefill(cb.handle, qp, kcs, kns, vcs, vns, B, Hq, Hkv, Sq, Ta, True, 0.125, po, pws,
-                                   stream)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                if it >= 3:
-                    tp.append(e0.elapsed_time(e1))
-            t_p = float(np.median(tp)) / 1e3
-            pairs = B * Hq * sum(Ta - Sq + i + 1 for i in range(Sq))
-            useful = 4.0 * D * pairs
-            line["prefill_b16_t32k_q64"] = {
-                "workload": "B=16, Hq=32, Hkv=4, T=32768, 64 causal queries per head (the last 64 positions), "
-                            "k=4, N=256 codes + fp16 norms, caches evicted before every launch",
-                "us_per_step": t_p * 1e6, "query_key_pairs": pairs,
-                "roofline": {"kernel": "attn_prefill_k4b8 (+ attn_combine)", "bound": "mfma",
-                             "achieved": useful / t_p / 1e12, "peak": FP16_MFMA_PEAK_T, "unit": "TFLOP/s",
-                             "frac": useful / t_p / 1e12 / FP16_MFMA_PEAK_T, "traffic": None,
-                             "issued_TFLOPs": 1.5 * useful / t_p / 1e12},
-            }
-            del flush
-
-        # ------------------------------------------------------------ decode loop over the same cache
-        # One decode step per sequence: the new token's K and V go to slot len_b of their
-        # (batch, KV head) slab (fq_encode_scatter), then attention runs over len_b + 1
-        # keys (fq_attn_decode_varlen).  Lengths start spread over [T/2, T - iters) and
-        # grow by one per step; slots and lengths of every step are on the device
-        # before timing, and the caches are evicted before every step.
-        if not args.no_decode_loop:
-            iters = args.attn_iters
-            rng = np.random.default_rng(106)
-            len0 = rng.integers(Ta // 2, Ta - iters - 4, size=B)
-            base = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None, :]) * Ta  # [B, Hkv] slab starts
-            # K and V caches are the two halves of one store (records [0, na) and [na, 2 na)),
-            # so one call appends both
-            slots_all = torch.from_numpy(np.stack([np.concatenate([(base + (len0 + it)[:, None]).reshape(-1)] * 2)
-                                                   + np.repeat([0, na], B * Hkv)
-                                                   for it in range(iters + 3)]).astype(np.int64)).to(dev)
-            lens_all = torch.from_numpy(np.stack([len0 + it + 1 for it in range(iters + 3)]).astype(np.int32)).to(dev)
-            newkv = torch.from_numpy(np.ascontiguousarray(kv_np[:, :, :, :iters + 3].transpose(3, 0, 1, 2, 4))
-                                     .reshape(iters + 3, 2 * B * Hkv, D)).to(dev)
-            flush = torch.ones(128 * 1024 * 1024, dtype=torch.int32, device=dev)
-            t_app, t_var = [], []
-            for it in range(iters + 3):
-                flush.max()
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                e[0].record(stream)
-                fq.fq_encode_scatter(cb.handle, newkv[it], slots_all[it], 2 * na, ac, an, stream)
-                e[1].record(stream)
-                fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, lens_all[it], B, Hq, Hkv, Ta, 0.125, ao,
-                                         aws, stream)
-                e[2].record(stream)
-                torch.cuda.synchronize()
-                if it >= 3:
-                    t_app.append(e[0].elapsed_time(e[1]))
-                    t_var.append(e[1].elapsed_time(e[2]))
-            t_a, t_v = float(np.median(t_app)) / 1e3, float(np.median(t_var)) / 1e3
-            # The same step captured once as a HIP graph: every replay reads this step's new
-            # vectors, slots and lengths from fixed device buffers, refreshed before replay.
-            x_buf, s_buf, l_buf = newkv[0].clone(), slots_all[0].clone(), lens_all[0].clone()
-            gs = torch.cuda.Stream()
-            gs.wait_stream(stream)
-            with torch.cuda.stream(gs):  # warm-up on the capture stream
-                fq.fq_encode_scatter(cb.handle, x_buf, s_buf, 2 * na, ac, an, gs)
-                fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, l_buf, B, Hq, Hkv, Ta, 0.125, ao, aws, gs)
-            stream.wait_stream(gs)
-            graph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(graph):
-                cs = torch.cuda.current_stream()
-                fq.fq_encode_scatter(cb.handle, x_buf, s_buf, 2 * na, ac, an, cs)
-                fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, l_buf, B, Hq, Hkv, Ta, 0.125, ao, aws, cs)
-            t_graph = []
-            for it in range(iters + 3):
-                x_buf.copy_(newkv[it])
-                s_buf.copy_(slots_all[it])
-                l_buf.copy_(lens_all[it])
-                flush.max()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                graph.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                if it >= 3:
-                    t_graph.append(e0.elapsed_time(e1))
-            t_g = float(np.median(t_graph)) / 1e3
-            del graph
-            keys = int(lens_all[3:].sum().item()) * Hkv / iters  # keys read per step, all slabs
-            vbytes = keys * (16 + 16 + 2 + 2) + B * Hq * D * 2 + B * Hq * D * 4
-            line["decode_loop_b16_t32k"] = {
-                "workload": "B=16, Hq=32, Hkv=4, cache capacity T=32768, per-batch lengths uniform in [T/2, T); per "
-                            "step: 64 new K and 64 new V vectors encoded into their slots (one call), then attention "
-                            "over each "
-                            "batch's valid keys; caches evicted before every step",
-                "us_per_step": (t_a + t_v) * 1e6, "breakdown_us": {"append": t_a * 1e6, "attention": t_v * 1e6},
-                "us_per_step_graph": t_g * 1e6,
-                "keys_per_step": keys, "hbm_bytes_attention": vbytes,
-                "roofline": {"kernel": "attn_k4b8 with per-batch lengths (+ attn_combine)", "bound": "hbm",
-                             "achieved": vbytes / t_v / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": vbytes / t_v / 1e9 / HBM_PEAK_GBPS, "traffic": None},
-            }
-            del flush
-
+    # ------------------------------------------------------------ decode loop over the attention cache
+    # One decode step per sequence: the new token's K and V go to slot len_b of their
+    # (batch, KV head) slab (fq_encode_scatter), then attention runs over len_b + 1
+    # keys (fq_attn_decode_varlen).  Lengths start spread over [T/2, T - iters) and
+    # grow by one per step; slots and lengths of every step are on the device
+    # before timing, and the caches are evicted before every step.
+    if not args.no_decode_loop:
+        progress("decode loop")
+        line["decode_loop_b16_t32k"] = decode_loop(fq, cba, dev, stream, flush, args.attn_iters, kv_np, qa, ac, an,
+                                                   kcs, kns, vcs, vns, ao, aws)
+    del kv_np
     if not args.no_workloads:
-        line["workloads"] = workload_timings(fq, workloads, dev, stream)
+        progress("other codec workloads")
+        line["workloads"] = workload_timings(fq, workloads, dev, stream, flush)
     if not args.no_rate_axis:
-        line["rate_axis"] = rate_axis_timings(fq, workloads, dev, stream)
+        progress("rate axis")
+        line["rate_axis"] = rate_axis_timings(fq, workloads, dev, stream, flush)
     if not args.no_build:
+        progress("codebook construction")
         line["codebook_build"] = build_timings(fq, workloads, dev, stream)
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline()
     cb.close()
+    cba.close()
     print(json.dumps(line), flush=True)
+
+
+def decode_loop(fq, cb, dev, stream, flush, iters, kv_np, qa, ac, an, kcs, kns, vcs, vns, ao, aws):
+    import torch
+
+    import workloads
+
+    B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+    na = B * Hkv * Ta
+    rng = np.random.default_rng(106)
+    len0 = rng.integers(Ta // 2, Ta - iters - 4, size=B)
+    base = (np.arange(B)[:, None] * Hkv + np.arange(Hkv)[None, :]) * Ta  # [B, Hkv] slab starts
+    # K and V caches are the two halves of one store (records [0, na) and [na, 2 na)),
+    # so one call appends both
+    slots_all = torch.from_numpy(np.stack([np.concatenate([(base + (len0 + it)[:, None]).reshape(-1)] * 2)
+                                           + np.repeat([0, na], B * Hkv)
+                                           for it in range(iters + 3)]).astype(np.int64)).to(dev)
+    lens_all = torch.from_numpy(np.stack([len0 + it + 1 for it in range(iters + 3)]).astype(np.int32)).to(dev)
+    newkv = torch.from_numpy(np.ascontiguousarray(kv_np[:, :, :, :iters + 3].transpose(3, 0, 1, 2, 4))
+                             .reshape(iters + 3, 2 * B * Hkv, D)).to(dev)
+    t_app, t_var = [], []
+    for it in range(iters + 3):
+        flush.max()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        fq.fq_encode_scatter(cb.handle, newkv[it], slots_all[it], 2 * na, ac, an, stream)
+        e[1].record(stream)
+        fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, lens_all[it], B, Hq, Hkv, Ta, 0.125, ao, aws,
+                                 stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t_app.append(e[0].elapsed_time(e[1]))
+            t_var.append(e[1].elapsed_time(e[2]))
+    t_a, t_v = float(np.median(t_app)) / 1e3, float(np.median(t_var)) / 1e3
+    # The same step captured once as a HIP graph: every replay reads this step's new
+    # vectors, slots and lengths from fixed device buffers, refreshed before replay.
+    x_buf, s_buf, l_buf = newkv[0].clone(), slots_all[0].clone(), lens_all[0].clone()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):  # warm-up on the capture stream
+        fq.fq_encode_scatter(cb.handle, x_buf, s_buf, 2 * na, ac, an, gs)
+        fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, l_buf, B, Hq, Hkv, Ta, 0.125, ao, aws, gs)
+    stream.wait_stream(gs)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        fq.fq_encode_scatter(cb.handle, x_buf, s_buf, 2 * na, ac, an, cs)
+        fq.fq_attn_decode_varlen(cb.handle, qa, kcs, kns, vcs, vns, l_buf, B, Hq, Hkv, Ta, 0.125, ao, aws, cs)
+    t_graph = []
+    for it in range(iters + 3):
+        x_buf.copy_(newkv[it])
+        s_buf.copy_(slots_all[it])
+        l_buf.copy_(lens_all[it])
+        flush.max()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if it >= 3:
+            t_graph.append(e0.elapsed_time(e1))
+    t_g = float(np.median(t_graph)) / 1e3
+    del graph
+    keys = int(lens_all[3:].sum().item()) * Hkv / iters  # keys read per step, all slabs
+    vbytes = keys * (16 + 16 + 2 + 2) + B * Hq * D * 2 + B * Hq * D * 4
+    return {
+        "workload": "B=16, Hq=32, Hkv=4, cache capacity T=32768, per-batch lengths uniform in [T/2, T); per "
+                    "step: 64 new K and 64 new V vectors encoded into their slots (one call), then attention "
+                    "over each batch's valid keys; caches evicted before every step",
+        "us_per_step": (t_a + t_v) * 1e6, "breakdown_us": {"append": t_a * 1e6, "attention": t_v * 1e6},
+        "us_per_step_graph": t_g * 1e6,
+        "keys_per_step": keys, "hbm_bytes_attention": vbytes,
+        "roofline": {"kernel": "attn_k4b8 with per-batch lengths (+ attn_combine)", "bound": "hbm",
+                     "achieved": vbytes / t_v / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": vbytes / t_v / 1e9 / HBM_PEAK_GBPS, "traffic": None},
+    }
 
 
 if __name__ == "__main__":

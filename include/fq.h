@@ -102,6 +102,15 @@ int64_t fq_code_bytes(const fq_codebook* cb, int64_t n);
 fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                     void* norms, fq_dtype norm_dtype, void* stream);
 
+/* Name of the encoder kernel fq_encode (and fq_encode_scatter) launches for n
+ * vectors of dtype x_dtype with this codebook: "encode_wave" (batches of at most
+ * 2048 vectors), "encode_h16" (fp16 input, k = 4 or 8), "encode_full" (fp16
+ * input, k = d), "encode_mfma" (k = 4 or 8) or "encode_valu" (every shape).  The
+ * environment variable FQ_ENCODE_KERNEL, read by fq_codebook_load, forces one of
+ * them (small, h16, full, mfma, valu) wherever it covers the call.  A diagnostic:
+ * static string, NULL for a NULL handle, n < 0 or an invalid dtype. */
+const char* fq_encode_kernel(const fq_codebook* cb, fq_dtype x_dtype, int64_t n);
+
 /* Encode n vectors into chosen records of an existing code store: the append
  * step of a growing cache (FibQuant summary §1 and §5: every record has a fixed
  * size and address, so one record is rewritten without touching the others).
@@ -145,8 +154,10 @@ size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, in
  *   k_norms, v_norms: device fp16 [B][Hkv][T].
  *   out:      device fp32 [B][Hq][d].
  *   workspace: device, at least fq_attn_workspace_bytes(...) bytes.
- * Hq must be a multiple of Hkv with Hq/Hkv <= 16, and the codebook must fit
- * N*k <= 32768 (its fp16 copy lives in LDS); otherwise FQ_ERR_UNSUPPORTED.
+ * Hq must be a multiple of Hkv with Hq/Hkv <= 16, and the kernel's LDS must hold
+ * the codebook: its fp16 copy (2 N k bytes) plus 20,992 bytes of the kernel's own
+ * buffers must fit in one workgroup's LDS, i.e. N*k <= 65536 on gfx950 (160 KiB);
+ * otherwise FQ_ERR_UNSUPPORTED (and fq_attn_workspace_bytes returns 0).
  * There is no mask: the single query attends to all T keys. */
 fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,

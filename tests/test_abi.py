@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
                                   "fq_attn_prefill_workspace_bytes", "fq_attn_workspace_bytes",
                                   "fq_code_bytes", "fq_codebook_free", "fq_codebook_load", "fq_decode",
                                   "fq_codebook_train", "fq_codebook_train_workspace_bytes",
-                                  "fq_encode", "fq_encode_scatter", "fq_status_string"])
+                                  "fq_encode", "fq_encode_kernel", "fq_encode_scatter", "fq_status_string"])
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -54,6 +54,8 @@ def test_status_strings(L):
 def test_null_handle_paths_without_gpu(L):
     vp = ctypes.c_void_p
     assert L.fq_code_bytes(None, 10) == -1
+    L.fq_encode_kernel.restype = ctypes.c_char_p
+    assert L.fq_encode_kernel(None, fq.FQ_F16, 10) is None
     assert L.fq_encode(None, vp(16), fq.FQ_F16, 1, vp(16), vp(16), fq.FQ_F16, None) == fq.FQ_ERR_ARG
     assert L.fq_decode(None, vp(16), vp(16), fq.FQ_F16, 1, vp(16), fq.FQ_F16, None) == fq.FQ_ERR_ARG
     assert L.fq_attn_workspace_bytes(None, 1, 8, 1, 10) == 0

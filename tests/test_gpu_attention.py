@@ -135,6 +135,52 @@ def test_attention_on_oracle_encoded_cache(dev, cb4):
     assert max_rel_rows(got, ref) <= TOL
 
 
+def test_attention_full_size_oracle_encoded_slabs(dev, cb4):
+    # The benchmark's launch (B=16, Hq=32, Hkv=4, T=32768) on the GPU encode of the
+    # attention workload's whole K and V draw.  For three (batch, KV head) slabs the
+    # oracle encodes all 32,768 keys and values: the GPU's codes must meet the codec
+    # bar there, and the attention rows of the slab's 8 query heads must match the
+    # oracle's attention over those (accepted) codes.
+    import torch
+
+    cb, cw, rot = cb4
+    B, Hq, Hkv, T = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+    G = Hq // Hkv
+    q, kv = workloads.attention_inputs()
+    n = B * Hkv * T
+    print("[attention full size, oracle-encoded slabs] encode K and V on the GPU", flush=True)
+    x = torch.from_numpy(kv.reshape(2 * n, D)).to(dev)
+    codes = torch.empty(cb.code_bytes(2 * n), dtype=torch.uint8, device=dev)
+    norms = torch.empty(2 * n, dtype=torch.float16, device=dev)
+    fq.fq_encode(cb.handle, x, codes, norms)
+    del x
+    half = cb.code_bytes(n)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, T), dtype=torch.uint8, device=dev)
+    fq.fq_attn_decode(cb.handle, to_dev(q, dev), codes[:half], norms[:n], codes[half:], norms[n:], B, Hq, Hkv, T,
+                      0.125, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gc, gn = codes.cpu().numpy(), norms.cpu().numpy()
+    del codes, norms, ws
+    for b, g in [(0, 0), (6, 2), (15, 3)]:
+        idx = np.arange(T) + (b * Hkv + g) * T
+        kx, vx = kv[0, b, g], kv[1, b, g]
+        kcodes = unpack_sampled(gc[:half], idx, 16, 8)
+        vcodes = unpack_sampled(gc[half:], idx, 16, 8)
+        print(f"[attention full size, oracle-encoded slabs] oracle encode of slab b={b} g={g}", flush=True)
+        for xx, cc, nn in ((kx, kcodes, gn[:n][idx]), (vx, vcodes, gn[n:][idx])):
+            enc = oc.encode(xx, rot, cw, np.float16)
+            mism = cc != enc.codes
+            assert not (mism & ~enc.near_tie).any()
+            assert oc.accepted(enc.y, cw, enc, cc).all()
+            assert np.array_equal(nn.view(np.uint16), enc.norms.view(np.uint16))
+        ref = oatt.attention(q[b:b + 1, g * G:(g + 1) * G], kcodes.reshape(1, 1, T, 16),
+                             gn[:n][idx].reshape(1, 1, T), vcodes.reshape(1, 1, T, 16),
+                             gn[n:][idx].reshape(1, 1, T), rot, cw, 0.125)
+        assert max_rel_rows(got[b:b + 1, g * G:(g + 1) * G], ref) <= TOL
+
+
 def test_attention_deterministic_and_workspace_errors(dev, cb4):
     import torch
 

@@ -35,7 +35,8 @@ RATES = [
     (32, 512),    # b = 0.28125
     (64, 16384),  # b = 0.21875: 64 coordinates in 14 bits (+ a 16-bit norm: 34.1x)
 ]
-ATTN_RATES = [(k, N) for k, N in RATES if k * N <= 16384]  # the codebook must fit in LDS
+# the general attention kernel holds the fp16 codebook in LDS: N k <= 65536 on gfx950
+ATTN_RATES = [(k, N) for k, N in RATES if k * N <= 65536]
 
 
 @pytest.fixture(scope="module")
@@ -132,13 +133,26 @@ def test_attention_rate_axis(dev, k, N):
     assert max_rel_rows(out.cpu().numpy(), ref) <= TOL
 
 
-def test_attention_rejects_codebooks_beyond_lds(dev):
+def test_attention_codebook_limit(dev):
+    # At the limit (k = 4, N = 16384: 65536 fp16 values, 128 KiB of LDS) the call is
+    # accepted (its parity is test_attention_rate_axis); one step past it (k = 8,
+    # N = 16384) it is refused before any launch.
     import torch
 
-    cb, _, _ = codebook(4, 16384)
+    at, _, _ = codebook(4, 16384)
+    assert fq.fq_attn_workspace_bytes(at.handle, 1, 8, 1, 4) > 0
+    rng = np.random.default_rng(17)
+    cw = (rng.standard_normal((16384, 8)) * 0.15).astype(np.float16).astype(np.float32)
+    cw[np.abs(cw) < 2.0 ** -14] = 0.0
+    _, rot = fq.load_artifact(4, 256)
+    past = fq.Codebook(cw, rot)
+    assert fq.fq_attn_workspace_bytes(past.handle, 1, 8, 1, 4) == 0
     q = torch.zeros((1, 8, D), dtype=torch.float16, device=dev)
-    z = torch.zeros(16, dtype=torch.uint8, device=dev)
+    z = torch.zeros(64, dtype=torch.uint8, device=dev)
+    out = torch.full((1, 8, D), 5.0, dtype=torch.float32, device=dev)
     with pytest.raises(fq.FQError) as e:
-        fq.fq_attn_decode(cb.handle, q, z, z, z, z, 1, 8, 1, 4, 0.125,
-                          torch.zeros((1, 8, D), dtype=torch.float32, device=dev), z)
+        fq.fq_attn_decode(past.handle, q, z, z, z, z, 1, 8, 1, 4, 0.125, out, z)
     assert e.value.status == fq.FQ_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert float(out.min()) == 5.0  # nothing was launched
+    past.close()

@@ -19,7 +19,7 @@ import numpy as np
 __all__ = [
     "FQ_OK", "FQ_ERR_ARG", "FQ_ERR_UNSUPPORTED", "FQ_ERR_WORKSPACE", "FQ_ERR_HIP", "FQ_F32", "FQ_F16",
     "FQError", "lib", "library_path", "fq_status_string", "fq_codebook_load", "fq_codebook_free", "fq_code_bytes",
-    "fq_encode", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
+    "fq_encode", "fq_encode_kernel", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
     "fq_attn_decode_varlen", "fq_attn_prefill_workspace_bytes", "fq_attn_prefill",
     "fq_codebook_train_workspace_bytes", "fq_codebook_train", "Codebook",
     "load_artifact",
@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.fq_code_bytes.argtypes, L.fq_code_bytes.restype = [vp, i64], i64
         L.fq_encode.argtypes = [vp, vp, i32, i64, vp, vp, i32, vp]
         L.fq_encode.restype = i32
+        L.fq_encode_kernel.argtypes, L.fq_encode_kernel.restype = [vp, i32, i64], ctypes.c_char_p
         L.fq_encode_scatter.argtypes = [vp, vp, i32, i64, vp, i64, vp, vp, i32, vp]
         L.fq_encode_scatter.restype = i32
         L.fq_decode.argtypes = [vp, vp, vp, i32, i64, vp, i32, vp]
@@ -141,6 +142,14 @@ def fq_encode(cb: int, x, codes, norms, stream=None) -> None:
     n = x.shape[0] if x.dim() else 0
     _check("fq_encode", lib().fq_encode(cb, _ptr(x), _dtype_code(x), n, _ptr(codes), _ptr(norms),
                                         _dtype_code(norms), _stream(stream)))
+
+
+def fq_encode_kernel(cb: int, x_dtype: int, n: int) -> str:
+    """Name of the encoder kernel fq_encode launches for n vectors of x_dtype (FQ_F16 / FQ_F32)."""
+    r = lib().fq_encode_kernel(cb, int(x_dtype), int(n))
+    if r is None:
+        raise ValueError("invalid arguments")
+    return r.decode()
 
 
 def fq_encode_scatter(cb: int, x, slots, capacity: int, codes, norms, stream=None) -> None:

@@ -14,6 +14,7 @@
 
 #define FQ_EXPORT extern "C" __attribute__((visibility("default")))
 
+
 namespace fq {
 
 hipError_t resident_workgroups(const void* kernel, int block, size_t lds, int device, int64_t* out) {
@@ -279,7 +280,10 @@ fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const fl
 }  // namespace
 
 FQ_EXPORT const char* fq_status_string(fq_status st) {
-  switch (st) {
+  // C callers may pass any int: read its bytes, never the value as the C++ enum type
+  int v;
+  memcpy(&v, &st, sizeof v);
+  switch (v) {
     case FQ_OK: return "ok";
     case FQ_ERR_ARG: return "invalid argument";
     case FQ_ERR_UNSUPPORTED: return "unsupported configuration";
@@ -313,8 +317,14 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   cb->B = cb->nblk * cb->bits;
   {
     const char* ek = getenv("FQ_ENCODE_KERNEL");
-    cb->force_valu = ek && strcmp(ek, "valu") == 0;
-    cb->force_mfma64 = ek && strcmp(ek, "mfma64") == 0;
+    cb->force_encoder = fq::ENC_AUTO;
+    if (ek) {
+      if (!strcmp(ek, "valu")) cb->force_encoder = fq::ENC_VALU;
+      if (!strcmp(ek, "mfma64") || !strcmp(ek, "mfma")) cb->force_encoder = fq::ENC_MFMA;
+      if (!strcmp(ek, "h16")) cb->force_encoder = fq::ENC_H16;
+      if (!strcmp(ek, "full")) cb->force_encoder = fq::ENC_FULL;
+      if (!strcmp(ek, "small")) cb->force_encoder = fq::ENC_SMALL;
+    }
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
     cb->force_cache_codebook = dk && strcmp(dk, "cached") == 0;
@@ -411,6 +421,11 @@ FQ_EXPORT fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_d
              : FQ_ERR_HIP;
 }
 
+FQ_EXPORT const char* fq_encode_kernel(const fq_codebook* cb, fq_dtype x_dtype, int64_t n) {
+  if (!cb || n < 0 || !valid_dtype(x_dtype)) return nullptr;
+  return fq::encode_kernel_name(fq::encode_kernel(cb, x_dtype, n));
+}
+
 FQ_EXPORT fq_status fq_encode_scatter(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n,
                                       const int64_t* slots, int64_t capacity, uint8_t* codes, void* norms,
                                       fq_dtype norm_dtype, void* stream) {
@@ -448,7 +463,7 @@ fq_status attn_check_sizes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_
   if (!cb || B < 0 || Hq <= 0 || Hkv <= 0 || T < 0) return FQ_ERR_ARG;
   if (Hq % Hkv != 0) return FQ_ERR_ARG;
   if (Hq / Hkv > 16) return FQ_ERR_UNSUPPORTED;
-  if ((int64_t)cb->N * cb->k > 16384) return FQ_ERR_UNSUPPORTED;
+  if (!fq::attn_supported(cb)) return FQ_ERR_UNSUPPORTED;
   if (B > 65535 || Hkv > 65535 || (int64_t)B * Hq > ((int64_t)1 << 31) - 1) return FQ_ERR_UNSUPPORTED;
   if (T > ((int64_t)1 << 40)) return FQ_ERR_UNSUPPORTED;
   return FQ_OK;
@@ -461,9 +476,11 @@ FQ_EXPORT size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, i
 }
 
 namespace {
-fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
-                      const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
-                      int64_t T, float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+// Checks shared by the decode-attention entry points; *launch is false for a no-op.
+fq_status attn_validate(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                        const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T, float scale,
+                        const float* out, size_t* need, bool* launch) {
+  *launch = false;
   const fq_status ss = attn_check_sizes(cb, B, Hq, Hkv, T);
   if (ss != FQ_OK) return ss;
   if (!isfinite(scale)) return FQ_ERR_ARG;
@@ -474,7 +491,19 @@ fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_cod
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_norms) || !aligned16(v_codes) || !aligned16(v_norms) ||
       !aligned16(out))
     return FQ_ERR_ARG;
-  const size_t need = fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
+  *need = fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
+  *launch = true;
+  return FQ_OK;
+}
+
+fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                      const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
+                      int64_t T, float scale, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  bool launch = false;
+  const fq_status vs =
+      attn_validate(cb, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv, T, scale, out, &need, &launch);
+  if (vs != FQ_OK || !launch) return vs;
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return FQ_ERR_WORKSPACE;
   const fq_status ds = check_device(cb);
   if (ds != FQ_OK) return ds;

@@ -905,6 +905,9 @@ bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
   return cb->k == 4 && cb->bits == 8 && cb->rot16 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
 }
 
+// The general kernel keeps the fp16 codebook in LDS beside its own buffers.
+bool attn_supported(const fq_codebook* cb) { return attn_smem_bytes(cb->N, cb->k) <= cb->max_lds; }
+
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   if (attn_fast_path(cb, Hq, Hkv, T)) {
     // about 1024 workgroups (4 per CU), each over a multiple of 512 consecutive tokens
@@ -958,6 +961,11 @@ hipError_t launch_attn_split_k(dim3 grid, size_t sh, hipStream_t s, const _Float
                                const _Float16* kn, const uint8_t* vc, const _Float16* vn, const fq_codebook* cb,
                                int Hq, int Hkv, int64_t T, const int32_t* lens, int64_t Tc, int nchunks,
                                float qscale, float* ws) {
+  if (sh > 65536) {  // codebooks beyond 32 KiB of fp16 values: raise the dynamic LDS limit
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_split<K>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_split<K>), grid, dim3(AW * 64), sh, s, q, kc, kn, vc, vn, cb->cw16, cb->pi32, cb->N,
                      cb->bits, Hq, Hkv, T, lens, Tc, nchunks, qscale, ws);
   return hipGetLastError();

@@ -256,18 +256,47 @@ extern template hipError_t launch_encode_k<32>(const fq_codebook*, const void*, 
 extern template hipError_t launch_encode_k<64>(const fq_codebook*, const void*, fq_dtype, int64_t, uint8_t*,
                                                  void*, fq_dtype, const int64_t*, int64_t, hipStream_t);
 
+namespace {
+bool covers(const fq_codebook* cb, EncodeKernel e, fq_dtype x_dtype, int64_t n) {
+  switch (e) {
+    case ENC_SMALL: return n <= SMALL_ENCODE_MAX && encode_small_supported(cb);
+    case ENC_H16: return x_dtype == FQ_F16 && encode_h16_supported(cb);
+    case ENC_FULL: return x_dtype == FQ_F16 && encode_full_supported(cb);
+    case ENC_MFMA: return encode_mfma_supported(cb);
+    case ENC_VALU: return true;
+    default: return false;
+  }
+}
+}  // namespace
+
+EncodeKernel encode_kernel(const fq_codebook* cb, fq_dtype x_dtype, int64_t n) {
+  const EncodeKernel forced = (EncodeKernel)cb->force_encoder;
+  if (forced != ENC_AUTO && covers(cb, forced, x_dtype, n)) return forced;
+  // a few vectors (the decode loop's append): latency of one launch is what counts
+  for (EncodeKernel e : {ENC_SMALL, ENC_H16, ENC_FULL, ENC_MFMA})
+    if (covers(cb, e, x_dtype, n)) return e;
+  return ENC_VALU;
+}
+
+const char* encode_kernel_name(EncodeKernel e) {
+  switch (e) {
+    case ENC_SMALL: return "encode_wave";
+    case ENC_H16: return "encode_h16";
+    case ENC_FULL: return "encode_full";
+    case ENC_MFMA: return "encode_mfma";
+    case ENC_VALU: return "encode_valu";
+    default: return "none";
+  }
+}
+
 hipError_t launch_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                          void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
-  // a few vectors (the decode loop's append): latency of one launch is what counts
-  if (!cb->force_valu && !cb->force_mfma64 && n <= SMALL_ENCODE_MAX && encode_small_supported(cb))
-    return launch_encode_small(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
-  if (!cb->force_valu && !cb->force_mfma64 && x_dtype == FQ_F16 && encode_h16_supported(cb))
-    return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
-  if (!cb->force_valu && x_dtype == FQ_F16 && encode_full_supported(cb))
-    return launch_encode_full(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
-  if (!cb->force_valu && cb->amfma) {
-    const hipError_t e = launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
-    if (e != hipErrorNotSupported) return e;
+  switch (encode_kernel(cb, x_dtype, n)) {
+    case ENC_SMALL: return launch_encode_small(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    case ENC_H16: return launch_encode_h16(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
+    case ENC_FULL: return launch_encode_full(cb, x, n, codes, norms, norm_dtype, slots, cap, s);
+    case ENC_MFMA: return launch_encode_mfma(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);
+    default: break;
   }
   switch (cb->k) {
     case 1: return launch_encode_k<1>(cb, x, x_dtype, n, codes, norms, norm_dtype, slots, cap, s);

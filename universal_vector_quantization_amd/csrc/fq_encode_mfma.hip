@@ -380,11 +380,14 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
 
 }  // namespace
 
+bool encode_mfma_supported(const fq_codebook* cb) {
+  return cb->amfma && (cb->k == 4 || cb->k == 8) && cb->N % 32 == 0 && !(cb->k == 4 && cb->N > 1024);
+}
+
 hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int64_t n, uint8_t* codes,
                               void* norms, fq_dtype norm_dtype, const int64_t* slots, int64_t cap,
                               hipStream_t s) {
-  if (!cb->amfma || !(cb->k == 4 || cb->k == 8) || cb->N % 32 != 0 || (cb->k == 4 && cb->N > 1024))
-    return hipErrorNotSupported;
+  if (!encode_mfma_supported(cb)) return hipErrorNotSupported;
   const int VG = 256 / (kD / cb->k);
   const int64_t ngroups = (n + VG - 1) / VG;
   int64_t wgs = (ngroups + WAVES - 1) / WAVES;

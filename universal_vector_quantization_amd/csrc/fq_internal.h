@@ -44,8 +44,8 @@ struct fq_codebook {
                     // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
   size_t max_lds;   // bytes of LDS one workgroup may use on the device
-  bool force_valu;  // FQ_ENCODE_KERNEL=valu at load time: always use the one-lane-per-vector encoder
-  bool force_mfma64;  // FQ_ENCODE_KERNEL=mfma64: the fp64-rotation matrix-core encoder for every input dtype
+  int force_encoder;  // FQ_ENCODE_KERNEL at load time (an fq::EncodeKernel): that encoder wherever it covers
+                      // the call (valu: every call), else the automatic choice
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
   bool force_cache_codebook;  // FQ_DECODE_KERNEL=cached: the matrix-core decoders read codebooks of more
                               // than 32 KiB from L1 / L2 (the path of devices with less LDS)
@@ -54,6 +54,14 @@ struct fq_codebook {
 namespace fq {
 
 constexpr int kD = 64;
+
+// The encoders.  Auto (0) = the automatic choice: Small for batches of at most
+// SMALL_ENCODE_MAX vectors, then H16, Full, Mfma, Valu, the first that covers the call.
+enum EncodeKernel { ENC_AUTO = 0, ENC_SMALL, ENC_H16, ENC_FULL, ENC_MFMA, ENC_VALU };
+// The encoder fq_encode / fq_encode_scatter launch for n vectors of dtype x_dtype.
+EncodeKernel encode_kernel(const fq_codebook* cb, fq_dtype x_dtype, int64_t n);
+const char* encode_kernel_name(EncodeKernel e);
+bool encode_mfma_supported(const fq_codebook* cb);
 
 // Encoder launchers.  With slots == null vector v goes to record v of the code store;
 // otherwise to record slots[v] of a store of `cap` records (slots outside [0, cap) are
@@ -96,6 +104,8 @@ struct AttnPlan {
   bool fast;
 };
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
+// Decode attention covers this codebook (its kernel's LDS fits one workgroup).
+bool attn_supported(const fq_codebook* cb);
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
 // Partial records per (batch, query head) the workspace must hold for this plan.
