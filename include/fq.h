@@ -178,6 +178,26 @@ fq_status fq_attn_decode_varlen(const fq_codebook* cb, const void* q, const uint
                                 int Hkv, int64_t T, float scale, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* fq_attn_decode / fq_attn_decode_varlen for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, with the partial-record
+ * workspace held in the library's own fixed device buffer instead of a caller's
+ * (fq_attn_noalloc_max_workspace_bytes() bytes, 16 MiB, one per device, held
+ * until the process ends; its device address is looked up once per device when
+ * the first codebook is loaded there).  The call allocates nothing.
+ *   lens: NULL (every batch attends to all T keys, as fq_attn_decode) or device
+ *         int32 [B], 4-byte aligned (as fq_attn_decode_varlen).
+ *   other arguments as for fq_attn_decode.
+ * Returns FQ_ERR_WORKSPACE when fq_attn_workspace_bytes(cb, B, Hq, Hkv, T)
+ * exceeds the buffer.  Every call on one device shares that device's buffer and
+ * nothing in it needs clearing between calls: calls that overlap on one device
+ * (different streams, or graphs replayed concurrently) race and give undefined
+ * results. */
+size_t fq_attn_noalloc_max_workspace_bytes(void);
+fq_status fq_attn_decode_noalloc(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                                 const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq,
+                                 int Hkv, int64_t T, float scale, float* out, void* stream);
+
 /* Workspace bytes fq_attn_prefill needs (0 for invalid sizes, T = 0, B = 0 or Sq = 0). */
 size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T);
 

@@ -37,6 +37,9 @@ int main(void) {
                         1 << 16, NULL) == FQ_ERR_ARG);
   EXPECT(fq_attn_decode_varlen(NULL, v, (const uint8_t*)v, v, (const uint8_t*)v, v, (const int32_t*)v, 1, 8, 1, 10,
                                0.125f, (float*)v, v, 1 << 16, NULL) == FQ_ERR_ARG);
+  EXPECT(fq_attn_decode_noalloc(NULL, v, (const uint8_t*)v, v, (const uint8_t*)v, v, NULL, 1, 8, 1, 10, 0.125f,
+                                (float*)v, NULL) == FQ_ERR_ARG);
+  EXPECT(fq_attn_noalloc_max_workspace_bytes() == ((size_t)16 << 20));
   EXPECT(fq_attn_prefill_workspace_bytes(NULL, 1, 8, 1, 4, 10) == 0);
   EXPECT(fq_attn_prefill(NULL, v, (const uint8_t*)v, v, (const uint8_t*)v, v, 1, 8, 1, 4, 10, 1, 0.125f, (float*)v,
                          v, 1 << 16, NULL) == FQ_ERR_ARG);

@@ -27,7 +27,8 @@ def L():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_varlen", "fq_attn_prefill",
+    assert _declared() == sorted(["fq_attn_decode", "fq_attn_decode_noalloc", "fq_attn_decode_varlen",
+                                  "fq_attn_noalloc_max_workspace_bytes", "fq_attn_prefill",
                                   "fq_attn_prefill_workspace_bytes", "fq_attn_workspace_bytes",
                                   "fq_code_bytes", "fq_codebook_free", "fq_codebook_load", "fq_decode",
                                   "fq_codebook_train", "fq_codebook_train_workspace_bytes",

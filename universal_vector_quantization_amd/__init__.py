@@ -20,7 +20,8 @@ __all__ = [
     "FQ_OK", "FQ_ERR_ARG", "FQ_ERR_UNSUPPORTED", "FQ_ERR_WORKSPACE", "FQ_ERR_HIP", "FQ_F32", "FQ_F16",
     "FQError", "lib", "library_path", "fq_status_string", "fq_codebook_load", "fq_codebook_free", "fq_code_bytes",
     "fq_encode", "fq_encode_kernel", "fq_encode_scatter", "fq_decode", "fq_attn_workspace_bytes", "fq_attn_decode",
-    "fq_attn_decode_varlen", "fq_attn_prefill_workspace_bytes", "fq_attn_prefill",
+    "fq_attn_decode_varlen", "fq_attn_noalloc_max_workspace_bytes", "fq_attn_decode_noalloc",
+    "fq_attn_prefill_workspace_bytes", "fq_attn_prefill",
     "fq_codebook_train_workspace_bytes", "fq_codebook_train", "Codebook",
     "load_artifact",
     "artifact_dir",
@@ -69,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.fq_attn_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp,
                                             sz, vp]
         L.fq_attn_decode_varlen.restype = i32
+        L.fq_attn_noalloc_max_workspace_bytes.argtypes, L.fq_attn_noalloc_max_workspace_bytes.restype = [], sz
+        L.fq_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp]
+        L.fq_attn_decode_noalloc.restype = i32
         L.fq_attn_prefill_workspace_bytes.argtypes = [vp, i32, i32, i32, i32, i64]
         L.fq_attn_prefill_workspace_bytes.restype = sz
         L.fq_attn_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i64, i32, ctypes.c_float, vp, vp,
@@ -200,6 +204,23 @@ def fq_attn_decode_varlen(cb: int, q, k_codes, k_norms, v_codes, v_norms, lens, 
            lib().fq_attn_decode_varlen(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
                                        _ptr(lens), B, Hq, Hkv, T, float(scale), _ptr(out), ws_ptr, ws_bytes,
                                        _stream(stream)))
+
+
+def fq_attn_noalloc_max_workspace_bytes() -> int:
+    return int(lib().fq_attn_noalloc_max_workspace_bytes())
+
+
+def fq_attn_decode_noalloc(cb: int, q, k_codes, k_norms, v_codes, v_norms, B: int, Hq: int, Hkv: int, T: int,
+                           scale: float, out, lens=None, stream=None) -> None:
+    """As fq_attn_decode (lens None) or fq_attn_decode_varlen (lens int32 [B]) with the
+    workspace in the library's fixed device buffer: no allocation."""
+    import torch
+
+    if lens is not None and (lens.dtype != torch.int32 or lens.numel() != B):
+        raise ValueError("lens must be int32 [B]")
+    _check("fq_attn_decode_noalloc",
+           lib().fq_attn_decode_noalloc(cb, _ptr(q), _ptr(k_codes), _ptr(k_norms), _ptr(v_codes), _ptr(v_norms),
+                                        _ptr(lens), B, Hq, Hkv, T, float(scale), _ptr(out), _stream(stream)))
 
 
 def fq_attn_prefill_workspace_bytes(cb: int, B: int, Hq: int, Hkv: int, Sq: int, T: int) -> int:

@@ -14,6 +14,13 @@
 
 #define FQ_EXPORT extern "C" __attribute__((visibility("default")))
 
+// Device memory of fq_attn_decode_noalloc: its partial-record workspace lives in this
+// array instead of a caller's buffer.  Every device the library runs on holds one copy
+// until the process ends.  Host code must never use the array's name as an address
+// (on the host it is only a stand-in): the device address of the current device's
+// copy comes from hipGetSymbolAddress, looked up once per device at codebook load.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace fq {
 
@@ -73,6 +80,24 @@ fq_status check_device(const fq_codebook* cb) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return FQ_ERR_HIP;
   return dev == cb->device ? FQ_OK : FQ_ERR_ARG;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev`, which must be current: looked up on
+// the first call for that device, then cached.
+fq_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return FQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FQ_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FQ_OK;
 }
 
 void release(fq_codebook* cb) {
@@ -336,6 +361,15 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
     return FQ_ERR_HIP;
   }
   cb->max_lds = (size_t)lds_max;
+  {
+    // set-up of the no-allocation attention entry point for this device
+    void* sp = nullptr;
+    const fq_status ss = scratch_address(cb->device, &sp);
+    if (ss == FQ_ERR_HIP) {
+      delete cb;
+      return FQ_ERR_HIP;
+    }
+  }
 
   // Host staging: fp16 copy (padded to 16 bytes), ||c||^2, bounds, rotations.
   const size_t cw16_bytes = ((nk * 2 + 15) / 16) * 16;
@@ -513,6 +547,30 @@ fq_status attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_cod
              : FQ_ERR_HIP;
 }
 }  // namespace
+
+FQ_EXPORT size_t fq_attn_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
+
+FQ_EXPORT fq_status fq_attn_decode_noalloc(const fq_codebook* cb, const void* q, const uint8_t* k_codes,
+                                           const void* k_norms, const uint8_t* v_codes, const void* v_norms,
+                                           const int32_t* lens, int B, int Hq, int Hkv, int64_t T, float scale,
+                                           float* out, void* stream) {
+  if (lens && (reinterpret_cast<uintptr_t>(lens) & 3) != 0) return FQ_ERR_ARG;
+  size_t need = 0;
+  bool launch = false;
+  const fq_status vs =
+      attn_validate(cb, q, k_codes, k_norms, v_codes, v_norms, B, Hq, Hkv, T, scale, out, &need, &launch);
+  if (vs != FQ_OK || !launch) return vs;
+  if (need > kNoAllocScratchBytes) return FQ_ERR_WORKSPACE;
+  const fq_status ds = check_device(cb);
+  if (ds != FQ_OK) return ds;
+  void* ws = nullptr;
+  const fq_status ss = scratch_address(cb->device, &ws);
+  if (ss != FQ_OK) return ss;
+  return fq::launch_attn(cb, q, k_codes, k_norms, v_codes, v_norms, lens, B, Hq, Hkv, T, scale, out, ws,
+                         (hipStream_t)stream) == hipSuccess
+             ? FQ_OK
+             : FQ_ERR_HIP;
+}
 
 FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                                    const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,
