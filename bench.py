@@ -67,6 +67,7 @@ def parse():
     ap.add_argument("--no-rate-axis", action="store_true", help="skip the rate-axis timings")
     ap.add_argument("--no-build", action="store_true", help="skip the codebook-construction timings")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill attention timing")
+    ap.add_argument("--no-lut-attention", action="store_true", help="skip the lookup-table attention timings")
     ap.add_argument("--no-workloads", action="store_true", help="skip the per-workload encode/decode timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy (reference for HBM byte counters)")
@@ -236,6 +237,45 @@ def codec_record(fq, cb, x, n, norms, w, t_e, t_d):
             "encode_cmp_frac": (D // w.k) * w.N * n / t_e / 1e12 / CMP_PEAK_T,
             "encode_traffic": measured_traffic(*ek) if ek else None,
             "decode_traffic": measured_traffic(dk, "fq_decode_mfma.hip") if dk else None}
+
+
+def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: int):
+    """Decode attention through per-head lookup tables at the attention workload's
+    shape (B=16, Hq=32, Hkv=4, T=32768; K and V draws encoded on the GPU): the
+    full-vector code (k = d = 64, N = 4096, the kernel it is built for), and the
+    k = 4, N = 256 code forced through it (FQ_ATTN_KERNEL=lut) beside the gather
+    kernel that code normally takes."""
+    import torch
+
+    B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+    na = B * Hkv * Ta
+    out = {}
+    for name, (k, N, force) in {"fullvec_k64_n4096": (64, 4096, False), "k4_n256_lut": (4, 256, True)}.items():
+        if force:
+            os.environ["FQ_ATTN_KERNEL"] = "lut"
+        try:
+            cb = fq.Codebook.from_artifact(k, N)
+        finally:
+            os.environ.pop("FQ_ATTN_KERNEL", None)
+        kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
+        codes = torch.zeros(cb.code_bytes(2 * na), dtype=torch.uint8, device=dev)
+        norms = torch.empty(2 * na, dtype=torch.float16, device=dev)
+        fq.fq_encode(cb.handle, kv, codes, norms, stream)
+        del kv
+        half = cb.code_bytes(na)
+        ao = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+        ws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, Ta), dtype=torch.uint8, device=dev)
+        t = timed_evicted(lambda: fq.fq_attn_decode(cb.handle, qa, codes[:half], norms[:na], codes[half:], norms[na:],
+                                                    B, Hq, Hkv, Ta, 0.125, ao, ws, stream), stream, flush, reps)
+        abytes = 2 * half + 2 * na * 2 + B * Hq * D * 2 + B * Hq * D * 4
+        out[name] = {"k": k, "N": N, "us_per_step": t * 1e6, "hbm_bytes": abytes, "GBps": abytes / t / 1e9,
+                     "hbm_frac": abytes / t / 1e9 / HBM_PEAK_GBPS,
+                     "fp16_equiv_GBps": 2 * na * D * 2 / t / 1e9,
+                     "kernels": "attn_lut_prep + attn_lut + attn_combine (events bracket the call)"}
+        cb.close()
+        del codes, norms, ao, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 # Rate-axis points (k, N) with frozen initial codebooks: b = log2(N) / k from 4 down to 0.22.
@@ -514,6 +554,10 @@ def main():
         progress("decode loop")
         line["decode_loop_b16_t32k"] = decode_loop(fq, cba, dev, stream, flush, args.attn_iters, kv_np, qa, ac, an,
                                                    kcs, kns, vcs, vns, ao, aws)
+    if not args.no_lut_attention:
+        progress("lookup-table attention")
+        line["attn_lut_b16_t32k"] = lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np,
+                                                          args.attn_iters)
     del kv_np
     if not args.no_workloads:
         progress("other codec workloads")

@@ -35,8 +35,9 @@ RATES = [
     (32, 512),    # b = 0.28125
     (64, 16384),  # b = 0.21875: 64 coordinates in 14 bits (+ a 16-bit norm: 34.1x)
 ]
-# the general attention kernel holds the fp16 codebook in LDS: N k <= 65536 on gfx950
-ATTN_RATES = [(k, N) for k, N in RATES if k * N <= 65536]
+# every rate-axis point has an attention kernel: the general one holds the fp16 codebook
+# in LDS (N k <= 65536 on gfx950), the full-vector code goes through lookup tables
+ATTN_RATES = RATES
 
 
 @pytest.fixture(scope="module")

@@ -27,7 +27,7 @@ PER_K = ("fq_encode", "fq_decode", "fq_attn")
 # min / max need no canonicalisation, and matrix-core results stay in VGPRs.
 KERNEL_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 NO_KERNEL_FLAGS = ("fq_api",)
-SINGLE = ("fq_api", "fq_encode_mfma", "fq_encode_h16", "fq_encode_full", "fq_encode_small", "fq_decode_mfma", "fq_train", "fq_prefill")
+SINGLE = ("fq_api", "fq_attn_lut", "fq_encode_mfma", "fq_encode_h16", "fq_encode_full", "fq_encode_small", "fq_decode_mfma", "fq_train", "fq_prefill")
 ARCH = os.environ.get("FQ_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}",
          # no packed-fp32 instruction forms in any kernel

@@ -130,7 +130,8 @@ fq_status upload(T** dst, const T* src, size_t count) {
 // Operand layouts of the matrix-core encoder, built once per codebook.
 // Operands of the k = d = 64 encoder: the rotation as 32 x 32 x 16 A operands (three
 // fp16 parts of 1024 Pi, rows permuted so that a lane ends up with 32 consecutive
-// coordinates) and the codeword tiles in their LDS layout.
+// coordinates) and the codeword rows in their LDS layout (64 fp16 coordinates, then
+// 256 ||c||^2 as fp16 hi + lo and six zeros).
 fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const float* rotation) {
   const int d = cb->d, N = cb->N;
   const int tiles = N / 32, chunks = (tiles + 7) / 8;
@@ -164,8 +165,12 @@ fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const fl
       memcpy(row + 2 * t, &hv, 2);
       c2 += v * v;
     }
-    const float s2 = (float)(256.0 * c2);
-    memcpy(rc + (size_t)(n & ~3) * 144 + 128 + 4 * (n & 3), &s2, 4);
+    // 256 ||c||^2 as fp16 hi + lo (22 bits) in the row's norm slots, then zeros
+    const double s2 = 256.0 * c2;
+    const _Float16 nh = (_Float16)s2;
+    const _Float16 nl = (_Float16)(s2 - (double)nh);
+    memcpy(row + 128, &nh, 2);
+    memcpy(row + 130, &nl, 2);
   }
   fq_status st = upload(&cb->rot32, rt, (size_t)2 * 4 * 3 * 64 * 8);
   if (st == FQ_OK) st = upload(&cb->frec, rc, rec_bytes);
@@ -350,6 +355,8 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
       if (!strcmp(ek, "full")) cb->force_encoder = fq::ENC_FULL;
       if (!strcmp(ek, "small")) cb->force_encoder = fq::ENC_SMALL;
     }
+    const char* ak = getenv("FQ_ATTN_KERNEL");
+    cb->force_attn_lut = ak && strcmp(ak, "lut") == 0;
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
     cb->force_cache_codebook = dk && strcmp(dk, "cached") == 0;
@@ -506,7 +513,9 @@ fq_status attn_check_sizes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_
 
 FQ_EXPORT size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   if (attn_check_sizes(cb, B, Hq, Hkv, T) != FQ_OK || T == 0 || B == 0) return 0;
-  return fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
+  const fq::AttnPlan p = fq::attn_plan(cb, B, Hq, Hkv, T);
+  if (!fq::attn_plan_launchable(p, B, Hq, Hkv)) return 0;
+  return fq::attn_plan_workspace_bytes(cb, p, B, Hq, Hkv);
 }
 
 namespace {
@@ -525,7 +534,9 @@ fq_status attn_validate(const fq_codebook* cb, const void* q, const uint8_t* k_c
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_norms) || !aligned16(v_codes) || !aligned16(v_norms) ||
       !aligned16(out))
     return FQ_ERR_ARG;
-  *need = fq::attn_workspace_bytes(B, Hq, Hkv, fq::attn_record_stride(fq::attn_plan(cb, B, Hq, Hkv, T)));
+  const fq::AttnPlan plan = fq::attn_plan(cb, B, Hq, Hkv, T);
+  if (!fq::attn_plan_launchable(plan, B, Hq, Hkv)) return FQ_ERR_UNSUPPORTED;
+  *need = fq::attn_plan_workspace_bytes(cb, plan, B, Hq, Hkv);
   *launch = true;
   return FQ_OK;
 }

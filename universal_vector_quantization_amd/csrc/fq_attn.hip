@@ -905,18 +905,41 @@ bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
   return cb->k == 4 && cb->bits == 8 && cb->rot16 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
 }
 
-// The general kernel keeps the fp16 codebook in LDS beside its own buffers.
-bool attn_supported(const fq_codebook* cb) { return attn_smem_bytes(cb->N, cb->k) <= cb->max_lds; }
+// The general kernel keeps the fp16 codebook in LDS beside its own buffers; the
+// lookup-table kernel keeps one table (and weight histogram) per query head.
+bool attn_supported(const fq_codebook* cb) {
+  return attn_smem_bytes(cb->N, cb->k) <= cb->max_lds || attn_lut_supported(cb);
+}
+
+namespace {
+bool attn_use_lut(const fq_codebook* cb) {
+  return (cb->k == D || cb->force_attn_lut) && attn_lut_supported(cb);
+}
+}  // namespace
 
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
-  if (attn_fast_path(cb, Hq, Hkv, T)) {
+  if (attn_use_lut(cb)) {
+    // one workgroup per CU: about 256 workgroups over (batch, KV head, head set, chunk)
+    const int G = Hq / Hkv, gw = attn_lut_heads(cb, G);
+    const int64_t sets = (int64_t)B * Hkv * (G / (gw > 0 ? gw : 1));
+    int64_t nc = (256 + sets - 1) / sets;
+    const int64_t most = (T + 63) / 64;
+    if (nc > most) nc = most;
+    if (nc < 1) nc = 1;
+    int64_t tc = (T + nc - 1) / nc;
+    tc = ((tc + 63) / 64) * 64;
+    nc = (T + tc - 1) / tc;
+    if (nc < 1) nc = 1;
+    return AttnPlan{(int)nc, tc, 0, 0, false, gw};
+  }
+  if (!cb->force_attn_lut && attn_fast_path(cb, Hq, Hkv, T)) {
     // about 1024 workgroups (4 per CU), each over a multiple of 512 consecutive tokens
     const int64_t units = (T + WG_TOKENS_UNIT - 1) / WG_TOKENS_UNIT, slabs = (int64_t)B * Hkv;
     int64_t upw = units * slabs / 1024;
     if (upw < 1) upw = 1;
     if (upw > units) upw = units;
     const int64_t nrec = (units + upw - 1) / upw;
-    return AttnPlan{(int)nrec, upw * WG_TOKENS_UNIT, (int)units, (int)upw, true};
+    return AttnPlan{(int)nrec, upw * WG_TOKENS_UNIT, (int)units, (int)upw, true, 0};
   }
   const int64_t per = (int64_t)AW * TILE;
   const int64_t groups = (int64_t)B * Hkv;
@@ -927,7 +950,7 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   int64_t tc = (T + nc - 1) / nc;
   tc = ((tc + per - 1) / per) * per;
   nc = (T + tc - 1) / tc;
-  return AttnPlan{(int)nc, tc, 0, 0, false};
+  return AttnPlan{(int)nc, tc, 0, 0, false, 0};
 }
 
 hipError_t launch_attn_combine(const float* ws, const float* pi32, int64_t rows, int nchunks, float* out,
@@ -945,6 +968,15 @@ size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks) {
   (void)Hkv;
   // partial records, then one record count per batch (balanced split under lengths)
   return attn_records_bytes(B, Hq, nchunks) + (((size_t)B * sizeof(int32_t) + 255) & ~(size_t)255);
+}
+
+size_t attn_plan_workspace_bytes(const fq_codebook* cb, const AttnPlan& p, int B, int Hq, int Hkv) {
+  return attn_workspace_bytes(B, Hq, Hkv, attn_record_stride(p)) + (p.lut_heads ? attn_lut_table_bytes(cb, B, Hq) : 0);
+}
+
+bool attn_plan_launchable(const AttnPlan& p, int B, int Hq, int Hkv) {
+  const int64_t gy = p.lut_heads ? (int64_t)Hkv * (Hq / Hkv / p.lut_heads) : Hkv;
+  return gy <= 65535 && B <= 65535 && (!p.lut_heads || (int64_t)B * Hkv <= 0x7fffffff);
 }
 
 int attn_record_stride(const AttnPlan& p) {
@@ -990,6 +1022,9 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
                        const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
                        int64_t T, float scale, float* out, void* workspace, hipStream_t s) {
   const AttnPlan plan = attn_plan(cb, B, Hq, Hkv, T);
+  if (plan.lut_heads)
+    return launch_attn_lut(cb, q, k_codes, k_norms, v_codes, v_norms, lens, B, Hq, Hkv, T, scale, plan, out,
+                           workspace, s);
   const float qscale = scale * 1.4426950408889634f;  // log2(e)
   const dim3 grid((unsigned)plan.nchunks, (unsigned)Hkv, (unsigned)B);
   const size_t sh = attn_smem_bytes(cb->N, cb->k);

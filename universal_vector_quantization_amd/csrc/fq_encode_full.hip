@@ -12,23 +12,31 @@
 //     into fp16 hi + mid + lo, x is fp16, products exact, hi and mid / lo
 //     products summed in fp32 separately.  The rows of Pi are permuted so that
 //     lane l holds coordinates 32 (l / 32) .. + 31 of vector l % 32.
-//  2. -512 y is split into fp16 hi + lo; lanes exchange halves so that lane c
-//     holds hi of all 64 coordinates of vector c and lane c + 32 the lo parts:
-//     the B operands of 8 K-steps (coordinates 8 s .. 8 s + 7).
-//  3. Per codeword tile: 8 chained matrix ops starting from 256 ||c||^2; the
-//     lane keeps the minimum of its 16 rows, the second-best tile minimum, and
-//     the 16 scores of its best tile (copied when a tile improves the minimum).
-//  4. The best row of the best tile, merged over the two lanes of the column,
-//     is certified with the same error bound as the k = 4 / 8 encoder:
-//     E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y|) + 35840 sqrt(k) cmax u
-//               + 2^-25 (1 + sqrt(k) cmax)); |y| <= 1 here.
-//  5. Uncertified vectors are searched again in fp64 with the direct distance
-//     (lowest index on exact ties) by the whole workgroup: each wave queues its
-//     vectors (y in fp64) in LDS, then every wave scores its sixteenth of the
-//     codebook (fp16 records read straight from global memory, four lanes per
-//     codeword, 16 coordinates each) for up to four queued vectors per pass.
-//     Searched by their own wave alone, one uncertified vector held up the
-//     workgroup's barriers for the length of a 4096-codeword fp64 scan.
+//  2. -512 y is rounded to fp16 ("hi"); lanes exchange halves so that each holds
+//     the B operands of 4 K-steps of 16 coordinates.  A fifth K-step multiplies
+//     the record's norm slots (256 ||c||^2 as fp16 hi + lo) by 1, so the
+//     accumulator starts at 0 and no per-tile LDS reads seed it.
+//  3. Per codeword tile: 5 chained matrix ops; the lane keeps the minimum of its
+//     16 rows, the best, second and third tile minima (with the tiles of the
+//     first two) and the 16 scores of its best tile.
+//  4. Certificate.  The residual r = -512 y - hi is known exactly per vector, and
+//     leaving it out moves a score by at most |c| |r|_2, so every score is within
+//        E = E0 + 1.0001 cmax |r|_2 + 2^-22 256 c2max 1.01
+//     of the exact scaled score, E0 the bound of the k = 4 / 8 encoder
+//     (1.01 ((2k+7) u (256 c2max + 512 cmax |y|) + 35840 sqrt(k) cmax u
+//     + 2^-25 (1 + sqrt(k) cmax)), |y| <= 1) and the last term the fp16 hi + lo
+//     split of 256 ||c||^2.  If second - best > 2E the winner is the exact
+//     minimiser.
+//  5. Uncertified vectors (about 2 % of the full-vector workload): every codeword
+//     whose computed score is within 2E of the best lies in the best or second
+//     tile of a half unless a third tile minimum is that close too; those at most
+//     4 x 16 rows are scored in fp64 with the direct distance by the owning wave,
+//     one row per lane (lowest index on exact ties).  Otherwise the vector is
+//     searched again in fp64 over the whole codebook by the whole workgroup: each
+//     wave queues its vectors (y in fp64) in LDS, then every wave scores its
+//     sixteenth of the codebook (fp16 records read straight from global memory,
+//     four lanes per codeword, 16 coordinates each) for up to four queued vectors
+//     per pass.
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -38,7 +46,7 @@ namespace {
 constexpr int D = kD;
 constexpr int WAVES = 16;
 constexpr int CT = 8;                          // codeword tiles per LDS chunk
-constexpr int ROWB = 144;                      // bytes per codeword row: 64 fp16 + 16 (256 ||c||^2 of 4 rows)
+constexpr int ROWB = 144;                      // bytes per codeword row: 64 fp16, 256 ||c||^2 as fp16 hi, lo, 0 x 6
 constexpr int TILEB = 32 * ROWB;               // 4608
 constexpr int CHUNKB = CT * TILEB;             // 36864
 constexpr int SCR_DW = 2 * 64 * 2 + 16;        // per wave: x and y (fp64) of a re-searched vector + codes
@@ -46,7 +54,8 @@ constexpr int QMAX = 16;                       // queued re-searches per workgro
 constexpr int QB = 4;                          // queued vectors scored per pass over the codebook
 // queue: y (fp64) per entry, owner (wave << 8 | column) per entry, per-wave best
 // (distance, index) per entry, and the count
-constexpr int Q_BYTES = QMAX * 64 * 8 + QMAX * 4 + QMAX * WAVES * 16 + 16;
+constexpr int UMAX = WAVES * 32;               // list of uncertified vectors: every column of a round fits
+constexpr int Q_BYTES = QMAX * 64 * 8 + QMAX * 4 + QMAX * WAVES * 16 + 16 + UMAX * 12 + 16;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -87,13 +96,16 @@ __device__ inline void load_chunk(const uint8_t* __restrict__ rec, int ch, int n
     lds_dma16(src + p * 1024 + lane * 16, dst + p * 1024);
 }
 
-constexpr size_t full_lds_bytes() { return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4 + Q_BYTES; }
+// chunk buffers, per-wave scratch, queue and list, Pi^T in fp64 (for the exact y of re-searches)
+constexpr size_t full_lds_bytes() {
+  return 2 * (size_t)CHUNKB + (size_t)WAVES * SCR_DW * 4 + Q_BYTES + (size_t)D * D * 8;
+}
 
 template <bool NF16>
 __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rotA,
     const uint8_t* __restrict__ rec, const float* __restrict__ cw, const double* __restrict__ pi64t, int N, int bits,
-    float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
+    float e_abs, float e_rel, float cmax, float c2max, uint8_t* __restrict__ codes, void* __restrict__ norms,
     const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   extern __shared__ uint4 smem[];
   char* buf0 = reinterpret_cast<char*>(smem);
@@ -110,8 +122,13 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
   double* qbd = reinterpret_cast<double*>(qbase + QMAX * 64 * 8 + QMAX * 4);  // [QMAX][WAVES]
   int* qbi = reinterpret_cast<int*>(qbd + QMAX * WAVES);                  // [QMAX][WAVES]
   int* qcnt = qbi + QMAX * WAVES;
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(qcnt + 4);  // [UMAX][3]: owner << 8 | column | few << 16, candidates
+  int* ucnt = reinterpret_cast<int*>(ulist + UMAX * 3);
   const int NT = N / 32;
   const int nch = (NT + CT - 1) / CT;
+  double* piL = reinterpret_cast<double*>(qbase + Q_BYTES);  // Pi^T: piL[j D + r] = Pi[r][j]
+  for (int i = fq_tid(); i < D * D; i += WAVES * 64) piL[i] = pi64t[i];
+  // (visible after the first barrier of the stream below)
 
   for (int64_t base = (int64_t)fq_bid_x() * WAVES; base < ngroups; base += (int64_t)nwg * WAVES) {
     const int64_t g = base + w;
@@ -159,7 +176,8 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     // the loop instead of hoisted into (spilled) registers.
     int rot_off = 0;
     __asm__ volatile("" : "+s"(rot_off));
-    uint32_t hi[16], lo[16];  // coordinates 32 h + 16 r + e as packed fp16 pairs
+    uint32_t hi[16];  // coordinates 32 h + 16 r + e of -512 y rounded to fp16, packed in pairs
+    float rr = 0.f;   // sum of the squared residuals -512 y - hi of these coordinates
 #pragma unroll
     for (int r = 0; r < 2; r++) {
       f32x16 ah, am;
@@ -182,31 +200,50 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
         const float vb = -512.0f * ((ah[e + 1] + am[e + 1]) * inv);
         const float ha = (float)(_Float16)va, hb = (float)(_Float16)vb;
         hi[8 * r + e / 2] = pack_h2(ha, hb);
-        lo[8 * r + e / 2] = pack_h2(va - ha, vb - hb);
+        rr = fmaf(va - ha, va - ha, rr);  // the differences are exact in fp32
+        rr = fmaf(vb - hb, vb - hb, rr);
       }
     }
-    // ---- 2. B operands: lane c gets hi of coordinates 32 .. 63 from lane c + 32,
-    //         lane c + 32 gets lo of 0 .. 31 from lane c.
-    uint32_t bq[8][4];
+    rr += __shfl_xor(rr, 32);
+    // error bound of this vector's scores (see 4.)
+    const float E = e_abs + e_rel * 1.01f + 1.0001f * cmax * __builtin_sqrtf(rr) * 1.0001f +
+                    256.0f * c2max * 2.4e-7f;
+    // ---- 2. B operands: step s covers coordinates 16 s .. 16 s + 15, lanes 0-31 the
+    //         first 8, lanes 32-63 the last 8.  Lane c holds coordinates 0 .. 31 of
+    //         vector c, lane c + 32 coordinates 32 .. 63: one exchange of 8 dwords.
+    uint32_t bq[4][4];
+    {
+      uint32_t recv[8];
 #pragma unroll
-    for (int d = 0; d < 16; d++) {
-      const uint32_t recv = (uint32_t)__shfl_xor((int)(h == 0 ? lo[d] : hi[d]), 32);
-      // coordinates 0..31 are dwords 0..15 of lane c's packs, 32..63 those of lane c + 32
-      bq[d / 4][d % 4] = h == 0 ? hi[d] : recv;
-      bq[4 + d / 4][d % 4] = h == 0 ? recv : lo[d];
+      for (int d = 0; d < 8; d++) {
+        const int src = h == 0 ? (d < 4 ? 4 + d : 8 + d) : (d < 4 ? d : 4 + d);
+        recv[d] = (uint32_t)__shfl_xor((int)hi[src], 32);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        bq[0][d] = h == 0 ? hi[d] : recv[d];           // 0 .. 7   | 8 .. 15
+        bq[1][d] = h == 0 ? hi[8 + d] : recv[4 + d];   // 16 .. 23 | 24 .. 31
+        bq[2][d] = h == 0 ? recv[d] : hi[4 + d];       // 32 .. 39 | 40 .. 47
+        bq[3][d] = h == 0 ? recv[4 + d] : hi[12 + d];  // 48 .. 55 | 56 .. 63
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 8; s++)
+    for (int s = 0; s < 4; s++)
 #pragma unroll
       for (int d = 0; d < 4; d++) __asm__ volatile("" : "+v"(bq[s][d]));
+    // step 4: the norm slots (K 0, 1 of lanes 0-31) times 1
+    const half8 bnorm = __builtin_bit_cast(half8, make_uint4(h == 0 ? 0x3c003c00u : 0u, 0u, 0u, 0u));
 
     // ---- 3. stream the codebook
-    float m1 = __builtin_huge_valf(), m2 = __builtin_huge_valf();
-    int tid = 0;
+    float m1 = __builtin_huge_valf(), m2 = __builtin_huge_valf(), m3 = __builtin_huge_valf();
+    int tid = 0, tid2 = 0;
     f32x16 bestD;
 #pragma unroll
     for (int e = 0; e < 16; e++) bestD[e] = __builtin_huge_valf();
-    if (w == 0 && lane == 0) *qcnt = 0;  // read after the barriers below
+    if (w == 0 && lane == 0) {  // read after the barriers below
+      *qcnt = 0;
+      *ucnt = 0;
+    }
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces of chunk 0 are in LDS
     __syncthreads();
     for (int ch = 0; ch < nch; ch++) {
@@ -217,29 +254,29 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       }
       const int nt = (NT - ch * CT) < CT ? (NT - ch * CT) : CT;
       for (int tt = 0; tt < nt; tt++) {
-        const char* tile = cur + tt * TILEB;
+        const char* arow = cur + tt * TILEB + c * ROWB;
+        half8 A[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) A[s] = *reinterpret_cast<const half8*>(arow + 32 * s + 16 * h);
+        // lanes 32-63 read the same finite norm slots against a zero B: no contribution
+        const half8 An = *reinterpret_cast<const half8*>(arow + 128);
         f32x16 acc;
 #pragma unroll
-        for (int a = 0; a < 4; a++) {
-          const float4 cv = *reinterpret_cast<const float4*>(tile + (8 * a + 4 * h) * ROWB + 128);
-          acc[4 * a] = cv.x;
-          acc[4 * a + 1] = cv.y;
-          acc[4 * a + 2] = cv.z;
-          acc[4 * a + 3] = cv.w;
-        }
-        const char* arow = tile + c * ROWB;
+        for (int e = 0; e < 16; e++) acc[e] = 0.f;
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(An, bnorm, acc, 0, 0, 0);
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-          const half8 A = *reinterpret_cast<const half8*>(arow + 16 * s);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[s]), acc, 0, 0, 0);
-        }
+        for (int s = 0; s < 4; s++)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s], __builtin_bit_cast(half8, bq[s]), acc, 0, 0, 0);
         const float tm = min16(acc);
-        const bool better = tm < m1;
+        const int t = ch * CT + tt;
+        const bool c1 = tm < m1, c2 = tm < m2;
+        m3 = __builtin_amdgcn_fmed3f(m2, m3, tm);
+        tid2 = c1 ? tid : (c2 ? t : tid2);
         m2 = __builtin_amdgcn_fmed3f(m1, m2, tm);
-        tid = better ? ch * CT + tt : tid;
+        tid = c1 ? t : tid;
         m1 = fminf(m1, tm);
 #pragma unroll
-        for (int e = 0; e < 16; e++) bestD[e] = better ? acc[e] : bestD[e];
+        for (int e = 0; e < 16; e++) bestD[e] = c1 ? acc[e] : bestD[e];
       }
       __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
       __syncthreads();
@@ -262,7 +299,13 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
     const float best = other ? o1 : r1;
     const float second = fminf(fminf(fmaxf(r1, o1), fminf(r2, o2)), fminf(m2, om));
     const uint32_t code = (uint32_t)(other ? oi : ri);
-    const bool sure = (second - best) > 2.0f * (e_abs + e_rel * 1.01f);
+    const bool sure = (second - best) > 2.0f * E;
+    // candidate tiles of an uncertified column, per half: the best tile always, the
+    // second if its minimum is within 2E of the best; a third that close sends the
+    // vector to the full search
+    const float lim = best + 2.0f * E;
+    const uint32_t cand = (uint32_t)(tid & 0xffff) | ((uint32_t)(m2 <= lim ? (tid2 & 0x7fff) | 0x8000 : 0) << 16);
+    const bool far3 = m3 > lim;
 
     const int words = bits;  // 32 codes x bits
     for (int i = lane; i < words; i += 64) spk[i] = 0u;
@@ -272,13 +315,19 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       atomicOr(&spk[bo >> 5], code << sh);
       if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], code >> (32 - sh));
     }
-    // ---- 5. fp64 re-search of the uncertified vectors: y of each goes to the workgroup's
-    //      queue (or, past QMAX entries, the wave searches alone)
-    uint64_t todo = __ballot(h == 0 && valid && !sure);
-    while (todo) {
-      const int cc = __builtin_ctzll(todo);
-      todo &= todo - 1;
-      const double xj = (double)x[(v0 + cc) * D + lane];
+    // ---- 5. uncertified vectors: the owner lists them; after a barrier every wave takes
+    //      list entries (the exact y of a vector costs a chain of dependent loads, so one
+    //      wave per entry; the list holds every column of a round).  A vector whose candidates lie in its listed tiles is scored
+    //      over those rows; any other goes to the workgroup's fp64 queue (or, past QMAX
+    //      entries, is searched by the wave alone).  Codes go to the owner's packing words.
+    auto research = [&](int ow, int cc, bool few, uint32_t cd0, uint32_t cd1) {
+      uint32_t* ospk = reinterpret_cast<uint32_t*>(buf0 + 2 * CHUNKB) + ow * SCR_DW + 256;
+      auto put = [&](uint32_t cv) {
+        const int bo = cc * bits, sh = bo & 31;
+        atomicOr(&ospk[bo >> 5], cv << sh);
+        if (sh + bits > 32) atomicOr(&ospk[(bo >> 5) + 1], cv >> (32 - sh));
+      };
+      const double xj = (double)x[((base + ow) * 32 + cc) * D + lane];
       xs[lane] = xj;
       double s2 = xj * xj;
 #pragma unroll
@@ -286,16 +335,64 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
       const double nuf = sqrt(s2);
       const double iv = nuf > 0.0 ? 1.0 / nuf : 0.0;
       wave_lds_sync();
-      double yt = 0.0;  // coordinate `lane` of y
-      for (int j = 0; j < D; j++) yt = fma(pi64t[j * D + lane], xs[j], yt);
+      double yt = 0.0;  // coordinate `lane` of y, Pi from LDS
+#pragma unroll 8
+      for (int j = 0; j < D; j++) yt = fma(piL[j * D + lane], xs[j], yt);
       yt *= iv;
+      if (few) {
+        // lane L scores row L % 16 of candidate (tile, half) L / 16: the best and second
+        // tiles of half 0 (lanes 0-31) and of half 1 (lanes 32-63)
+        ys[lane] = yt;
+        wave_lds_sync();
+        const int hh = lane >> 5;
+        const uint32_t cd = hh ? cd1 : cd0;
+        const bool sec = ((lane >> 4) & 1) != 0;
+        const bool use = !sec || (cd & 0x80000000u);
+        const int tl = sec ? (int)((cd >> 16) & 0x7fff) : (int)(cd & 0xffff);
+        const int j = lane & 15;
+        const int nn = 32 * tl + 8 * (j >> 2) + 4 * hh + (j & 3);
+        double dd = __builtin_huge_val();
+        if (use) {
+          const uint4* rowp = reinterpret_cast<const uint4*>(rec + (size_t)nn * ROWB);
+          dd = 0.0;
+          for (int q0 = 0; q0 < 8; q0 += 4) {
+            uint4 rw[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) rw[q] = rowp[q0 + q];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const uint32_t ww[4] = {rw[q].x, rw[q].y, rw[q].z, rw[q].w};
+#pragma unroll
+              for (int i = 0; i < 4; i++) {
+                const double d0 = ys[8 * (q0 + q) + 2 * i] - (double)h_lo(ww[i]);
+                const double d1 = ys[8 * (q0 + q) + 2 * i + 1] - (double)h_hi(ww[i]);
+                dd = fma(d0, d0, dd);
+                dd = fma(d1, d1, dd);
+              }
+            }
+          }
+        }
+        int bn = use ? nn : 0x7fffffff;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+          const double od = shfl_xor_f64(dd, m);
+          const int on = __shfl_xor(bn, m);
+          if (od < dd || (od == dd && on < bn)) {
+            dd = od;
+            bn = on;
+          }
+        }
+        if (lane == 0) put((uint32_t)bn);
+        wave_lds_sync();
+        return;
+      }
       int slot = 0;
       if (lane == 0) slot = atomicAdd(qcnt, 1);
       slot = __builtin_amdgcn_readfirstlane(__shfl(slot, 0));
       if (slot < QMAX) {
         qy[slot * 64 + lane] = yt;
-        if (lane == 0) qown[slot] = (w << 8) | cc;
-        continue;
+        if (lane == 0) qown[slot] = (ow << 8) | cc;
+        return;
       }
       ys[lane] = yt;
       wave_lds_sync();
@@ -322,16 +419,36 @@ __global__ __launch_bounds__(WAVES * 64, 4) void encode_full(
           bn = on;
         }
       }
-      if (lane == 0) {
-        const uint32_t cv = (uint32_t)bn;
-        const int bo = cc * bits, sh = bo & 31;
-        atomicOr(&spk[bo >> 5], cv << sh);
-        if (sh + bits > 32) atomicOr(&spk[(bo >> 5) + 1], cv >> (32 - sh));
-      }
+      if (lane == 0) put((uint32_t)bn);
       wave_lds_sync();
+    };
+    const bool far3_col = far3 && __shfl_xor((int)far3, 32);
+    uint64_t todo = __ballot(h == 0 && valid && !sure);
+    while (todo) {
+      const int cc = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const bool few = __shfl((int)far3_col, cc) != 0;  // every candidate in the listed tiles
+      const uint32_t cd0 = (uint32_t)__shfl((int)cand, cc), cd1 = (uint32_t)__shfl((int)cand, cc + 32);
+      if (lane == 0) {
+        const int slot = atomicAdd(ucnt, 1);  // < UMAX: at most every column of the round
+        ulist[3 * slot] = (uint32_t)((w << 8) | cc | (few ? 0x10000 : 0));
+        ulist[3 * slot + 1] = cd0;
+        ulist[3 * slot + 2] = cd1;
+      }
+    }
+    __syncthreads();  // the list is complete
+    {
+      const int nu0 = *ucnt;
+      const int nu = __builtin_amdgcn_readfirstlane(nu0 < UMAX ? nu0 : UMAX);
+      for (int e = w; e < nu; e += WAVES) {
+        const uint32_t ent = __builtin_amdgcn_readfirstlane(ulist[3 * e]);
+        const uint32_t cd0 = __builtin_amdgcn_readfirstlane(ulist[3 * e + 1]);
+        const uint32_t cd1 = __builtin_amdgcn_readfirstlane(ulist[3 * e + 2]);
+        research((int)((ent >> 8) & 0xff), (int)(ent & 0xff), (ent & 0x10000) != 0, cd0, cd1);
+      }
     }
     __syncthreads();  // the queue is complete
-    const int nq0 = *qcnt;
+    const int nq0 = *qcnt;  // the queue is complete: the list's entries were processed above
     const int nq = __builtin_amdgcn_readfirstlane(nq0 < QMAX ? nq0 : QMAX);
     // Workgroup pass(es) over the codebook for the queued vectors, QB at a time: lane l
     // of wave w scores codewords 256 i + 16 w + l / 4 over coordinates 16 (l % 4) .. + 15;
@@ -458,7 +575,7 @@ hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t*
   hipLaunchKernelGGL((encode_full<NF16>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
                      reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot32),
                      reinterpret_cast<const uint8_t*>(cb->frec), cb->cw, cb->pi64t, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms, slots, cap, (int)wgs);
+                     cb->h16_erel, cb->cmax, cb->c2max, codes, norms, slots, cap, (int)wgs);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ struct fq_codebook {
   _Float16* rot32;  // [2 row tiles][4 k steps][hi, mid, lo][64 lanes][8]: 1024 Pi as the A operand of
                     // mfma_f32_32x32x16_f16; row 8 a + 4 hh + b of tile r is coordinate 32 hh + 16 r + 4 a + b
   uint8_t* frec;    // [N / 32 tiles][32 rows][144 bytes], zero-padded to whole chunks of 8 tiles:
-                    // 64 fp16 coordinates, then (rows 4 m only) 256 ||c||^2 of rows 4 m .. 4 m + 3 (fp32)
+                    // 64 fp16 coordinates, then 256 ||c||^2 as fp16 hi, lo and six zero halves
   float* dec_full;  // k = d only: [N][d] Pi^T c_n in fp32 (rounded once from fp64), the decoded unit
                     // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
@@ -47,6 +47,7 @@ struct fq_codebook {
   int force_encoder;  // FQ_ENCODE_KERNEL at load time (an fq::EncodeKernel): that encoder wherever it covers
                       // the call (valu: every call), else the automatic choice
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
+  bool force_attn_lut;  // FQ_ATTN_KERNEL=lut at load time: the lookup-table attention for k = 4 codebooks too
   bool force_cache_codebook;  // FQ_DECODE_KERNEL=cached: the matrix-core decoders read codebooks of more
                               // than 32 KiB from L1 / L2 (the path of devices with less LDS)
 };
@@ -102,6 +103,7 @@ struct AttnPlan {
   int fast_chunks;
   int cpw;
   bool fast;
+  int lut_heads;  // > 0: the lookup-table kernel with this many query heads per workgroup
 };
 bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T);
 // Decode attention covers this codebook (its kernel's LDS fits one workgroup).
@@ -110,6 +112,18 @@ AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T);
 size_t attn_workspace_bytes(int B, int Hq, int Hkv, int nchunks);
 // Partial records per (batch, query head) the workspace must hold for this plan.
 int attn_record_stride(const AttnPlan& p);
+// Workspace bytes of a plan: partial records (+ the lookup tables on that path).
+size_t attn_plan_workspace_bytes(const fq_codebook* cb, const AttnPlan& p, int B, int Hq, int Hkv);
+// The plan's grid fits the launch limits.
+bool attn_plan_launchable(const AttnPlan& p, int B, int Hq, int Hkv);
+
+// Lookup-table decode attention (k = d; k = 4 when forced at load time).
+bool attn_lut_supported(const fq_codebook* cb);
+int attn_lut_heads(const fq_codebook* cb, int G);
+size_t attn_lut_table_bytes(const fq_codebook* cb, int B, int Hq);
+hipError_t launch_attn_lut(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
+                           const uint8_t* v_codes, const void* v_norms, const int32_t* lens, int B, int Hq, int Hkv,
+                           int64_t T, float scale, const AttnPlan& p, float* out, void* workspace, hipStream_t s);
 
 // Workgroups of `kernel` (block threads, lds bytes of dynamic LDS) resident at once on
 // `device`: per-CU occupancy times the CU count, at least 1.  Cached per (kernel, block,
