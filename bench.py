@@ -313,7 +313,9 @@ def rate_axis_timings(fq, workloads, dev, stream, flush, reps: int = 3):
         t_e = timed(lambda: fq.fq_encode(cb.handle, x, codes, norms, stream))
         t_d = timed(lambda: fq.fq_decode(cb.handle, codes, norms, xr, stream))
         dbytes = cb.code_bytes(n) + 2 * n + 2 * D * n  # codes + norms read, fp16 output written
-        rec = {"b": bits / k, "record_bits": (D // k) * bits, "encode_us": t_e * 1e6, "encode_vec_per_s": n / t_e,
+        rec = {"b": bits / k, "record_bits": (D // k) * bits,
+               "encode_kernel": fq.fq_encode_kernel(cb.handle, fq.FQ_F16, n), "encode_us": t_e * 1e6,
+               "encode_vec_per_s": n / t_e,
                "encode_cmp_frac": (D // k) * N * n / t_e / 1e12 / CMP_PEAK_T, "decode_us": t_d * 1e6,
                "decode_GBps": dbytes / t_d / 1e9, "decode_hbm_frac": dbytes / t_d / 1e9 / HBM_PEAK_GBPS}
         if fq.fq_attn_workspace_bytes(cb.handle, L, H, H, T) > 0:

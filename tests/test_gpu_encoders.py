@@ -63,7 +63,7 @@ def _edge_inputs(n_plain, seed):
     return x
 
 
-CASES = [("h16", 4, 32), ("h16", 4, 256), ("h16", 4, 2048),
+CASES = [("h16", 4, 32), ("h16", 4, 256), ("h16", 4, 2048), ("h16", 4, 4096),  # 4096: codebook streamed
          ("h16", 8, 32), ("h16", 8, 64), ("h16", 8, 512), ("h16", 8, 2048), ("h16", 8, 4096),
          ("mfma", 4, 32), ("mfma", 4, 1024), ("mfma", 8, 32), ("mfma", 8, 4096),
          ("full", 64, 32), ("full", 64, 4096),
@@ -126,4 +126,30 @@ def test_automatic_encoder_choice(dev):
     cw, rot = artifact_or_skip(4, 256)
     cb = _forced(cw, rot, "full")
     assert fq.fq_encode_kernel(cb.handle, fq.FQ_F16, 100000) == "encode_h16"
+    cb.close()
+
+
+def test_streamed_codebook_many_rounds_sampled(dev):
+    # k = 4, N = 16384 (the b = 3.5 rate-axis codebook, 256 KiB of records): the fp16
+    # encoder streams it through LDS; 100,013 vectors give every workgroup several
+    # rounds; sampled vectors (both ends and random ones) against the oracle
+    from gpu_util import unpack_sampled
+
+    try:
+        cw, rot = fq.load_artifact(4, 16384, initial=True)
+    except FileNotFoundError:
+        pytest.skip("rate-axis artifact k=4 N=16384 missing")
+    cb = fq.Codebook(cw, rot)
+    x = workloads.tinyllama_kv()[: 100_000 + 13]
+    n = len(x)
+    assert fq.fq_encode_kernel(cb.handle, fq.FQ_F16, n) == "encode_h16"
+    print(f"[streamed codebook] k=4 N=16384 n={n}", flush=True)
+    gc, gn = gpu_encode(cb, x, dev, np.float16)
+    rng = np.random.default_rng(8)
+    idx = np.unique(np.concatenate([rng.choice(n, 600, replace=False), np.arange(16), np.arange(n - 16, n)]))
+    g = unpack_sampled(gc, idx, 16, 14)
+    enc = oc.encode(x[idx], rot, cw, np.float16)
+    assert not ((g != enc.codes) & ~enc.near_tie).any()
+    assert oc.accepted(enc.y, cw, enc, g).all()
+    assert np.array_equal(gn[idx].view(np.uint16), enc.norms.view(np.uint16))
     cb.close()

@@ -42,6 +42,10 @@
 //     (lowest index on exact ties), after an fp32 screen that leaves (nearly
 //     always) one fp64 candidate per lane.
 //  7. Codes are assembled in LDS and written as whole dwords.
+// k = 4 codebooks too large for LDS (beyond 2048 words) are streamed instead (ST): the workgroup's waves take one group each per round and
+// the codebook passes through two LDS buffers of CN codewords, loaded straight
+// from global memory while the previous chunk is searched; recovery and the
+// re-search read their few codewords from global memory.
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -69,7 +73,8 @@ struct Shape<8> {
 
 constexpr int ROT_OPS = 2 * 4 * 3 * 64;  // [k step][row tile][piece][lane] half8 operands
 constexpr int SPK_WORDS = 128;           // 256 codes x 16 bits
-constexpr int WAVE_WORDS = SPK_WORDS + 128;  // + 256 uint16 entries of uncertified blocks
+// + 256 uint16 entries of uncertified blocks, 32 fp64 inverse norms, fp64 y of a re-searched block
+constexpr int WAVE_WORDS = SPK_WORDS + 128 + 64 + 16;
 
 __device__ inline float min16(const f32x16& v) {
   float m = fminf(fminf(v[0], v[1]), v[2]);
@@ -107,12 +112,16 @@ __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(_Flo
 __host__ __device__ constexpr size_t h16_lds_bytes(int K, int N, int waves) {
   return (size_t)ROT_OPS * 16 + (size_t)(N + N / 32) * 16 + (size_t)(N + N / 8) * 4 + (size_t)waves * WAVE_WORDS * 4;
 }
+constexpr int CN = 1024;  // codewords per streamed chunk
+__host__ __device__ constexpr size_t h16s_lds_bytes(int waves) {
+  return (size_t)ROT_OPS * 16 + (size_t)2 * CN * 16 + (size_t)2 * CN * 4 + (size_t)waves * WAVE_WORDS * 4;
+}
 __device__ inline int rslot(int n) { return n + (n >> 5); }
 __device__ inline int cslot(int n) { return n + 4 * (n >> 5); }
 
 // SC: records and norms go to the slots given per vector (an instantiation of its own,
 // so the contiguous kernel keeps its register allocation).
-template <int K, bool NF16, bool SC>
+template <int K, bool NF16, bool SC, bool ST>
 __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
     const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
@@ -125,26 +134,36 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   constexpr int SLOTS = 4 / NSUB;  // block slots a lane fills per sub-group
   extern __shared__ uint4 smem[];
   uint4* rotL = smem;
-  uint4* recL = smem + ROT_OPS;
-  float* c2L = reinterpret_cast<float*>(recL + N + N / 32);
+  uint4* recL = smem + ROT_OPS;  // ST: two chunk buffers of CN records (unpadded)
+  float* c2L = reinterpret_cast<float*>(recL + (ST ? 2 * CN : N + N / 32));  // ST: two of CN floats
   const int w = __builtin_amdgcn_readfirstlane((int)(fq_tid() >> 6));
-  uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + N + N / 8) + w * WAVE_WORDS;
+  uint32_t* spk = reinterpret_cast<uint32_t*>(c2L + (ST ? 2 * CN : N + N / 8)) + w * WAVE_WORDS;
   uint16_t* todoL = reinterpret_cast<uint16_t*>(spk + SPK_WORDS);
+  double* invL = reinterpret_cast<double*>(spk + SPK_WORDS + 128);  // [VG] 1 / nu (0 for nu = 0)
+  double* ysL = invL + 32;                                           // [K] y of a re-searched block
   for (int i = fq_tid(); i < ROT_OPS; i += WAVES * 64) rotL[i] = rot16[i];
-  for (int i = fq_tid(); i < N; i += WAVES * 64) {
-    recL[rslot(i)] = crec[i];
-    c2L[cslot(i)] = cn2s[i];
+  if constexpr (!ST) {
+    for (int i = fq_tid(); i < N; i += WAVES * 64) {
+      recL[rslot(i)] = crec[i];
+      c2L[cslot(i)] = cn2s[i];
+    }
   }
   __syncthreads();
 
   const int lane = fq_tid() & 63;
   const int c = lane & 31, h = lane >> 5, q = lane >> 4, vl = lane & 15;
   const int NT = N / 32;
-  const _Float16* cbh = reinterpret_cast<const _Float16*>(recL);  // record n: halfs 8 rslot(n) .. + 7
+  // codeword n as 8 halves: in LDS at slot rslot(n), or (ST) in global memory
+  const _Float16* cbh = ST ? reinterpret_cast<const _Float16*>(crec) : reinterpret_cast<const _Float16*>(recL);
+  auto rec_of = [&](int nn) { return ST ? nn : rslot(nn); };
 
-  for (int64_t g = (int64_t)fq_bid_x() * WAVES + w; g < ngroups; g += (int64_t)nwg * WAVES) {
+  // ST: rounds are uniform across the workgroup (every wave meets every barrier); a
+  // wave past the last group searches zero inputs and stores nothing
+  for (int64_t gb = (int64_t)fq_bid_x() * WAVES; gb < ngroups; gb += (int64_t)nwg * WAVES) {
+    const int64_t g = gb + w;
+    if (!ST && g >= ngroups) break;
     const int64_t v0 = g * VG;
-    const int nv = (int)((n - v0) < VG ? (n - v0) : VG);
+    const int nv = g < ngroups ? (int)((n - v0) < VG ? (n - v0) : VG) : 0;
 
     // ---- 1-3 per 16-vector sub-group: x, nu, rotation, B operands
     // bq[2 sigma + hp]: B operand of the tile whose column c is block slot sigma of lane c + 32 hp.
@@ -181,6 +200,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
         }
       }
       const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
+      if (q == 0) invL[vec] = nu > 0.0 ? 1.0 / nu : 0.0;  // for the fp64 re-search
 
       f32x4 ah[4], am[4];
 #pragma unroll
@@ -250,35 +270,66 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       m2[tb] = __builtin_huge_valf();
       tid[tb] = 0;
     }
-    half8 A = __builtin_bit_cast(half8, recL[c]);
-    for (int t = 0; t < NT; t++) {
-      const half8 An = __builtin_bit_cast(half8, recL[(t + 1 < NT ? 33 * (t + 1) : 0) + c]);
-      f32x16 C;
-      if constexpr (K == 8) {
+    // tile t of the codebook; `tiles` tiles of `buf` (LDS, padded unless ST), first tile t0
+    auto search = [&](const uint4* buf, const float* c2b, int tiles, int t0) {
+      const int RS = ST ? 32 : 33, CS = ST ? 32 : 36;  // record / norm slots per tile
+      half8 A = __builtin_bit_cast(half8, buf[c]);
+      for (int tl = 0; tl < tiles; tl++) {
+        const int t = t0 + tl;
+        const half8 An = __builtin_bit_cast(half8, buf[(tl + 1 < tiles ? RS * (tl + 1) : 0) + c]);
+        f32x16 C;
+        if constexpr (K == 8) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const float4 cv = *reinterpret_cast<const float4*>(c2L + 36 * t + 8 * j + 4 * h);
-          C[4 * j] = cv.x;
-          C[4 * j + 1] = cv.y;
-          C[4 * j + 2] = cv.z;
-          C[4 * j + 3] = cv.w;
+          for (int j = 0; j < 4; j++) {
+            const float4 cv = *reinterpret_cast<const float4*>(c2b + CS * tl + 8 * j + 4 * h);
+            C[4 * j] = cv.x;
+            C[4 * j + 1] = cv.y;
+            C[4 * j + 2] = cv.z;
+            C[4 * j + 3] = cv.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; e++) C[e] = 0.f;
         }
-      } else {
+        f32x16 Dc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[0]), C, 0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 16; e++) C[e] = 0.f;
+        for (int tb = 0; tb < 8; tb++) {
+          f32x16 Dn;
+          if (tb < 7) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[tb + 1]), C, 0, 0, 0);
+          const float tm = min16(Dc);
+          m2[tb] = __builtin_amdgcn_fmed3f(m1[tb], m2[tb], tm);
+          tid[tb] = tm < m1[tb] ? t : tid[tb];
+          m1[tb] = fminf(m1[tb], tm);
+          if (tb < 7) Dc = Dn;
+        }
+        A = An;
       }
-      f32x16 Dc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[0]), C, 0, 0, 0);
-#pragma unroll
-      for (int tb = 0; tb < 8; tb++) {
-        f32x16 Dn;
-        if (tb < 7) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[tb + 1]), C, 0, 0, 0);
-        const float tm = min16(Dc);
-        m2[tb] = __builtin_amdgcn_fmed3f(m1[tb], m2[tb], tm);
-        tid[tb] = tm < m1[tb] ? t : tid[tb];
-        m1[tb] = fminf(m1[tb], tm);
-        if (tb < 7) Dc = Dn;
+    };
+    if constexpr (!ST) {
+      search(recL, c2L, NT, 0);
+    } else {
+      // chunk ch in buffer ch & 1: CN records (16 KiB, 1 KiB per wave-wide load) and,
+      // for k = 8, CN norms (4 KiB)
+      auto stage = [&](int ch) {
+        const char* src = reinterpret_cast<const char*>(crec + (size_t)ch * CN);
+        char* dst = reinterpret_cast<char*>(recL + (ch & 1) * CN);
+        for (int pc = w; pc < CN * 16 / 1024; pc += WAVES) lds_dma16(src + pc * 1024 + lane * 16, dst + pc * 1024);
+        if constexpr (K == 8) {
+          const char* s2 = reinterpret_cast<const char*>(cn2s + (size_t)ch * CN);
+          char* d2 = reinterpret_cast<char*>(c2L + (ch & 1) * CN);
+          for (int pc = w; pc < CN * 4 / 1024; pc += WAVES) lds_dma16(s2 + pc * 1024 + lane * 16, d2 + pc * 1024);
+        }
+      };
+      const int nchunk = N / CN;
+      stage(0);
+      __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's pieces of chunk 0 are in LDS
+      __syncthreads();
+      for (int ch = 0; ch < nchunk; ch++) {
+        if (ch + 1 < nchunk) stage(ch + 1);
+        search(recL + (ch & 1) * CN, c2L + (ch & 1) * CN, CN / 32, ch * (CN / 32));
+        __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the next chunk's pieces of this wave
+        __syncthreads();                      // every wave is done with this chunk
       }
-      A = An;
     }
 
     // ---- 4-5. recovery and certificate; uncertified blocks go to a list.  Each
@@ -326,11 +377,12 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
 #pragma unroll
       for (int qq = 0; qq < 4; qq++) {
         const int n0 = 32 * t0 + 8 * qq + 4 * hw;  // rows n0 .. n0 + 3 of the winning half
-        const float4 c2v = *reinterpret_cast<const float4*>(c2L + cslot(n0));  // fp32 256 ||c||^2
+        const float4 c2v = ST ? *reinterpret_cast<const float4*>(cn2s + n0)   // fp32 256 ||c||^2
+                              : *reinterpret_cast<const float4*>(c2L + cslot(n0));
         const float c2a[4] = {c2v.x, c2v.y, c2v.z, c2v.w};
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          const uint4 rw = recL[rslot(n0 + e)];
+          const uint4 rw = ST ? crec[n0 + e] : recL[rslot(n0 + e)];
           const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
           float sc = c2a[e];
 #pragma unroll
@@ -384,21 +436,37 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       const int oc = cc + 32 * hp;
       const int fvec = K == 4 ? (oc & 15) : 16 * (sigma >> 1) + (oc & 15);
       const int fbi = K == 4 ? 4 * (oc >> 4) + sigma : 2 * (oc >> 4) + (sigma & 1);
-      // exact y_b: every lane contributes coordinate j = lane of x
-      const double xj = (double)x[(v0 + fvec) * D + lane];
-      double s2 = xj * xj;
+      // exact y_b in fp64: D / K lanes per coordinate i of the block, each summing
+      // K products of Pi[fbi K + i][j] x_j over its own K inputs j, then a butterfly
+      // over those lanes; 1 / nu from the rotation phase (fp64)
+      constexpr int LPO = D / K;
+      // lane-derived offsets the compiler cannot see through: otherwise it keeps the
+      // re-search's addresses (spilled) across the whole search loop
+      int ln = lane;
+      __asm__ volatile("" : "+v"(ln));
+      const int oi = ln / LPO, qq = ln % LPO;
+      double part = 0.0;
+      {
+        const _Float16* xr = x + (v0 + fvec) * D + K * qq;
+        const double* pr = pi64 + (fbi * K + oi) * D + K * qq;
+        _Float16 xh[K];
+        if constexpr (K == 8) {
+          const uint4 xv = *reinterpret_cast<const uint4*>(xr);
+          __builtin_memcpy(xh, &xv, 16);
+        } else {
+          const uint2 xv = *reinterpret_cast<const uint2*>(xr);
+          __builtin_memcpy(xh, &xv, 8);
+        }
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) s2 += shfl_xor_f64(s2, m);
-      const double nuf = sqrt(s2);
-      const double inv = nuf > 0.0 ? 1.0 / nuf : 0.0;
+        for (int j = 0; j < K; j++) part = fma(pr[j], (double)xh[j], part);
+      }
+#pragma unroll
+      for (int m = 1; m < LPO; m <<= 1) part += shfl_xor_f64(part, m);
+      if (qq == 0) ysL[oi] = part * invL[fvec];
+      wave_lds_sync();
       double yb[K];
 #pragma unroll
-      for (int i = 0; i < K; i++) {
-        double p = pi64[(fbi * K + i) * D + lane] * xj;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) p += shfl_xor_f64(p, m);
-        yb[i] = p * inv;
-      }
+      for (int i = 0; i < K; i++) yb[i] = ysL[i];
       // Large codebooks (16 or more codewords per lane) are screened in fp32 first
       // (for smaller ones the screen costs more than it saves): every fp32 distance is
       // within e of the fp64 one, so the fp64 minimiser and all its ties lie within 2 e
@@ -422,7 +490,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
         float f1 = __builtin_huge_valf(), f2 = __builtin_huge_valf();
         int fi = 0x7fffffff;
         for (int nn = lane; nn < N; nn += 64) {
-          const uint4 rw = *reinterpret_cast<const uint4*>(cbh + 8 * rslot(nn));
+          const uint4 rw = *reinterpret_cast<const uint4*>(cbh + 8 * rec_of(nn));
           const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
           float df = 0.f;
 #pragma unroll
@@ -448,7 +516,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
           double dd = 0.0;
 #pragma unroll
           for (int i = 0; i < K; i++) {
-            const double df = yb[i] - (double)cbh[8 * rslot(fi) + i];
+            const double df = yb[i] - (double)cbh[8 * rec_of(fi) + i];
             dd = fma(df, df, dd);
           }
           bd = dd;
@@ -460,7 +528,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
           double dd = 0.0;
 #pragma unroll
           for (int i = 0; i < K; i++) {
-            const double df = yb[i] - (double)cbh[8 * rslot(nn) + i];
+            const double df = yb[i] - (double)cbh[8 * rec_of(nn) + i];
             dd = fma(df, df, dd);
           }
           if (dd < bd) {
@@ -500,45 +568,63 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
   }
 }
 
-template <int K, bool NF16, bool SC>
+template <int K, bool NF16, bool SC, bool ST>
 hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
                       const int64_t* slots, int64_t cap, hipStream_t s) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int VG = 16 * Shape<K>::NSUB;
-  const size_t lds = h16_lds_bytes(K, cb->N, WAVES);
+  const auto kern = encode_h16<K, NF16, SC, ST>;
+  const size_t lds = ST ? h16s_lds_bytes(WAVES) : h16_lds_bytes(K, cb->N, WAVES);
+  hipError_t e = hipSuccess;
+  if (lds > 65536)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   int64_t resident = 0;
-  const hipError_t e = resident_workgroups(reinterpret_cast<const void*>(encode_h16<K, NF16, SC>), WAVES * 64, lds,
-                                           cb->device, &resident);
+  e = resident_workgroups(reinterpret_cast<const void*>(kern), WAVES * 64, lds, cb->device, &resident);
   if (e != hipSuccess) return e;
   const int64_t ngroups = (n + VG - 1) / VG;
   int64_t wgs = (ngroups + WAVES - 1) / WAVES;
   if (wgs > resident) wgs = resident;
-  hipLaunchKernelGGL((encode_h16<K, NF16, SC>), dim3((unsigned)wgs), dim3(WAVES * 64), lds, s,
-                     reinterpret_cast<const _Float16*>(x), n, ngroups, reinterpret_cast<const uint4*>(cb->rot16),
-                     reinterpret_cast<const uint4*>(cb->crec), cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs,
-                     cb->h16_erel, codes, norms, slots, cap, (int)wgs);
+  hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, reinterpret_cast<const _Float16*>(x), n,
+                     ngroups, reinterpret_cast<const uint4*>(cb->rot16), reinterpret_cast<const uint4*>(cb->crec),
+                     cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs, cb->h16_erel, codes, norms, slots, cap,
+                     (int)wgs);
   return hipGetLastError();
+}
+
+// The whole codebook fits in LDS beside the rotation operands and the waves' scratch.
+bool h16_in_lds(const fq_codebook* cb) {
+  if (!((cb->k == 4 && cb->N <= 2048) || (cb->k == 8 && cb->N <= 4096))) return false;
+  const int waves = cb->k == 4 ? Shape<4>::WAVES : Shape<8>::WAVES;
+  return h16_lds_bytes(cb->k, cb->N, waves) <= cb->max_lds;
 }
 
 }  // namespace
 
 bool encode_h16_supported(const fq_codebook* cb) {
   if (!cb->rot16 || !cb->crec || cb->N % 32 != 0 || cb->N < 32) return false;
-  if (!((cb->k == 4 && cb->N <= 2048) || (cb->k == 8 && cb->N <= 4096))) return false;
-  const int waves = cb->k == 4 ? Shape<4>::WAVES : Shape<8>::WAVES;
-  return h16_lds_bytes(cb->k, cb->N, waves) <= cb->max_lds;
+  if (cb->k != 4 && cb->k != 8) return false;
+  if (h16_in_lds(cb)) return true;
+  // streamed: k = 4 only (the k = 8 search's registers leave no room for it)
+  return cb->k == 4 && cb->N % CN == 0 && h16s_lds_bytes(Shape<4>::WAVES) <= cb->max_lds;
 }
 
 hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
                              fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s) {
   if (!encode_h16_supported(cb)) return hipErrorNotSupported;
-  const bool nf = norm_dtype == FQ_F16;
-#define FQ_H16(KK, NF) \
-  (slots ? launch_h16<KK, NF, true>(cb, x, n, codes, norms, slots, cap, s) \
-         : launch_h16<KK, NF, false>(cb, x, n, codes, norms, slots, cap, s))
+  const bool nf = norm_dtype == FQ_F16, st = !h16_in_lds(cb);
+#define FQ_H16S(KK, NF, SCC) \
+  (st ? launch_h16<KK, NF, SCC, true>(cb, x, n, codes, norms, slots, cap, s) \
+      : launch_h16<KK, NF, SCC, false>(cb, x, n, codes, norms, slots, cap, s))
+#define FQ_H16(KK, NF) (slots ? FQ_H16S(KK, NF, true) : FQ_H16S(KK, NF, false))
   if (cb->k == 4) return nf ? FQ_H16(4, true) : FQ_H16(4, false);
-  return nf ? FQ_H16(8, true) : FQ_H16(8, false);
+#define FQ_H16_8(NF) \
+  (slots ? launch_h16<8, NF, true, false>(cb, x, n, codes, norms, slots, cap, s) \
+         : launch_h16<8, NF, false, false>(cb, x, n, codes, norms, slots, cap, s))
+  return nf ? FQ_H16_8(true) : FQ_H16_8(false);
+#undef FQ_H16_8
 #undef FQ_H16
+#undef FQ_H16S
 }
 
 }  // namespace fq
