@@ -278,6 +278,45 @@ def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: in
     return out
 
 
+def prefill_codebook_timings(fq, workloads, dev, stream, flush, kv_np, reps: int):
+    """Prefill attention of other codebooks at the prefill workload's shape (B=16,
+    Hq=32, Hkv=4, T=32768, 64 causal queries per head; K and V draws encoded on the
+    GPU): the generic decode stage with the codebook read from global memory (k = d
+    = 64, N = 4096: 512 KiB; k = 8, N = 4096: 64 KiB) or from LDS (k = 2, N = 16)."""
+    import torch
+
+    B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
+    na = B * Hkv * Ta
+    Sq = 64
+    qp = torch.from_numpy(np.random.default_rng(107).standard_normal((B, Hq, Sq, D)).astype(np.float16)).to(dev)
+    po = torch.empty((B, Hq, Sq, D), dtype=torch.float32, device=dev)
+    pairs = B * Hq * sum(Ta - Sq + i + 1 for i in range(Sq))
+    useful = 4.0 * D * pairs
+    out = {}
+    for k, N in [(64, 4096), (8, 4096), (2, 16)]:
+        cb = fq.Codebook.from_artifact(k, N)
+        kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
+        codes = torch.zeros(cb.code_bytes(2 * na), dtype=torch.uint8, device=dev)
+        norms = torch.empty(2 * na, dtype=torch.float16, device=dev)
+        fq.fq_encode(cb.handle, kv, codes, norms, stream)
+        del kv
+        # V's records start at vector na: a whole byte for every codebook here
+        half = cb.code_bytes(na)
+        pws = torch.empty(fq.fq_attn_prefill_workspace_bytes(cb.handle, B, Hq, Hkv, Sq, Ta), dtype=torch.uint8,
+                          device=dev)
+        t = timed_evicted(lambda: fq.fq_attn_prefill(cb.handle, qp, codes[:half], norms[:na], codes[half:],
+                                                     norms[na:], B, Hq, Hkv, Sq, Ta, True, 0.125, po, pws, stream),
+                          stream, flush, reps)
+        out[f"k{k}_N{N}"] = {"k": k, "N": N, "us_per_step": t * 1e6,
+                             "codebook": "LDS" if N * k * 2 <= 32768 else "global memory",
+                             "mfma_frac": useful / t / 1e12 / FP16_MFMA_PEAK_T}
+        cb.close()
+        del codes, norms, pws
+        torch.cuda.empty_cache()
+    del qp, po
+    return out
+
+
 # Rate-axis points (k, N) with frozen initial codebooks: b = log2(N) / k from 4 down to 0.22.
 RATE_AXIS = [(1, 16), (2, 32), (2, 128), (4, 1024), (4, 16384), (16, 1024), (32, 512), (64, 16384)]
 
@@ -545,6 +584,8 @@ def main():
                          "issued_TFLOPs": 1.5 * useful / t_p / 1e12},
         }
         del qp, po, pws
+        line["prefill_b16_t32k_q64"]["other_codebooks"] = prefill_codebook_timings(fq, workloads, dev, stream, flush,
+                                                                                   kv_np, args.attn_iters)
 
     # ------------------------------------------------------------ decode loop over the attention cache
     # One decode step per sequence: the new token's K and V go to slot len_b of their

@@ -101,14 +101,67 @@ def test_prefill_full_size_sampled(dev, cb4):
         assert max_rel_rows(got[b:b + 1, g * G:(g + 1) * G].reshape(-1, D), ref.reshape(-1, D)) <= TOL
 
 
-def test_prefill_rejects_other_codebooks(dev):
-    import torch
+def _cache_for(B, Hkv, T, vec_bits, seed):
+    n = B * Hkv * T
+    nbytes = (n * vec_bits + 7) // 8
+    return (workloads.random_code_store(nbytes, seed), workloads.random_norms(n, seed + 1),
+            workloads.random_code_store(nbytes, seed + 2), workloads.random_norms(n, seed + 3))
 
-    cw, rot = artifact_or_skip(2, 16)
+
+def _prefill_case(dev, cw, rot, B, Hq, Hkv, Sq, T, causal, seed):
     cb = fq.Codebook(cw, rot)
-    q = torch.zeros((1, 8, 4, D), dtype=torch.float16, device=dev)
-    z = torch.zeros(16, dtype=torch.uint8, device=dev)
-    out = torch.zeros((1, 8, 4, D), dtype=torch.float32, device=dev)
-    with pytest.raises(fq.FQError) as e:
-        fq.fq_attn_prefill(cb.handle, q, z, z, z, z, 1, 8, 1, 4, 10, True, 0.125, out, z)
-    assert e.value.status == fq.FQ_ERR_UNSUPPORTED
+    N, k = cw.shape
+    nblk, bits = D // k, oc.code_bits(N)
+    kc, kn, vc, vn = _cache_for(B, Hkv, T, nblk * bits, seed)
+    q = np.random.default_rng(seed + 9).standard_normal((B, Hq, Sq, D)).astype(np.float16)
+    print(f"[prefill parity] k={k} N={N} B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} T={T} causal={causal}", flush=True)
+    got = _gpu_prefill(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, Sq, T, causal)
+    n = B * Hkv * T
+    unp = lambda s: oc.unpack_codes(s, n, nblk, bits).reshape(B, Hkv, T, nblk)
+    ref = oatt.prefill_attention(q, unp(kc), kn.reshape(B, Hkv, T), unp(vc), vn.reshape(B, Hkv, T), rot, cw, 0.125,
+                                 causal)
+    assert max_rel_rows(got.reshape(-1, D), ref.reshape(-1, D)) <= TOL
+
+
+# every decode mode of the prefill kernel: codebook in LDS (<= 32 KiB of fp16: k = 1, 2, 4 / N = 1024,
+# 16 / 1024 and 32 / 512 at the limit) or read from global memory (k = 4 / 16384, 8 / 4096, 64 / 4096
+# and 16384); records of 12, 88 or 14 bits straddle bytes
+@pytest.mark.parametrize("k,N", [(1, 16), (2, 16), (2, 128), (4, 1024), (4, 16384), (8, 4096), (16, 1024),
+                                 (32, 512), (64, 4096), (64, 16384)])
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,T,causal", [
+    (2, 8, 2, 5, 300, True),
+    (1, 16, 2, 20, 133, False),   # 160 rows per slab, ragged last unit
+])
+def test_prefill_other_codebooks(dev, k, N, B, Hq, Hkv, Sq, T, causal):
+    # the trained artifact where there is one, else the construction's initial codebook
+    try:
+        cw, rot = fq.load_artifact(k, N)
+    except FileNotFoundError:
+        cw, rot = fq.load_artifact(k, N, initial=True)
+    _prefill_case(dev, cw, rot, B, Hq, Hkv, Sq, T, causal, 900 + k + N + T)
+
+
+def test_prefill_tiny_codebook(dev):
+    # k = 1, N = 4: a codebook of four fp16 halves (copied to LDS one half at a time)
+    _, rot = artifact_or_skip(4, 256)
+    cw = np.array([[-1.5], [-0.25], [0.375], [2.0]], dtype=np.float32)
+    _prefill_case(dev, cw, rot, 1, 4, 1, 7, 70, True, 950)
+
+
+def test_prefill_full_size_sampled_full_vector_code(dev):
+    # the benchmark's prefill launch over a k = d = 64, N = 4096 cache (12-bit records, codebook in global memory)
+    cw, rot = artifact_or_skip(64, 4096)
+    cb = fq.Codebook(cw, rot)
+    B, Hq, Hkv, T, Sq = 16, 32, 4, 32768, 64
+    kc, kn, vc, vn = _cache_for(B, Hkv, T, 12, 960)
+    q = np.random.default_rng(961).standard_normal((B, Hq, Sq, D)).astype(np.float16)
+    print("[prefill full size, k=64 N=4096] B=16 Hq=32 Hkv=4 Sq=64 T=32768 causal", flush=True)
+    got = _gpu_prefill(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, Sq, T, True)
+    G = Hq // Hkv
+    for b, g in [(0, 1), (15, 3)]:
+        idx = np.arange(T) + (b * Hkv + g) * T
+        ref = oatt.prefill_attention(q[b:b + 1, g * G:(g + 1) * G],
+                                     unpack_sampled(kc, idx, 1, 12).reshape(1, 1, T, 1), kn[idx].reshape(1, 1, T),
+                                     unpack_sampled(vc, idx, 1, 12).reshape(1, 1, T, 1), vn[idx].reshape(1, 1, T),
+                                     rot, cw, 0.125, True)
+        assert max_rel_rows(got[b:b + 1, g * G:(g + 1) * G].reshape(-1, D), ref.reshape(-1, D)) <= TOL

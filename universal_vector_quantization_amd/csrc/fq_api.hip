@@ -500,13 +500,20 @@ FQ_EXPORT fq_status fq_decode(const fq_codebook* cb, const uint8_t* codes, const
 }
 
 namespace {
-fq_status attn_check_sizes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
+// Shapes both attention kernels take; decode attention also needs fq::attn_supported.
+fq_status attn_check_shape(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
   if (!cb || B < 0 || Hq <= 0 || Hkv <= 0 || T < 0) return FQ_ERR_ARG;
   if (Hq % Hkv != 0) return FQ_ERR_ARG;
   if (Hq / Hkv > 16) return FQ_ERR_UNSUPPORTED;
-  if (!fq::attn_supported(cb)) return FQ_ERR_UNSUPPORTED;
   if (B > 65535 || Hkv > 65535 || (int64_t)B * Hq > ((int64_t)1 << 31) - 1) return FQ_ERR_UNSUPPORTED;
   if (T > ((int64_t)1 << 40)) return FQ_ERR_UNSUPPORTED;
+  return FQ_OK;
+}
+
+fq_status attn_check_sizes(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
+  const fq_status st = attn_check_shape(cb, B, Hq, Hkv, T);
+  if (st != FQ_OK) return st;
+  if (!fq::attn_supported(cb)) return FQ_ERR_UNSUPPORTED;
   return FQ_OK;
 }
 }  // namespace
@@ -591,7 +598,8 @@ FQ_EXPORT fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const u
 }
 
 FQ_EXPORT size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T) {
-  if (attn_check_sizes(cb, B, Hq, Hkv, T) != FQ_OK || Sq <= 0 || T == 0 || B == 0) return 0;
+  if (attn_check_shape(cb, B, Hq, Hkv, T) != FQ_OK || !fq::prefill_supported(cb) || Sq <= 0 || T == 0 || B == 0)
+    return 0;
   if ((int64_t)B * Hq * Sq > ((int64_t)1 << 31) - 1) return 0;
   const fq::PrefillPlan p = fq::prefill_plan(B, Hq, Hkv, Sq, T);
   return ((size_t)B * Hq * Sq * p.nchunks * (2 + fq::kD) * sizeof(float) + 255) & ~(size_t)255;
@@ -601,7 +609,7 @@ FQ_EXPORT fq_status fq_attn_prefill(const fq_codebook* cb, const void* q, const 
                                     const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq,
                                     int64_t T, int causal, float scale, float* out, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-  const fq_status ss = attn_check_sizes(cb, B, Hq, Hkv, T);
+  const fq_status ss = attn_check_shape(cb, B, Hq, Hkv, T);
   if (ss != FQ_OK) return ss;
   if (Sq < 0 || (causal != 0 && causal != 1) || !isfinite(scale)) return FQ_ERR_ARG;
   if (!fq::prefill_supported(cb)) return FQ_ERR_UNSUPPORTED;

@@ -9,9 +9,14 @@
 //   * a workgroup takes 64 query rows of one (batch, KV head) slab (row r = head
 //     r / Sq of the group, query r % Sq) and a range of its keys; each of its 4
 //     waves owns 16 rows (the MFMA columns);
-//   * per 64-key unit every thread decodes one key's quarter record into LDS: K
-//     as [key][dim] fp16 (the A operand of S^T = K Qrot^T), V transposed as
-//     [dim][key] (the A operand of O^T += V^T P^T), norms as fp32;
+//   * per 64-key unit the threads decode the keys' records into LDS: K as
+//     [key][dim] fp16 (the A operand of S^T = K Qrot^T), V transposed as
+//     [dim][key] (the A operand of O^T += V^T P^T), norms as fp32.  For k = 4
+//     with 8-bit codes every thread takes one quarter record, loaded a unit ahead
+//     into registers; for other codebooks a thread takes pieces of min(k, 16)
+//     dimensions of a key (the code read at its fixed bit address), copied from
+//     an LDS copy of the codebook when that is at most 32 KiB, else from the
+//     fp16 codebook in global memory (L2-resident: 512 KiB for k = d, N = 4096);
 //   * the rotated, scaled query is split fp16 hi + lo (two products per K step:
 //     scores carry ~22 bits); P' = p * nu_v enters as one fp16 operand (relative
 //     rounding 2^-12 of each weight);
@@ -36,6 +41,14 @@ constexpr int REC_F = 2 + D;
 // touches on the same banks; 144- and 136-byte rows spread them over all 64 banks
 constexpr int KS = D + 8;   // K tile [key][KS]
 constexpr int VS = PU + 4;  // V tile [dim][VS]
+constexpr int QSCR = 17;    // floats per lane of the query rotation's scratch (odd: no bank conflicts)
+// How a workgroup gets codewords: the k = 4, 8-bit path (registers a unit ahead, LDS
+// codebook), or pieces read from an LDS copy of the codebook, or from global memory.
+enum CbMode { CB_K4B8 = 0, CB_LDS = 1, CB_GLOBAL = 2 };
+constexpr size_t CB_LDS_MAX = 32768;  // bytes of fp16 codebook held in LDS
+// the query rotation's scratch shares the LDS of the K and V tiles (used before them)
+constexpr int TILE_BYTES = (PU * KS + D * VS) * 2;
+static_assert(PW * 64 * QSCR * 4 <= TILE_BYTES, "query scratch must fit the tile space");
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
@@ -54,16 +67,62 @@ struct UnitRegs {
   _Float16 kn, vn;
 };
 
-__global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
+// Copy one piece of KW fp16 codeword coordinates (KW-aligned) from src into registers.
+template <int KW>
+__device__ inline void load_piece(const _Float16* src, _Float16 (&v)[KW]) {
+  if constexpr (KW >= 8) {
+#pragma unroll
+    for (int c = 0; c < KW / 8; c++) {
+      const half8 h = *reinterpret_cast<const half8*>(src + 8 * c);
+#pragma unroll
+      for (int j = 0; j < 8; j++) v[8 * c + j] = h[j];
+    }
+  } else if constexpr (KW == 4) {
+    const half4 h = *reinterpret_cast<const half4*>(src);
+#pragma unroll
+    for (int j = 0; j < 4; j++) v[j] = h[j];
+  } else if constexpr (KW == 2) {
+    const half2_t h = *reinterpret_cast<const half2_t*>(src);
+    v[0] = h[0];
+    v[1] = h[1];
+  } else {
+    v[0] = src[0];
+  }
+}
+
+// Store a piece to KW consecutive fp16 slots (KW-aligned, 16-byte aligned for KW >= 8).
+template <int KW>
+__device__ inline void store_piece(_Float16* dst, const _Float16 (&v)[KW]) {
+  if constexpr (KW >= 8) {
+#pragma unroll
+    for (int c = 0; c < KW / 8; c++) {
+      half8 h;
+#pragma unroll
+      for (int j = 0; j < 8; j++) h[j] = v[8 * c + j];
+      *reinterpret_cast<half8*>(dst + 8 * c) = h;
+    }
+  } else if constexpr (KW == 4) {
+    *reinterpret_cast<half4*>(dst) = half4{v[0], v[1], v[2], v[3]};
+  } else if constexpr (KW == 2) {
+    *reinterpret_cast<half2_t*>(dst) = half2_t{v[0], v[1]};
+  } else {
+    dst[0] = v[0];
+  }
+}
+
+// KW = min(k, 16) dimensions per decode piece (CB_K4B8: 4); CM: a CbMode.
+template <int KW, int CM>
+__global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
     const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
-    const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T, int Sq, int causal, int64_t chunk_tokens,
-    int nchunks, float* __restrict__ ws) {
-  __shared__ __align__(16) _Float16 cbL[256 * 4];
-  __shared__ __align__(16) _Float16 Kt[PU * KS];  // [key][dim]
-  __shared__ __align__(16) _Float16 Vt[D * VS];   // [dim][key]
+    const _Float16* __restrict__ cw16, int k, int bits, int N, int Hq, int Hkv, int64_t T, int Sq, int causal,
+    int64_t chunk_tokens, int nchunks, float* __restrict__ ws) {
+  extern __shared__ __align__(16) _Float16 cbL[];  // the codebook [N][k] (CB_K4B8, CB_LDS)
+  __shared__ __align__(16) unsigned char tiles[TILE_BYTES];
+  _Float16* const Kt = reinterpret_cast<_Float16*>(tiles);  // [key][KS]
+  _Float16* const Vt = Kt + PU * KS;                        // [dim][VS]
+  float* const qscr = reinterpret_cast<float*>(tiles);      // per-lane scratch of the query rotation
   __shared__ float knL[PU], vnL[PU];
-  __shared__ float qscr[PW * 64 * 17];  // per-lane scratch of the query rotation (stride 17: no bank conflicts)
   const int tid = fq_tid(), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = fq_bid_x(), rb = fq_bid_y(), slab = fq_bid_z();
@@ -92,8 +151,15 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
   }
 
   // codebook
-  for (int e = tid; e < 256 * 4 / 8; e += PW * 64)
-    reinterpret_cast<uint4*>(cbL)[e] = reinterpret_cast<const uint4*>(cw16)[e];
+  if constexpr (CM != CB_GLOBAL) {
+    const int nh = N * k;  // a power of two
+    if (nh % 8 == 0) {
+      for (int e = tid; e < nh / 8; e += PW * 64)
+        reinterpret_cast<uint4*>(cbL)[e] = reinterpret_cast<const uint4*>(cw16)[e];
+    } else {
+      for (int e = tid; e < nh; e += PW * 64) cbL[e] = cw16[e];
+    }
+  }
 
   // B operands of QK: column col = query row r, k = 8 hq + j is dimension 32 s + 8 hq + j
   // of the rotated query (Pi q) * scale * log2(e), split fp16 hi + lo
@@ -116,13 +182,13 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
       float a = 0.0f;
 #pragma unroll
       for (int e = 0; e < D; e++) a = __builtin_fmaf(pi32[d * D + e], qv[e], a);
-      qscr[tid * 17 + jj] = a * qscale;
+      qscr[tid * QSCR + jj] = a * qscale;
     }
 #pragma unroll
     for (int s = 0; s < 2; s++)
 #pragma unroll
       for (int j = 0; j < 8; j++) {
-        const float a = qscr[tid * 17 + 8 * s + j];
+        const float a = qscr[tid * QSCR + 8 * s + j];
         const _Float16 h = (_Float16)a;
         qhi[s][j] = h;
         qlo[s][j] = (_Float16)(a - (float)h);
@@ -152,13 +218,41 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
     }
   };
   UnitRegs cur{}, nxt{};
-  if (t_begin < t_end) load_unit(t_begin, cur);
+  if (CM == CB_K4B8 && t_begin < t_end) load_unit(t_begin, cur);
   __syncthreads();  // codebook in place
 
+  const int lk = __builtin_ctz((unsigned)k);
+  const int64_t vbits = (int64_t)(D / k) * bits;  // bits of one vector's record
   for (int64_t t0 = t_begin; t0 < t_end; t0 += PU) {
     // ---- decode the unit into LDS
-    __syncthreads();  // the previous unit's tiles are no longer read
-    {
+    __syncthreads();  // the previous unit's tiles (or the query scratch) are no longer read
+    if constexpr (CM != CB_K4B8) {
+      // item it: piece p = it % P of key (it / P) % PU, of V when it >= PU P (wave-uniform)
+      constexpr int P = D / KW;
+      const int64_t nt = t_end - t0;
+#pragma unroll 2
+      for (int it = tid; it < 2 * PU * P; it += PW * 64) {
+        const int p = it % P, key = (it / P) % PU;
+        const bool isv = it >= PU * P;
+        const int dim0 = p * KW, blk = dim0 >> lk, off = dim0 & (k - 1);
+        const int64_t kk = slab0 + t0 + (key < nt ? key : nt - 1);
+        const uint32_t code = load_code(isv ? vc : kc, kk * vbits + (int64_t)blk * bits, bits);
+        const _Float16* src = (CM == CB_LDS ? cbL : cw16) + (size_t)code * k + off;
+        _Float16 v[KW];
+        load_piece<KW>(src, v);
+        if (isv) {
+#pragma unroll
+          for (int e = 0; e < KW; e++) Vt[(dim0 + e) * VS + key] = v[e];
+        } else {
+          store_piece<KW>(Kt + key * KS + dim0, v);
+        }
+      }
+      if (tid < PU) {
+        const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
+        knL[tid] = (float)kn[kk];
+        vnL[tid] = (float)vn[kk];
+      }
+    } else {
       const uint32_t w0 = cur.w0, w1 = cur.w1;
 #pragma unroll
       for (int c = 0; c < 4; c++) {
@@ -182,7 +276,7 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill_k4b8(
         vnL[tid] = (float)cur.vn;
       }
     }
-    if (t0 + PU < t_end) load_unit(t0 + PU, nxt);
+    if (CM == CB_K4B8 && t0 + PU < t_end) load_unit(t0 + PU, nxt);
     __syncthreads();
 
     // keys of this unit the lane's row may see: kk <= bound (32-bit; -1 = none)
@@ -288,19 +382,73 @@ PrefillPlan prefill_plan(int B, int Hq, int Hkv, int Sq, int64_t T) {
   return PrefillPlan{(int)nc, ct, rblocks};
 }
 
-bool prefill_supported(const fq_codebook* cb) { return cb->k == 4 && cb->bits == 8; }
+bool prefill_supported(const fq_codebook* cb) { return cb->k >= 1 && cb->k <= D && D % cb->k == 0; }
+
+namespace {
+CbMode prefill_cb_mode(const fq_codebook* cb) {
+  if (cb->k == 4 && cb->bits == 8) return CB_K4B8;
+  return (size_t)cb->N * cb->k * 2 <= CB_LDS_MAX ? CB_LDS : CB_GLOBAL;
+}
+
+struct PrefillArgs {
+  const _Float16* q;
+  float qscale;
+  const uint8_t *kc, *vc;
+  const _Float16 *kn, *vn;
+  int Hq, Hkv, Sq, causal;
+  int64_t T;
+  PrefillPlan p;
+  dim3 grid;
+  float* ws;
+};
+
+template <int KW, int CM>
+hipError_t launch_variant(const fq_codebook* cb, const PrefillArgs& a, hipStream_t s) {
+  const size_t lds = CM == CB_GLOBAL ? 0 : (size_t)cb->N * cb->k * sizeof(_Float16);
+  hipLaunchKernelGGL((attn_prefill<KW, CM>), a.grid, dim3(PW * 64), lds, s, a.q, a.qscale, cb->pi32, a.kc, a.kn,
+                     a.vc, a.vn, cb->cw16, cb->k, cb->bits, cb->N, a.Hq, a.Hkv, a.T, a.Sq, a.causal,
+                     a.p.chunk_tokens, a.p.nchunks, a.ws);
+  return hipGetLastError();
+}
+
+template <int KW>
+hipError_t launch_generic(const fq_codebook* cb, CbMode m, const PrefillArgs& a, hipStream_t s) {
+  return m == CB_LDS ? launch_variant<KW, CB_LDS>(cb, a, s) : launch_variant<KW, CB_GLOBAL>(cb, a, s);
+}
+}  // namespace
 
 hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                           const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
                           int causal, float scale, float* out, void* workspace, hipStream_t s) {
   const PrefillPlan p = prefill_plan(B, Hq, Hkv, Sq, T);
-  const float qscale = scale * 1.4426950408889634f;  // log2(e)
-  hipLaunchKernelGGL(attn_prefill_k4b8, dim3((unsigned)p.nchunks, (unsigned)p.rblocks, (unsigned)(B * Hkv)),
-                     dim3(PW * 64), 0, s, reinterpret_cast<const _Float16*>(q), qscale, cb->pi32, k_codes,
-                     reinterpret_cast<const _Float16*>(k_norms), v_codes, reinterpret_cast<const _Float16*>(v_norms),
-                     cb->cw16, Hq, Hkv, T, Sq, causal, p.chunk_tokens, p.nchunks,
-                     reinterpret_cast<float*>(workspace));
-  const hipError_t e = hipGetLastError();
+  PrefillArgs a;
+  a.q = reinterpret_cast<const _Float16*>(q);
+  a.qscale = scale * 1.4426950408889634f;  // log2(e)
+  a.kc = k_codes;
+  a.vc = v_codes;
+  a.kn = reinterpret_cast<const _Float16*>(k_norms);
+  a.vn = reinterpret_cast<const _Float16*>(v_norms);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Sq = Sq;
+  a.causal = causal;
+  a.T = T;
+  a.p = p;
+  a.grid = dim3((unsigned)p.nchunks, (unsigned)p.rblocks, (unsigned)(B * Hkv));
+  a.ws = reinterpret_cast<float*>(workspace);
+  const CbMode m = prefill_cb_mode(cb);
+  hipError_t e;
+  if (m == CB_K4B8) {
+    e = launch_variant<4, CB_K4B8>(cb, a, s);
+  } else {
+    switch (cb->k < 16 ? cb->k : 16) {
+      case 1: e = launch_generic<1>(cb, m, a, s); break;
+      case 2: e = launch_generic<2>(cb, m, a, s); break;
+      case 4: e = launch_generic<4>(cb, m, a, s); break;
+      case 8: e = launch_generic<8>(cb, m, a, s); break;
+      default: e = launch_generic<16>(cb, m, a, s); break;
+    }
+  }
   if (e != hipSuccess) return e;
   return launch_attn_combine(reinterpret_cast<const float*>(workspace), cb->pi32, (int64_t)B * Hq * Sq, p.nchunks,
                              out, s);
