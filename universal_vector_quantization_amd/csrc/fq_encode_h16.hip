@@ -64,11 +64,13 @@ template <>
 struct Shape<4> {
   static constexpr int WAVES = 8;  // 2 workgroups of 8 waves per CU
   static constexpr int NSUB = 1;   // 16-vector rotation sub-groups per group
+  static constexpr int OCC = 4;    // waves per SIMD the register budget is set for (128 registers)
 };
 template <>
 struct Shape<8> {
   static constexpr int WAVES = 16;  // the 4096-word codebook fills most of the LDS
   static constexpr int NSUB = 2;
+  static constexpr int OCC = 4;
 };
 
 constexpr int ROT_OPS = 2 * 4 * 3 * 64;  // [k step][row tile][piece][lane] half8 operands
@@ -122,7 +124,7 @@ __device__ inline int cslot(int n) { return n + 4 * (n >> 5); }
 // SC: records and norms go to the slots given per vector (an instantiation of its own,
 // so the contiguous kernel keeps its register allocation).
 template <int K, bool NF16, bool SC, bool ST>
-__global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
+__global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h16(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
     const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
     int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
@@ -173,9 +175,13 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       const int vec = 16 * sg + vl;
       uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
       if (vec < nv) {
-        const uint4* xp = reinterpret_cast<const uint4*>(x + (v0 + vec) * D);
-        xa = xp[q];
-        xb = xp[4 + q];
+        // a uniform group base plus a 32-bit lane offset the compiler cannot carry from
+        // one group to the next (a per-lane 64-bit pointer would live across the search)
+        int off = vec * (D / 8) + q;
+        __asm__ volatile("" : "+v"(off));
+        const uint4* xp = reinterpret_cast<const uint4*>(x + v0 * D);
+        xa = xp[off];
+        xb = xp[off + 4];
       }
       double s = 0.0;
       {
@@ -560,7 +566,9 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, 4) void encode_h16(
       const int64_t nbytes = ((int64_t)nv * (D / K) * bits + 7) / 8;
       uint8_t* dst = codes + g * (int64_t)(32 * bits);  // group g starts at bit g * 256 * bits
       const int nfull = (int)(nbytes / 4);
-      for (int i = lane; i < nfull; i += 64) reinterpret_cast<uint32_t*>(dst)[i] = spk[i];
+      int i0 = lane;  // opaque: no per-lane 64-bit store pointer carried across groups
+      __asm__ volatile("" : "+v"(i0));
+      for (int i = i0; i < nfull; i += 64) reinterpret_cast<uint32_t*>(dst)[i] = spk[i];
       const int rem = (int)(nbytes - 4 * (int64_t)nfull);
       if (lane < rem) dst[4 * nfull + lane] = (uint8_t)((spk[nfull] >> (8 * lane)) & 0xffu);
     }
