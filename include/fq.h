@@ -105,7 +105,8 @@ fq_status fq_encode(const fq_codebook* cb, const void* x, fq_dtype x_dtype, int6
 /* Name of the encoder kernel fq_encode (and fq_encode_scatter) launches for n
  * vectors of dtype x_dtype with this codebook: "encode_wave" (batches of at most
  * 2048 vectors), "encode_h16" (fp16 input, k = 4 or 8), "encode_full" (fp16
- * input, k = d), "encode_mfma" (k = 4 or 8) or "encode_valu" (every shape).  The
+ * input, k = 16, 32 or d), "encode_mfma" (k = 4 or 8) or "encode_valu" (every
+ * shape).  The
  * environment variable FQ_ENCODE_KERNEL, read by fq_codebook_load, forces one of
  * them (small, h16, full, mfma, valu) wherever it covers the call.  A diagnostic:
  * static string, NULL for a NULL handle, n < 0 or an invalid dtype. */

@@ -67,6 +67,8 @@ CASES = [("h16", 4, 32), ("h16", 4, 256), ("h16", 4, 2048), ("h16", 4, 4096),  #
          ("h16", 8, 32), ("h16", 8, 64), ("h16", 8, 512), ("h16", 8, 2048), ("h16", 8, 4096),
          ("mfma", 4, 32), ("mfma", 4, 1024), ("mfma", 8, 32), ("mfma", 8, 4096),
          ("full", 64, 32), ("full", 64, 4096),
+         ("full", 32, 32), ("full", 32, 512), ("full", 32, 2048),    # two blocks per vector
+         ("full", 16, 32), ("full", 16, 1024), ("full", 16, 4096),   # four blocks, two codebook passes
          ("valu", 4, 256), ("small", 8, 512)]
 NAMES = {"h16": "encode_h16", "mfma": "encode_mfma", "full": "encode_full", "valu": "encode_valu",
          "small": "encode_wave"}
@@ -122,6 +124,12 @@ def test_automatic_encoder_choice(dev):
     assert fq.fq_encode_kernel(cb.handle, fq.FQ_F16, 100000) == "encode_full"
     assert fq.fq_encode_kernel(cb.handle, fq.FQ_F32, 100000) == "encode_valu"
     cb.close()
+    for k, N in [(16, 1024), (32, 512)]:
+        cw, rot = fq.load_artifact(k, N, initial=True)
+        cb = fq.Codebook(cw, rot)
+        assert fq.fq_encode_kernel(cb.handle, fq.FQ_F16, 100000) == "encode_full"
+        assert fq.fq_encode_kernel(cb.handle, fq.FQ_F32, 100000) == "encode_valu"
+        cb.close()
     # a forced kernel that does not cover the call leaves the automatic choice
     cw, rot = artifact_or_skip(4, 256)
     cb = _forced(cw, rot, "full")
@@ -148,6 +156,30 @@ def test_streamed_codebook_many_rounds_sampled(dev):
     rng = np.random.default_rng(8)
     idx = np.unique(np.concatenate([rng.choice(n, 600, replace=False), np.arange(16), np.arange(n - 16, n)]))
     g = unpack_sampled(gc, idx, 16, 14)
+    enc = oc.encode(x[idx], rot, cw, np.float16)
+    assert not ((g != enc.codes) & ~enc.near_tie).any()
+    assert oc.accepted(enc.y, cw, enc, g).all()
+    assert np.array_equal(gn[idx].view(np.uint16), enc.norms.view(np.uint16))
+    cb.close()
+
+
+@pytest.mark.parametrize("k,N", [(16, 1024), (32, 512)])
+def test_block_encoder_many_rounds_sampled(dev, k, N):
+    # the rate-axis codebooks of k = 16 and 32 on the matrix core: 100,013 vectors give
+    # every workgroup several rounds; sampled vectors (both ends and random ones) against
+    # the oracle
+    from gpu_util import unpack_sampled
+
+    cw, rot = fq.load_artifact(k, N, initial=True)
+    cb = fq.Codebook(cw, rot)
+    x = workloads.gpt2_small_kv()[: 100_000 + 13]
+    n = len(x)
+    assert fq.fq_encode_kernel(cb.handle, fq.FQ_F16, n) == "encode_full"
+    print(f"[block encoder] k={k} N={N} n={n}", flush=True)
+    gc, gn = gpu_encode(cb, x, dev, np.float16)
+    rng = np.random.default_rng(9 + k)
+    idx = np.unique(np.concatenate([rng.choice(n, 1500, replace=False), np.arange(40), np.arange(n - 40, n)]))
+    g = unpack_sampled(gc, idx, D // k, oc.code_bits(N))
     enc = oc.encode(x[idx], rot, cw, np.float16)
     assert not ((g != enc.codes) & ~enc.near_tie).any()
     assert oc.accepted(enc.y, cw, enc, g).all()

@@ -128,14 +128,15 @@ fq_status upload(T** dst, const T* src, size_t count) {
 }
 
 // Operand layouts of the matrix-core encoder, built once per codebook.
-// Operands of the k = d = 64 encoder: the rotation as 32 x 32 x 16 A operands (three
+// Operands of the k = 16, 32, 64 encoder: the rotation as 32 x 32 x 16 A operands (three
 // fp16 parts of 1024 Pi, rows permuted so that a lane ends up with 32 consecutive
-// coordinates) and the codeword rows in their LDS layout (64 fp16 coordinates, then
-// 256 ||c||^2 as fp16 hi + lo and six zeros).
+// coordinates) and the codeword rows in their LDS layout (k fp16 coordinates, then
+// 256 ||c||^2 as fp16 hi + lo and six zeros), zero-padded to whole chunks of 8 tiles.
 fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const float* rotation) {
-  const int d = cb->d, N = cb->N;
+  const int d = cb->d, k = cb->k, N = cb->N;
   const int tiles = N / 32, chunks = (tiles + 7) / 8;
-  const size_t rec_bytes = (size_t)chunks * 8 * 32 * 144;
+  const int rowb = 2 * k + 16;
+  const size_t rec_bytes = (size_t)chunks * 8 * 32 * rowb;
   _Float16* rt = new (std::nothrow) _Float16[2 * 4 * 3 * 64 * 8];
   uint8_t* rc = new (std::nothrow) uint8_t[rec_bytes]();
   if (!rt || !rc) {
@@ -157,10 +158,10 @@ fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const fl
           for (int p = 0; p < 3; p++) rt[((((r * 4 + s) * 3 + p) * 64) + l) * 8 + j] = parts[p];
         }
   for (int n = 0; n < N; n++) {
-    uint8_t* row = rc + (size_t)n * 144;
+    uint8_t* row = rc + (size_t)n * rowb;
     double c2 = 0.0;
-    for (int t = 0; t < d; t++) {
-      const double v = (double)codewords[(size_t)n * d + t];
+    for (int t = 0; t < k; t++) {
+      const double v = (double)codewords[(size_t)n * k + t];
       const _Float16 hv = (_Float16)v;  // exact: codewords are fp16 values
       memcpy(row + 2 * t, &hv, 2);
       c2 += v * v;
@@ -169,8 +170,8 @@ fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const fl
     const double s2 = 256.0 * c2;
     const _Float16 nh = (_Float16)s2;
     const _Float16 nl = (_Float16)(s2 - (double)nh);
-    memcpy(row + 128, &nh, 2);
-    memcpy(row + 130, &nl, 2);
+    memcpy(row + 2 * k, &nh, 2);
+    memcpy(row + 2 * k + 2, &nl, 2);
   }
   fq_status st = upload(&cb->rot32, rt, (size_t)2 * 4 * 3 * 64 * 8);
   if (st == FQ_OK) st = upload(&cb->frec, rc, rec_bytes);
@@ -216,7 +217,7 @@ fq_status upload_mfma_operands(fq_codebook* cb, const float* codewords, const fl
   delete[] da;
   delete[] pr;
   delete[] pm;
-  if (st == FQ_OK && k == 64 && N % 32 == 0) st = upload_full_operands(cb, codewords, rotation);
+  if (st == FQ_OK && (k == 16 || k == 32 || k == 64) && N % 32 == 0) st = upload_full_operands(cb, codewords, rotation);
   if (st == FQ_OK && k == d) {
     // full-vector code: decoded unit vectors Pi^T c_n, summed in fp64 and rounded once to fp32
     float* tab = new (std::nothrow) float[(size_t)N * d];

@@ -35,11 +35,11 @@ struct fq_codebook {
                     // fp16 parts, as the A operand of mfma_f32_16x16x32_f16; row rho of tile r is
                     // coordinate 16 (rho / 4) + 4 r + rho % 4, k is input 32 s + 8 (lane / 16) + j
   _Float16* crec;   // [N][8]: codeword records, k = 4: c0..c3, hi, lo of 256 ||c||^2, 0, 0; k = 8: c0..c7
-  // Operands of the k = d = 64 matrix-core encoder (N a multiple of 32; else null):
+  // Operands of the k = 16, 32, 64 matrix-core encoder (N a multiple of 32; else null):
   _Float16* rot32;  // [2 row tiles][4 k steps][hi, mid, lo][64 lanes][8]: 1024 Pi as the A operand of
                     // mfma_f32_32x32x16_f16; row 8 a + 4 hh + b of tile r is coordinate 32 hh + 16 r + 4 a + b
-  uint8_t* frec;    // [N / 32 tiles][32 rows][144 bytes], zero-padded to whole chunks of 8 tiles:
-                    // 64 fp16 coordinates, then 256 ||c||^2 as fp16 hi, lo and six zero halves
+  uint8_t* frec;    // [N / 32 tiles][32 rows][2 k + 16 bytes], zero-padded to whole chunks of 8 tiles:
+                    // k fp16 coordinates, then 256 ||c||^2 as fp16 hi, lo and six zero halves
   float* dec_full;  // k = d only: [N][d] Pi^T c_n in fp32 (rounded once from fp64), the decoded unit
                     // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
@@ -74,7 +74,7 @@ hipError_t launch_encode_mfma(const fq_codebook* cb, const void* x, fq_dtype x_d
 bool encode_h16_supported(const fq_codebook* cb);
 hipError_t launch_encode_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
                              fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
-// Matrix-core encoder for k = d = 64 and fp16 input; see encode_full_supported.
+// Matrix-core encoder for k = 16, 32 and d = 64 with fp16 input; see encode_full_supported.
 bool encode_full_supported(const fq_codebook* cb);
 hipError_t launch_encode_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms,
                               fq_dtype norm_dtype, const int64_t* slots, int64_t cap, hipStream_t s);
