@@ -1,6 +1,9 @@
 // FibQuant encoder (FibQuant summary §2.3): norm, rotation, d/k blocks of k
 // consecutive coordinates, nearest codeword per block, fixed-address packing
-// (§1).  One lane owns one vector.
+// (§1).  For k <= 16 a workgroup of 4 waves owns 64 vectors and wave q the
+// coordinates 16 q .. 16 q + 15 of every one (lane = vector), so Pi and the
+// codebook are read with wave-uniform addresses and a lane holds a quarter of
+// a vector's state; for k = 32, 64 one lane owns one vector.
 //
 // Precision plan (the codes must be the exact nearest codewords):
 //   * nu and y = Pi x / nu are computed in fp64 (products of fp32 Pi entries and
@@ -13,6 +16,8 @@
 //     second - best > 2 E_b the fp32 winner is the exact unique minimiser.
 //   * Otherwise the block is searched again in fp64 with the direct distance
 //     sum_t (y_t - c_t)^2, lowest index on exact ties.
+#include <type_traits>
+
 #include "fq_device.h"
 #include "fq_internal.h"
 
@@ -46,6 +51,31 @@ __device__ inline void load_row(const void* __restrict__ xv, int64_t i, float (&
       xf[4 * q + 2] = w.z;
       xf[4 * q + 3] = w.w;
     }
+  }
+}
+
+// Inputs j0 .. j0 + 7 of a row (fp16 or fp32), zeros for a vector past the end.
+template <bool F16>
+using row_t = typename std::conditional<F16, const _Float16*, const float*>::type;
+template <bool F16>
+__device__ inline void load_piece(row_t<F16> row, int j0, bool valid, float (&v)[8]) {
+  if (!valid) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = 0.f;
+    return;
+  }
+  if constexpr (F16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + j0);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      v[2 * h] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[h] & 0xffffu));
+      v[2 * h + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ws[h] >> 16));
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(row + j0), b = *reinterpret_cast<const float4*>(row + j0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
 }
 
@@ -213,6 +243,190 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
   }
 }
 
+// k <= 16: wave q of the workgroup takes coordinates 16 q .. 16 q + 15 (blocks
+// 16 q / k ..) of the workgroup's 64 vectors; records are assembled in LDS by all
+// four waves and stored by the workgroup.
+template <int K, bool XF16, bool NF16>
+__global__ __launch_bounds__(WG) void encode_valu_q(const void* __restrict__ xv, int64_t n,
+                                                    const float* __restrict__ cw, const float* __restrict__ cn2,
+                                                    const double* __restrict__ pi64t, int N, int bits, float cmax,
+                                                    float c2max, uint8_t* __restrict__ codes, void* __restrict__ norms,
+                                                    const int64_t* __restrict__ slots, int64_t cap) {
+  static_assert(K <= 16, "a quarter of a vector holds whole blocks");
+  constexpr int QC = 16;       // coordinates per wave
+  constexpr int NBQ = QC / K;  // blocks per lane
+  constexpr int NB = D / K;
+  __shared__ uint32_t pk[2 * NB * 16];  // 64 records of B = NB bits <= 16 bits each
+
+  const int lane = fq_tid() & 63;
+  const int q = __builtin_amdgcn_readfirstlane(fq_tid() >> 6);
+  const int64_t v0 = (int64_t)fq_bid_x() * 64;
+  const int64_t i = v0 + lane;
+  const bool valid = i < n;
+  const int B = NB * bits;
+
+  // ---- norm and fp64 rotation of this quarter in one pass over the row, 8 inputs at
+  //      a time (a row held whole in registers would cost 64 of them through the search)
+  const double* piq = pi64t + QC * q;  // pi64t[j D + 16 q + t] = Pi[16 q + t][j], wave-uniform
+  // this lane's input row (only read when the vector exists)
+  const row_t<XF16> xrow = reinterpret_cast<row_t<XF16>>(xv) + (valid ? i : 0) * D;
+  double acc[QC];
+#pragma unroll
+  for (int t = 0; t < QC; t++) acc[t] = 0.0;
+  double nu2 = 0.0;
+#pragma unroll 1
+  for (int j0 = 0; j0 < D; j0 += 8) {
+    float xp[8];
+    load_piece<XF16>(xrow, j0, valid, xp);
+#pragma unroll
+    for (int jj = 0; jj < 8; jj++) {
+      const double xj = (double)xp[jj];
+      nu2 = fma(xj, xj, nu2);
+#pragma unroll
+      for (int t = 0; t < QC; t++) acc[t] = fma(piq[(j0 + jj) * D + t], xj, acc[t]);
+    }
+  }
+  const double nu = sqrt(nu2);
+  const double inv = nu > 0.0 ? 1.0 / nu : 0.0;
+  float m2y[QC];  // -2 y in fp32 (exact doubling of the rounded y)
+#pragma unroll
+  for (int t = 0; t < QC; t++) m2y[t] = -2.0f * (float)(acc[t] * inv);
+
+  // ---- fp32 search with best / second-best per block
+  float m1[NBQ], m2[NBQ];
+  int ix[NBQ];
+#pragma unroll
+  for (int b = 0; b < NBQ; b++) {
+    m1[b] = __builtin_huge_valf();
+    m2[b] = __builtin_huge_valf();
+    ix[b] = 0;
+  }
+  for (int nn = 0; nn < N; nn++) {
+    float c[K];
+#pragma unroll
+    for (int t = 0; t < K; t++) c[t] = cw[nn * K + t];
+    const float cn = cn2[nn];
+#pragma unroll
+    for (int b = 0; b < NBQ; b++) {
+      float sc = cn;
+#pragma unroll
+      for (int t = 0; t < K; t++) sc = fmaf(m2y[b * K + t], c[t], sc);
+      m2[b] = __builtin_amdgcn_fmed3f(m1[b], m2[b], sc);
+      const bool lt = sc < m1[b];
+      ix[b] = lt ? nn : ix[b];
+      m1[b] = lt ? sc : m1[b];
+    }
+  }
+
+  // ---- certificate (as in encode_valu)
+  const double u = 5.9604644775390625e-08;  // 2^-24
+  uint32_t unsure = 0;
+#pragma unroll
+  for (int b = 0; b < NBQ; b++) {
+    float yn2 = 0.f;
+#pragma unroll
+    for (int t = 0; t < K; t++) yn2 = fmaf(m2y[b * K + t], m2y[b * K + t], yn2);
+    const double yn = 0.5 * sqrt((double)yn2) * 1.01;  // ||y_b||, rounded up
+    const double E = 1.01 * (K + 2) * u * ((double)c2max + 2.0 * yn * (double)cmax);
+    if (!(((double)m2[b] - (double)m1[b]) > 2.0 * E)) unsure |= 1u << b;
+  }
+  if (!valid) unsure = 0;
+
+  // ---- norm store (fp64 -> storage dtype, one rounding), by the first wave
+  const int64_t slot = valid ? out_slot(slots, cap, i) : -1;
+  if (q == 0 && slot >= 0) {
+    if constexpr (NF16)
+      reinterpret_cast<uint16_t*>(norms)[slot] = f64_to_f16_bits(nu);
+    else
+      reinterpret_cast<float*>(norms)[slot] = (float)nu;
+  }
+
+  // ---- pack the 64 records (64 B bits, dword aligned) through LDS
+  for (int w = fq_tid(); w < 2 * B; w += WG) pk[w] = 0u;
+  __syncthreads();
+  const uint32_t cmask = (1u << bits) - 1u;
+  if (valid) {
+#pragma unroll
+    for (int b = 0; b < NBQ; b++) {
+      const uint32_t code = (uint32_t)ix[b];
+      const int bo = lane * B + (q * NBQ + b) * bits;
+      const int sh = bo & 31;
+      atomicOr(&pk[bo >> 5], code << sh);
+      if (sh + bits > 32) atomicOr(&pk[(bo >> 5) + 1], code >> (32 - sh));
+    }
+  }
+
+  // ---- fp64 direct-distance search of the uncertified blocks (y_b from the input row
+  //      again, 8 inputs at a time); patch their bits
+  while (unsure) {
+    const int b = __builtin_ctz(unsure);
+    unsure &= unsure - 1;
+    double yb[K];
+#pragma unroll
+    for (int t = 0; t < K; t++) yb[t] = 0.0;
+#pragma unroll 1
+    for (int j0 = 0; j0 < D; j0 += 8) {
+      float xp[8];
+      load_piece<XF16>(xrow, j0, true, xp);
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++)
+#pragma unroll
+        for (int t = 0; t < K; t++) yb[t] = fma(piq[(j0 + jj) * D + b * K + t], (double)xp[jj], yb[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < K; t++) yb[t] *= inv;
+    double best = __builtin_huge_val();
+    uint32_t bi = 0;
+    for (int nn = 0; nn < N; nn++) {
+      double dd = 0.0;
+#pragma unroll
+      for (int t = 0; t < K; t++) {
+        const double df = yb[t] - (double)cw[nn * K + t];
+        dd = fma(df, df, dd);
+      }
+      if (dd < best) {
+        best = dd;
+        bi = (uint32_t)nn;
+      }
+    }
+    const int bo = lane * B + (q * NBQ + b) * bits;
+    const int sh = bo & 31;
+    atomicAnd(&pk[bo >> 5], ~(cmask << sh));
+    atomicOr(&pk[bo >> 5], bi << sh);
+    if (sh + bits > 32) {
+      atomicAnd(&pk[(bo >> 5) + 1], ~(cmask >> (32 - sh)));
+      atomicOr(&pk[(bo >> 5) + 1], bi >> (32 - sh));
+    }
+  }
+  __syncthreads();
+  if (v0 >= n) return;
+  const int nv = (n - v0) < 64 ? (int)(n - v0) : 64;
+  if (slots) {
+    if (q == 0) scatter_records(pk, nv, B / 8, slots, cap, v0, codes, lane);
+  } else {
+    const int64_t nbytes = ((int64_t)nv * B + 7) / 8;
+    uint8_t* dst = codes + (v0 / 64) * (int64_t)(8 * B);
+    const int nfull = (int)(nbytes / 4);
+    for (int w = fq_tid(); w < nfull; w += WG) reinterpret_cast<uint32_t*>(dst)[w] = pk[w];
+    const int rem = (int)(nbytes - 4 * (int64_t)nfull);
+    if (fq_tid() < rem) dst[4 * nfull + fq_tid()] = (uint8_t)((pk[nfull] >> (8 * fq_tid())) & 0xffu);
+  }
+}
+
+}  // namespace
+
+namespace {
+template <int K, bool XF, bool NF>
+void launch_valu(const fq_codebook* cb, const void* x, int64_t n, uint8_t* codes, void* norms, const int64_t* slots,
+                 int64_t cap, hipStream_t s) {
+  if constexpr (K <= 16) {  // a workgroup per 64 vectors, a wave per quarter
+    hipLaunchKernelGGL((encode_valu_q<K, XF, NF>), dim3((unsigned)((n + 63) / 64)), dim3(WG), 0, s, x, n, cb->cw,
+                       cb->cn2, cb->pi64t, cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms, slots, cap);
+  } else {  // a lane per vector
+    hipLaunchKernelGGL((encode_valu<K, XF, NF>), dim3((unsigned)((n + WG - 1) / WG)), dim3(WG), 0, s, x, n, cb->cw,
+                       cb->cn2, cb->pi64t, cb->N, cb->bits, cb->cmax, cb->c2max, codes, norms, slots, cap);
+  }
+}
 }  // namespace
 
 // Launcher for one block size; each K is instantiated in its own translation
@@ -220,20 +434,15 @@ __global__ __launch_bounds__(WG) void encode_valu(const void* __restrict__ xv, i
 template <int K>
 hipError_t launch_encode_k(const fq_codebook* cb, const void* x, fq_dtype xd, int64_t n, uint8_t* codes,
                            void* norms, fq_dtype nd, const int64_t* slots, int64_t cap, hipStream_t s) {
-  const dim3 grid((unsigned)((n + WG - 1) / WG)), block(WG);
   const bool xf16 = xd == FQ_F16, nf16 = nd == FQ_F16;
-#define FQ_ENC(XF, NF)                                                                                          \
-  hipLaunchKernelGGL((encode_valu<K, XF, NF>), grid, block, 0, s, x, n, cb->cw, cb->cn2, cb->pi64t, cb->N,     \
-                     cb->bits, cb->cmax, cb->c2max, codes, norms, slots, cap)
   if (xf16 && nf16)
-    FQ_ENC(true, true);
+    launch_valu<K, true, true>(cb, x, n, codes, norms, slots, cap, s);
   else if (xf16)
-    FQ_ENC(true, false);
+    launch_valu<K, true, false>(cb, x, n, codes, norms, slots, cap, s);
   else if (nf16)
-    FQ_ENC(false, true);
+    launch_valu<K, false, true>(cb, x, n, codes, norms, slots, cap, s);
   else
-    FQ_ENC(false, false);
-#undef FQ_ENC
+    launch_valu<K, false, false>(cb, x, n, codes, norms, slots, cap, s);
   return hipGetLastError();
 }
 
