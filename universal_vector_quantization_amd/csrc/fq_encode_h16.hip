@@ -163,7 +163,10 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
   // wave past the last group searches zero inputs and stores nothing
   for (int64_t gb = (int64_t)fq_bid_x() * WAVES; gb < ngroups; gb += (int64_t)nwg * WAVES) {
     const int64_t g = gb + w;
-    if (!ST && g >= ngroups) break;
+    // (a signed 64-bit compare has no scalar form: as one, ngroups would be held, and
+    // spilled, in vector registers)
+    const int64_t left = ngroups - g;
+    if (!ST && ((int)(left >> 32) < 0 || left == 0)) break;
     const int64_t v0 = g * VG;
     const int nv = g < ngroups ? (int)((n - v0) < VG ? (n - v0) : VG) : 0;
 
@@ -176,9 +179,11 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       uint4 xa = make_uint4(0u, 0u, 0u, 0u), xb = xa;
       if (vec < nv) {
         // a uniform group base plus a 32-bit lane offset the compiler cannot carry from
-        // one group to the next (a per-lane 64-bit pointer would live across the search)
-        int off = vec * (D / 8) + q;
-        __asm__ volatile("" : "+v"(off));
+        // one group to the next (a per-lane 64-bit pointer, or the offset itself, would
+        // live across the search)
+        int ln = lane;
+        __asm__ volatile("" : "+v"(ln));
+        const int off = (16 * sg + (ln & 15)) * (D / 8) + (ln >> 4);
         const uint4* xp = reinterpret_cast<const uint4*>(x + v0 * D);
         xa = xp[off];
         xb = xp[off + 4];
@@ -277,6 +282,9 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       tid[tb] = 0;
     }
     // tile t of the codebook; `tiles` tiles of `buf` (LDS, padded unless ST), first tile t0
+    int lh = lane;  // the lane's half for the norm seeds' LDS base, formed per group
+    __asm__ volatile("" : "+v"(lh));
+    lh >>= 5;
     auto search = [&](const uint4* buf, const float* c2b, int tiles, int t0) {
       const int RS = ST ? 32 : 33, CS = ST ? 32 : 36;  // record / norm slots per tile
       half8 A = __builtin_bit_cast(half8, buf[c]);
@@ -287,7 +295,7 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
         if constexpr (K == 8) {
 #pragma unroll
           for (int j = 0; j < 4; j++) {
-            const float4 cv = *reinterpret_cast<const float4*>(c2b + CS * tl + 8 * j + 4 * h);
+            const float4 cv = *reinterpret_cast<const float4*>(c2b + CS * tl + 8 * j + 4 * lh);
             C[4 * j] = cv.x;
             C[4 * j + 1] = cv.y;
             C[4 * j + 2] = cv.z;
@@ -403,8 +411,10 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       }
       const uint32_t cbest = (uint32_t)(32 * t0 + 8 * (ri >> 2) + 4 * hw + (ri & 3));
       const float second = fminf(r2, fminf(m2w, m1l));
-      // block of this column: slot p of lane o = c + 32 h
-      const int o = c + 32 * h;
+      // block of this column: slot p of lane o = c + 32 h (formed per group from an opaque
+      // value: hoisted out of the group loop these constants would be spilled)
+      int o = lane;
+      __asm__ volatile("" : "+v"(o));
       const int vec = K == 4 ? (o & 15) : 16 * (p >> 1) + (o & 15);
       const int bi = K == 4 ? 4 * (o >> 4) + p : 2 * (o >> 4) + (p & 1);
       const float yn = __builtin_sqrtf(vn2) * (1.01f / 512.0f);
