@@ -219,6 +219,35 @@ def test_decode_large_sampled(dev, k, N, n, norm_dtype, out_dtype):
     assert max_rel_rows(got[idx], ref) <= TOL
 
 
+@pytest.mark.parametrize("k,N", [(4, 256), (8, 4096)])
+@pytest.mark.parametrize("n", [32, 32 * 5 + 3, 32 * 3840, 32 * 3841 + 1, 32 * 7681 + 7, 32 * 15355 + 9,
+                               32 * 15360])
+def test_decode_stream_round_counts(dev, k, N, n):
+    # Whole groups go to the producer / consumer decoder in rounds of one group per
+    # consumer wave (15 per workgroup, one workgroup per CU) when that gives at least
+    # four rounds, else to the per-wave ring decoder.  On a 256-CU part: one group, a
+    # partial first round, exactly and just past one round, three rounds with a ragged
+    # tail (ring decoder), four rounds with a partial last one and exactly four full
+    # rounds (producer / consumer); every row checked (sampled beyond 20,000)
+    cb, cw, rot = codebook(k, N)
+    bits = oc.code_bits(N)
+    B = (D // k) * bits
+    store = workloads.random_code_store((n * B + 7) // 8, 80 + n % 97)
+    norms = workloads.random_norms(n, 81 + n % 89, np.float16)
+    print(f"[decode rounds] k={k} N={N} n={n}", flush=True)
+    got = gpu_decode(cb, store, norms, dev, np.float16)
+    if n <= 20000:
+        idx = np.arange(n)
+    else:
+        rng = np.random.default_rng(n)
+        full = (n // 32) * 32
+        idx = np.unique(np.concatenate([rng.choice(n, 4000, replace=False), np.arange(64), np.arange(n - 64, n),
+                                        np.arange(full - 32 * 16, full)]))
+        idx = idx[idx < n]
+    ref = oc.decode(unpack_sampled(store, idx, D // k, bits), norms[idx], rot, cw)
+    assert max_rel_rows(got[idx], ref) <= TOL
+
+
 def test_decode_of_oracle_encode_roundtrip(dev):
     cb, cw, rot = codebook(4, 256)
     x = workloads.gpt2_small_kv()[:8192]
