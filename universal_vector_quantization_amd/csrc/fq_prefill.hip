@@ -353,17 +353,24 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
   float l = l_run;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (!row_ok) return;
-  const int64_t bh = ((int64_t)b * Hq + (int64_t)g * G + hl) * Sq + qi;
+  // the row's indices again, from the lane index the shuffles use (mbcnt): carried
+  // across the loop from the prologue (where the query load forms the same offset)
+  // they were spilled
+  const int ln = __lane_id();
+  const int ecol = ln & 15, ehq = ln >> 4;
+  const int er = rb * PROWS + 16 * w + ecol;
+  if (er >= rows) return;
+  const int ehl = er / Sq, eqi = er - ehl * Sq;
+  const int64_t bh = ((int64_t)b * Hq + (int64_t)g * G + ehl) * Sq + eqi;
   float* rec = ws + (bh * nchunks + chunk) * REC_F;
-  if (hq == 0) {
+  if (ehq == 0) {
     rec[0] = m_run;
     rec[1] = l;
   }
 #pragma unroll
   for (int dt = 0; dt < 4; dt++)
 #pragma unroll
-    for (int i = 0; i < 4; i++) rec[2 + 16 * dt + 4 * hq + i] = O[dt][i];
+    for (int i = 0; i < 4; i++) rec[2 + 16 * dt + 4 * ehq + i] = O[dt][i];
 }
 
 }  // namespace
