@@ -18,9 +18,11 @@
 //     into fp16 hi (lanes 0-31) + lo (lanes 32-63).  For k = 4 the record also
 //     carries 256 ||c||^2 as fp16 hi + lo in K slots the block does not use (B
 //     holds 1 there), so the accumulator starts at 0; for k = 8 it starts at
-//     256 ||c||^2 read from LDS.  A lane keeps the minimum of its 16 rows
-//     (v_min3 chains), the best and second-best such minimum and the best
-//     tile; the next tile's matrix op is issued before this one is reduced.
+//     256 ||c||^2 read from LDS.  A lane takes the minimum of its 16 rows
+//     (v_min3 chains), writes the tile index into its low mantissa bits (one
+//     and-or) and keeps the best and second-best such tagged minimum (so the
+//     best one names its tile); the next tile's matrix op is issued before this
+//     one is reduced.
 //  4. Recovery: per column, the half whose tile minimum won recomputes that
 //     tile's 16 rows in fp32 FMAs from the fp32 256 ||c||^2 (lane c takes
 //     column c of one tile of a pair, lane c + 32 the other tile's); the second
@@ -36,7 +38,11 @@
 //     1 / nu and the product; the mid / lo sums are 2^-11 smaller), which moves
 //     a score by at most 512 |c| sqrt(k) 70 u.  The host folds E into
 //     e_abs + e_rel |y_b| (with 1.02 for the fp32 evaluation here).  If
-//     second - best > 2E the winner is the exact unique minimiser.
+//     second - best > 2E the winner is the exact unique minimiser; "second"
+//     is first lowered by what a tile tag can have moved it (2^(tagbits - 23)
+//     of itself, tagbits = ceil(log2(N / 32))), and a tag that picked another
+//     tile than the true best can only do so within that amount, which the
+//     lowered second then fails.
 //  6. Uncertified blocks are listed in LDS and searched again, one at a time by
 //     the whole wave, in fp64 with the direct distance sum_t (y_t - c_t)^2
 //     (lowest index on exact ties), after an fp32 screen that leaves (nearly
@@ -155,6 +161,11 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
   const int lane = fq_tid() & 63;
   const int c = lane & 31, h = lane >> 5, q = lane >> 4, vl = lane & 15;
   const int NT = N / 32;
+  // tile tags: the low tagbits bits of a tile minimum hold its tile index, which moves the
+  // value by less than 2^(tagbits - 23) of itself (1 % slack)
+  const int tagbits = NT > 1 ? 32 - __builtin_clz((unsigned)(NT - 1)) : 0;
+  const uint32_t tmask = ~((1u << tagbits) - 1u);
+  const float tag_rel = (float)(1u << tagbits) * (1.01f / 8388608.0f);
   // codeword n as 8 halves: in LDS at slot rslot(n), or (ST) in global memory
   const _Float16* cbh = ST ? reinterpret_cast<const _Float16*>(crec) : reinterpret_cast<const _Float16*>(recL);
   auto rec_of = [&](int nn) { return ST ? nn : rslot(nn); };
@@ -272,14 +283,14 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
 #pragma unroll
       for (int d = 0; d < 4; d++) __asm__ volatile("" : "+v"(bq[tb][d]));
 
-    // ---- 3b. matrix-core search with per-lane tile minima
+    // ---- 3b. matrix-core search with per-lane tile minima.  A tile minimum carries its
+    //      tile index in its low tagbits mantissa bits (one and-or instead of a compare and
+    //      a select per tile and column); the certificate allows for the change of value.
     float m1[8], m2[8];
-    int tid[8];
 #pragma unroll
     for (int tb = 0; tb < 8; tb++) {
       m1[tb] = __builtin_huge_valf();
       m2[tb] = __builtin_huge_valf();
-      tid[tb] = 0;
     }
     // tile t of the codebook; `tiles` tiles of `buf` (LDS, padded unless ST), first tile t0
     int lh = lane;  // the lane's half for the norm seeds' LDS base, formed per group
@@ -290,6 +301,10 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       half8 A = __builtin_bit_cast(half8, buf[c]);
       for (int tl = 0; tl < tiles; tl++) {
         const int t = t0 + tl;
+        // the tile index in a vector register (one move per tile): the tag's and-or may
+        // read only one scalar operand, which the mask takes
+        uint32_t tv = (uint32_t)t;
+        __asm__ volatile("" : "+v"(tv));
         const half8 An = __builtin_bit_cast(half8, buf[(tl + 1 < tiles ? RS * (tl + 1) : 0) + c]);
         f32x16 C;
         if constexpr (K == 8) {
@@ -310,9 +325,8 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
         for (int tb = 0; tb < 8; tb++) {
           f32x16 Dn;
           if (tb < 7) Dn = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, __builtin_bit_cast(half8, bq[tb + 1]), C, 0, 0, 0);
-          const float tm = min16(Dc);
+          const float tm = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, min16(Dc)) & tmask) | tv);
           m2[tb] = __builtin_amdgcn_fmed3f(m1[tb], m2[tb], tm);
-          tid[tb] = tm < m1[tb] ? t : tid[tb];
           m1[tb] = fminf(m1[tb], tm);
           if (tb < 7) Dc = Dn;
         }
@@ -357,13 +371,11 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       // statistics of this tile from both halves (the partner sends those of the tile it takes)
       const float mm1 = h == 0 ? m1[2 * p] : m1[2 * p + 1];
       const float mm2 = h == 0 ? m2[2 * p] : m2[2 * p + 1];
-      const int mtid = h == 0 ? tid[2 * p] : tid[2 * p + 1];
       const float pm1 = __shfl_xor(h == 0 ? m1[2 * p + 1] : m1[2 * p], 32);
       const float pm2 = __shfl_xor(h == 0 ? m2[2 * p + 1] : m2[2 * p], 32);
-      const int ptid = __shfl_xor(h == 0 ? tid[2 * p + 1] : tid[2 * p], 32);
       const bool win = (mm1 < pm1) || (mm1 == pm1 && h == 0);
       const int hw = win ? h : 1 - h;       // half (rows 4 hw + ..) holding the tile minimum
-      const int t0 = win ? mtid : ptid;     // its tile
+      const int t0 = (int)(__builtin_bit_cast(uint32_t, win ? mm1 : pm1) & ~tmask);  // its tile (the tag)
       const float m2w = win ? mm2 : pm2;    // its other tiles' minimum
       const float m1l = win ? pm1 : mm1;    // minimum over the other half's rows
       // hi and lo of this column's block: this lane's operand half plus the partner's
@@ -418,7 +430,8 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       const int vec = K == 4 ? (o & 15) : 16 * (p >> 1) + (o & 15);
       const int bi = K == 4 ? 4 * (o >> 4) + p : 2 * (o >> 4) + (p & 1);
       const float yn = __builtin_sqrtf(vn2) * (1.01f / 512.0f);
-      const bool sure = (second - r1) > 2.0f * (e_abs + e_rel * yn);
+      // second may be a tagged tile minimum: the tag moved it by at most tag_rel of itself
+      const bool sure = (second - fabsf(second) * tag_rel - r1) > 2.0f * (e_abs + e_rel * yn);
       const bool mine_ = vec < nv;
       code[p] = (mine_ && sure) ? (cbest | ((uint32_t)(vec * (D / K) + bi) << 16)) : ~0u;
       const uint64_t um = __ballot(mine_ && !sure);
