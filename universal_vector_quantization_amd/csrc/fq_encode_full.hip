@@ -20,8 +20,13 @@
 //     record's norm slots (256 ||c||^2 as fp16 hi + lo) by 1, so the accumulator
 //     starts at 0 and no per-tile LDS reads seed it.
 //  3. Per codeword tile and column tile: KB / 16 + 1 chained matrix ops; the lane
-//     keeps the minimum of its 16 rows, the best, second and third tile minima
-//     (with the tiles of the first two) and the 16 scores of its best tile.
+//     takes the minimum of its 16 rows, writes the tile index into its low
+//     tagbits = ceil(log2(N / 32)) mantissa bits (one and-or), keeps the best,
+//     second and third such tagged minima (so the first two name their tiles)
+//     and the 16 scores of its best tile.  A tag moves a minimum by less than
+//     2^(tagbits - 23) of itself; every test below that reads a tagged minimum
+//     (the runner-up of the certificate, the second and third tiles' distance
+//     from the best) allows for that in the safe direction.
 //  4. Certificate.  The residual r_b = (-512 y - hi) over block b is known exactly,
 //     and leaving it out moves a score by at most |c| |r_b|_2, so every score is
 //     within
@@ -154,6 +159,9 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
   uint32_t* ulist = reinterpret_cast<uint32_t*>(qcnt + 4);
   int* ucnt = reinterpret_cast<int*>(ulist + UMAX * 3);
   const int NT = N / 32;
+  const int tagbits = NT > 1 ? 32 - __builtin_clz((unsigned)(NT - 1)) : 0;
+  const uint32_t tmask = ~((1u << tagbits) - 1u);
+  const float tag_rel = (float)(1u << tagbits) * (1.01f / 8388608.0f);
   const int nch = (NT + CT - 1) / CT;
   double* piL = reinterpret_cast<double*>(qbase + q_bytes<KB>());  // Pi^T: piL[j D + r] = Pi[r][j]
   for (int i = fq_tid(); i < D * D; i += WAVES * 64) piL[i] = pi64t[i];
@@ -293,13 +301,11 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
       if (pb > 0) {  // every wave is past the previous pass's last barrier: buffer 0 is free
         load_chunk<KB>(rec, 0, (NT < CT ? NT : CT) * TILEB, buf0, w, lane);
       }
-      float m1[CBP], m2[CBP], m3[CBP];
-      int tid[CBP], tid2[CBP];
+      float m1[CBP], m2[CBP], m3[CBP];  // tagged tile minima
       f32x16 bestD[CBP];
 #pragma unroll
       for (int j = 0; j < CBP; j++) {
         m1[j] = m2[j] = m3[j] = __builtin_huge_valf();
-        tid[j] = tid2[j] = 0;
 #pragma unroll
         for (int e = 0; e < 16; e++) bestD[j][e] = __builtin_huge_valf();
       }
@@ -319,7 +325,10 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
           for (int s = 0; s < KS; s++) A[s] = *reinterpret_cast<const half8*>(arow + 32 * s + 16 * h);
           // lanes 32-63 read the same finite norm slots against a zero B: no contribution
           const half8 An = *reinterpret_cast<const half8*>(arow + 2 * KB);
-          const int t = ch * CT + tt;
+          // the tile index in a vector register (one move per tile): the tag's and-or may
+          // read only one scalar operand, which the mask takes
+          uint32_t tv = (uint32_t)(ch * CT + tt);
+          __asm__ volatile("" : "+v"(tv));
 #pragma unroll
           for (int j = 0; j < CBP; j++) {
             const int b = pb + j;
@@ -331,12 +340,10 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
             for (int s = 0; s < KS; s++)
               acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s], __builtin_bit_cast(half8, bq[KS * b + s]), acc, 0,
                                                             0, 0);
-            const float tm = min16(acc);
-            const bool c1 = tm < m1[j], c2 = tm < m2[j];
+            const float tm = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, min16(acc)) & tmask) | tv);
+            const bool c1 = tm < m1[j];
             m3[j] = __builtin_amdgcn_fmed3f(m2[j], m3[j], tm);
-            tid2[j] = c1 ? tid[j] : (c2 ? t : tid2[j]);
             m2[j] = __builtin_amdgcn_fmed3f(m1[j], m2[j], tm);
-            tid[j] = c1 ? t : tid[j];
             m1[j] = fminf(m1[j], tm);
 #pragma unroll
             for (int e = 0; e < 16; e++) bestD[j][e] = c1 ? acc[e] : bestD[j][e];
@@ -358,20 +365,24 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
           ri = v < r1 ? e : ri;  // first (lowest row) minimum: rows grow with e
           r1 = fminf(r1, v);
         }
-        ri = 32 * tid[j] + (ri >> 2) * 8 + 4 * h + (ri & 3);
+        const int tid = (int)(__builtin_bit_cast(uint32_t, m1[j]) & ~tmask);
+        const int tid2 = (int)(__builtin_bit_cast(uint32_t, m2[j]) & ~tmask);  // read only when m2 is finite
+        ri = 32 * tid + (ri >> 2) * 8 + 4 * h + (ri & 3);
         const float o1 = __shfl_xor(r1, 32), o2 = __shfl_xor(r2, 32), om = __shfl_xor(m2[j], 32);
         const int oi = __shfl_xor(ri, 32);
         const bool other = (o1 < r1) || (o1 == r1 && oi < ri);
         const float best = other ? o1 : r1;
         const float second = fminf(fminf(fmaxf(r1, o1), fminf(r2, o2)), fminf(m2[j], om));
         code[b] = (uint32_t)(other ? oi : ri);
-        sure[b] = (second - best) > 2.0f * E[b];
+        // second may be a tagged minimum: lowered by what its tag can have added
+        sure[b] = (second - fabsf(second) * tag_rel - best) > 2.0f * E[b];
         // candidate tiles of an uncertified column, per half: the best tile always, the
-        // second if its minimum is within 2E of the best; a third that close sends the
-        // block to the full search
+        // second if its minimum may be within 2E of the best; a third that may be that
+        // close sends the block to the full search (tagged minima lowered by their tags)
         const float lim = best + 2.0f * E[b];
-        cand[b] = (uint32_t)(tid[j] & 0xffff) | ((uint32_t)(m2[j] <= lim ? (tid2[j] & 0x7fff) | 0x8000 : 0) << 16);
-        far3[b] = m3[j] > lim;
+        const bool near2 = m2[j] - fabsf(m2[j]) * tag_rel <= lim;
+        cand[b] = (uint32_t)(tid & 0xffff) | ((uint32_t)(near2 ? (tid2 & 0x7fff) | 0x8000 : 0) << 16);
+        far3[b] = m3[j] - fabsf(m3[j]) * tag_rel > lim;
       }
     }
 
