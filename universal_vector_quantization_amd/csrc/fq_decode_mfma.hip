@@ -505,7 +505,8 @@ __global__ __launch_bounds__(WAVES * 64) void decode_mfma(const uint8_t* __restr
 // rotation left to do.  Eight lanes per vector, 8 output dims each (two 16-byte table
 // loads; one 16-byte fp16 store or two fp32 ones); a workgroup takes FULL_PASSES x 32
 // consecutive vectors per step, every pass's loads issued before its first store, and
-// steps through the input at a stride of nwg steps.
+// steps through the input at a stride of nwg steps (the launch gives every step its own
+// workgroup).
 constexpr int FULL_PASSES = 4;
 constexpr int FULL_VEC_PER_STEP = 32 * FULL_PASSES;
 
@@ -694,12 +695,9 @@ template <bool NF, bool OF>
 hipError_t launch_full(const fq_codebook* cb, const uint8_t* codes, const void* norms, int64_t n, void* out,
                        hipStream_t s) {
   const int64_t nsteps = (n + FULL_VEC_PER_STEP - 1) / FULL_VEC_PER_STEP;
-  int64_t wgs = 0;
-  // 8 resident waves per SIMD's worth of workgroups, each walking several steps
-  hipError_t e = resident_workgroups(reinterpret_cast<const void*>(decode_full<NF, OF>), 256, 0, cb->device, &wgs);
-  if (e != hipSuccess) return e;
-  wgs = nsteps < wgs ? nsteps : wgs;
-  if (wgs < 1) wgs = 1;
+  // one step per workgroup: a wave that walked several steps waited, at each step's code
+  // loads, for its own older stores as well (one completion counter), about 5 % slower
+  const int64_t wgs = nsteps < INT32_MAX ? nsteps : INT32_MAX;
   hipLaunchKernelGGL((decode_full<NF, OF>), dim3((unsigned)wgs), dim3(256), 0, s, codes, norms, n, cb->bits,
                      cb->dec_full, out, nsteps, (int)wgs);
   return hipGetLastError();
