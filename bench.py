@@ -181,11 +181,6 @@ def timed_evicted(fn, stream, flush, reps: int, warm: int = 2):
     return float(np.median(ts)) / 1e3
 
 
-# decoder kernel whose HBM bytes per launch (rocprofv3 counters) each workload reports
-DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_stream_k4", "tinyllama_kv": "decode_stream_k8",
-                       "fullvec_kv": "decode_full_k64"}
-
-
 def workload_timings(fq, workloads, dev, stream, flush, reps: int = 5):
     """Encode and decode time of the other codec workloads at full size (event-timed
     medians of ``reps`` launches, each after an eviction of L2 and the last-level
@@ -217,7 +212,7 @@ def workload_timings(fq, workloads, dev, stream, flush, reps: int = 5):
 
 
 # decoder kernel whose HBM bytes per launch (rocprofv3 counters) each workload reports
-DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_stream_k4", "tinyllama_kv": "decode_stream_k8",
+DECODE_TRAFFIC_KEYS = {"gpt2s_kv": "decode_ring_k4", "tinyllama_kv": "decode_stream_k8",
                        "fullvec_kv": "decode_full_k64"}
 ENCODE_TRAFFIC_KEYS = {"gpt2s_kv": ("encode_h16_k4", "fq_encode_h16.hip"),
                        "tinyllama_kv": ("encode_h16_k8", "fq_encode_h16.hip"),
