@@ -396,13 +396,15 @@ def test_encode_kernels_agree_on_full_gpt2s(dev):
     cbv.close()
 
 
-@pytest.mark.parametrize("out_dtype", [np.float16, np.float32])
-def test_decode_cached_codebook_path_parity(dev, out_dtype):
-    # FQ_DECODE_KERNEL=cached at load time: the k = 8, N = 4096 stream decoder reads its
-    # 64 KiB codebook from L1 / L2, the path taken where LDS per workgroup is smaller.
+@pytest.mark.parametrize("out_dtype,n", [(np.float16, 100_000 + 7), (np.float32, 100_000 + 7),
+                                         (np.float16, 600_000 + 9)])
+def test_decode_cached_codebook_path_parity(dev, out_dtype, n):
+    # FQ_DECODE_KERNEL=cached at load time: the k = 8, N = 4096 stream decoders read their
+    # 64 KiB codebook from L1 / L2, the path taken where LDS per workgroup is smaller
+    # (100,007 vectors: the per-wave ring decoder; 600,009: the producer / consumer one)
     import os
 
-    k, N, n = 8, 4096, 100_000 + 7
+    k, N = 8, 4096
     cw, rot = artifact_or_skip(k, N)
     os.environ["FQ_DECODE_KERNEL"] = "cached"
     try:
