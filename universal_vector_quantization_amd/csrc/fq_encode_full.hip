@@ -345,8 +345,13 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
             m3[j] = __builtin_amdgcn_fmed3f(m2[j], m3[j], tm);
             m2[j] = __builtin_amdgcn_fmed3f(m1[j], m2[j], tm);
             m1[j] = fminf(m1[j], tm);
+            // k = d (128 tiles and more): after the first tiles most tiles improve no lane, so
+            // the copy is skipped wave-wide when none does (the smaller codebooks of k = 16 / 32
+            // improve some lane at nearly every tile: there the test only costs)
+            if (KB != 64 || __ballot(c1)) {
 #pragma unroll
-            for (int e = 0; e < 16; e++) bestD[j][e] = c1 ? acc[e] : bestD[j][e];
+              for (int e = 0; e < 16; e++) bestD[j][e] = c1 ? acc[e] : bestD[j][e];
+            }
           }
         }
         __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
