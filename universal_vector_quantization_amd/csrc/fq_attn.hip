@@ -789,6 +789,21 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   };
   // one steady-state iteration: unit h + 1 is full; its scores (into Lnxt) overlap unit h's PV
   auto step = [&](int h, const float (&Lcur)[2][4], float (&Lnxt)[2][4]) {
+    // Waves of different workgroups share a SIMD, and its arbiter favours the oldest:
+    // the last workgroups dispatched to a CU lagged by up to 8 us over their loop
+    // (per-workgroup timestamps) and finished alone at low occupancy.  A wave lowers its
+    // own priority as it gets through its units, so laggards catch up.
+    {
+      const int lvl = (4 * h) / nu;
+      if (lvl == 0)
+        __builtin_amdgcn_s_setprio(3);
+      else if (lvl == 1)
+        __builtin_amdgcn_s_setprio(2);
+      else if (lvl == 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     if (h + 3 < nu) {
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): reads of unit h - 1's buffer are done
       load_unit(h + 3);
@@ -844,6 +859,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       attn_pv<true>(buf(h), cbL, col, grp, own_tok, ntl, Lc, m_run, l_run, O);
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- merge the waves: rows 4 grp + i (grp < 2) plus their lo rows (lane + 32)
   float l = l_run;  // lanes col and col ^ 8 summed different tokens of the same head
   l += swap8(l);

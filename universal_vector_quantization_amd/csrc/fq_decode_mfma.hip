@@ -189,6 +189,7 @@ __global__ __launch_bounds__(WV * 64) void decode_ring(const uint8_t* __restrict
   int64_t g = (int64_t)fq_bid_x() * WV + w;
   if (g >= ngroups) return;
   int64_t left = (ngroups - 1 - g) / step + 1;  // groups of this wave
+  const int64_t total = left;
 
   auto issue = [&](int sl, int64_t gg) {
     gg = gg < ngroups ? gg : ngroups - 1;
@@ -222,6 +223,19 @@ __global__ __launch_bounds__(WV * 64) void decode_ring(const uint8_t* __restrict
   constexpr int L = S::LOADS, T = S::STORES;
   static_assert(PF == 4, "one wait case per prologue slot");
   for (int i = 0;; i++) {
+    // progress-based priority: the SIMD's arbiter favours the oldest waves, which left the
+    // youngest to finish alone; a wave lowers its priority as it gets through its groups
+    {
+      const int lvl = (int)((4 * (int64_t)i) / total);
+      if (lvl == 0)
+        __builtin_amdgcn_s_setprio(3);
+      else if (lvl == 1)
+        __builtin_amdgcn_s_setprio(2);
+      else if (lvl == 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     switch (i < PF ? i : PF) {
       case 0: wait_vmcnt<(PF - 1) * L>(); break;
       case 1: wait_vmcnt<(PF - 1) * L + T>(); break;

@@ -172,8 +172,24 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
 
   // ST: rounds are uniform across the workgroup (every wave meets every barrier); a
   // wave past the last group searches zero inputs and stores nothing
-  for (int64_t gb = (int64_t)fq_bid_x() * WAVES; gb < ngroups; gb += (int64_t)nwg * WAVES) {
+  // Progress-based wave priority: a SIMD's arbiter favours its oldest waves, so without
+  // this the youngest waves of the persistent grid lagged and finished their last groups
+  // alone at low occupancy; a wave lowers its priority as it gets through its groups.
+  const int64_t gstep = (int64_t)nwg * WAVES, gfirst = (int64_t)fq_bid_x() * WAVES;
+  const int64_t gtotal = gfirst < ngroups ? (ngroups - gfirst + gstep - 1) / gstep : 1;
+  for (int64_t gb = gfirst; gb < ngroups; gb += gstep) {
     const int64_t g = gb + w;
+    {
+      const int lvl = (int)((4 * ((gb - gfirst) / gstep)) / gtotal);
+      if (lvl == 0)
+        __builtin_amdgcn_s_setprio(3);
+      else if (lvl == 1)
+        __builtin_amdgcn_s_setprio(2);
+      else if (lvl == 2)
+        __builtin_amdgcn_s_setprio(1);
+      else
+        __builtin_amdgcn_s_setprio(0);
+    }
     // (a signed 64-bit compare has no scalar form: as one, ngroups would be held, and
     // spilled, in vector registers)
     const int64_t left = ngroups - g;
