@@ -630,14 +630,18 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
           return launch_one<K, NF, OF, RW, false, false>(cb, codes, norms, n, out, s);
       }
       hipError_t e = hipSuccess;
-      if (lds > 65536)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-      if (e != hipSuccess) return e;
-      int64_t wgs = 0;
-      e = persistent_grid(cb, kern, S::THREADS, lds, (ngroups + C - 1) / C, &wgs);
-      if (e != hipSuccess) return e;
-      const int64_t rounds = (ngroups + wgs * C - 1) / (wgs * C);
+      int64_t wgs = 0, rounds = 0;
+      // (a device with less LDS per workgroup than the consumers' staging tiles need runs
+      // the per-wave ring decoder)
+      if (lds <= cb->max_lds) {
+        if (lds > 65536)
+          e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        if (e != hipSuccess) return e;
+        e = persistent_grid(cb, kern, S::THREADS, lds, (ngroups + C - 1) / C, &wgs);
+        if (e != hipSuccess) return e;
+        rounds = (ngroups + wgs * C - 1) / (wgs * C);
+      }
       if (rounds >= MIN_ROUNDS) {
         if (rounds > INT32_MAX) return hipErrorInvalidValue;
         hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(S::THREADS), lds, s, codes, norms, ngroups, cb->cw16,
