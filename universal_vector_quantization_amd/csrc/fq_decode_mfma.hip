@@ -31,11 +31,11 @@ namespace {
 constexpr int D = kD;
 constexpr int WAVES = 4;
 constexpr int LDS_CB_HALFS = 16384;  // codebooks up to N*k = 16384 (32 KiB) live in LDS
-// The stream decoder also holds codebooks of up to 64 KiB (k = 8, N = 4096) in LDS, in
-// one workgroup per CU of 12 waves for fp16 output or 8 for fp32 output (136 / 146 KiB
-// of LDS with the waves' rings and staging tiles): gathered from L1 / L2 instead,
-// every 16-byte codeword read fills a whole cache line, and that path ran at a third
-// of the write bandwidth.
+// The stream decoders also hold codebooks of up to 64 KiB (k = 8, N = 4096) in LDS, in
+// one workgroup per CU (the producer / consumer decoder: 15 consumers for fp16 output,
+// 8 for fp32, 156 / 151 KiB with the ring and staging tiles; the per-wave ring decoder:
+// 12 or 8 waves, 136 / 146 KiB): gathered from L1 / L2 instead, every 16-byte codeword
+// read fills a whole cache line, and that path ran at a third of the write bandwidth.
 constexpr int LDS_CB_HALFS_BIG = 32768;
 constexpr int LDS_MAX_BYTES = 160 * 1024;
 constexpr int RING = 4;  // rounds in the LDS ring: one read by the consumers, up to three loading
