@@ -27,7 +27,9 @@
 //     tile's 16 rows in fp32 FMAs from the fp32 256 ||c||^2 (lane c takes
 //     column c of one tile of a pair, lane c + 32 the other tile's); the second
 //     best is the least of the recomputed runner-up, the winning half's other
-//     tiles and the other half's minimum.
+//     tiles and the other half's minimum.  The recomputed scores carry their row
+//     in the low 4 mantissa bits (one and-or per row instead of a compare and a
+//     select), so the best one names its row.
 //  5. Certificate: every computed score is within
 //        E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 35840 sqrt(k) cmax u
 //                  + 2^-25 (1 + sqrt(k) cmax)),   u = 2^-24,
@@ -39,10 +41,11 @@
 //     a score by at most 512 |c| sqrt(k) 70 u.  The host folds E into
 //     e_abs + e_rel |y_b| (with 1.02 for the fp32 evaluation here).  If
 //     second - best > 2E the winner is the exact unique minimiser; "second"
-//     is first lowered by what a tile tag can have moved it (2^(tagbits - 23)
-//     of itself, tagbits = ceil(log2(N / 32))), and a tag that picked another
-//     tile than the true best can only do so within that amount, which the
-//     lowered second then fails.
+//     is first lowered and "best" raised by what a tag can have moved them
+//     (2^(tagbits - 23) of itself for a tile tag, tagbits = ceil(log2(N / 32)),
+//     2^-19 for a row tag), and a tag that picked another tile or row than the
+//     true best can only do so within that amount, which the adjusted test then
+//     fails.
 //  6. Uncertified blocks are listed in LDS and searched again, one at a time by
 //     the whole wave, in fp64 with the direct distance sum_t (y_t - c_t)^2
 //     (lowest index on exact ties), after an fp32 screen that leaves (nearly
@@ -166,6 +169,8 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
   const int tagbits = NT > 1 ? 32 - __builtin_clz((unsigned)(NT - 1)) : 0;
   const uint32_t tmask = ~((1u << tagbits) - 1u);
   const float tag_rel = (float)(1u << tagbits) * (1.01f / 8388608.0f);
+  const float row_rel = 16.0f * (1.01f / 8388608.0f);  // the recovery's row tags (4 bits)
+  const float sec_rel = tag_rel > row_rel ? tag_rel : row_rel;
   // codeword n as 8 halves: in LDS at slot rslot(n), or (ST) in global memory
   const _Float16* cbh = ST ? reinterpret_cast<const _Float16*>(crec) : reinterpret_cast<const _Float16*>(recL);
   auto rec_of = [&](int nn) { return ST ? nn : rslot(nn); };
@@ -414,8 +419,9 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       float vn2 = 0.f;
 #pragma unroll
       for (int i = 0; i < K; i++) vn2 = fmaf(vp[i], vp[i], vn2);
+      // best and second row scores, each tagged with its row (4 qq + e) in the low 4
+      // mantissa bits (one and-or instead of a compare and a select per row)
       float r1 = __builtin_huge_valf(), r2 = __builtin_huge_valf();
-      int ri = 0;
 #pragma unroll
       for (int qq = 0; qq < 4; qq++) {
         const int n0 = 32 * t0 + 8 * qq + 4 * hw;  // rows n0 .. n0 + 3 of the winning half
@@ -432,11 +438,12 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
             sc = fmaf(h_lo(ww[i / 2]), vp[i], sc);
             sc = fmaf(h_hi(ww[i / 2]), vp[i + 1], sc);
           }
-          r2 = __builtin_amdgcn_fmed3f(r1, r2, sc);
-          ri = sc < r1 ? (4 * qq + e) : ri;  // row 8 qq + 4 hw + e of the tile
-          r1 = fminf(r1, sc);
+          const float st = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) & ~15u) | (uint32_t)(4 * qq + e));
+          r2 = __builtin_amdgcn_fmed3f(r1, r2, st);
+          r1 = fminf(r1, st);
         }
       }
+      const int ri = (int)(__builtin_bit_cast(uint32_t, r1) & 15u);  // row 8 (ri / 4) + 4 hw + ri % 4
       const uint32_t cbest = (uint32_t)(32 * t0 + 8 * (ri >> 2) + 4 * hw + (ri & 3));
       const float second = fminf(r2, fminf(m2w, m1l));
       // block of this column: slot p of lane o = c + 32 h (formed per group from an opaque
@@ -446,8 +453,9 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       const int vec = K == 4 ? (o & 15) : 16 * (p >> 1) + (o & 15);
       const int bi = K == 4 ? 4 * (o >> 4) + p : 2 * (o >> 4) + (p & 1);
       const float yn = __builtin_sqrtf(vn2) * (1.01f / 512.0f);
-      // second may be a tagged tile minimum: the tag moved it by at most tag_rel of itself
-      const bool sure = (second - fabsf(second) * tag_rel - r1) > 2.0f * (e_abs + e_rel * yn);
+      // second is a tagged tile minimum or row score and r1 a tagged row score: a tag moved
+      // each by at most sec_rel (row tags: 2^-19) of itself
+      const bool sure = (second - fabsf(second) * sec_rel - (r1 + fabsf(r1) * row_rel)) > 2.0f * (e_abs + e_rel * yn);
       const bool mine_ = vec < nv;
       code[p] = (mine_ && sure) ? (cbest | ((uint32_t)(vec * (D / K) + bi) << 16)) : ~0u;
       const uint64_t um = __ballot(mine_ && !sure);
