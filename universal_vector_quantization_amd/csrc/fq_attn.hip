@@ -414,8 +414,10 @@ __global__ __launch_bounds__(64) void attn_combine(const float* __restrict__ ws,
 // attn_split:
 //   * Query hi and lo parts sit in different MFMA columns (heads in 0..7, their
 //     lo parts in 8..15) of QK; partner lanes (col, col ^ 8) hold the two parts
-//     of different 16-token tiles and recombine them with one DPP add, so every
-//     score and every exponential is computed once.
+//     of both 16-token tiles: one add with the partner's value as a DPP operand
+//     per tile and a select give each lane whole scores of its own tile, so every
+//     score and every exponential is computed once.  Scores are kept relative to
+//     the running softmax offset, which rides in the norm product's FMA.
 //   * PV puts P' hi in rows 0..7 and lo in rows 8..15 (summed once at the end)
 //     and reads the value operand transposed straight from the LDS codebook
 //     with ds_read_tr16_b64: lane 4a + b of a 16-lane group receives element b
@@ -445,14 +447,25 @@ typedef short short4_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_ lds_s4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t c0, uint32_t c1) {
-  const half4 a = *reinterpret_cast<const half4*>(cbL + c0 * 4);
-  const half4 b = *reinterpret_cast<const half4*>(cbL + c1 * 4);
+// two codewords at LDS byte offsets o0, o1 (8 bytes each) as one operand
+__device__ inline half8 gather2(const _Float16* __restrict__ cbL, uint32_t o0, uint32_t o1) {
+  const half4 a = *reinterpret_cast<const half4*>(reinterpret_cast<const char*>(cbL) + o0);
+  const half4 b = *reinterpret_cast<const half4*>(reinterpret_cast<const char*>(cbL) + o1);
   return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 __device__ inline _Float16 hlo(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ inline _Float16 hhi(uint32_t w) { return __builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+// LDS byte offset of the codeword whose code is byte 0 of a record dword: one shift with
+// a byte operand select, as the code generator forms for bytes 1 to 3 by itself (for byte
+// 0 it emits a shift and a mask)
+__device__ inline uint32_t off_byte0(uint32_t w) {
+  uint32_t r;
+  __asm__("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+          : "=v"(r)
+          : "v"(3u), "v"(w));
+  return r;
+}
 
 // A value that is the same in every lane, declared so (scalar registers).
 __device__ inline int64_t uniform64(int64_t v) {
@@ -502,12 +515,13 @@ __device__ inline void attn_unit_load(const uint8_t* __restrict__ kc, const uint
 //   part, rows 4 grp + i.  After the recombination the lane holds whole scores
 //   of head col & 7 for tokens tb + own_tok + i (own_tok = 16 ah + 4 grp, ah =
 //   0 in lanes col < 8 and 1 in lanes col >= 8).
-// Returns the maximum of the lane's own 8 scores; MASK: tokens at or past nt
-// score -inf.
+// L = score - mref, the lane's head's current softmax offset folded into the norm
+// product (one rounding).  Returns the maximum of the lane's own 8 values; MASK:
+// tokens at or past nt give -inf.
 template <bool MASK>
 __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16* __restrict__ cbL,
                                     const half8 (&qb)[2], int nt, int col, int grp, bool hi_col, int own_tok,
-                                    float (&L)[2][4]) {
+                                    float mref, float (&L)[2][4]) {
   const float NEG = -__builtin_huge_valf();
 #pragma unroll
   for (int u = 0; u < 2; u++) {
@@ -516,8 +530,8 @@ __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16
 #pragma unroll
     for (int a = 0; a < 2; a++) {
       const uint32_t w = reinterpret_cast<const uint32_t*>(cur + U_KC + (tb + 16 * a + col) * 16)[grp];
-      const half8 k0 = gather2(cbL, w & 0xffu, (w >> 8) & 0xffu);
-      const half8 k1 = gather2(cbL, (w >> 16) & 0xffu, w >> 24);
+      const half8 k0 = gather2(cbL, off_byte0(w), ((w >> 8) & 0xffu) * 8u);
+      const half8 k1 = gather2(cbL, ((w >> 16) & 0xffu) * 8u, (w >> 24) * 8u);
       S[a] = mfma16(k0, qb[0], f32x4{0.f, 0.f, 0.f, 0.f});
       S[a] = mfma16(k1, qb[1], S[a]);
     }
@@ -525,13 +539,16 @@ __device__ inline float attn_scores(const char* __restrict__ cur, const _Float16
     const _Float16 kv[4] = {hlo(nw.x), hhi(nw.x), hlo(nw.y), hhi(nw.y)};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      // own part: tile 0 in hi lanes, tile 1 in lo lanes; the partner lane (col ^ 8)
-      // sends the other part of the same score
-      const float mine = hi_col ? S[0][i] : S[1][i];
-      const float send = hi_col ? S[1][i] : S[0][i];
-      const float st = mine + swap8(send);
-      L[u][i] = __builtin_fmaf(st, (float)kv[i], 0.0f);
+      // lanes col and col ^ 8 hold the hi and lo parts of both tiles' scores: each sum
+      // is one add with the partner's value as a DPP operand; hi lanes keep tile 0's
+      const float s0 = S[0][i] + swap8(S[0][i]);
+      const float s1 = S[1][i] + swap8(S[1][i]);
+      const float st = hi_col ? s0 : s1;
+      L[u][i] = __builtin_fmaf(st, (float)kv[i], -mref);
       if constexpr (MASK) L[u][i] = (tb + own_tok + i) < nt ? L[u][i] : NEG;
+      // formed here: sunk past the offset branch that follows, the sums would leave the
+      // partner moves behind and lose their fused form
+      __asm__ volatile("" : "+v"(L[u][i]));
     }
   }
   return fmaxf(fmaxf(fmaxf(L[0][0], L[0][1]), fmaxf(L[0][2], L[0][3])),
@@ -545,7 +562,8 @@ __device__ inline float head_max(float v) {
   return fmaxf(v, __shfl_xor(v, 32));
 }
 
-// Stage B of one unit: p = 2^(L - m), l += p, P' = p nu_v split hi + lo and
+// Stage B of one unit: p = 2^L (L is already relative to the offset), l += p,
+// P' = p nu_v split hi + lo and
 // exchanged with the partner lane, O += V^T P'.  Masked tokens have p = 0; with
 // MASK their value weight is set to 0 outright (their norm may be any bits).  Value operand dt,
 // lane c = 4 a' + b: the lane addresses token tb + 16 a + 4 grp + c / 4 and the
@@ -554,7 +572,8 @@ __device__ inline float head_max(float v) {
 // accumulator dt is dimension 16 (c / 4) + 4 dt + c % 4.
 template <bool MASK>
 __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __restrict__ cbL, int col, int grp,
-                               int own_tok, int nt, const float (&L)[2][4], float m, float& l_run, f32x4 (&O)[4]) {
+                               int own_tok, int nt, const float (&L)[2][4], float one, float& l_run,
+                               f32x4 (&O)[4]) {
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const int tb = 32 * u;
@@ -563,18 +582,20 @@ __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __r
     float pv[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const float p = __builtin_amdgcn_exp2f(L[u][i] - m);
+      const float p = __builtin_amdgcn_exp2f(L[u][i]);
       l_run += p;
       pv[i] = __builtin_fmaf(p, (float)vv[i], 0.0f);
       if constexpr (MASK) pv[i] = (tb + own_tok + i) < nt ? pv[i] : 0.f;
     }
-    // hi rounds toward zero (any rounding works: lo takes the exact remainder)
+    // hi rounds toward zero (any rounding works: lo takes the exact remainder, formed by
+    // one mixed-precision FMA from the packed hi half; `one` is 1.0 in a register the
+    // compiler cannot see through, or it would turn the FMA into a convert and a subtract)
     uint32_t hw[2], lw[2];
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       hw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2 * e], pv[2 * e + 1]));
-      const float ra = __builtin_fmaf((float)hlo(hw[e]), -1.0f, pv[2 * e]);
-      const float rb = __builtin_fmaf((float)hhi(hw[e]), -1.0f, pv[2 * e + 1]);
+      const float ra = __builtin_fmaf(-(float)hlo(hw[e]), one, pv[2 * e]);
+      const float rb = __builtin_fmaf(-(float)hhi(hw[e]), one, pv[2 * e + 1]);
       lw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ra, rb));
     }
     // rows < 8 (hi lanes): hi parts of tile 0 (own) and tile 1 (from lane col + 8);
@@ -589,7 +610,8 @@ __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __r
           reinterpret_cast<const uint32_t*>(cur + U_VC + (tb + 16 * a + 4 * grp + (col >> 2)) * 16)[col & 3];
 #pragma unroll
       for (int dt = 0; dt < 4; dt++)
-        vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(cbL + ((w >> (8 * dt)) & 0xffu) * 4));
+        vt[a][dt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(reinterpret_cast<const char*>(cbL) + (dt == 0 ? off_byte0(w) : ((w >> (8 * dt)) & 0xffu) * 8u)));
     }
 #pragma unroll
     for (int dt = 0; dt < 4; dt++) {
@@ -598,16 +620,6 @@ __device__ inline void attn_pv(const char* __restrict__ cur, const _Float16* __r
       O[dt] = mfma16(P, V, O[dt]);
     }
   }
-}
-
-// Offset update to m_new = max(m_old, mx): the factor for the lane's own sum and
-// the factors for the accumulator rows 4 grp + i (head 4 (grp & 1) + i).
-__device__ inline void attn_rescale_factors(float m_old, float mx, int grp, float& m_new, float& a_own,
-                                            float (&a_row)[4]) {
-  m_new = fmaxf(m_old, mx);
-  a_own = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 while m_old is -inf
-#pragma unroll
-  for (int i = 0; i < 4; i++) a_row[i] = __shfl(a_own, 4 * (grp & 1) + i);
 }
 
 __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restrict__ q,
@@ -743,20 +755,40 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   // rescales its accumulators only when some head's scores rise by more than TAU
   // (after the first unit, rarely).  The decision is wave-uniform (one ballot); the
   // cross-lane maximum is formed only then.
+  // Scores are kept relative to the offset (L = score - m_run): the subtraction rides in
+  // the norm product, and a unit whose scores arrive before an offset move is shifted
+  // once, in the rare moving path.  The first unit sets m_run.
   constexpr float TAU = 4.0f;
-  float m_run = -__builtin_huge_valf(), l_run = 0.f;
+  float m_run = 0.f, l_run = 0.f;
+  // 1.0 in a scalar register the compiler cannot fold (the P' remainder's FMA)
+  float one = 1.0f;
+  __asm__ volatile("" : "+s"(one));
   f32x4 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto buf = [&](int h) -> const char* { return mybuf + (h & (NBUF - 1)) * U_BYTES; };
-  // pipeline state: scores Lc of unit h, the offset m_run, and (when pend) the factors
+  // pipeline state: scores Lc of unit h relative to m_run, and (when pend) the factors
   // that move O and l_run from the previous offset to m_run
   float Lc[2][4], a_own = 0.f, a_row[4] = {0.f, 0.f, 0.f, 0.f};
   bool pend = false;
-  // offset update after a unit whose lanes' own maxima are lmx
-  auto update_offset = [&](float lmx) {
-    pend = __builtin_amdgcn_ballot_w64(lmx > m_run) != 0;
-    if (pend) attn_rescale_factors(m_run, head_max(lmx) + TAU, grp, m_run, a_own, a_row);
+  // offset update after a unit (not the first) whose scores Lu, relative to m_run, have
+  // lane maxima lmx: when some score exceeds the offset, every head's offset moves to TAU
+  // above its maximum if that is higher (dm >= 0) and Lu is shifted to the new offset;
+  // the factors for the lane's own sum and for the accumulator rows 4 grp + i (head
+  // 4 (grp & 1) + i) are 2^-dm
+  auto update_offset = [&](float lmx, float (&Lu)[2][4]) {
+    pend = __builtin_amdgcn_ballot_w64(lmx > 0.f) != 0;
+    if (pend) {
+      const float dm = fmaxf(head_max(lmx) + TAU, 0.f);
+      a_own = __builtin_amdgcn_exp2f(-dm);
+#pragma unroll
+      for (int i = 0; i < 4; i++) a_row[i] = __shfl(a_own, 4 * (grp & 1) + i);
+      m_run += dm;
+#pragma unroll
+      for (int u = 0; u < 2; u++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) Lu[u][i] -= dm;
+    }
   };
   if (nu > 0) {
     if (pre == 3)
@@ -765,10 +797,17 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       __builtin_amdgcn_s_waitcnt(0x3f73);  // vmcnt(3)
     else
       __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
-    const float mx = unit_nt(0) == UT ? attn_scores<false>(buf(0), cbL, qb, UT, col, grp, hi_col, own_tok, Lc)
-                                      : attn_scores<true>(buf(0), cbL, qb, unit_nt(0), col, grp, hi_col, own_tok, Lc);
-    update_offset(mx);
+    // the first unit sets the offset (scores relative to 0 until then)
+    const float mx = unit_nt(0) == UT
+                         ? attn_scores<false>(buf(0), cbL, qb, UT, col, grp, hi_col, own_tok, 0.f, Lc)
+                         : attn_scores<true>(buf(0), cbL, qb, unit_nt(0), col, grp, hi_col, own_tok, 0.f, Lc);
+    m_run = head_max(mx) + TAU;
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) Lc[u][i] -= m_run;
   }
+  // the pending offset move, applied to what is accumulated before the next PV
   auto apply_factors = [&]() {
     if (pend) {
       l_run *= a_own;
@@ -779,11 +818,11 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     }
   };
   // B(h) from scores Lcur at the current offset, then the offset update for unit h + 1
-  // (lane maxima mxn)
-  auto finish_unit = [&](int h, float mxn, const float (&Lcur)[2][4]) {
+  // (scores Lnxt, lane maxima mxn)
+  auto finish_unit = [&](int h, float mxn, const float (&Lcur)[2][4], float (&Lnxt)[2][4]) {
     apply_factors();
-    attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lcur, m_run, l_run, O);
-    update_offset(mxn);
+    attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lcur, one, l_run, O);
+    update_offset(mxn, Lnxt);
   };
   // one steady-state iteration: unit h + 1 is full; its scores (into Lnxt) overlap unit h's PV
   auto step = [&](int h, const float (&Lcur)[2][4], float (&Lnxt)[2][4]) {
@@ -811,8 +850,8 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     } else {
       __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     }
-    const float mxn = attn_scores<false>(buf(h + 1), cbL, qb, UT, col, grp, hi_col, own_tok, Lnxt);
-    finish_unit(h, mxn, Lcur);
+    const float mxn = attn_scores<false>(buf(h + 1), cbL, qb, UT, col, grp, hi_col, own_tok, m_run, Lnxt);
+    finish_unit(h, mxn, Lcur, Lnxt);
   };
   auto steady = [&](int h) { return h + 1 < nu && unit_nt(h + 1) == UT; };
   int h = 0;
@@ -840,8 +879,8 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   if (h + 1 < nu) {  // unit h + 1 is the wave's last unit and is partial; all its loads were issued
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0)
     float Ln[2][4];
-    const float mxn = attn_scores<true>(buf(h + 1), cbL, qb, unit_nt(h + 1), col, grp, hi_col, own_tok, Ln);
-    finish_unit(h, mxn, Lc);
+    const float mxn = attn_scores<true>(buf(h + 1), cbL, qb, unit_nt(h + 1), col, grp, hi_col, own_tok, m_run, Ln);
+    finish_unit(h, mxn, Lc, Ln);
 #pragma unroll
     for (int u = 0; u < 2; u++)
 #pragma unroll
@@ -852,9 +891,9 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
     apply_factors();
     const int ntl = unit_nt(h);
     if (ntl == UT)
-      attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lc, m_run, l_run, O);
+      attn_pv<false>(buf(h), cbL, col, grp, own_tok, UT, Lc, one, l_run, O);
     else
-      attn_pv<true>(buf(h), cbL, col, grp, own_tok, ntl, Lc, m_run, l_run, O);
+      attn_pv<true>(buf(h), cbL, col, grp, own_tok, ntl, Lc, one, l_run, O);
   }
 
   __builtin_amdgcn_s_setprio(0);
@@ -873,7 +912,7 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
       if (grp < 2) so[(w * GF + 4 * grp + i) * D + 16 * (col >> 2) + 4 * dt + (col & 3)] = v;
     }
   if (grp == 0 && col < GF) {
-    sm[w * GF + col] = m_run;
+    sm[w * GF + col] = nu > 0 ? m_run : -__builtin_huge_valf();  // a wave without keys: empty
     sl[w * GF + col] = l;
   }
   __syncthreads();
