@@ -136,8 +136,8 @@ template <int K, bool NF16, bool SC, bool ST>
 __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h16(
     const _Float16* __restrict__ x, int64_t n, int64_t ngroups, const uint4* __restrict__ rot16,
     const uint4* __restrict__ crec, const float* __restrict__ cn2s, const double* __restrict__ pi64, int N,
-    int bits, float e_abs, float e_rel, uint8_t* __restrict__ codes, void* __restrict__ norms,
-    const int64_t* __restrict__ slots, int64_t cap, int nwg) {
+    int bits, float e_abs, float e_rel, float c2max, float cmax, uint8_t* __restrict__ codes,
+    void* __restrict__ norms, const int64_t* __restrict__ slots, int64_t cap, int nwg) {
   constexpr int WAVES = Shape<K>::WAVES;
   constexpr int NSUB = Shape<K>::NSUB;
   constexpr int VG = 16 * NSUB;    // vectors per group
@@ -521,48 +521,61 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
 #pragma unroll
       for (int i = 0; i < K; i++) yb[i] = ysL[i];
       // Large codebooks (16 or more codewords per lane) are screened in fp32 first
-      // (for smaller ones the screen costs more than it saves): every fp32 distance is
-      // within e of the fp64 one, so the fp64 minimiser and all its ties lie within 2 e
-      // of the smallest fp32 distance m.  When no lane holds two such candidates, each
-      // lane scores its one candidate in fp64; otherwise every codeword is scored in
-      // fp64.  e <= u (2 sqrt(d) |y_b| +
-      // (k + 2) d) for a distance d (rounding of y to fp32, of each difference and of
-      // each fused square-add) up to terms of order u^2 |y_b|^2, which the absolute
-      // 1e-12 covers; the bound is doubled again for slack.
+      // (for smaller ones the screen costs more than it saves), with the expanded score
+      // s = 256 ||c||^2 - 512 y.c: the stored fp32 256 ||c||^2 plus one mixed-precision
+      // FMA per coordinate (fp32 -512 y times the fp16 codeword).  Every screened s is
+      // within e = (k + 2) u (256 c2max + 512 cmax |y_b|) of the exact s of the fp64 y
+      // (the rounding of y to fp32, of ||c||^2 to fp32, and of each of the k FMAs, whose
+      // partial sums stay below 256 c2max + 512 cmax |y_b|), and s is 256 (d - |y_b|^2)
+      // for the distance d, so the fp64 minimiser and all its ties lie within 2 e of the
+      // smallest screened s (plus the fp64 rounding of the distances, far below the
+      // absolute 1e-12).  When no lane holds two such candidates, each lane scores its
+      // one candidate in fp64; otherwise every codeword is scored in fp64.  The bound
+      // carries 2 % of slack for its own fp32 evaluation.
       double bd = __builtin_huge_val();
       int bn = 0x7fffffff;
       bool full_scan = N < 1024;
       if (!full_scan) {
-        float yf[K];
+        float v[K];
         float yn2 = 0.f;
 #pragma unroll
         for (int i = 0; i < K; i++) {
-          yf[i] = (float)yb[i];
-          yn2 = fmaf(yf[i], yf[i], yn2);
+          const float yf = (float)yb[i];
+          v[i] = -512.0f * yf;  // exact scaling
+          yn2 = fmaf(yf, yf, yn2);
         }
         float f1 = __builtin_huge_valf(), f2 = __builtin_huge_valf();
         int fi = 0x7fffffff;
-        for (int nn = lane; nn < N; nn += 64) {
-          const uint4 rw = *reinterpret_cast<const uint4*>(cbh + 8 * rec_of(nn));
-          const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
-          float df = 0.f;
+        // lane l scores codewords l + 64 r: their record and norm slots advance by a
+        // constant per round (66 and 72 in the padded LDS layout); the lane keeps the round
+        // of its minimum (a scalar), its codeword is formed after the loop
+        auto screen = [&](const uint4* rp, float c2, int tag) {
+          const uint32_t ww[4] = {rp->x, rp->y, rp->z, rp->w};
+          float sf = c2;
 #pragma unroll
           for (int i = 0; i < K; i += 2) {
-            const float d0 = yf[i] - h_lo(ww[i / 2]);
-            const float d1 = yf[i + 1] - h_hi(ww[i / 2]);
-            df = fmaf(d0, d0, df);
-            df = fmaf(d1, d1, df);
+            sf = fmaf(v[i], h_lo(ww[i / 2]), sf);
+            sf = fmaf(v[i + 1], h_hi(ww[i / 2]), sf);
           }
-          f2 = fminf(f2, fmaxf(f1, df));
-          fi = df < f1 ? nn : fi;
-          f1 = fminf(f1, df);
+          f2 = __builtin_amdgcn_fmed3f(f1, f2, sf);
+          fi = sf < f1 ? tag : fi;
+          f1 = fminf(f1, sf);
+        };
+        {
+          const int RST = ST ? 64 : 66, CST = ST ? 64 : 72;
+          const uint4* rp = reinterpret_cast<const uint4*>(cbh) + rec_of(lane);
+          const float* cp = ST ? cn2s + lane : c2L + cslot(lane);
+          // N is a power of two of at least 1024 here: whole rounds of 64
+#pragma unroll 4
+          for (int r = 0; r < (N >> 6); r++) screen(rp + RST * r, cp[CST * r], r);
+          if (fi != 0x7fffffff) fi = 64 * fi + lane;
         }
         float mf = f1;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) mf = fminf(mf, __shfl_xor(mf, m));
-        const float dm = mf * 1.0001f + 1e-30f;
-        const float tol = 4.0f * 5.9604645e-8f * (2.0f * __builtin_sqrtf(dm) * __builtin_sqrtf(yn2) * 1.0001f +
-                                                  (float)(K + 2) * dm) + 1e-12f;
+        const float tol = 2.0f * (1.02f * (float)(K + 2) * 5.9604645e-8f) *
+                              (256.0f * c2max + 512.0f * cmax * (__builtin_sqrtf(yn2) * 1.0001f)) +
+                          1e-12f;
         const bool cand = f1 <= mf + tol;
         full_scan = __ballot(cand && f2 <= mf + tol) != 0;
         if (!full_scan && cand) {
@@ -642,7 +655,8 @@ hipError_t launch_h16(const fq_codebook* cb, const void* x, int64_t n, uint8_t* 
   if (wgs > resident) wgs = resident;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, reinterpret_cast<const _Float16*>(x), n,
                      ngroups, reinterpret_cast<const uint4*>(cb->rot16), reinterpret_cast<const uint4*>(cb->crec),
-                     cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs, cb->h16_erel, codes, norms, slots, cap,
+                     cb->cn2s, cb->pi64, cb->N, cb->bits, cb->h16_eabs, cb->h16_erel, cb->c2max, cb->cmax, codes,
+                     norms, slots, cap,
                      (int)wgs);
   return hipGetLastError();
 }
