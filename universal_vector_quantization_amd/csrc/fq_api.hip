@@ -130,7 +130,9 @@ fq_status upload(T** dst, const T* src, size_t count) {
 // Operand layouts of the matrix-core encoder, built once per codebook.
 // Operands of the k = 16, 32, 64 encoder: the rotation as 32 x 32 x 16 A operands (three
 // fp16 parts of 1024 Pi, rows permuted so that a lane ends up with 32 consecutive
-// coordinates) and the codeword rows in their LDS layout (k fp16 coordinates, then
+// coordinates) and the codeword rows in their LDS layout (k fp16 coordinates, then a
+// 16-byte norm slot: for k = d row 4 g's holds the fp32 256 ||c||^2 of rows
+// 4 g .. 4 g + 3 and the other rows' are zero; for k = 16, 32 each row's holds its own
 // 256 ||c||^2 as fp16 hi + lo and six zeros), zero-padded to whole chunks of 8 tiles.
 fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const float* rotation) {
   const int d = cb->d, k = cb->k, N = cb->N;
@@ -166,12 +168,19 @@ fq_status upload_full_operands(fq_codebook* cb, const float* codewords, const fl
       memcpy(row + 2 * t, &hv, 2);
       c2 += v * v;
     }
-    // 256 ||c||^2 as fp16 hi + lo (22 bits) in the row's norm slots, then zeros
-    const double s2 = 256.0 * c2;
-    const _Float16 nh = (_Float16)s2;
-    const _Float16 nl = (_Float16)(s2 - (double)nh);
-    memcpy(row + 2 * k, &nh, 2);
-    memcpy(row + 2 * k + 2, &nl, 2);
+    if (k == d) {
+      // 256 ||c||^2 in fp32, in the norm slot of the first row of its group of four
+      // (rows 4 g .. 4 g + 3 of a tile are the four accumulator rows a lane starts from)
+      const float s2 = (float)(256.0 * c2);
+      memcpy(rc + (size_t)(n & ~3) * rowb + 2 * k + 4 * (n & 3), &s2, 4);
+    } else {
+      // 256 ||c||^2 as fp16 hi + lo (22 bits) in the row's norm slot, then zeros
+      const double s2 = 256.0 * c2;
+      const _Float16 nh = (_Float16)s2;
+      const _Float16 nl = (_Float16)(s2 - (double)nh);
+      memcpy(row + 2 * k, &nh, 2);
+      memcpy(row + 2 * k + 2, &nl, 2);
+    }
   }
   fq_status st = upload(&cb->rot32, rt, (size_t)2 * 4 * 3 * 64 * 8);
   if (st == FQ_OK) st = upload(&cb->frec, rc, rec_bytes);

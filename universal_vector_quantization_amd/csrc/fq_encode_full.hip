@@ -16,10 +16,14 @@
 //     lane l holds coordinates 32 (l / 32) .. + 31 of vector l % 32.
 //  2. -512 y is rounded to fp16 ("hi"); lanes exchange halves so that each holds
 //     the B operands of 4 K-steps of 16 coordinates: block b of size KB is the
-//     K-steps KB / 16 b .. KB / 16 (b + 1) - 1.  A further K-step multiplies the
-//     record's norm slots (256 ||c||^2 as fp16 hi + lo) by 1, so the accumulator
-//     starts at 0 and no per-tile LDS reads seed it.
-//  3. Per codeword tile and column tile: KB / 16 + 1 chained matrix ops; the lane
+//     K-steps KB / 16 b .. KB / 16 (b + 1) - 1.  For KB = 64 the accumulators
+//     start at the fp32 256 ||c||^2 of the lane's rows, read from the tile's norm
+//     slots in LDS (four 16-byte reads per tile, each shared by half the wave); for
+//     KB = 16, 32 a further K-step multiplies the record's norm slot (256 ||c||^2 as
+//     fp16 hi + lo) by 1, so the accumulator starts at 0 (there each codeword tile
+//     serves two column tiles, and the per-tile seed registers measured slower).
+//  3. Per codeword tile and column tile: KB / 16 (KB = 64) or KB / 16 + 1 chained
+//     matrix ops; the lane
 //     takes the minimum of its 16 rows, writes the tile index into its low
 //     tagbits = ceil(log2(N / 32)) mantissa bits (one and-or), keeps the best,
 //     second and third such tagged minima (so the first two name their tiles)
@@ -34,8 +38,8 @@
 //     of the exact scaled score, E0 the bound of the k = 4 / 8 encoder for this k
 //     (1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 35840 sqrt(k) cmax u
 //     + 2^-25 (1 + sqrt(k) cmax)), |y_b| <= 1) and the last term the fp16 hi + lo
-//     split of 256 ||c||^2.  If second - best > 2E the winner is the exact
-//     minimiser.
+//     split of 256 ||c||^2 (KB = 16, 32), which also covers its rounding to fp32
+//     (KB = 64).  If second - best > 2E the winner is the exact minimiser.
 //  5. Uncertified blocks (about 2 % on the full-vector workload): every codeword
 //     whose computed score is within 2E of the best lies in the best or second
 //     tile of a half unless a third tile minimum is that close too; those at most
@@ -66,7 +70,9 @@ struct FullShape {
   static constexpr int OCC = KB == 64 ? 4 : 3;
   static constexpr int CBP = KB == 64 ? 1 : 2;
 };
-// bytes per codeword row: KB fp16, then 256 ||c||^2 as fp16 hi, lo and six zeros
+// bytes per codeword row: KB fp16, then a 16-byte norm slot (KB = 64: row 4 g's holds
+// the fp32 256 ||c||^2 of rows 4 g .. 4 g + 3, the others are zero; KB = 16, 32: the
+// row's 256 ||c||^2 as fp16 hi, lo and six zeros)
 __host__ __device__ constexpr int row_bytes(int KB) { return 2 * KB + 16; }
 __host__ __device__ constexpr int chunk_bytes(int KB) { return CT * 32 * row_bytes(KB); }
 // per wave: x and y (fp64) of a re-searched vector, then the packing words
@@ -284,7 +290,8 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
     for (int s = 0; s < 4; s++)
 #pragma unroll
       for (int d = 0; d < 4; d++) __asm__ volatile("" : "+v"(bq[s][d]));
-    // the norm step: the norm slots (K 0, 1 of lanes 0-31) times 1
+
+    // the norm step of KB = 16, 32: the norm slots (K 0, 1 of lanes 0-31) times 1
     const half8 bnorm = __builtin_bit_cast(half8, make_uint4(h == 0 ? 0x3c003c00u : 0u, 0u, 0u, 0u));
 
     // ---- 3-4. stream the codebook (once per CBP column tiles), then per column tile the
@@ -323,8 +330,25 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
           half8 A[KS];
 #pragma unroll
           for (int s = 0; s < KS; s++) A[s] = *reinterpret_cast<const half8*>(arow + 32 * s + 16 * h);
-          // lanes 32-63 read the same finite norm slots against a zero B: no contribution
-          const half8 An = *reinterpret_cast<const half8*>(arow + 2 * KB);
+          // KB = 64: accumulators start at the fp32 256 ||c||^2 of the lane's rows
+          // 8 i + 4 h + 0..3, held in the norm slot of row 8 i + 4 h.  KB = 16, 32: they
+          // start at 0 and the norm step multiplies the row's norm slot by 1 (lanes 32-63
+          // read the same finite slots against a zero B: no contribution)
+          f32x16 seed;
+          half8 An;
+          if constexpr (KB == 64) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const float4 sv =
+                  *reinterpret_cast<const float4*>(cur + tt * TILEB + (8 * i + 4 * h) * ROWB + 2 * KB);
+              seed[4 * i] = sv.x;
+              seed[4 * i + 1] = sv.y;
+              seed[4 * i + 2] = sv.z;
+              seed[4 * i + 3] = sv.w;
+            }
+          } else {
+            An = *reinterpret_cast<const half8*>(arow + 2 * KB);
+          }
           // the tile index in a vector register (one move per tile): the tag's and-or may
           // read only one scalar operand, which the mask takes
           uint32_t tv = (uint32_t)(ch * CT + tt);
@@ -333,9 +357,13 @@ __global__ __launch_bounds__(FullShape<KB>::WAVES * 64, FullShape<KB>::OCC) void
           for (int j = 0; j < CBP; j++) {
             const int b = pb + j;
             f32x16 acc;
+            if constexpr (KB == 64) {
+              acc = seed;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 16; e++) acc[e] = 0.f;
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(An, bnorm, acc, 0, 0, 0);
+              for (int e = 0; e < 16; e++) acc[e] = 0.f;
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(An, bnorm, acc, 0, 0, 0);
+            }
 #pragma unroll
             for (int s = 0; s < KS; s++)
               acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[s], __builtin_bit_cast(half8, bq[KS * b + s]), acc, 0,

@@ -39,7 +39,9 @@ struct fq_codebook {
   _Float16* rot32;  // [2 row tiles][4 k steps][hi, mid, lo][64 lanes][8]: 1024 Pi as the A operand of
                     // mfma_f32_32x32x16_f16; row 8 a + 4 hh + b of tile r is coordinate 32 hh + 16 r + 4 a + b
   uint8_t* frec;    // [N / 32 tiles][32 rows][2 k + 16 bytes], zero-padded to whole chunks of 8 tiles:
-                    // k fp16 coordinates, then 256 ||c||^2 as fp16 hi, lo and six zero halves
+                    // k fp16 coordinates, then a norm slot: for k = d row 4 g's holds fp32
+                    // 256 ||c||^2 of rows 4 g .. 4 g + 3 (the others are zero), for k = 16, 32
+                    // each row's holds its 256 ||c||^2 as fp16 hi, lo and six zero halves
   float* dec_full;  // k = d only: [N][d] Pi^T c_n in fp32 (rounded once from fp64), the decoded unit
                     // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
