@@ -433,10 +433,12 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
           const uint4 rw = ST ? crec[n0 + e] : recL[rslot(n0 + e)];
           const uint32_t ww[4] = {rw.x, rw.y, rw.z, rw.w};
           float sc = c2a[e];
+          // the fp32 operand first: with the fp16 one first the code generator puts a wait
+          // state between every two mixed-precision FMAs of the chain
 #pragma unroll
           for (int i = 0; i < K; i += 2) {
-            sc = fmaf(h_lo(ww[i / 2]), vp[i], sc);
-            sc = fmaf(h_hi(ww[i / 2]), vp[i + 1], sc);
+            sc = fmaf(vp[i], h_lo(ww[i / 2]), sc);
+            sc = fmaf(vp[i + 1], h_hi(ww[i / 2]), sc);
           }
           const float st = __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, sc) & ~15u) | (uint32_t)(4 * qq + e));
           r2 = __builtin_amdgcn_fmed3f(r1, r2, st);

@@ -284,7 +284,8 @@ __global__ __launch_bounds__(WAVES * 64) void encode_mfma(
         for (int e = 0; e < 4; e++) {
           float sc = c2a[e];
 #pragma unroll
-          for (int i = 0; i < K; i++) sc = fmaf((float)cv[e][i], my[i], sc);
+          // the fp32 operand first (else a wait state between every two mixed FMAs)
+          for (int i = 0; i < K; i++) sc = fmaf(my[i], (float)cv[e][i], sc);
           r2 = __builtin_amdgcn_fmed3f(r1, r2, sc);
           const bool lt = sc < r1;
           ri = lt ? (n0 + e) : ri;
