@@ -137,7 +137,10 @@ __device__ inline void wait_vmcnt() {
 // the last group) ahead of use; the output leaves through the staging tile as
 // STORES 16-byte stores per group.  With these fixed counts the wait for a slot is
 // an exact vmcnt, and no compiler-inserted wait ever covers the ring.
-template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV>
+// OPL: the Pi^T operands are staged in LDS once per workgroup (the small-codebook
+// configurations; with the 64 KiB codebook the LDS has no room and every wave loads
+// them into registers)
+template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV, bool OPL>
 struct RingShape {
   static constexpr int ROWB = stage_row_bytes<OF16>();
   static constexpr int REC_BYTES = 32 * RW * 4;
@@ -146,19 +149,20 @@ struct RingShape {
   static constexpr int LOADS = REC_DMA + 1;
   static constexpr int STORES = OF16 ? 4 : 8;
   static constexpr int WAIT_STEADY = (PF - 1) * LOADS + PF * STORES;
+  static constexpr int OP_BYTES = OPL ? 16 * 64 * 16 : 0;  // the staged Pi^T operands
   static size_t lds_bytes(int N) {
     const size_t cb = CBL ? (size_t)((N * K * 2 + 15) & ~15) : 0;
-    return cb + (size_t)WV * (32 * ROWB + PF * SLOT_BYTES);
+    return cb + (size_t)WV * (32 * ROWB + PF * SLOT_BYTES) + OP_BYTES;
   }
 };
 
-template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV>
+template <int K, bool NF16, bool OF16, int RW, bool CBL, int WV, bool OPL>
 __global__ __launch_bounds__(WV * 64) void decode_ring(const uint8_t* __restrict__ codes,
                                                             const void* __restrict__ norms, int64_t ngroups,
                                                             const _Float16* __restrict__ cw16,
                                                             const half8* __restrict__ dec_a, int N, int bits,
                                                             void* __restrict__ out, int nwg) {
-  typedef RingShape<K, NF16, OF16, RW, CBL, WV> S;
+  typedef RingShape<K, NF16, OF16, RW, CBL, WV, OPL> S;
   constexpr int NC = 8 / K > 0 ? 8 / K : 1;
   constexpr int BITS = RW * K / 2;  // (64 / K) blocks of BITS bits fill RW words
   static_assert((D / K) * BITS == 32 * RW, "whole-word records");
@@ -171,23 +175,40 @@ __global__ __launch_bounds__(WV * 64) void decode_ring(const uint8_t* __restrict
   const int cb_bytes = CBL ? ((N * K * 2 + 15) & ~15) : 0;
   char* stage = reinterpret_cast<char*>(smem) + cb_bytes + w * 32 * ROWB;
   char* ring = reinterpret_cast<char*>(smem) + cb_bytes + WV * 32 * ROWB + w * PF * S::SLOT_BYTES;
+  char* opL = reinterpret_cast<char*>(smem) + cb_bytes + WV * (32 * ROWB + PF * S::SLOT_BYTES);
 
+  // OPL: the Pi^T operands (16 sets of 64 lanes x 16 bytes) and the codebook go to LDS once
+  // per workgroup by direct loads, issued ahead of the wave's first ring loads: those first
+  // waits then cover them too (one load counter, completed in order), so the operand fetch
+  // overlaps the ring's first loads instead of preceding them.  Otherwise every wave loads
+  // the operands into registers (16 KiB a wave from L2) before any ring load.
   half8 da[2][4][2];  // Pi^T operands (hi, lo) of both 32-row tiles and all 4 k-steps
+  if constexpr (OPL) {
+    for (int pc = w; pc < 16; pc += WV)
+      lds_dma16(reinterpret_cast<const char*>(dec_a) + pc * 1024 + lane * 16, opL + pc * 1024);
+  } else {
 #pragma unroll
-  for (int r = 0; r < 2; r++)
+    for (int r = 0; r < 2; r++)
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+      for (int s = 0; s < 4; s++)
 #pragma unroll
-      for (int p = 0; p < 2; p++) da[r][s][p] = dec_a[((r * 4 + s) * 2 + p) * 64 + lane];
+        for (int p = 0; p < 2; p++) da[r][s][p] = dec_a[((r * 4 + s) * 2 + p) * 64 + lane];
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the operands are in registers before any ring load
+  }
   if constexpr (CBL)
-    for (int i = tid; i < cb_bytes / 16; i += WV * 64) smem[i] = reinterpret_cast<const uint4*>(cw16)[i];
-  __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): the operands are in registers before any ring load
-  if constexpr (CBL) __syncthreads();
+    for (int pc = w; pc * 1024 < cb_bytes; pc += WV)
+      if (pc * 1024 + lane * 16 < cb_bytes)
+        lds_dma16(reinterpret_cast<const char*>(cw16) + pc * 1024 + lane * 16,
+                  reinterpret_cast<char*>(smem) + pc * 1024);
   const _Float16* cb = CBL ? reinterpret_cast<const _Float16*>(smem) : cw16;
 
   const int64_t step = (int64_t)nwg * WV;
   int64_t g = (int64_t)fq_bid_x() * WV + w;
-  if (g >= ngroups) return;
+  if (g >= ngroups) {  // no groups: only its share of the staging, then the barrier
+    wait_vmcnt<0>();
+    __syncthreads();
+    return;
+  }
   int64_t left = (ngroups - 1 - g) / step + 1;  // groups of this wave
   const int64_t total = left;
 
@@ -237,7 +258,21 @@ __global__ __launch_bounds__(WV * 64) void decode_ring(const uint8_t* __restrict
         __builtin_amdgcn_s_setprio(0);
     }
     switch (i < PF ? i : PF) {
-      case 0: wait_vmcnt<(PF - 1) * L>(); break;
+      case 0:
+        // this wave's operand and codebook pieces and its first ring slot have landed;
+        // after the barrier every wave's pieces have
+        wait_vmcnt<(PF - 1) * L>();
+        __syncthreads();
+        if constexpr (OPL) {
+#pragma unroll
+          for (int r = 0; r < 2; r++)
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+              for (int p = 0; p < 2; p++)
+                da[r][s][p] = *reinterpret_cast<const half8*>(opL + ((r * 4 + s) * 2 + p) * 1024 + lane * 16);
+        }
+        break;
       case 1: wait_vmcnt<(PF - 1) * L + T>(); break;
       case 2: wait_vmcnt<(PF - 1) * L + 2 * T>(); break;
       case 3: wait_vmcnt<(PF - 1) * L + 3 * T>(); break;
@@ -649,8 +684,8 @@ hipError_t launch_one(const fq_codebook* cb, const uint8_t* codes, const void* n
       } else {
         // a few groups per consumer: waves that load and store for themselves start sooner
         constexpr int WV = BIG ? waves_ring(OF) : WAVES;
-        typedef RingShape<K, NF, OF, RW, SCBL, WV> RS;
-        const auto rkern = decode_ring<K, NF, OF, RW, SCBL, WV>;
+        typedef RingShape<K, NF, OF, RW, SCBL, WV, !BIG> RS;
+        const auto rkern = decode_ring<K, NF, OF, RW, SCBL, WV, !BIG>;
         const size_t rlds = RS::lds_bytes(cb->N);
         if (rlds > 65536)
           e = hipFuncSetAttribute(reinterpret_cast<const void*>(rkern), hipFuncAttributeMaxDynamicSharedMemorySize,
