@@ -414,13 +414,18 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
   cb->c2max = nextafterf((float)c2max, INFINITY);
   cb->cmax = nextafterf((float)sqrt(c2max), INFINITY);
   {
-    // Score error bound of the fp16-input matrix-core encoder (derivation at the kernel);
-    // 1.02 covers the 1.01 slack of the bound and its fp32 evaluation in the kernel.
+    // Score error bounds of the fp16-input matrix-core encoders (derivations at the kernels);
+    // 1.02 covers the 1.01 slack of the bound and its fp32 evaluation in the kernel.  The
+    // rotation term is 512 |c| sqrt(k) times the per-coordinate error of y: 38 u for the
+    // k = 4 / 8 encoder (two sums of 32 products added once), 70 u for the k = 16, 32, 64
+    // encoder (one chain of 64).
     const double u = 0x1p-24, sk = sqrt((double)k), cm = cb->cmax, c2 = cb->c2max;
     const double rel = 1.02 * (2 * k + 7) * u * 512.0 * cm;
-    const double abs_ = 1.02 * ((2 * k + 7) * u * 256.0 * c2 + 35840.0 * sk * cm * u + 0x1p-25 * (1.0 + sk * cm));
+    const double abs_h16 = 1.02 * ((2 * k + 7) * u * 256.0 * c2 + 19456.0 * sk * cm * u + 0x1p-25 * (1.0 + sk * cm));
+    const double abs_full = 1.02 * ((2 * k + 7) * u * 256.0 * c2 + 35840.0 * sk * cm * u + 0x1p-25 * (1.0 + sk * cm));
     cb->h16_erel = nextafterf((float)rel, INFINITY);
-    cb->h16_eabs = nextafterf((float)abs_, INFINITY);
+    cb->h16_eabs = nextafterf((float)abs_h16, INFINITY);
+    cb->full_eabs = nextafterf((float)abs_full, INFINITY);
   }
   for (int i = 0; i < d; i++)
     for (int j = 0; j < d; j++) hpi64t[j * d + i] = (double)rotation[i * d + j];

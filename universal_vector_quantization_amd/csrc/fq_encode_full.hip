@@ -707,7 +707,7 @@ hipError_t launch_full(const fq_codebook* cb, const void* x, int64_t n, uint8_t*
   if (wgs > resident) wgs = resident;
   hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(WAVES * 64), lds, s, reinterpret_cast<const _Float16*>(x), n,
                      ngroups, reinterpret_cast<const uint4*>(cb->rot32), reinterpret_cast<const uint8_t*>(cb->frec),
-                     cb->cw, cb->pi64t, cb->N, cb->bits, cb->h16_eabs, cb->h16_erel, cb->cmax, cb->c2max, codes, norms,
+                     cb->cw, cb->pi64t, cb->N, cb->bits, cb->full_eabs, cb->h16_erel, cb->cmax, cb->c2max, codes, norms,
                      slots, cap, (int)wgs);
   return hipGetLastError();
 }

@@ -31,14 +31,18 @@
 //     in the low 4 mantissa bits (one and-or per row instead of a compare and a
 //     select), so the best one names its row.
 //  5. Certificate: every computed score is within
-//        E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 35840 sqrt(k) cmax u
+//        E = 1.01 ((2k+7) u (256 c2max + 512 cmax |y_b|) + 19456 sqrt(k) cmax u
 //                  + 2^-25 (1 + sqrt(k) cmax)),   u = 2^-24,
 //     of the exact scaled score: (2k+3) roundings of the matrix / FMA sums, the
 //     fp16 lo parts of -512 y and of 256 ||c||^2 (2^-22 relative, 2^-25 absolute
-//     when subnormal), and the rotation: each coordinate of y is within 70 u of
-//     Pi x / nu (64 + 2 roundings of the hi sum over |Pi_t| |x| <= nu, the add,
-//     1 / nu and the product; the mid / lo sums are 2^-11 smaller), which moves
-//     a score by at most 512 |c| sqrt(k) 70 u.  The host folds E into
+//     when subnormal), and the rotation: each coordinate of y is within 38 u of
+//     Pi x / nu (the hi products of each K-step summed apart, at most 33
+//     roundings each over its share of |Pi_t| |x| <= nu, one to add the two,
+//     then the add of the mid / lo sums, 1 / nu and the product; the mid / lo
+//     sums are 2^-11 smaller, and one u of slack), which moves a score by at most
+//     512 |c| sqrt(k) 38 u.  (With one chain of 64 products it was 70 u; the
+//     certificate's width is mostly this term, and the blocks it leaves to the
+//     re-search fell with it.)  The host folds E into
 //     e_abs + e_rel |y_b| (with 1.02 for the fp32 evaluation here).  If
 //     second - best > 2E the winner is the exact unique minimiser; "second"
 //     is first lowered and "best" raised by what a tag can have moved them
@@ -245,22 +249,22 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
       const float inv = nu > 0.0 ? (float)(1.0 / (1024.0 * nu)) : 0.0f;
       if (q == 0) invL[vec] = nu > 0.0 ? 1.0 / nu : 0.0;  // for the fp64 re-search
 
+      // hi products of the two K-steps summed separately and added once: each sum of 32
+      // products carries at most 33 roundings over its own |terms| (64 + 2 with one chain)
       f32x4 ah[4], am[4];
 #pragma unroll
       for (int r = 0; r < 4; r++) {
-        ah[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-        am[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++) {
-        const half8 xv = __builtin_bit_cast(half8, ks ? xb : xa);
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const uint4* op = rotL + ((ks * 4 + r) * 3) * 64 + lane;
-          ah[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[0]), xv, ah[r], 0, 0, 0);
-          am[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[64]), xv, am[r], 0, 0, 0);
-          am[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op[128]), xv, am[r], 0, 0, 0);
-        }
+        const uint4* op0 = rotL + (r * 3) * 64 + lane;
+        const uint4* op1 = rotL + ((4 + r) * 3) * 64 + lane;
+        const half8 xv0 = __builtin_bit_cast(half8, xa), xv1 = __builtin_bit_cast(half8, xb);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 h0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op0[0]), xv0, z, 0, 0, 0);
+        const f32x4 h1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op1[0]), xv1, z, 0, 0, 0);
+        ah[r] = h0 + h1;
+        f32x4 m = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op0[64]), xv0, z, 0, 0, 0);
+        m = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op0[128]), xv0, m, 0, 0, 0);
+        m = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op1[64]), xv1, m, 0, 0, 0);
+        am[r] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, op1[128]), xv1, m, 0, 0, 0);
       }
       // v = -512 y for coordinates 16 q + 4 r + i; hi / lo fp16 parts packed two per dword.
       uint32_t hi[8], lo[8];
@@ -473,7 +477,11 @@ __global__ __launch_bounds__(Shape<K>::WAVES * 64, Shape<K>::OCC) void encode_h1
 
     // ---- 6-7. pack the certified codes, search the listed blocks again in fp64, store
     const int words = 8 * bits;
-    for (int i = lane; i < words; i += 64) spk[i] = 0u;
+    {
+      int li = lane;  // opaque: the lane's packing-word address is formed per group, not carried
+      __asm__ volatile("" : "+v"(li));
+      for (int i = li; i < words; i += 64) spk[i] = 0u;
+    }
     wave_lds_sync();
 #pragma unroll
     for (int p = 0; p < 4; p++) {

@@ -45,6 +45,7 @@ struct fq_codebook {
   float* dec_full;  // k = d only: [N][d] Pi^T c_n in fp32 (rounded once from fp64), the decoded unit
                     // vector of code n, so a full-vector decode is a row gather scaled by the norm
   float h16_eabs, h16_erel;  // its certificate: scores are within h16_eabs + h16_erel |y_b| of exact
+  float full_eabs;           // the same for the k = 16, 32, 64 encoder (its longer rotation sums)
   size_t max_lds;   // bytes of LDS one workgroup may use on the device
   int force_encoder;  // FQ_ENCODE_KERNEL at load time (an fq::EncodeKernel): that encoder wherever it covers
                       // the call (valu: every call), else the automatic choice
