@@ -616,7 +616,7 @@ FQ_EXPORT size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, i
   if (attn_check_shape(cb, B, Hq, Hkv, T) != FQ_OK || !fq::prefill_supported(cb) || Sq <= 0 || T == 0 || B == 0)
     return 0;
   if ((int64_t)B * Hq * Sq > ((int64_t)1 << 31) - 1) return 0;
-  const fq::PrefillPlan p = fq::prefill_plan(B, Hq, Hkv, Sq, T);
+  const fq::PrefillPlan p = fq::prefill_plan(cb, B, Hq, Hkv, Sq, T);
   return ((size_t)B * Hq * Sq * p.nchunks * (2 + fq::kD) * sizeof(float) + 255) & ~(size_t)255;
 }
 
@@ -632,7 +632,7 @@ FQ_EXPORT fq_status fq_attn_prefill(const fq_codebook* cb, const void* q, const 
   if (!q || !out) return FQ_ERR_ARG;
   if (T == 0) return FQ_OK;  // nothing to attend to
   if ((int64_t)B * Hq * Sq > ((int64_t)1 << 31) - 1 || (int64_t)B * Hkv > 65535) return FQ_ERR_UNSUPPORTED;
-  if (fq::prefill_plan(B, Hq, Hkv, Sq, T).rblocks > 65535) return FQ_ERR_UNSUPPORTED;  // grid y
+  if (fq::prefill_plan(cb, B, Hq, Hkv, Sq, T).rblocks > 65535) return FQ_ERR_UNSUPPORTED;  // grid y
   if (!k_codes || !k_norms || !v_codes || !v_norms) return FQ_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_codes) || !aligned16(k_norms) || !aligned16(v_codes) || !aligned16(v_norms) ||
       !aligned16(out))

@@ -143,14 +143,14 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
 hipError_t launch_attn_combine(const float* ws, const float* pi32, int64_t rows, int nchunks, float* out,
                                hipStream_t s);
 
-// Multi-query (prefill) attention: k = 4, 8-bit codes.  Split over keys into nchunks
-// ranges of chunk_tokens keys, 64 query rows per workgroup.
+// Multi-query (prefill) attention.  Split over keys into nchunks ranges of chunk_tokens
+// keys, 128 (k = 4 with 8-bit codes) or 64 query rows per workgroup.
 struct PrefillPlan {
   int nchunks;
   int64_t chunk_tokens;
   int rblocks;
 };
-PrefillPlan prefill_plan(int B, int Hq, int Hkv, int Sq, int64_t T);
+PrefillPlan prefill_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T);
 bool prefill_supported(const fq_codebook* cb);
 hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                           const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,

@@ -5,10 +5,11 @@
 // Sq queries per query head attend to the T keys of their KV head's slab; with
 // the causal flag the queries are the slab's last Sq positions, so query i sees
 // keys 0 .. T - Sq + i.  Many query rows share every key, so the products run on
-// the matrix core (mfma_f32_16x16x32_f16) over codeword tiles decoded into LDS:
-//   * a workgroup takes 64 query rows of one (batch, KV head) slab (row r = head
-//     r / Sq of the group, query r % Sq) and a range of its keys; each of its 4
-//     waves owns 16 rows (the MFMA columns);
+// the matrix core over codeword tiles decoded into LDS:
+//   * a workgroup takes a block of query rows of one (batch, KV head) slab (row r =
+//     head r / Sq of the group, query r % Sq) and a range of its keys; each of its 4
+//     waves owns the MFMA columns of 32 rows (k = 4 with 8-bit codes, the wide kernel,
+//     mfma_f32_32x32x16_f16) or 16 rows (every other codebook, mfma_f32_16x16x32_f16);
 //   * per 64-key unit the threads decode the keys' records into LDS: K as
 //     [key][dim] fp16 (the A operand of S^T = K Qrot^T), V transposed as
 //     [dim][key] (the A operand of O^T += V^T P^T), norms as fp32.  For k = 4
@@ -16,16 +17,17 @@
 //     into registers; for other codebooks a thread takes pieces of min(k, 16)
 //     dimensions of a key (the code read at its fixed bit address), copied from
 //     an LDS copy of the codebook when that is at most 32 KiB, else from the
-//     fp16 codebook in global memory (L2-resident: 512 KiB for k = d, N = 4096);
+//     fp16 codebook in global memory (L2-resident: 512 KiB for k = d, N = 4096).
+//     Units are double-buffered: unit h + 1 is decoded before unit h is computed,
+//     one barrier per unit;
 //   * the rotated, scaled query is split fp16 hi + lo (two products per K step:
 //     scores carry ~22 bits); P' = p * nu_v enters as one fp16 operand (relative
 //     rounding 2^-12 of each weight);
-//   * the key order inside a 32-key PV step is chosen so that the score
-//     registers of a lane are exactly its P^T operand (no shuffles): operand k
-//     index 8 h + j is key 4 h + j (j < 4) or 16 + 4 h + j - 4 of the step;
-//   * online softmax in base 2 per query column; the workgroup writes one
-//     partial record (m, l, acc[64], rotated domain) per row and key range, and
-//     the decode combine kernel merges the records and applies Pi^T.
+//   * the key order inside a PV step is chosen so that the score registers of a
+//     lane are exactly its P^T operand (no shuffles);
+//   * online softmax in base 2 per query row; the workgroup writes one partial
+//     record (m, l, acc[64], rotated domain) per row and key range, and the decode
+//     combine kernel merges the records and applies Pi^T.
 #include "fq_internal.h"
 #include "fq_device.h"
 
@@ -42,8 +44,9 @@ constexpr int REC_F = 2 + D;
 constexpr int KS = D + 8;   // K tile [key][KS]
 constexpr int VS = PU + 4;  // V tile [dim][VS]
 constexpr int QSCR = 17;    // floats per lane of the query rotation's scratch (odd: no bank conflicts)
-// How a workgroup gets codewords: the k = 4, 8-bit path (registers a unit ahead, LDS
-// codebook), or pieces read from an LDS copy of the codebook, or from global memory.
+// How a workgroup gets codewords: the k = 4, 8-bit path (the wide kernel: registers a
+// unit ahead, LDS codebook), or pieces read from an LDS copy of the codebook, or from
+// global memory.
 enum CbMode { CB_K4B8 = 0, CB_LDS = 1, CB_GLOBAL = 2 };
 constexpr size_t CB_LDS_MAX = 32768;  // bytes of fp16 codebook held in LDS
 // the query rotation's scratch shares the LDS of the K and V tiles (used before them)
@@ -110,19 +113,20 @@ __device__ inline void store_piece(_Float16* dst, const _Float16 (&v)[KW]) {
   }
 }
 
-// KW = min(k, 16) dimensions per decode piece (CB_K4B8: 4); CM: a CbMode.
+// General kernel (every codebook but k = 4 with 8-bit codes): KW = min(k, 16) dimensions
+// per decode piece; CM: CB_LDS or CB_GLOBAL.
 template <int KW, int CM>
 __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
     const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
     const _Float16* __restrict__ cw16, int k, int bits, int N, int Hq, int Hkv, int64_t T, int Sq, int causal,
     int64_t chunk_tokens, int nchunks, float* __restrict__ ws) {
-  extern __shared__ __align__(16) _Float16 cbL[];  // the codebook [N][k] (CB_K4B8, CB_LDS)
-  __shared__ __align__(16) unsigned char tiles[TILE_BYTES];
-  _Float16* const Kt = reinterpret_cast<_Float16*>(tiles);  // [key][KS]
-  _Float16* const Vt = Kt + PU * KS;                        // [dim][VS]
-  float* const qscr = reinterpret_cast<float*>(tiles);      // per-lane scratch of the query rotation
-  __shared__ float knL[PU], vnL[PU];
+  extern __shared__ __align__(16) _Float16 cbL[];  // the codebook [N][k] (CB_LDS)
+  // two unit buffers, each K [key][KS] then V [dim][VS]; the query rotation's per-lane
+  // scratch uses buffer 1 before any unit reaches it
+  __shared__ __align__(16) unsigned char tiles[2][TILE_BYTES];
+  float* const qscr = reinterpret_cast<float*>(tiles[1]);
+  __shared__ float knL[2][PU], vnL[2][PU];
   const int tid = fq_tid(), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunk = fq_bid_x(), rb = fq_bid_y(), slab = fq_bid_z();
@@ -201,32 +205,13 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
 #pragma unroll
   for (int dt = 0; dt < 4; dt++) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // unit loads (registers), one unit ahead
-  const bool vhalf = tid >= 128;  // wave-uniform: waves 2, 3 decode V
-  const int kp = (tid & 127) >> 2, lp = tid & 3;
-  const uint8_t* __restrict__ store = vhalf ? vc : kc;
-  auto load_unit = [&](int64_t t0, UnitRegs& u) {
-    const int64_t nt = t_end - t0;
-    const int64_t key0 = slab0 + t0 + (2 * kp < nt ? 2 * kp : nt - 1);
-    const int64_t key1 = slab0 + t0 + (2 * kp + 1 < nt ? 2 * kp + 1 : nt - 1);
-    u.w0 = reinterpret_cast<const uint32_t*>(store + key0 * 16)[lp];
-    u.w1 = reinterpret_cast<const uint32_t*>(store + key1 * 16)[lp];
-    if (tid < PU) {
-      const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
-      u.kn = kn[kk];
-      u.vn = vn[kk];
-    }
-  };
-  UnitRegs cur{}, nxt{};
-  if (CM == CB_K4B8 && t_begin < t_end) load_unit(t_begin, cur);
-  __syncthreads();  // codebook in place
-
   const int lk = __builtin_ctz((unsigned)k);
   const int64_t vbits = (int64_t)(D / k) * bits;  // bits of one vector's record
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += PU) {
-    // ---- decode the unit into LDS
-    __syncthreads();  // the previous unit's tiles (or the query scratch) are no longer read
-    if constexpr (CM != CB_K4B8) {
+  // decode the unit at t0 into buffer bf: K as [key][dim], V transposed, norms as fp32
+  auto decode_unit = [&](int64_t t0, int bf) {
+    _Float16* const Kt = reinterpret_cast<_Float16*>(tiles[bf]);
+    _Float16* const Vt = Kt + PU * KS;
+    {
       // item it: piece p = it % P of key (it / P) % PU, of V when it >= PU P (wave-uniform)
       constexpr int P = D / KW;
       const int64_t nt = t_end - t0;
@@ -249,35 +234,27 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
       }
       if (tid < PU) {
         const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
-        knL[tid] = (float)kn[kk];
-        vnL[tid] = (float)vn[kk];
-      }
-    } else {
-      const uint32_t w0 = cur.w0, w1 = cur.w1;
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const half4 c0 = *reinterpret_cast<const half4*>(cbL + ((w0 >> (8 * c)) & 0xffu) * 4);
-        const half4 c1 = *reinterpret_cast<const half4*>(cbL + ((w1 >> (8 * c)) & 0xffu) * 4);
-        const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
-        if (vhalf) {
-          // the two keys' values of one dimension are neighbours in the transposed tile
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const half2_t pair = {c0[e], c1[e]};
-            *reinterpret_cast<half2_t*>(Vt + (d0 + e) * VS + 2 * kp) = pair;
-          }
-        } else {
-          *reinterpret_cast<half4*>(Kt + (2 * kp) * KS + d0) = c0;
-          *reinterpret_cast<half4*>(Kt + (2 * kp + 1) * KS + d0) = c1;
-        }
-      }
-      if (tid < PU) {
-        knL[tid] = (float)cur.kn;
-        vnL[tid] = (float)cur.vn;
+        knL[bf][tid] = (float)kn[kk];
+        vnL[bf][tid] = (float)vn[kk];
       }
     }
-    if (CM == CB_K4B8 && t0 + PU < t_end) load_unit(t0 + PU, nxt);
-    __syncthreads();
+  };
+
+  // Units are double-buffered: unit h + 1 is decoded into the other buffer before unit h
+  // is computed, so one barrier per unit both publishes the next unit and retires the
+  // buffer the one after it overwrites; different waves overlap decoding and matrix work.
+  if (t_begin < t_end) {
+    __syncthreads();  // codebook in place; every lane is done with its query scratch
+    decode_unit(t_begin, 0);
+    __syncthreads();  // unit 0 in buffer 0
+  }
+  int bf = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += PU, bf ^= 1) {
+    if (t0 + PU < t_end) decode_unit(t0 + PU, bf ^ 1);
+    const _Float16* const Kt = reinterpret_cast<const _Float16*>(tiles[bf]);
+    const _Float16* const Vt = Kt + PU * KS;
+    const float* const knU = knL[bf];
+    const float* const vnU = vnL[bf];
 
     // keys of this unit the lane's row may see: kk <= bound (32-bit; -1 = none)
     const int64_t nt = t_end - t0;
@@ -302,7 +279,7 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
         acc = mfma16(A, qlo[s], acc);
       }
 #pragma unroll
-      for (int i = 0; i < 4; i++) sc[a][i] = acc[i] * knL[16 * a + 4 * hq + i];
+      for (int i = 0; i < 4; i++) sc[a][i] = acc[i] * knU[16 * a + 4 * hq + i];
     }
     if (need_mask) {  // uniform: the last units of a range, the causal diagonal, short blocks
 #pragma unroll
@@ -335,7 +312,7 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
         const int a = 2 * st + (j >> 2), i = j & 3;
         const float p = __builtin_amdgcn_exp2f(sc[a][i] - m_use);
         l_run += p;
-        P[j] = (_Float16)(p * vnL[16 * a + 4 * hq + i]);
+        P[j] = (_Float16)(p * vnU[16 * a + 4 * hq + i]);
       }
 #pragma unroll
       for (int dt = 0; dt < 4; dt++) {
@@ -346,7 +323,7 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
         O[dt] = mfma16(A, P, O[dt]);
       }
     }
-    cur = nxt;
+    __syncthreads();  // unit h + 1 is in its buffer; this unit's buffer is free again
   }
 
   // ---- this row's partial record: O^T rows 16 dt + 4 hq + i of column col
@@ -373,13 +350,297 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
     for (int i = 0; i < 4; i++) rec[2 + 16 * dt + 4 * ehq + i] = O[dt][i];
 }
 
+
+// Wide variant for k = 4 with 8-bit codes (the prefill workload's codebook): a wave owns
+// 32 query rows and works with mfma_f32_32x32x16_f16, so every K or V operand it reads
+// from LDS feeds 32 queries instead of 16.  The first version (16 rows a wave) spent most
+// of its time in LDS (four waves each reading the whole unit's K and V tiles; 82 % of the
+// cycles LDS-active, half of that bank conflicts), not on the matrix core.
+//   * QK: A = K tile rows (keys 32 kt + 0..31) x 16 dimensions per K-step, B = the
+//     rotated query, fp16 hi and lo (lane col + 32 h holds dimensions 16 s + 8 h + 0..7
+//     of query row col); output rows (keys) 8 i + 4 h + j of query col in acc[4 i + j].
+//   * PV over 16-key steps: operand k index 8 h + 4 a + j is key 16 ks + 8 a + 4 h + j,
+//     so a lane's P' operand is 8 of its own scores and the V^T operand is two 8-byte
+//     reads per lane; O^T tile dtt holds dimensions 32 dtt + 8 i + 4 h + j of query col.
+constexpr int WROWS = 32 * PW;  // query rows per workgroup
+constexpr int WQS = 33;         // floats per lane of the query rotation's scratch (odd)
+static_assert(PW * 64 * WQS * 4 <= 2 * TILE_BYTES, "wide query scratch must fit both unit buffers");
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ inline f32x16 mfma32(half8 a, half8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Value of lane l ^ 32 (the other half of the wave), by one permute from the lane index
+// (no width handling, which kept a per-lane bound alive across the loop).
+__device__ inline float xor32(float v) {
+  const int src = (int)(__lane_id() ^ 32u) << 2;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, v)));
+}
+
+__global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
+    const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
+    const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
+    const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T, int Sq, int causal, int64_t chunk_tokens,
+    int nchunks, float* __restrict__ ws) {
+  __shared__ __align__(16) _Float16 cbL[256 * 4];
+  __shared__ __align__(16) unsigned char tiles[2][TILE_BYTES];
+  float* const qscr = reinterpret_cast<float*>(&tiles[0][0]);  // spans both buffers, used before them
+  __shared__ float knL[2][PU], vnL[2][PU];
+  const int tid = fq_tid(), lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunk = fq_bid_x(), rb = fq_bid_y(), slab = fq_bid_z();
+  const int b = slab / Hkv, g = slab - b * Hkv;
+  const int G = Hq / Hkv, rows = G * Sq;
+  const int64_t slab0 = (int64_t)slab * T;
+  const int col = lane & 31, h = lane >> 5;
+  const int r = rb * WROWS + 32 * w + col;  // this lane's query row (an MFMA column)
+  const bool row_ok = r < rows;
+  const int hl = row_ok ? r / Sq : 0, qi = row_ok ? r - hl * Sq : 0;
+  const int64_t lim = causal ? T - Sq + qi : T - 1;  // last key this row sees
+  const int64_t t_begin = (int64_t)chunk * chunk_tokens;
+  int64_t t_end = t_begin + chunk_tokens < T ? t_begin + chunk_tokens : T;
+  if (causal) {
+    const int rlast = rb * WROWS + WROWS - 1 < rows - 1 ? rb * WROWS + WROWS - 1 : rows - 1;
+    int imax = 0;  // the largest query index among the block's rows
+    for (int rr = rb * WROWS; rr <= rlast && imax < Sq - 1; rr++) {
+      const int ii = rr % Sq;
+      imax = ii > imax ? ii : imax;
+    }
+    const int64_t kmax = T - Sq + imax + 1;
+    t_end = t_end < kmax ? t_end : kmax;
+  }
+  if (tid < 128) reinterpret_cast<uint4*>(cbL)[tid] = reinterpret_cast<const uint4*>(cw16)[tid];
+
+  // B operands of QK: dimensions 16 s + 8 h + j of the rotated query (Pi q) * scale *
+  // log2(e) of row r, split fp16 hi + lo
+  half8 qhi[4], qlo[4];
+  {
+    float qv[D];
+    const uint4* qr = reinterpret_cast<const uint4*>(q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D);
+#pragma unroll
+    for (int e8 = 0; e8 < D / 8; e8++) {
+      const half8 h8 = __builtin_bit_cast(half8, qr[e8]);
+#pragma unroll
+      for (int j = 0; j < 8; j++) qv[8 * e8 + j] = row_ok ? (float)h8[j] : 0.0f;
+    }
+#pragma unroll 1
+    for (int jj = 0; jj < 32; jj++) {
+      const int d = 16 * (jj >> 3) + 8 * h + (jj & 7);
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < D; e++) a = __builtin_fmaf(pi32[d * D + e], qv[e], a);
+      qscr[tid * WQS + jj] = a * qscale;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const float a = qscr[tid * WQS + 8 * s + j];
+        const _Float16 hv = (_Float16)a;
+        qhi[s][j] = hv;
+        qlo[s][j] = (_Float16)(a - (float)hv);
+      }
+  }
+
+  // Softmax offset per row, lazily: scores are kept relative to m_run (the subtraction
+  // rides in the norm product's FMA); m_run moves only when a score exceeds it, to TAU above
+  // the row's maximum, so weights 2^L stay <= 1 (the fp16 P' cannot overflow) and the
+  // rescale is rare after the first units.  `have`: the row has seen a key (until then
+  // m_run is 0 and its first finite maximum sets it).
+  const float NEG = -__builtin_huge_valf();
+  constexpr float TAU = 4.0f;
+  float m_run = 0.0f, l_run = 0.0f;
+  bool have = false;
+  f32x16 O[2];
+#pragma unroll
+  for (int e = 0; e < 16; e++) O[0][e] = O[1][e] = 0.f;
+
+  // unit records in registers, a unit ahead: threads 0..127 decode K, 128..255 V; thread t
+  // of a half takes keys 2 (t / 4) and 2 (t / 4) + 1, record dword t % 4 of each
+  const bool vhalf = tid >= 128;
+  const int kp = (tid & 127) >> 2, lp = tid & 3;
+  const uint8_t* __restrict__ store = vhalf ? vc : kc;
+  auto load_unit = [&](int64_t t0, UnitRegs& u) {
+    const int64_t nt = t_end - t0;
+    const int64_t key0 = slab0 + t0 + (2 * kp < nt ? 2 * kp : nt - 1);
+    const int64_t key1 = slab0 + t0 + (2 * kp + 1 < nt ? 2 * kp + 1 : nt - 1);
+    u.w0 = reinterpret_cast<const uint32_t*>(store + key0 * 16)[lp];
+    u.w1 = reinterpret_cast<const uint32_t*>(store + key1 * 16)[lp];
+    if (tid < PU) {
+      const int64_t kk = slab0 + t0 + (tid < nt ? tid : nt - 1);
+      u.kn = kn[kk];
+      u.vn = vn[kk];
+    }
+  };
+  auto decode_unit = [&](int bf, const UnitRegs& u) {
+    _Float16* const Kt = reinterpret_cast<_Float16*>(tiles[bf]);
+    _Float16* const Vt = Kt + PU * KS;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const half4 c0 = *reinterpret_cast<const half4*>(cbL + ((u.w0 >> (8 * c)) & 0xffu) * 4);
+      const half4 c1 = *reinterpret_cast<const half4*>(cbL + ((u.w1 >> (8 * c)) & 0xffu) * 4);
+      const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
+      if (vhalf) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const half2_t pair = {c0[e], c1[e]};
+          *reinterpret_cast<half2_t*>(Vt + (d0 + e) * VS + 2 * kp) = pair;
+        }
+      } else {
+        *reinterpret_cast<half4*>(Kt + (2 * kp) * KS + d0) = c0;
+        *reinterpret_cast<half4*>(Kt + (2 * kp + 1) * KS + d0) = c1;
+      }
+    }
+    if (tid < PU) {
+      int t = tid;  // opaque: the norm slots' address is formed per unit, not carried (spilled)
+      __asm__ volatile("" : "+v"(t));
+      knL[bf][t] = (float)u.kn;
+      vnL[bf][t] = (float)u.vn;
+    }
+  };
+
+  UnitRegs cur{}, nxt{};
+  if (t_begin < t_end) {
+    load_unit(t_begin, cur);
+    __syncthreads();  // codebook in place; every lane is done with its query scratch
+    decode_unit(0, cur);
+    if (t_begin + PU < t_end) load_unit(t_begin + PU, nxt);
+    __syncthreads();  // unit 0 in buffer 0
+  }
+  int bf = 0;
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += PU, bf ^= 1) {
+    if (t0 + PU < t_end) {  // the next unit into the other buffer (retired by the last barrier)
+      cur = nxt;
+      decode_unit(bf ^ 1, cur);
+      if (t0 + 2 * PU < t_end) load_unit(t0 + 2 * PU, nxt);
+    }
+    const _Float16* const Kt = reinterpret_cast<const _Float16*>(tiles[bf]);
+    const _Float16* const Vt = Kt + PU * KS;
+    const float* const knU = knL[bf];
+    const float* const vnU = vnL[bf];
+    const int64_t nt = t_end - t0;
+    const bool need_mask = nt < PU || (causal && t0 + PU - 1 > T - Sq) || !row_ok;
+    int bound = PU - 1;  // keys of this unit the lane's row may see: index <= bound
+    if (need_mask) {
+      const int64_t bl = lim - t0, bn = nt - 1;
+      int64_t bb = bl < bn ? bl : bn;
+      bb = bb < -1 ? -1 : (bb > PU - 1 ? PU - 1 : bb);
+      bound = row_ok ? (int)bb : -1;
+    }
+    // ---- S^T = K Qrot^T: key tile kt covers keys 32 kt .. 32 kt + 31
+    float sc[2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++) {
+      f32x16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[e] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const half8 A = *reinterpret_cast<const half8*>(Kt + (32 * kt + col) * KS + 16 * s + 8 * h);
+        acc = mfma32(A, qhi[s], acc);
+        acc = mfma32(A, qlo[s], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const float4 kv = *reinterpret_cast<const float4*>(knU + 32 * kt + 8 * i + 4 * h);
+        sc[kt][4 * i] = __builtin_fmaf(acc[4 * i], kv.x, -m_run);
+        sc[kt][4 * i + 1] = __builtin_fmaf(acc[4 * i + 1], kv.y, -m_run);
+        sc[kt][4 * i + 2] = __builtin_fmaf(acc[4 * i + 2], kv.z, -m_run);
+        sc[kt][4 * i + 3] = __builtin_fmaf(acc[4 * i + 3], kv.w, -m_run);
+      }
+    }
+    if (need_mask) {  // uniform: the last units of a range, the causal diagonal, short blocks
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int e = 0; e < 16; e++)
+          sc[kt][e] = 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3) <= bound ? sc[kt][e] : NEG;
+    }
+    float mx = NEG;
+#pragma unroll
+    for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) mx = fmaxf(mx, sc[kt][e]);
+    mx = fmaxf(mx, xor32(mx));  // the row's maximum relative to m_run (-inf: no key)
+    const bool first = !have && mx != NEG;
+    if (__ballot(first || mx > 0.0f)) {  // some row's offset moves (rare after the first units)
+      const float dm = mx == NEG ? 0.0f : (have ? fmaxf(mx + TAU, 0.0f) : mx + TAU);
+      const float alpha = have ? __builtin_amdgcn_exp2f(-dm) : 0.0f;  // nothing accumulated before
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; e++) {
+        O[0][e] *= alpha;
+        O[1][e] *= alpha;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) sc[kt][e] -= dm;
+      m_run += dm;
+      have = have || mx != NEG;
+    }
+    // ---- O^T += V^T P'^T over four 16-key steps
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const int kt = ks >> 1;
+      half8 P;
+#pragma unroll
+      for (int jj = 0; jj < 8; jj++) {
+        const int i = 2 * (ks & 1) + (jj >> 2), j = jj & 3;
+        const float p = __builtin_amdgcn_exp2f(sc[kt][4 * i + j]);
+        l_run += p;
+        P[jj] = (_Float16)(p * vnU[32 * kt + 8 * i + 4 * h + j]);
+      }
+#pragma unroll
+      for (int dtt = 0; dtt < 2; dtt++) {
+        const _Float16* vrow = Vt + (32 * dtt + col) * VS + 16 * ks + 4 * h;
+        const half4 a0 = *reinterpret_cast<const half4*>(vrow);
+        const half4 a1 = *reinterpret_cast<const half4*>(vrow + 8);
+        const half8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        O[dtt] = mfma32(A, P, O[dtt]);
+      }
+    }
+    __syncthreads();  // unit h + 1 is in its buffer; this unit's buffer is free again
+  }
+
+  // ---- this row's partial record: O^T rows 32 dtt + 8 i + 4 h + j of column col
+  float l = l_run + xor32(l_run);
+  // the row's indices again, from a lane index formed here (one carried across the loop
+  // from the prologue was spilled)
+  uint32_t all = ~0u;
+  __asm__ volatile("" : "+s"(all));
+  const int ln = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
+  const int ecol = ln & 31, eh = ln >> 5;
+  const int er = rb * WROWS + 32 * w + ecol;
+  if (er >= rows) return;
+  const int ehl = er / Sq, eqi = er - ehl * Sq;
+  const int64_t bh = ((int64_t)b * Hq + (int64_t)g * G + ehl) * Sq + eqi;
+  float* rec = ws + (bh * nchunks + chunk) * REC_F;
+  if (eh == 0) {
+    rec[0] = have ? m_run : NEG;  // a row without keys in this range: an empty record
+    rec[1] = l;
+  }
+#pragma unroll
+  for (int dtt = 0; dtt < 2; dtt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) rec[2 + 32 * dtt + 8 * i + 4 * eh + j] = O[dtt][4 * i + j];
+}
+
 }  // namespace
 
-PrefillPlan prefill_plan(int B, int Hq, int Hkv, int Sq, int64_t T) {
+PrefillPlan prefill_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T) {
+  // the wide k = 4 / 8-bit kernel: 128 rows per workgroup, three workgroups per CU, so the
+  // key ranges are cut for one wave of 768 workgroups; the general kernel: 64 rows, 1024
+  const bool wide = cb->k == 4 && cb->bits == 8;
+  const int prows = wide ? WROWS : PROWS;
+  const int64_t target = wide ? 768 : 1024;
   const int rows = (Hq / Hkv) * Sq;
-  const int rblocks = (rows + PROWS - 1) / PROWS;
+  const int rblocks = (rows + prows - 1) / prows;
   const int64_t wgs = (int64_t)rblocks * B * Hkv;
-  int64_t nc = (1024 + wgs - 1) / wgs;
+  int64_t nc = (target + wgs - 1) / wgs;
   const int64_t most = (T + 511) / 512;
   if (nc > most) nc = most;
   if (nc < 1) nc = 1;
@@ -427,7 +688,7 @@ hipError_t launch_generic(const fq_codebook* cb, CbMode m, const PrefillArgs& a,
 hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                           const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
                           int causal, float scale, float* out, void* workspace, hipStream_t s) {
-  const PrefillPlan p = prefill_plan(B, Hq, Hkv, Sq, T);
+  const PrefillPlan p = prefill_plan(cb, B, Hq, Hkv, Sq, T);
   PrefillArgs a;
   a.q = reinterpret_cast<const _Float16*>(q);
   a.qscale = scale * 1.4426950408889634f;  // log2(e)
@@ -446,7 +707,9 @@ hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k
   const CbMode m = prefill_cb_mode(cb);
   hipError_t e;
   if (m == CB_K4B8) {
-    e = launch_variant<4, CB_K4B8>(cb, a, s);
+    hipLaunchKernelGGL(attn_prefill_w, a.grid, dim3(PW * 64), 0, s, a.q, a.qscale, cb->pi32, a.kc, a.kn, a.vc, a.vn,
+                       cb->cw16, a.Hq, a.Hkv, a.T, a.Sq, a.causal, a.p.chunk_tokens, a.p.nchunks, a.ws);
+    e = hipGetLastError();
   } else {
     switch (cb->k < 16 ? cb->k : 16) {
       case 1: e = launch_generic<1>(cb, m, a, s); break;
