@@ -473,13 +473,18 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
       u.vn = vn[kk];
     }
   };
+  // the four blocks of a record dword are taken in a lane-rotated order, so the lanes of
+  // one write instruction spread over all LDS banks (in order, the K writes of a wave hit
+  // 16 of the 64 banks and the V writes paired up)
+  const int rot = vhalf ? 2 * (lp >> 1) : lp;
   auto decode_unit = [&](int bf, const UnitRegs& u) {
     _Float16* const Kt = reinterpret_cast<_Float16*>(tiles[bf]);
     _Float16* const Vt = Kt + PU * KS;
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const half4 c0 = *reinterpret_cast<const half4*>(cbL + ((u.w0 >> (8 * c)) & 0xffu) * 4);
-      const half4 c1 = *reinterpret_cast<const half4*>(cbL + ((u.w1 >> (8 * c)) & 0xffu) * 4);
+    for (int cr = 0; cr < 4; cr++) {
+      const int c = (cr + rot) & 3;
+      const half4 c0 = *reinterpret_cast<const half4*>(cbL + __builtin_amdgcn_ubfe(u.w0, 8 * c, 8) * 4);
+      const half4 c1 = *reinterpret_cast<const half4*>(cbL + __builtin_amdgcn_ubfe(u.w1, 8 * c, 8) * 4);
       const int d0 = 16 * lp + 4 * c;  // block 4 lp + c covers dims d0 .. d0 + 3
       if (vhalf) {
 #pragma unroll
