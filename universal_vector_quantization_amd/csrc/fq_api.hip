@@ -107,6 +107,7 @@ void release(fq_codebook* cb) {
   (void)hipFree(cb->cn2);
   (void)hipFree(cb->pi64t);
   (void)hipFree(cb->pi32);
+  (void)hipFree(cb->rotp);
   (void)hipFree(cb->amfma);
   (void)hipFree(cb->cinit);
   (void)hipFree(cb->cn2s);
@@ -125,6 +126,30 @@ template <class T>
 fq_status upload(T** dst, const T* src, size_t count) {
   if (hipMalloc(dst, count * sizeof(T)) != hipSuccess) return FQ_ERR_HIP;
   return hipMemcpy(*dst, src, count * sizeof(T), hipMemcpyHostToDevice) == hipSuccess ? FQ_OK : FQ_ERR_HIP;
+}
+
+// The wide prefill's query rotation: 1024 Pi as fp16 hi + mid (the rest is 2^-22 of it),
+// rows permuted so that the output rows a lane holds are exactly the query coordinates
+// its QK operand needs (coordinates 16 s + 8 hh + jj for lane half hh).
+fq_status upload_prefill_rotation(fq_codebook* cb, const float* rotation) {
+  const int d = cb->d;
+  _Float16* rp = new (std::nothrow) _Float16[2 * 4 * 2 * 64 * 8];
+  if (!rp) return FQ_ERR_HIP;
+  for (int t = 0; t < 2; t++)
+    for (int s = 0; s < 4; s++)
+      for (int l = 0; l < 64; l++)
+        for (int jj = 0; jj < 8; jj++) {
+          const int m = l % 32, i = m / 8, hh = (m / 4) % 2, j = m % 4;
+          const int coord = 32 * t + 16 * (i / 2) + 8 * hh + 4 * (i % 2) + j, in = 16 * s + 8 * (l / 32) + jj;
+          const double P = 1024.0 * (double)rotation[coord * d + in];
+          const _Float16 hi = (_Float16)P;
+          const _Float16 mid = (_Float16)(P - (double)hi);
+          rp[((((t * 4 + s) * 2 + 0) * 64) + l) * 8 + jj] = hi;
+          rp[((((t * 4 + s) * 2 + 1) * 64) + l) * 8 + jj] = mid;
+        }
+  const fq_status st = upload(&cb->rotp, rp, (size_t)2 * 4 * 2 * 64 * 8);
+  delete[] rp;
+  return st;
 }
 
 // Operand layouts of the matrix-core encoder, built once per codebook.
@@ -443,6 +468,7 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
        hipMemcpy(cb->pi64t, hpi64t, (size_t)d * d * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
        hipMemcpy(cb->pi32, rotation, (size_t)d * d * sizeof(float), hipMemcpyHostToDevice) != hipSuccess))
     st = FQ_ERR_HIP;
+  if (st == FQ_OK) st = upload_prefill_rotation(cb, rotation);
   if (st == FQ_OK) st = upload_mfma_operands(cb, codewords, rotation, hcn2);
   delete[] h16;
   delete[] hcn2;

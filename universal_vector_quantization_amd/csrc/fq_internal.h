@@ -18,6 +18,10 @@ struct fq_codebook {
   float* cn2;       // [N] fp32 ||c_n||^2, rounded to nearest from an fp64 sum
   double* pi64t;    // [d][d] Pi transposed, fp64: pi64t[j*d + i] = Pi[i][j]
   float* pi32;      // [d][d] Pi row-major, fp32
+  _Float16* rotp;   // [2 row tiles][4 k steps][hi, mid][64 lanes][8]: 1024 Pi as the A operand of
+                    // mfma_f32_32x32x16_f16 for the wide prefill's query rotation; row 8 i + 4 hh + j
+                    // of tile t is coordinate 32 t + 16 (i / 2) + 8 hh + 4 (i % 2) + j, k is input
+                    // 16 s + 8 (lane / 32) + jj
   float cmax;       // max_n ||c_n||, rounded up
   float c2max;      // max_n ||c_n||^2, rounded up
   // Operands of the matrix-core encoder (k = 4 or 8, N a multiple of 32; else null):

@@ -363,8 +363,6 @@ __global__ __launch_bounds__(PW * 64, 4) void attn_prefill(
 //     so a lane's P' operand is 8 of its own scores and the V^T operand is two 8-byte
 //     reads per lane; O^T tile dtt holds dimensions 32 dtt + 8 i + 4 h + j of query col.
 constexpr int WROWS = 32 * PW;  // query rows per workgroup
-constexpr int WQS = 33;         // floats per lane of the query rotation's scratch (odd)
-static_assert(PW * 64 * WQS * 4 <= 2 * TILE_BYTES, "wide query scratch must fit both unit buffers");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ inline f32x16 mfma32(half8 a, half8 b, f32x16 c) {
@@ -379,13 +377,12 @@ __device__ inline float xor32(float v) {
 }
 
 __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
-    const _Float16* __restrict__ q, float qscale, const float* __restrict__ pi32, const uint8_t* __restrict__ kc,
+    const _Float16* __restrict__ q, float qscale, const half8* __restrict__ rotp, const uint8_t* __restrict__ kc,
     const _Float16* __restrict__ kn, const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn,
     const _Float16* __restrict__ cw16, int Hq, int Hkv, int64_t T, int Sq, int causal, int64_t chunk_tokens,
     int nchunks, float* __restrict__ ws) {
   __shared__ __align__(16) _Float16 cbL[256 * 4];
   __shared__ __align__(16) unsigned char tiles[2][TILE_BYTES];
-  float* const qscr = reinterpret_cast<float*>(&tiles[0][0]);  // spans both buffers, used before them
   __shared__ float knL[2][PU], vnL[2][PU];
   const int tid = fq_tid(), lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -413,34 +410,40 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
   if (tid < 128) reinterpret_cast<uint4*>(cbL)[tid] = reinterpret_cast<const uint4*>(cw16)[tid];
 
   // B operands of QK: dimensions 16 s + 8 h + j of the rotated query (Pi q) * scale *
-  // log2(e) of row r, split fp16 hi + lo
+  // log2(e) of row r, split fp16 hi + lo.  The rotation runs on the matrix core: A = 1024 Pi
+  // as fp16 hi + mid with rows permuted so that output row 8 i + 4 h + j of tile t is
+  // dimension 16 (2 t + i / 2) + 8 h + 4 (i % 2) + j, i.e. exactly the lane's own operand
+  // coordinates; B = the raw fp16 query (exact products, fp32 sums).
   half8 qhi[4], qlo[4];
   {
-    float qv[D];
-    const uint4* qr = reinterpret_cast<const uint4*>(q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D);
+    half8 qb[4];
+    const half8* qr = reinterpret_cast<const half8*>(q + ((((int64_t)b * Hq + (int64_t)g * G + hl) * Sq) + qi) * D);
 #pragma unroll
-    for (int e8 = 0; e8 < D / 8; e8++) {
-      const half8 h8 = __builtin_bit_cast(half8, qr[e8]);
+    for (int s = 0; s < 4; s++) qb[s] = row_ok ? qr[2 * s + h] : half8{};
+    f32x16 ah[2], am[2];
 #pragma unroll
-      for (int j = 0; j < 8; j++) qv[8 * e8 + j] = row_ok ? (float)h8[j] : 0.0f;
-    }
-#pragma unroll 1
-    for (int jj = 0; jj < 32; jj++) {
-      const int d = 16 * (jj >> 3) + 8 * h + (jj & 7);
-      float a = 0.0f;
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-      for (int e = 0; e < D; e++) a = __builtin_fmaf(pi32[d * D + e], qv[e], a);
-      qscr[tid * WQS + jj] = a * qscale;
-    }
+      for (int e = 0; e < 16; e++) ah[t][e] = am[t][e] = 0.f;
 #pragma unroll
-    for (int s = 0; s < 4; s++)
+    for (int t = 0; t < 2; t++)
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const float a = qscr[tid * WQS + 8 * s + j];
-        const _Float16 hv = (_Float16)a;
-        qhi[s][j] = hv;
-        qlo[s][j] = (_Float16)(a - (float)hv);
+      for (int s = 0; s < 4; s++) {
+        ah[t] = mfma32(rotp[((t * 4 + s) * 2 + 0) * 64 + lane], qb[s], ah[t]);
+        am[t] = mfma32(rotp[((t * 4 + s) * 2 + 1) * 64 + lane], qb[s], am[t]);
       }
+    const float sc = qscale * (1.0f / 1024.0f);
+#pragma unroll
+    for (int t = 0; t < 2; t++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const float a = (ah[t][4 * i + j] + am[t][4 * i + j]) * sc;
+          const _Float16 hv = (_Float16)a;
+          qhi[2 * t + i / 2][4 * (i % 2) + j] = hv;
+          qlo[2 * t + i / 2][4 * (i % 2) + j] = (_Float16)(a - (float)hv);
+        }
   }
 
   // Softmax offset per row, lazily: scores are kept relative to m_run (the subtraction
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
   UnitRegs cur{}, nxt{};
   if (t_begin < t_end) {
     load_unit(t_begin, cur);
-    __syncthreads();  // codebook in place; every lane is done with its query scratch
+    __syncthreads();  // codebook in place
     decode_unit(0, cur);
     if (t_begin + PU < t_end) load_unit(t_begin + PU, nxt);
     __syncthreads();  // unit 0 in buffer 0
@@ -712,7 +715,8 @@ hipError_t launch_prefill(const fq_codebook* cb, const void* q, const uint8_t* k
   const CbMode m = prefill_cb_mode(cb);
   hipError_t e;
   if (m == CB_K4B8) {
-    hipLaunchKernelGGL(attn_prefill_w, a.grid, dim3(PW * 64), 0, s, a.q, a.qscale, cb->pi32, a.kc, a.kn, a.vc, a.vn,
+    hipLaunchKernelGGL(attn_prefill_w, a.grid, dim3(PW * 64), 0, s, a.q, a.qscale,
+                       reinterpret_cast<const half8*>(cb->rotp), a.kc, a.kn, a.vc, a.vn,
                        cb->cw16, a.Hq, a.Hkv, a.T, a.Sq, a.causal, a.p.chunk_tokens, a.p.nchunks, a.ws);
     e = hipGetLastError();
   } else {
