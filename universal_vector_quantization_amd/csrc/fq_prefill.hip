@@ -536,8 +536,9 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
       bb = bb < -1 ? -1 : (bb > PU - 1 ? PU - 1 : bb);
       bound = row_ok ? (int)bb : -1;
     }
-    // ---- S^T = K Qrot^T: key tile kt covers keys 32 kt .. 32 kt + 31
-    float sc[2][16];
+    // ---- per key tile kt (keys 32 kt .. 32 kt + 31): S^T = K Qrot^T, the offset check,
+    //      then O^T += V^T P'^T over its two 16-key steps (the lazy offset lets each tile
+    //      finish before the next one's scores exist: half the score registers live)
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
       f32x16 acc;
@@ -549,64 +550,57 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
         acc = mfma32(A, qhi[s], acc);
         acc = mfma32(A, qlo[s], acc);
       }
+      float sc[16];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const float4 kv = *reinterpret_cast<const float4*>(knU + 32 * kt + 8 * i + 4 * h);
-        sc[kt][4 * i] = __builtin_fmaf(acc[4 * i], kv.x, -m_run);
-        sc[kt][4 * i + 1] = __builtin_fmaf(acc[4 * i + 1], kv.y, -m_run);
-        sc[kt][4 * i + 2] = __builtin_fmaf(acc[4 * i + 2], kv.z, -m_run);
-        sc[kt][4 * i + 3] = __builtin_fmaf(acc[4 * i + 3], kv.w, -m_run);
+        sc[4 * i] = __builtin_fmaf(acc[4 * i], kv.x, -m_run);
+        sc[4 * i + 1] = __builtin_fmaf(acc[4 * i + 1], kv.y, -m_run);
+        sc[4 * i + 2] = __builtin_fmaf(acc[4 * i + 2], kv.z, -m_run);
+        sc[4 * i + 3] = __builtin_fmaf(acc[4 * i + 3], kv.w, -m_run);
       }
-    }
-    if (need_mask) {  // uniform: the last units of a range, the causal diagonal, short blocks
+      if (need_mask) {  // uniform: the last units of a range, the causal diagonal, short blocks
 #pragma unroll
-      for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-        for (int e = 0; e < 16; e++)
-          sc[kt][e] = 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3) <= bound ? sc[kt][e] : NEG;
-    }
-    float mx = NEG;
-#pragma unroll
-    for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-      for (int e = 0; e < 16; e++) mx = fmaxf(mx, sc[kt][e]);
-    mx = fmaxf(mx, xor32(mx));  // the row's maximum relative to m_run (-inf: no key)
-    const bool first = !have && mx != NEG;
-    if (__ballot(first || mx > 0.0f)) {  // some row's offset moves (rare after the first units)
-      const float dm = mx == NEG ? 0.0f : (have ? fmaxf(mx + TAU, 0.0f) : mx + TAU);
-      const float alpha = have ? __builtin_amdgcn_exp2f(-dm) : 0.0f;  // nothing accumulated before
-      l_run *= alpha;
-#pragma unroll
-      for (int e = 0; e < 16; e++) {
-        O[0][e] *= alpha;
-        O[1][e] *= alpha;
+        for (int e = 0; e < 16; e++) sc[e] = 32 * kt + 8 * (e >> 2) + 4 * h + (e & 3) <= bound ? sc[e] : NEG;
       }
+      float mx = NEG;
 #pragma unroll
-      for (int kt = 0; kt < 2; kt++)
+      for (int e = 0; e < 16; e++) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, xor32(mx));  // the row's maximum relative to m_run (-inf: no key)
+      const bool first = !have && mx != NEG;
+      if (__ballot(first || mx > 0.0f)) {  // some row's offset moves (rare after the first units)
+        const float dm = mx == NEG ? 0.0f : (have ? fmaxf(mx + TAU, 0.0f) : mx + TAU);
+        const float alpha = have ? __builtin_amdgcn_exp2f(-dm) : 0.0f;  // nothing accumulated before
+        l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < 16; e++) sc[kt][e] -= dm;
-      m_run += dm;
-      have = have || mx != NEG;
-    }
-    // ---- O^T += V^T P'^T over four 16-key steps
+        for (int e = 0; e < 16; e++) {
+          O[0][e] *= alpha;
+          O[1][e] *= alpha;
+        }
 #pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      const int kt = ks >> 1;
-      half8 P;
-#pragma unroll
-      for (int jj = 0; jj < 8; jj++) {
-        const int i = 2 * (ks & 1) + (jj >> 2), j = jj & 3;
-        const float p = __builtin_amdgcn_exp2f(sc[kt][4 * i + j]);
-        l_run += p;
-        P[jj] = (_Float16)(p * vnU[32 * kt + 8 * i + 4 * h + j]);
+        for (int e = 0; e < 16; e++) sc[e] -= dm;
+        m_run += dm;
+        have = have || mx != NEG;
       }
 #pragma unroll
-      for (int dtt = 0; dtt < 2; dtt++) {
-        const _Float16* vrow = Vt + (32 * dtt + col) * VS + 16 * ks + 4 * h;
-        const half4 a0 = *reinterpret_cast<const half4*>(vrow);
-        const half4 a1 = *reinterpret_cast<const half4*>(vrow + 8);
-        const half8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        O[dtt] = mfma32(A, P, O[dtt]);
+      for (int kh = 0; kh < 2; kh++) {
+        const int ks = 2 * kt + kh;
+        half8 P;
+#pragma unroll
+        for (int jj = 0; jj < 8; jj++) {
+          const int i = 2 * kh + (jj >> 2), j = jj & 3;
+          const float p = __builtin_amdgcn_exp2f(sc[4 * i + j]);
+          l_run += p;
+          P[jj] = (_Float16)(p * vnU[32 * kt + 8 * i + 4 * h + j]);
+        }
+#pragma unroll
+        for (int dtt = 0; dtt < 2; dtt++) {
+          const _Float16* vrow = Vt + (32 * dtt + col) * VS + 16 * ks + 4 * h;
+          const half4 a0 = *reinterpret_cast<const half4*>(vrow);
+          const half4 a1 = *reinterpret_cast<const half4*>(vrow + 8);
+          const half8 A = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          O[dtt] = mfma32(A, P, O[dtt]);
+        }
       }
     }
     __syncthreads();  // unit h + 1 is in its buffer; this unit's buffer is free again
