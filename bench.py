@@ -237,17 +237,23 @@ def codec_record(fq, cb, x, n, norms, w, t_e, t_d):
 def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: int):
     """Decode attention through per-head lookup tables at the attention workload's
     shape (B=16, Hq=32, Hkv=4, T=32768; K and V draws encoded on the GPU): the
-    full-vector code (k = d = 64, N = 4096, the kernel it is built for), and the
-    k = 4, N = 256 code forced through it (FQ_ATTN_KERNEL=lut) beside the gather
-    kernel that code normally takes."""
+    full-vector code (k = d = 64, N = 4096: the library's choice there), the same
+    code through the general kernel's global-memory gathers (FQ_ATTN_KERNEL=gather),
+    and the k = 4, N = 256 code forced through the tables (FQ_ATTN_KERNEL=lut)
+    beside the gather kernel that code normally takes."""
     import torch
 
     B, Hq, Hkv, Ta = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
     na = B * Hkv * Ta
     out = {}
-    for name, (k, N, force) in {"fullvec_k64_n4096": (64, 4096, False), "k4_n256_lut": (4, 256, True)}.items():
+    legs = {"fullvec_k64_n4096": (64, 4096, None), "fullvec_k64_n4096_gather": (64, 4096, "gather"),
+            "k4_n256_lut": (4, 256, "lut")}
+    kernels = {None: "attn_lut_prep + attn_lut + attn_combine (events bracket the call)",
+               "lut": "attn_lut_prep + attn_lut + attn_combine (events bracket the call)",
+               "gather": "attn_split<64> from the global codebook + attn_combine (events bracket the call)"}
+    for name, (k, N, force) in legs.items():
         if force:
-            os.environ["FQ_ATTN_KERNEL"] = "lut"
+            os.environ["FQ_ATTN_KERNEL"] = force
         try:
             cb = fq.Codebook.from_artifact(k, N)
         finally:
@@ -266,7 +272,7 @@ def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: in
         out[name] = {"k": k, "N": N, "us_per_step": t * 1e6, "hbm_bytes": abytes, "GBps": abytes / t / 1e9,
                      "hbm_frac": abytes / t / 1e9 / HBM_PEAK_GBPS,
                      "fp16_equiv_GBps": 2 * na * D * 2 / t / 1e9,
-                     "kernels": "attn_lut_prep + attn_lut + attn_combine (events bracket the call)"}
+                     "kernels": kernels[force]}
         cb.close()
         del codes, norms, ao, ws
         torch.cuda.empty_cache()

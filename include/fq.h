@@ -155,16 +155,18 @@ size_t fq_attn_workspace_bytes(const fq_codebook* cb, int B, int Hq, int Hkv, in
  *   k_norms, v_norms: device fp16 [B][Hkv][T].
  *   out:      device fp32 [B][Hq][d].
  *   workspace: device, at least fq_attn_workspace_bytes(...) bytes.
- * Hq must be a multiple of Hkv with Hq/Hkv <= 16.  Codebooks: the full-vector
- * code (k = d) goes through per-head lookup tables of the N scores (Pi q).c_n
- * and an LDS histogram of the value weights (two N-float arrays per query head in
- * one workgroup's LDS: N <= 16384 on gfx950); every other codebook keeps its fp16
- * copy (2 N k bytes) plus 20,992 bytes of the kernel's own buffers in one
- * workgroup's LDS, i.e. N*k <= 65536 on gfx950 (160 KiB).  Otherwise
- * FQ_ERR_UNSUPPORTED (and fq_attn_workspace_bytes returns 0).  The
- * lookup-table path adds its float atomics in no fixed order, so repeated calls
- * may differ in the last bits; FQ_ATTN_KERNEL=lut at fq_codebook_load selects it
- * for k = 4 codebooks as well.
+ * Hq must be a multiple of Hkv with Hq/Hkv <= 16 (else FQ_ERR_UNSUPPORTED, and
+ * fq_attn_workspace_bytes returns 0).  Every codebook is served: k = 4 with 8-bit
+ * codes and Hq/Hkv <= 8 by the fast kernel; the full-vector code (k = d) with
+ * Hq/Hkv >= 4, N <= 4096 and T >= 4 N through per-head lookup tables of the N
+ * scores (Pi q).c_n and LDS histograms of the value weights; every other case by
+ * the general kernel, which gathers codewords from an LDS copy of the fp16
+ * codebook when 2 N k bytes plus its own 20,992 fit one workgroup's LDS
+ * (N*k <= 65536 on gfx950, 160 KiB) and from the codebook in global memory
+ * otherwise.  The lookup-table path adds its float atomics in no fixed order, so
+ * its repeated calls may differ in the last bits; FQ_ATTN_KERNEL=lut at
+ * fq_codebook_load selects it wherever its LDS holds the tables (k = d with
+ * N <= 16384, and k = 4), FQ_ATTN_KERNEL=gather the general kernel for k = d.
  * There is no mask: the single query attends to all T keys. */
 fq_status fq_attn_decode(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                          const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int64_t T,

@@ -1,11 +1,14 @@
-"""GPU parity of decode attention through per-head lookup tables (FibQuant summary
-§5: decompression fused into attention; for the full-vector code k = d a key's
-score is nu_j times one table entry (Pi q) . c_n) against the CPU oracle's dense
-attention over the fp64-decoded cache.
+"""GPU parity of decode attention for the full-vector code (FibQuant summary §5:
+decompression fused into attention; for k = d a key's score is nu_j times one
+entry (Pi q) . c_n) against the CPU oracle's dense attention over the
+fp64-decoded cache.
 
-The full-vector codebooks (k = d = 64, N = 4096 and N = 16384: 12- and 14-bit
-records) always take this kernel; FQ_ATTN_KERNEL=lut at load time selects it for
-the k = 4, N = 256 code too (the head-to-head comparison with the gather kernel).
+Two kernels serve k = d: per-head lookup tables with LDS histograms of the value
+weights, and the general kernel gathering codewords from the codebook in global
+memory; the library picks one by shape, and FQ_ATTN_KERNEL=lut / gather at load
+time forces it, so every case here runs through both.  FQ_ATTN_KERNEL=lut also
+takes the k = 4, N = 256 code through the tables (the head-to-head comparison
+with the gather kernel).
 Bar: per (batch, query head) ||o_gpu - o_ref||_inf <= 1e-3 ||o_ref||_inf."""
 import os
 
@@ -31,8 +34,9 @@ def dev():
 _cbs = {}
 
 
-def codebook(k, N, initial=False, force=False):
-    key = (k, N, initial, force)
+def codebook(k, N, initial=False, kernel=None):
+    """kernel: None (the library's choice), "lut" or "gather" (forced at load time)."""
+    key = (k, N, initial, kernel)
     if key not in _cbs:
         if initial:
             try:
@@ -41,13 +45,16 @@ def codebook(k, N, initial=False, force=False):
                 pytest.skip(f"artifact k={k} N={N} missing")
         else:
             cw, rot = artifact_or_skip(k, N)
-        if force:
-            os.environ["FQ_ATTN_KERNEL"] = "lut"
+        if kernel:
+            os.environ["FQ_ATTN_KERNEL"] = kernel
         try:
             _cbs[key] = (fq.Codebook(cw, rot), cw, rot)
         finally:
             os.environ.pop("FQ_ATTN_KERNEL", None)
     return _cbs[key]
+
+
+KERNELS = ["lut", "gather"]
 
 
 def _cache(cb, B, Hkv, T, seed):
@@ -91,19 +98,21 @@ def _oracle(cb, rot, cw, q, kc, kn, vc, vn, B, Hkv, T, scale=0.125, lens=None):
     (1, 32, 2, 3000),   # group of 16
     (2, 6, 2, 700),     # group of 3: sets of one head
 ])
-def test_lut_attention_full_vector_code(dev, B, Hq, Hkv, T):
-    cb, cw, rot = codebook(64, 4096)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_vector_attention(dev, B, Hq, Hkv, T, kernel):
+    cb, cw, rot = codebook(64, 4096, kernel=kernel)
     kc, kn, vc, vn = _cache(cb, B, Hkv, T, 3000 + T)
     q = np.random.default_rng(T + 1).standard_normal((B, Hq, D)).astype(np.float16)
-    print(f"[lut attention] k=64 N=4096 B={B} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
+    print(f"[full-vector attention, {kernel}] k=64 N=4096 B={B} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
     got = _run(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, T)
     ref = _oracle(cb, rot, cw, q, kc, kn, vc, vn, B, Hkv, T)
     assert max_rel_rows(got, ref) <= TOL
 
 
-def test_lut_attention_34x_point(dev):
-    # k = d, N = 16384: 14-bit records, one head per workgroup (64 KiB tables)
-    cb, cw, rot = codebook(64, 16384, initial=True)
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_vector_attention_34x_point(dev, kernel):
+    # k = d, N = 16384: 14-bit records; the tables take one head per workgroup (64 KiB)
+    cb, cw, rot = codebook(64, 16384, initial=True, kernel=kernel)
     B, Hq, Hkv, T = 2, 8, 2, 1500
     kc, kn, vc, vn = _cache(cb, B, Hkv, T, 41)
     q = np.random.default_rng(5).standard_normal((B, Hq, D)).astype(np.float16)
@@ -112,10 +121,11 @@ def test_lut_attention_34x_point(dev):
     assert max_rel_rows(got, ref) <= TOL
 
 
-def test_lut_attention_peaked_scores_and_lengths(dev):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_full_vector_attention_peaked_scores_and_lengths(dev, kernel):
     # large logits (scale 1, norms x4): a nearly one-hot softmax; per-batch lengths
     # including an empty batch and one key
-    cb, cw, rot = codebook(64, 4096)
+    cb, cw, rot = codebook(64, 4096, kernel=kernel)
     B, Hq, Hkv, T = 4, 16, 2, 2000
     kc, kn, vc, vn = _cache(cb, B, Hkv, T, 51)
     kn = (kn.astype(np.float32) * 4).astype(np.float16)
@@ -127,12 +137,14 @@ def test_lut_attention_peaked_scores_and_lengths(dev):
     assert max_rel_rows(got, ref) <= TOL
 
 
-def test_lut_attention_full_size_sampled(dev):
+@pytest.mark.parametrize("kernel", [None, "gather"])
+def test_full_vector_attention_full_size_sampled(dev, kernel):
     # the attention workload's shape (B=16, Hq=32, Hkv=4, T=32768) on the full-vector
-    # code: GPU encode of the workload's K and V draws, three slabs checked
+    # code (the library's choice there: the tables): GPU encode of the workload's K
+    # and V draws, three slabs checked
     import torch
 
-    cb, cw, rot = codebook(64, 4096)
+    cb, cw, rot = codebook(64, 4096, kernel=kernel)
     B, Hq, Hkv, T = workloads.ATTN_B, workloads.ATTN_HQ, workloads.ATTN_HKV, workloads.ATTN_T
     G = Hq // Hkv
     q, kv = workloads.attention_inputs()
@@ -145,7 +157,7 @@ def test_lut_attention_full_size_sampled(dev):
     half = cb.code_bytes(n)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     ws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, T), dtype=torch.uint8, device=dev)
-    print("[lut attention full size] B=16 Hq=32 Hkv=4 T=32768 k=64 N=4096", flush=True)
+    print(f"[full-vector attention full size, {kernel or 'auto'}] B=16 Hq=32 Hkv=4 T=32768 k=64 N=4096", flush=True)
     fq.fq_attn_decode(cb.handle, to_dev(q, dev), codes[:half], norms[:n], codes[half:], norms[n:], B, Hq, Hkv, T,
                       0.125, out, ws)
     torch.cuda.synchronize()
@@ -162,7 +174,7 @@ def test_lut_attention_full_size_sampled(dev):
 
 @pytest.mark.parametrize("B,Hq,Hkv,T", [(2, 16, 2, 1000), (1, 4, 1, 33)])
 def test_lut_attention_forced_for_k4(dev, B, Hq, Hkv, T):
-    cb, cw, rot = codebook(4, 256, force=True)
+    cb, cw, rot = codebook(4, 256, kernel="lut")
     kc, kn, vc, vn = _cache(cb, B, Hkv, T, 61 + T)
     q = np.random.default_rng(7).standard_normal((B, Hq, D)).astype(np.float16)
     got = _run(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, T)

@@ -36,7 +36,8 @@ RATES = [
     (64, 16384),  # b = 0.21875: 64 coordinates in 14 bits (+ a 16-bit norm: 34.1x)
 ]
 # every rate-axis point has an attention kernel: the general one holds the fp16 codebook
-# in LDS (N k <= 65536 on gfx950), the full-vector code goes through lookup tables
+# in LDS (N k <= 65536 on gfx950) or gathers from global memory, the full-vector code
+# goes through lookup tables or the global gathers
 ATTN_RATES = RATES
 
 
@@ -134,26 +135,37 @@ def test_attention_rate_axis(dev, k, N):
     assert max_rel_rows(out.cpu().numpy(), ref) <= TOL
 
 
-def test_attention_codebook_limit(dev):
-    # At the limit (k = 4, N = 16384: 65536 fp16 values, 128 KiB of LDS) the call is
-    # accepted (its parity is test_attention_rate_axis); one step past it (k = 8,
-    # N = 16384) it is refused before any launch.
+@pytest.mark.parametrize("k,N", [(4, 32768), (8, 16384), (32, 4096)])
+def test_attention_beyond_lds(dev, k, N):
+    # Codebooks whose fp16 copy does not fit one workgroup's LDS beside the general
+    # kernel's buffers (N k > 65536 on gfx950; k = 4, N = 16384 is the last that does)
+    # are gathered from global memory: k = 4 a half-row per code, k = 8 and 32 through
+    # the prefetching loop.  Random fp16-exact codebooks; parity against the oracle.
     import torch
 
     at, _, _ = codebook(4, 16384)
     assert fq.fq_attn_workspace_bytes(at.handle, 1, 8, 1, 4) > 0
-    rng = np.random.default_rng(17)
-    cw = (rng.standard_normal((16384, 8)) * 0.15).astype(np.float16).astype(np.float32)
+    rng = np.random.default_rng(17 + k)
+    cw = (rng.standard_normal((N, k)) * 0.15).astype(np.float16).astype(np.float32)
     cw[np.abs(cw) < 2.0 ** -14] = 0.0
     _, rot = fq.load_artifact(4, 256)
-    past = fq.Codebook(cw, rot)
-    assert fq.fq_attn_workspace_bytes(past.handle, 1, 8, 1, 4) == 0
-    q = torch.zeros((1, 8, D), dtype=torch.float16, device=dev)
-    z = torch.zeros(64, dtype=torch.uint8, device=dev)
-    out = torch.full((1, 8, D), 5.0, dtype=torch.float32, device=dev)
-    with pytest.raises(fq.FQError) as e:
-        fq.fq_attn_decode(past.handle, q, z, z, z, z, 1, 8, 1, 4, 0.125, out, z)
-    assert e.value.status == fq.FQ_ERR_UNSUPPORTED
-    torch.cuda.synchronize()
-    assert float(out.min()) == 5.0  # nothing was launched
-    past.close()
+    cb = fq.Codebook(cw, rot)
+    try:
+        bits, m = oc.code_bits(N), D // k
+        B, Hq, Hkv, T = 2, 8, 2, 333
+        n = B * Hkv * T
+        nbytes = (n * m * bits + 7) // 8
+        kc, vc = workloads.random_code_store(nbytes, 60 + k), workloads.random_code_store(nbytes, 61 + k)
+        kn, vn = workloads.random_norms(n, 62), workloads.random_norms(n, 63)
+        q = np.random.default_rng(N + k).standard_normal((B, Hq, D)).astype(np.float16)
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=dev)
+        ws = torch.empty(fq.fq_attn_workspace_bytes(cb.handle, B, Hq, Hkv, T), dtype=torch.uint8, device=dev)
+        print(f"[attention beyond LDS] k={k} N={N} B={B} Hq={Hq} Hkv={Hkv} T={T}", flush=True)
+        fq.fq_attn_decode(cb.handle, to_dev(q, dev), to_dev(kc, dev), to_dev(kn, dev), to_dev(vc, dev),
+                          to_dev(vn, dev), B, Hq, Hkv, T, 0.125, out, ws)
+        torch.cuda.synchronize()
+        unp = lambda s: oc.unpack_codes(s, n, m, bits).reshape(B, Hkv, T, m)
+        ref = oatt.attention(q, unp(kc), kn.reshape(B, Hkv, T), unp(vc), vn.reshape(B, Hkv, T), rot, cw, 0.125)
+        assert max_rel_rows(out.cpu().numpy(), ref) <= TOL
+    finally:
+        cb.close()

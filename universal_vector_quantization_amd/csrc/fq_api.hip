@@ -392,6 +392,7 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
     }
     const char* ak = getenv("FQ_ATTN_KERNEL");
     cb->force_attn_lut = ak && strcmp(ak, "lut") == 0;
+    cb->force_attn_gather = ak && strcmp(ak, "gather") == 0;
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
     cb->force_cache_codebook = dk && strcmp(dk, "cached") == 0;

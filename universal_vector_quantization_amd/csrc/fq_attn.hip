@@ -154,15 +154,17 @@ __device__ inline half8 gather8(const _Float16* __restrict__ cbL, const uint8_t*
   return r;
 }
 
-template <int K>
+// CBG: the codewords are gathered from the fp16 codebook in global memory (through
+// L1 / L2) instead of an LDS copy, for codebooks beyond the LDS.
+template <int K, bool CBG>
 __global__ __launch_bounds__(AW * 64) void attn_split(
     const _Float16* __restrict__ q, const uint8_t* __restrict__ kc, const _Float16* __restrict__ kn,
     const uint8_t* __restrict__ vc, const _Float16* __restrict__ vn, const _Float16* __restrict__ cw16,
     const float* __restrict__ pi32, int N, int bits, int Hq, int Hkv, int64_t T, const int32_t* __restrict__ lens,
     int64_t Tc, int nchunks, float qscale, float* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int cbBytes = (N * K * 2 + 15) & ~15;
-  _Float16* cbL = reinterpret_cast<_Float16*>(smem);
+  const int cbBytes = CBG ? 0 : (N * K * 2 + 15) & ~15;
+  const _Float16* cbL = CBG ? cw16 : reinterpret_cast<const _Float16*>(smem);
   float* qt = reinterpret_cast<float*>(smem + cbBytes);  // [GMAX][64] rotated, scaled queries
   float* sm = qt + GMAX * D;                             // [AW][GMAX]
   float* sl = sm + AW * GMAX;                            // [AW][GMAX]
@@ -173,8 +175,9 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
   const int G = Hq / Hkv;
   const int B = (D / K) * bits;
 
-  for (int w = tid; w < cbBytes / 16; w += AW * 64)
-    reinterpret_cast<uint4*>(cbL)[w] = reinterpret_cast<const uint4*>(cw16)[w];
+  if constexpr (!CBG)
+    for (int w = tid; w < cbBytes / 16; w += AW * 64)
+      reinterpret_cast<uint4*>(smem)[w] = reinterpret_cast<const uint4*>(cw16)[w];
   {
     const int h = tid >> 4, r0 = (tid & 15) * 4;
 #pragma unroll
@@ -213,26 +216,24 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
 #pragma unroll
   for (int c = 0; c < 4; c++) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = c0 + (int64_t)wave * TILE; t0 < c1; t0 += AW * TILE) {
+  // One 32-token tile of a wave: kr / vr the gathered key and value rows (lane: token
+  // t0 + 16 a + col, dims 32 s + 8 grp .. + 7), nk / nv the norms of the lane's score
+  // tokens t0 + 16 a + 4 grp + i.
+  auto tile = [&](int64_t t0, const half8 (&kr)[2][2], const half8 (&vr)[2][2], const float (&nk)[2][4],
+                  const float (&nv)[2][4]) {
     // ---- scores for tokens t0 + 16a + 4grp + i (a = 0, 1; i = 0..3), head = col
     float L[2][4];
 #pragma unroll
     for (int a = 0; a < 2; a++) {
-      const int64_t tr = t0 + 16 * a + col;
-      half8 k0 = {}, k1 = {};
-      if (tr < c1) {
-        k0 = gather8<K>(cbL, kc, base + tr, 8 * grp, B, bits);
-        k1 = gather8<K>(cbL, kc, base + tr, 32 + 8 * grp, B, bits);
-      }
       f32x4 S = {0.f, 0.f, 0.f, 0.f};
-      S = mfma16(k0, qhi[0], S);
-      S = mfma16(k0, qlo[0], S);
-      S = mfma16(k1, qhi[1], S);
-      S = mfma16(k1, qlo[1], S);
+      S = mfma16(kr[a][0], qhi[0], S);
+      S = mfma16(kr[a][0], qlo[0], S);
+      S = mfma16(kr[a][1], qhi[1], S);
+      S = mfma16(kr[a][1], qlo[1], S);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int64_t tk = t0 + 16 * a + 4 * grp + i;
-        L[a][i] = tk < c1 ? S[i] * (float)kn[base + tk] : NEG;
+        L[a][i] = tk < c1 ? S[i] * nk[a][i] : NEG;
       }
     }
     // ---- online softmax (base 2: the log2(e) factor is folded into Qrot)
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
         const int64_t tk = t0 + 16 * a + 4 * grp + i;
         const float p = exp2f(L[a][i] - mn);
         l += p;
-        const float pv = tk < c1 ? p * (float)vn[base + tk] : 0.f;
+        const float pv = tk < c1 ? p * nv[a][i] : 0.f;
         const _Float16 hv = (_Float16)pv;
         phi[4 * a + i] = hv;
         plo[4 * a + i] = (_Float16)(pv - (float)hv);
@@ -266,15 +267,9 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
     half8 av[4];
 #pragma unroll
     for (int a = 0; a < 2; a++) {
-      const int64_t tr = t0 + 16 * a + col;
-      half8 v0 = {}, v1 = {};
-      if (tr < c1) {
-        v0 = gather8<K>(cbL, vc, base + tr, 8 * grp, B, bits);
-        v1 = gather8<K>(cbL, vc, base + tr, 32 + 8 * grp, B, bits);
-      }
 #pragma unroll
       for (int c = 0; c < 4; c++) {
-        const f32x4 X = mfma16(c < 2 ? v0 : v1, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 X = mfma16(vr[a][c >> 1], isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
       }
@@ -286,6 +281,153 @@ __global__ __launch_bounds__(AW * 64) void attn_split(
       o[c] = mfma16(av[c], plo, o[c]);
     }
     m = mn;
+  };
+  // norms of the lane's score tokens of the tile at t0 (0 past the chunk)
+  auto norms_at = [&](int64_t t0, float (&nk)[2][4], float (&nv)[2][4]) {
+#pragma unroll
+    for (int a = 0; a < 2; a++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int64_t tk = t0 + 16 * a + 4 * grp + i;
+        nk[a][i] = tk < c1 ? (float)kn[base + tk] : 0.f;
+        nv[a][i] = tk < c1 ? (float)vn[base + tk] : 0.f;
+      }
+  };
+
+  if constexpr (CBG && K >= 8) {
+    // Codebooks beyond the LDS, gathered from global memory: a tile's rows are one L2
+    // round trip after its codes, so the codes run two tiles ahead and the rows one
+    // tile ahead of the tile being computed (tokens past the chunk take code 0, whose
+    // row is read and never weighted).  A lane's 8 dimensions lie in one block.
+    const int64_t step = (int64_t)AW * TILE;
+    auto codes_at = [&](int64_t t0, uint32_t (&ck)[2][2], uint32_t (&cv)[2][2]) {
+#pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const int64_t tr = t0 + 16 * a + col;
+#pragma unroll
+        for (int sx = 0; sx < 2; sx++) {
+          const int64_t off = (base + tr) * B + (int64_t)((32 * sx + 8 * grp) / K) * bits;
+          ck[a][sx] = tr < c1 ? load_code(kc, off, bits) : 0u;
+          cv[a][sx] = tr < c1 ? load_code(vc, off, bits) : 0u;
+        }
+      }
+    };
+    auto rows_at = [&](const uint32_t (&ck)[2][2], const uint32_t (&cv)[2][2], half8 (&kr)[2][2],
+                       half8 (&vr)[2][2]) {
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int sx = 0; sx < 2; sx++) {
+          const int dim = (32 * sx + 8 * grp) % K;
+          kr[a][sx] = *reinterpret_cast<const half8*>(cbL + (size_t)ck[a][sx] * K + dim);
+          vr[a][sx] = *reinterpret_cast<const half8*>(cbL + (size_t)cv[a][sx] * K + dim);
+        }
+    };
+    int64_t t0 = c0 + (int64_t)wave * TILE;
+    uint32_t ck[2][2], cv[2][2];
+    half8 kr[2][2], vr[2][2];
+    float nk[2][4], nv[2][4];
+    codes_at(t0, ck, cv);
+    rows_at(ck, cv, kr, vr);
+    norms_at(t0, nk, nv);
+    codes_at(t0 + step, ck, cv);
+    for (; t0 < c1; t0 += step) {
+      half8 kr2[2][2], vr2[2][2];
+      float nk2[2][4], nv2[2][4];
+      rows_at(ck, cv, kr2, vr2);
+      norms_at(t0 + step, nk2, nv2);
+      codes_at(t0 + 2 * step, ck, cv);
+      tile(t0, kr, vr, nk, nv);
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int sx = 0; sx < 2; sx++) {
+          kr[a][sx] = kr2[a][sx];
+          vr[a][sx] = vr2[a][sx];
+        }
+#pragma unroll
+      for (int a = 0; a < 2; a++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          nk[a][i] = nk2[a][i];
+          nv[a][i] = nv2[a][i];
+        }
+    }
+  } else {
+    for (int64_t t0 = c0 + (int64_t)wave * TILE; t0 < c1; t0 += AW * TILE) {
+      // ---- scores for tokens t0 + 16a + 4grp + i (a = 0, 1; i = 0..3), head = col
+      float L[2][4];
+  #pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const int64_t tr = t0 + 16 * a + col;
+        half8 k0 = {}, k1 = {};
+        if (tr < c1) {
+          k0 = gather8<K>(cbL, kc, base + tr, 8 * grp, B, bits);
+          k1 = gather8<K>(cbL, kc, base + tr, 32 + 8 * grp, B, bits);
+        }
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        S = mfma16(k0, qhi[0], S);
+        S = mfma16(k0, qlo[0], S);
+        S = mfma16(k1, qhi[1], S);
+        S = mfma16(k1, qlo[1], S);
+  #pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int64_t tk = t0 + 16 * a + 4 * grp + i;
+          L[a][i] = tk < c1 ? S[i] * (float)kn[base + tk] : NEG;
+        }
+      }
+      // ---- online softmax (base 2: the log2(e) factor is folded into Qrot)
+      float mx = NEG;
+  #pragma unroll
+      for (int a = 0; a < 2; a++)
+  #pragma unroll
+        for (int i = 0; i < 4; i++) mx = fmaxf(mx, L[a][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);  // finite: the tile holds at least one token
+      const float alpha = exp2f(m - mn);
+      l *= alpha;
+  #pragma unroll
+      for (int c = 0; c < 4; c++) o[c] *= alpha;
+      half8 phi, plo;
+  #pragma unroll
+      for (int a = 0; a < 2; a++) {
+  #pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int64_t tk = t0 + 16 * a + 4 * grp + i;
+          const float p = exp2f(L[a][i] - mn);
+          l += p;
+          const float pv = tk < c1 ? p * (float)vn[base + tk] : 0.f;
+          const _Float16 hv = (_Float16)pv;
+          phi[4 * a + i] = hv;
+          plo[4 * a + i] = (_Float16)(pv - (float)hv);
+        }
+      }
+      // ---- gathered values, transposed to dim-major through the selector MFMA
+      half8 av[4];
+  #pragma unroll
+      for (int a = 0; a < 2; a++) {
+        const int64_t tr = t0 + 16 * a + col;
+        half8 v0 = {}, v1 = {};
+        if (tr < c1) {
+          v0 = gather8<K>(cbL, vc, base + tr, 8 * grp, B, bits);
+          v1 = gather8<K>(cbL, vc, base + tr, 32 + 8 * grp, B, bits);
+        }
+  #pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const f32x4 X = mfma16(c < 2 ? v0 : v1, isel[c & 1], f32x4{0.f, 0.f, 0.f, 0.f});
+  #pragma unroll
+          for (int i = 0; i < 4; i++) av[c][4 * a + i] = (_Float16)X[i];
+        }
+      }
+      // ---- accumulate in the rotated domain
+  #pragma unroll
+      for (int c = 0; c < 4; c++) {
+        o[c] = mfma16(av[c], phi, o[c]);
+        o[c] = mfma16(av[c], plo, o[c]);
+      }
+      m = mn;
+    }
   }
 
   // ---- merge the 4 waves, write this chunk's partial record per query head
@@ -945,8 +1087,10 @@ __global__ __launch_bounds__(AW * 64, 4) void attn_k4b8(const _Float16* __restri
   }
 }
 
-size_t attn_smem_bytes(int N, int K) {
-  return (size_t)((N * K * 2 + 15) & ~15) + sizeof(float) * (GMAX * D + 2 * AW * GMAX + AW * GMAX * D);
+// LDS of attn_split: the codebook copy (none with the global codebook), then its own buffers
+size_t attn_smem_bytes(int N, int K, bool cbg) {
+  return (cbg ? (size_t)0 : (size_t)((N * K * 2 + 15) & ~15)) +
+         sizeof(float) * (GMAX * D + 2 * AW * GMAX + AW * GMAX * D);
 }
 
 }  // namespace
@@ -958,20 +1102,34 @@ bool attn_fast_path(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
   return cb->k == 4 && cb->bits == 8 && cb->rot16 && Hq / Hkv <= GF && T % 8 == 0 && T < ((int64_t)1 << 40);
 }
 
-// The general kernel keeps the fp16 codebook in LDS beside its own buffers; the
-// lookup-table kernel keeps one table (and weight histogram) per query head.
+// Every codebook has a path: the general kernel gathers from an LDS copy of the fp16
+// codebook when it fits beside its own buffers, else from the codebook in global
+// memory; the lookup-table kernel serves the full-vector code where it is faster.
 bool attn_supported(const fq_codebook* cb) {
-  return attn_smem_bytes(cb->N, cb->k) <= cb->max_lds || attn_lut_supported(cb);
+  (void)cb;
+  return true;
 }
 
 namespace {
-bool attn_use_lut(const fq_codebook* cb) {
-  return (cb->k == D || cb->force_attn_lut) && attn_lut_supported(cb);
+// The lookup tables pay for their construction (N entries per query head) and for the
+// final product of the weight histograms with the codebook when many keys share them:
+// the full-vector code with at least 4 query heads per KV head, 4 heads' tables and
+// histograms in one workgroup's LDS (N <= 4096 here) and T >= 4 N.  Otherwise the
+// general kernel's gathers from global memory are faster (B = 12, Hq = Hkv = 12,
+// T = 1024: 38 against 62 us at N = 4096; B = 16, Hq = 32, Hkv = 4, T = 32768 at
+// N = 16384: 207 against 293 us; at N = 4096 the tables win, 155 against 198 us).
+bool attn_use_lut(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
+  if (cb->force_attn_gather) return false;
+  if (cb->force_attn_lut) return attn_lut_supported(cb);
+  const int G = Hkv > 0 ? Hq / Hkv : 0;
+  return cb->k == D && G >= 4 && attn_lut_heads(cb, G) >= 4 && T >= 4 * (int64_t)cb->N;
 }
+// the split kernel gathers from the global codebook when the LDS copy does not fit
+bool attn_split_global(const fq_codebook* cb) { return attn_smem_bytes(cb->N, cb->k, false) > cb->max_lds; }
 }  // namespace
 
 AttnPlan attn_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int64_t T) {
-  if (attn_use_lut(cb)) {
+  if (attn_use_lut(cb, Hq, Hkv, T)) {
     // one workgroup per CU: about 256 workgroups over (batch, KV head, head set, chunk)
     const int G = Hq / Hkv, gw = attn_lut_heads(cb, G);
     const int64_t sets = (int64_t)B * Hkv * (G / (gw > 0 ? gw : 1));
@@ -1042,22 +1200,28 @@ int attn_record_stride(const AttnPlan& p) {
 // Launcher of the split kernel for one block size, instantiated per K in its
 // own translation unit (compiled with -DFQ_ONLY_K=K).
 template <int K>
-hipError_t launch_attn_split_k(dim3 grid, size_t sh, hipStream_t s, const _Float16* q, const uint8_t* kc,
+hipError_t launch_attn_split_k(dim3 grid, bool cbg, hipStream_t s, const _Float16* q, const uint8_t* kc,
                                const _Float16* kn, const uint8_t* vc, const _Float16* vn, const fq_codebook* cb,
                                int Hq, int Hkv, int64_t T, const int32_t* lens, int64_t Tc, int nchunks,
                                float qscale, float* ws) {
+  const size_t sh = attn_smem_bytes(cb->N, K, cbg);
+  if (cbg) {
+    hipLaunchKernelGGL((attn_split<K, true>), grid, dim3(AW * 64), sh, s, q, kc, kn, vc, vn, cb->cw16, cb->pi32,
+                       cb->N, cb->bits, Hq, Hkv, T, lens, Tc, nchunks, qscale, ws);
+    return hipGetLastError();
+  }
   if (sh > 65536) {  // codebooks beyond 32 KiB of fp16 values: raise the dynamic LDS limit
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_split<K>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_split<K, false>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)sh);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((attn_split<K>), grid, dim3(AW * 64), sh, s, q, kc, kn, vc, vn, cb->cw16, cb->pi32, cb->N,
-                     cb->bits, Hq, Hkv, T, lens, Tc, nchunks, qscale, ws);
+  hipLaunchKernelGGL((attn_split<K, false>), grid, dim3(AW * 64), sh, s, q, kc, kn, vc, vn, cb->cw16, cb->pi32,
+                     cb->N, cb->bits, Hq, Hkv, T, lens, Tc, nchunks, qscale, ws);
   return hipGetLastError();
 }
 
 #define FQ_ATT_DECL(KK)                                                                                        \
-  template hipError_t launch_attn_split_k<KK>(dim3, size_t, hipStream_t, const _Float16*, const uint8_t*,      \
+  template hipError_t launch_attn_split_k<KK>(dim3, bool, hipStream_t, const _Float16*, const uint8_t*,        \
                                               const _Float16*, const uint8_t*, const _Float16*, const fq_codebook*, \
                                               int, int, int64_t, const int32_t*, int64_t, int, float, float*)
 #ifdef FQ_ONLY_K
@@ -1080,7 +1244,7 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
                            workspace, s);
   const float qscale = scale * 1.4426950408889634f;  // log2(e)
   const dim3 grid((unsigned)plan.nchunks, (unsigned)Hkv, (unsigned)B);
-  const size_t sh = attn_smem_bytes(cb->N, cb->k);
+  const bool cbg = attn_split_global(cb);
   float* ws = reinterpret_cast<float*>(workspace);
   const _Float16* qh = reinterpret_cast<const _Float16*>(q);
   const _Float16* kn = reinterpret_cast<const _Float16*>(k_norms);
@@ -1104,7 +1268,7 @@ hipError_t launch_attn(const fq_codebook* cb, const void* q, const uint8_t* k_co
     return hipGetLastError();
   }
 #define FQ_ATT(KK)                                                                                                \
-  e = launch_attn_split_k<KK>(grid, sh, s, qh, k_codes, kn, v_codes, vn, cb, Hq, Hkv, T, lens,                  \
+  e = launch_attn_split_k<KK>(grid, cbg, s, qh, k_codes, kn, v_codes, vn, cb, Hq, Hkv, T, lens,                  \
                               plan.chunk_tokens, plan.nchunks, qscale, ws)
   switch (cb->k) {
     case 1: FQ_ATT(1); break;

@@ -55,6 +55,7 @@ struct fq_codebook {
                       // the call (valu: every call), else the automatic choice
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
   bool force_attn_lut;  // FQ_ATTN_KERNEL=lut at load time: the lookup-table attention for k = 4 codebooks too
+  bool force_attn_gather;  // FQ_ATTN_KERNEL=gather: the split kernel (global codebook beyond LDS) for k = d too
   bool force_cache_codebook;  // FQ_DECODE_KERNEL=cached: the matrix-core decoders read codebooks of more
                               // than 32 KiB from L1 / L2 (the path of devices with less LDS)
 };
