@@ -247,6 +247,7 @@ def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: in
     na = B * Hkv * Ta
     out = {}
     legs = {"fullvec_k64_n4096": (64, 4096, None), "fullvec_k64_n4096_gather": (64, 4096, "gather"),
+            "fullvec_k64_n16384": (64, 16384, None), "fullvec_k64_n16384_lut": (64, 16384, "lut"),
             "k4_n256_lut": (4, 256, "lut")}
     kernels = {None: "attn_lut_prep + attn_lut + attn_combine (events bracket the call)",
                "lut": "attn_lut_prep + attn_lut + attn_combine (events bracket the call)",
@@ -255,7 +256,10 @@ def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: in
         if force:
             os.environ["FQ_ATTN_KERNEL"] = force
         try:
-            cb = fq.Codebook.from_artifact(k, N)
+            cb = fq.Codebook.from_artifact(k, N, initial=N > 4096)  # N = 16384: the construction's initial code
+        except FileNotFoundError:
+            out[name] = {"skipped": "codebook artifact missing"}
+            continue
         finally:
             os.environ.pop("FQ_ATTN_KERNEL", None)
         kv = torch.from_numpy(kv_np.reshape(-1, D)).to(dev)
@@ -272,7 +276,7 @@ def lut_attention_timings(fq, workloads, dev, stream, flush, qa, kv_np, reps: in
         out[name] = {"k": k, "N": N, "us_per_step": t * 1e6, "hbm_bytes": abytes, "GBps": abytes / t / 1e9,
                      "hbm_frac": abytes / t / 1e9 / HBM_PEAK_GBPS,
                      "fp16_equiv_GBps": 2 * na * D * 2 / t / 1e9,
-                     "kernels": kernels[force]}
+                     "kernels": kernels[force if force or (k == D and N <= 4096) else "gather"]}
         cb.close()
         del codes, norms, ao, ws
         torch.cuda.empty_cache()
@@ -366,6 +370,19 @@ def rate_axis_timings(fq, workloads, dev, stream, flush, reps: int = 3):
                                                   norms[n // 2:], L, H, H, T, 0.125, ao, ws, stream))
             abytes = cb.code_bytes(n) + 2 * n + L * H * D * 6
             rec.update({"attention_us": t_a * 1e6, "attention_GBps": abytes / t_a / 1e9})
+            if k == D:  # the full-vector code: the lookup tables at this shape too (the library takes the gathers)
+                os.environ["FQ_ATTN_KERNEL"] = "lut"
+                try:
+                    cbl = fq.Codebook.from_artifact(k, N, initial=True)
+                finally:
+                    os.environ.pop("FQ_ATTN_KERNEL", None)
+                wsl = torch.empty(max(fq.fq_attn_workspace_bytes(cbl.handle, L, H, H, T), 16), dtype=torch.uint8,
+                                  device=dev)
+                t_l = timed(lambda: fq.fq_attn_decode(cbl.handle, q, codes[:half], norms[: n // 2], codes[half:],
+                                                      norms[n // 2:], L, H, H, T, 0.125, ao, wsl, stream))
+                rec["attention_us_lookup_tables"] = t_l * 1e6
+                cbl.close()
+                del wsl
         out[f"k{k}_N{N}"] = rec
         cb.close()
         del codes, norms, xr

@@ -1115,9 +1115,10 @@ namespace {
 // final product of the weight histograms with the codebook when many keys share them:
 // the full-vector code with at least 4 query heads per KV head, 4 heads' tables and
 // histograms in one workgroup's LDS (N <= 4096 here) and T >= 4 N.  Otherwise the
-// general kernel's gathers from global memory are faster (B = 12, Hq = Hkv = 12,
-// T = 1024: 38 against 62 us at N = 4096; B = 16, Hq = 32, Hkv = 4, T = 32768 at
-// N = 16384: 207 against 293 us; at N = 4096 the tables win, 155 against 198 us).
+// general kernel's gathers from global memory are faster (encoded caches, evicted:
+// B = 12, Hq = Hkv = 12, T = 1024, N = 16384: 45 against 161 us; B = 16, Hq = 32,
+// Hkv = 4, T = 32768, N = 16384: 233 against 287 us; at N = 4096 there the tables
+// win, 157 against 215 us).
 bool attn_use_lut(const fq_codebook* cb, int Hq, int Hkv, int64_t T) {
   if (cb->force_attn_gather) return false;
   if (cb->force_attn_lut) return attn_lut_supported(cb);
