@@ -7,9 +7,10 @@
 // softmax (running max m, running sum l, accumulator in the rotated domain).
 // Per 32-token tile and wave, with the MFMA f32_16x16x32_f16 shape:
 //   QK  : S^T[16 tok x 16 heads] = Khat[16 tok x 64] . Qrot^T[64 x 16 heads].
-//         Khat rows are gathered straight from the fp16 codebook in LDS (a lane
-//         holds one token and 8 consecutive dims = whole codewords), Qrot is
-//         split hi + lo fp16 so the product keeps fp32-class accuracy.
+//         Khat rows are gathered straight from the fp16 codebook in LDS, or in
+//         global memory for codebooks beyond the LDS (a lane holds one token and
+//         8 consecutive dims of its codewords), Qrot is split hi + lo fp16 so the
+//         product keeps fp32-class accuracy.
 //   softmax: a lane owns one head and 8 tokens; the tile max needs 2 lane swaps.
 //   V transpose: Vhat . I (I a 0/1 selector) turns the token-major gather into
 //         the dim-major operand PV needs, exactly (products with 1 and 0).

@@ -6,7 +6,9 @@
 // log2 e holds the score per unit of norm of codeword n in block blk, so the
 // score of key j is nu_j sum_blk L[blk][code_j,blk]: d/k table reads per key and
 // head.  For the full-vector code (k = d) that is one read, and the table is N
-// floats per head.
+// floats per head.  The tables pay off where many keys share them (grouped query
+// heads, long contexts, N <= 4096); elsewhere the library sends k = d to the
+// general kernel, which gathers the codewords from global memory.
 // Values: sum_j p_j nu_j concat(c_j) taken block by block equals
 // sum_n W[blk][n] c_n, where W[blk][n] sums p_j nu_j over the keys whose block
 // blk holds code n.  Keys add their weights into W (LDS float atomics); one
