@@ -135,12 +135,13 @@ def test_attention_rate_axis(dev, k, N):
     assert max_rel_rows(out.cpu().numpy(), ref) <= TOL
 
 
-@pytest.mark.parametrize("k,N", [(4, 32768), (8, 16384), (32, 4096)])
+@pytest.mark.parametrize("k,N", [(2, 65536), (4, 32768), (8, 16384), (16, 8192), (32, 4096)])
 def test_attention_beyond_lds(dev, k, N):
     # Codebooks whose fp16 copy does not fit one workgroup's LDS beside the general
     # kernel's buffers (N k > 65536 on gfx950; k = 4, N = 16384 is the last that does)
-    # are gathered from global memory: k = 4 a half-row per code, k = 8 and 32 through
-    # the prefetching loop.  Random fp16-exact codebooks; parity against the oracle.
+    # are gathered from global memory: k = 2 and 4 several codes per 8 dimensions,
+    # k = 8, 16 and 32 through the prefetching loop.  Random fp16-exact codebooks;
+    # parity against the oracle.
     import torch
 
     at, _, _ = codebook(4, 16384)
