@@ -50,7 +50,7 @@ def _cache(B, Hkv, T, seed):
     (2, 8, 2, 5, 300, False),
     (2, 8, 2, 5, 300, True),
     (1, 4, 1, 37, 37, True),      # Sq = T: query 0 sees only key 0
-    (2, 16, 2, 20, 1000, True),   # 160 rows per slab: workgroups of 64, 64 and 32 rows
+    (2, 16, 2, 20, 1000, True),   # 160 rows per slab: workgroups of 128 and 32 rows
     (1, 32, 2, 3, 777, False),    # 16 heads per KV head, 48 rows (one partial workgroup)
     (1, 8, 1, 70, 50, True),      # more queries than keys: the first 20 see nothing
     (3, 12, 12, 1, 129, True),    # one query per head (the decode step as a prefill)
