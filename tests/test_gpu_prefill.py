@@ -68,6 +68,30 @@ def test_prefill_random_cache(dev, cb4, B, Hq, Hkv, Sq, T, causal):
     assert max_rel_rows(got.reshape(-1, D), ref.reshape(-1, D)) <= TOL
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,T,causal,seed", [
+    pytest.param(3, 48, 3, 60, 1000, False, 1, marks=pytest.mark.xfail(
+        reason="worst row 1.06e-3 of the 1e-3 bar: the wide k = 4 kernel's open precision issue at scale 0.5",
+        strict=False)),
+    (1, 48, 3, 54, 2047, False, 2),
+    (3, 8, 1, 39, 33, True, 3),
+    (2, 24, 3, 64, 777, True, 4),
+])
+def test_prefill_large_scale(dev, cb4, B, Hq, Hkv, Sq, T, causal, seed):
+    # scale 0.5 (four times 1/sqrt(d)): peaked weights over thousands of rows.  A random
+    # sweep at this scale found about 3 % of cases with a row past the bar (worst 5e-3) on
+    # the wide k = 4 kernel and none on the general one; the first case here is one of them
+    cb, cw, rot = cb4
+    kc, kn, vc, vn = _cache(B, Hkv, T, 700 + 13 * seed)
+    q = np.random.default_rng(seed).standard_normal((B, Hq, Sq, D)).astype(np.float16)
+    print(f"[prefill parity, scale 0.5] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} T={T} causal={causal}", flush=True)
+    got = _gpu_prefill(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, Sq, T, causal, scale=0.5)
+    n = B * Hkv * T
+    unp = lambda s: oc.unpack_codes(s, n, 16, 8).reshape(B, Hkv, T, 16)
+    ref = oatt.prefill_attention(q, unp(kc), kn.reshape(B, Hkv, T), unp(vc), vn.reshape(B, Hkv, T), rot, cw, 0.5,
+                                 causal)
+    assert max_rel_rows(got.reshape(-1, D), ref.reshape(-1, D)) <= TOL
+
+
 def test_prefill_peaked_scores(dev, cb4):
     # large logits: nearly one-hot rows stress the running max across units and ranges
     cb, cw, rot = cb4
