@@ -596,10 +596,11 @@ def main():
             "workload": "B=16, Hq=32, Hkv=4, T=32768, 64 causal queries per head (the last 64 positions), "
                         "k=4, N=256 codes + fp16 norms, caches evicted before every launch",
             "us_per_step": t_p * 1e6, "query_key_pairs": pairs,
-            "roofline": {"kernel": "attn_prefill_w (+ attn_combine)", "bound": "mfma",
+            "roofline": {"kernel": "attn_prefill<4, 1> (+ attn_combine; the general kernel, the default)",
+                         "bound": "mfma",
                          "achieved": useful / t_p / 1e12, "peak": FP16_MFMA_PEAK_T, "unit": "TFLOP/s",
                          "frac": useful / t_p / 1e12 / FP16_MFMA_PEAK_T,
-                         "traffic": measured_traffic("attn_prefill_w", "fq_prefill.hip"),
+                         "traffic": None,
                          "issued_TFLOPs": 1.5 * useful / t_p / 1e12},
         }
         del qp, po, pws

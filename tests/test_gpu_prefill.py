@@ -3,6 +3,8 @@ cache, FibQuant summary §5) against the oracle's prefill attention.
 
 Bar: per (batch, query head, query) row ||o_gpu - o_ref||_inf <= 1e-3
 ||o_ref||_inf; rows with no visible key are exactly 0."""
+import os
+
 import numpy as np
 import pytest
 
@@ -26,6 +28,18 @@ def dev():
 def cb4():
     cw, rot = artifact_or_skip(4, 256)
     return fq.Codebook(cw, rot), cw, rot
+
+
+@pytest.fixture(scope="module")
+def cb4w():
+    # the wide k = 4 / 8-bit kernel, selected at load time (not the default: a random sweep
+    # found rows past the bar on some inputs, none of them among the cases it runs here)
+    cw, rot = artifact_or_skip(4, 256)
+    os.environ["FQ_PREFILL_KERNEL"] = "wide"
+    try:
+        return fq.Codebook(cw, rot), cw, rot
+    finally:
+        os.environ.pop("FQ_PREFILL_KERNEL", None)
 
 
 def _gpu_prefill(cb, dev, q, kc, kn, vc, vn, B, Hq, Hkv, Sq, T, causal, scale=0.125):
@@ -55,8 +69,9 @@ def _cache(B, Hkv, T, seed):
     (1, 8, 1, 70, 50, True),      # more queries than keys: the first 20 see nothing
     (3, 12, 12, 1, 129, True),    # one query per head (the decode step as a prefill)
 ])
-def test_prefill_random_cache(dev, cb4, B, Hq, Hkv, Sq, T, causal):
-    cb, cw, rot = cb4
+@pytest.mark.parametrize("wide", [False, True])
+def test_prefill_random_cache(dev, cb4, cb4w, B, Hq, Hkv, Sq, T, causal, wide):
+    cb, cw, rot = cb4w if wide else cb4
     kc, kn, vc, vn = _cache(B, Hkv, T, 600 + T + Sq)
     q = np.random.default_rng(T * 7 + Sq).standard_normal((B, Hq, Sq, D)).astype(np.float16)
     print(f"[prefill parity] B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} T={T} causal={causal}", flush=True)
@@ -69,9 +84,7 @@ def test_prefill_random_cache(dev, cb4, B, Hq, Hkv, Sq, T, causal):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Sq,T,causal,seed", [
-    pytest.param(3, 48, 3, 60, 1000, False, 1, marks=pytest.mark.xfail(
-        reason="worst row 1.06e-3 of the 1e-3 bar: the wide k = 4 kernel's open precision issue at scale 0.5",
-        strict=False)),
+    (3, 48, 3, 60, 1000, False, 1),
     (1, 48, 3, 54, 2047, False, 2),
     (3, 8, 1, 39, 33, True, 3),
     (2, 24, 3, 64, 777, True, 4),
@@ -79,7 +92,8 @@ def test_prefill_random_cache(dev, cb4, B, Hq, Hkv, Sq, T, causal):
 def test_prefill_large_scale(dev, cb4, B, Hq, Hkv, Sq, T, causal, seed):
     # scale 0.5 (four times 1/sqrt(d)): peaked weights over thousands of rows.  A random
     # sweep at this scale found about 3 % of cases with a row past the bar (worst 5e-3) on
-    # the wide k = 4 kernel and none on the general one; the first case here is one of them
+    # the wide k = 4 kernel and none on the general one, the default; the first case here
+    # is one of them (1.06e-3 wide, 3.6e-4 general)
     cb, cw, rot = cb4
     kc, kn, vc, vn = _cache(B, Hkv, T, 700 + 13 * seed)
     q = np.random.default_rng(seed).standard_normal((B, Hq, Sq, D)).astype(np.float16)

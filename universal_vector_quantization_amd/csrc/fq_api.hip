@@ -396,6 +396,8 @@ FQ_EXPORT fq_status fq_codebook_load(int d, int k, int N, const float* codewords
     const char* dk = getenv("FQ_DECODE_KERNEL");
     cb->force_valu_decode = dk && strcmp(dk, "valu") == 0;
     cb->force_cache_codebook = dk && strcmp(dk, "cached") == 0;
+    const char* pk = getenv("FQ_PREFILL_KERNEL");
+    cb->prefill_wide = pk && strcmp(pk, "wide") == 0;
   }
   int lds_max = 0;
   if (hipGetDevice(&cb->device) != hipSuccess ||

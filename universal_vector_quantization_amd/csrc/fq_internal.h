@@ -56,6 +56,8 @@ struct fq_codebook {
   bool force_valu_decode;  // FQ_DECODE_KERNEL=valu at load time: the one-lane-per-vector decoder
   bool force_attn_lut;  // FQ_ATTN_KERNEL=lut at load time: the lookup-table attention for k = 4 codebooks too
   bool force_attn_gather;  // FQ_ATTN_KERNEL=gather: the split kernel (global codebook beyond LDS) for k = d too
+  bool prefill_wide;  // FQ_PREFILL_KERNEL=wide: the wide prefill kernel for k = 4 / 8-bit codes (faster; rows past the
+                     // 1e-3 bar on some inputs, so not the default)
   bool force_cache_codebook;  // FQ_DECODE_KERNEL=cached: the matrix-core decoders read codebooks of more
                               // than 32 KiB from L1 / L2 (the path of devices with less LDS)
 };

@@ -636,7 +636,7 @@ __global__ __launch_bounds__(PW * 64, 3) void attn_prefill_w(
 PrefillPlan prefill_plan(const fq_codebook* cb, int B, int Hq, int Hkv, int Sq, int64_t T) {
   // the wide k = 4 / 8-bit kernel: 128 rows per workgroup, three workgroups per CU, so the
   // key ranges are cut for one wave of 768 workgroups; the general kernel: 64 rows, 1024
-  const bool wide = cb->k == 4 && cb->bits == 8;
+  const bool wide = cb->k == 4 && cb->bits == 8 && cb->prefill_wide;
   const int prows = wide ? WROWS : PROWS;
   const int64_t target = wide ? 768 : 1024;
   const int rows = (Hq / Hkv) * Sq;
@@ -656,7 +656,7 @@ bool prefill_supported(const fq_codebook* cb) { return cb->k >= 1 && cb->k <= D 
 
 namespace {
 CbMode prefill_cb_mode(const fq_codebook* cb) {
-  if (cb->k == 4 && cb->bits == 8) return CB_K4B8;
+  if (cb->k == 4 && cb->bits == 8 && cb->prefill_wide) return CB_K4B8;
   return (size_t)cb->N * cb->k * 2 <= CB_LDS_MAX ? CB_LDS : CB_GLOBAL;
 }
 
