@@ -217,8 +217,10 @@ size_t fq_attn_prefill_workspace_bytes(const fq_codebook* cb, int B, int Hq, int
  * are the last Sq positions of the cache; a query that sees no key gets 0).
  *   q:   device fp16 [B][Hq][Sq][d].  out: device fp32 [B][Hq][Sq][d].
  *   cache, grouping, workspace rules as for fq_attn_decode.
- * Every codebook the library loads: unlike fq_attn_decode there is no limit on
- * N * k (codebooks of more than 32 KiB in fp16 are read from global memory).
+ * Every codebook the library loads (codebooks of more than 32 KiB in fp16 are
+ * read from global memory).  FQ_PREFILL_KERNEL=wide at fq_codebook_load selects
+ * a faster kernel for k = 4 with 8-bit codes whose worst rows can exceed 1e-3
+ * relative error on some inputs; the default kernel holds that bound.
  * B * Hq * Sq < 2^31 and B * Hkv <= 65535. */
 fq_status fq_attn_prefill(const fq_codebook* cb, const void* q, const uint8_t* k_codes, const void* k_norms,
                           const uint8_t* v_codes, const void* v_norms, int B, int Hq, int Hkv, int Sq, int64_t T,
